@@ -1,0 +1,218 @@
+"""Python binding of libmala (MALA fused causal attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels of libmala.so, reached through its C ABI (include/mala.h) with ctypes.
+PyTorch supplies device memory and the current HIP stream.  There is no CPU
+fallback: if the library is missing or the tensors are not on a HIP device,
+the calls raise.
+
+Names follow the C ABI: mala_fwd, mala_bwd, mala_decode, plus the autograd
+wrapper `mala_attention` (saves only q, k, v, o and lse for the backward).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmala.so")
+
+MALA_OK, MALA_ERR_INVALID_ARG, MALA_ERR_UNSUPPORTED, MALA_ERR_WORKSPACE, MALA_ERR_HIP = range(5)
+
+
+class MalaError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({code})")
+        self.code = code
+
+
+class MalaT4(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sl", ctypes.c_int64), ("sh", ctypes.c_int64)]
+
+
+class MalaTileStats(ctypes.Structure):
+    _fields_ = [("kept_tiles", ctypes.c_void_p), ("kept_slots", ctypes.c_void_p),
+                ("omitted_mass", ctypes.c_void_p), ("decision_bits", ctypes.c_void_p)]
+
+
+EXPORTS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
+           "mala_decode_workspace_size", "mala_status_string", "mala_version")
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libmala.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libmala.so not found at {p}: build it first "
+                           "(python -m adaptive_tile_skipping_amd._build or __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mala_fwd.argtypes = [MalaT4, MalaT4, MalaT4, I, I, I, I, I, F, I, I, MalaT4, P,
+                             ctypes.POINTER(MalaTileStats), P]
+    lib.mala_fwd.restype = I
+    lib.mala_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.mala_bwd_workspace_size.restype = S
+    lib.mala_bwd.argtypes = [MalaT4, MalaT4, MalaT4, MalaT4, MalaT4, P, I, I, I, I, I, F, I, I,
+                             MalaT4, MalaT4, MalaT4, P, S, ctypes.POINTER(MalaTileStats), P]
+    lib.mala_bwd.restype = I
+    lib.mala_decode_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.mala_decode_workspace_size.restype = S
+    lib.mala_decode.argtypes = [P, MalaT4, MalaT4, I, I, I, I, I, F, I, P, P, P, P, S, P]
+    lib.mala_decode.restype = I
+    lib.mala_status_string.argtypes = [I]
+    lib.mala_status_string.restype = ctypes.c_char_p
+    lib.mala_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int):
+    if code != MALA_OK:
+        raise MalaError(fn, code, load_library().mala_status_string(code).decode())
+
+
+def _t4(t: torch.Tensor) -> MalaT4:
+    if t.dim() != 4:
+        raise ValueError("expected a [B, L, H, d] tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError("libmala takes bfloat16 tensors")
+    if t.stride(3) != 1:
+        raise ValueError("the d dimension must be contiguous")
+    return MalaT4(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise RuntimeError("libmala runs on the GPU only: tensors must live on a HIP device")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stats_struct(stats: dict | None):
+    if not stats:
+        return None
+    s = MalaTileStats(*(_ptr(stats.get(n)) for n in ("kept_tiles", "kept_slots", "omitted_mass", "decision_bits")))
+    return ctypes.pointer(s)
+
+
+def make_stats(B: int, Hq: int, L: int, Bq: int, Bk: int, device, omitted: bool = False) -> dict:
+    """Allocate the optional statistics outputs of mala_fwd / mala_bwd."""
+    nQB, nKT = -(-L // Bq), -(-L // Bk)
+    st = {"kept_tiles": torch.empty((B, Hq, nQB), dtype=torch.int32, device=device),
+          "kept_slots": torch.empty((B, Hq, L), dtype=torch.int32, device=device),
+          "decision_bits": torch.empty((B, Hq, nQB, -(-nKT // 32)), dtype=torch.int32, device=device)}
+    if omitted:
+        st["omitted_mass"] = torch.empty((B, Hq, L), dtype=torch.float32, device=device)
+    return st
+
+
+def mala_fwd(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64, o=None, lse=None, stats: dict | None = None):
+    """Forward.  q [B,L,Hq,d], k/v [B,L,Hkv,d] bf16 on the GPU.
+    Returns (o [B,L,Hq,d] bf16, lse [B,Hq,L] fp32)."""
+    _dev_check(q, k, v)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, L, Hkv, d) or v.shape != k.shape:
+        raise ValueError("q, k, v shapes disagree")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise ValueError("lse must be a contiguous float32 [B, Hq, L] tensor")
+    lib = load_library()
+    rc = lib.mala_fwd(_t4(q), _t4(k), _t4(v), B, L, Hq, Hkv, d, float(tau), Bq, Bk, _t4(o),
+                      _ptr(lse), _stats_struct(stats), _stream(q))
+    _check("mala_fwd", rc)
+    return o, lse
+
+
+def bwd_workspace(B, L, Hq, Hkv, d, Bq=128, Bk=64, device="cuda"):
+    n = load_library().mala_bwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk)
+    if n == 0:
+        raise MalaError("mala_bwd_workspace_size", MALA_ERR_UNSUPPORTED, "unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mala_bwd(q, k, v, o, dout, lse, tau: float = 1.0, Bq: int = 128, Bk: int = 64,
+             dq=None, dk=None, dv=None, ws=None, stats: dict | None = None):
+    """Backward.  Returns (dq, dk, dv) bf16."""
+    _dev_check(q, k, v, o, dout, lse)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if ws is None:
+        ws = bwd_workspace(B, L, Hq, Hkv, d, Bq, Bk, q.device)
+    if not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise ValueError("lse must be a contiguous float32 [B, Hq, L] tensor")
+    lib = load_library()
+    rc = lib.mala_bwd(_t4(q), _t4(k), _t4(v), _t4(o), _t4(dout), _ptr(lse), B, L, Hq, Hkv, d, float(tau), Bq, Bk,
+                      _t4(dq), _t4(dk), _t4(dv), _ptr(ws), ws.numel(), _stats_struct(stats), _stream(q))
+    _check("mala_bwd", rc)
+    return dq, dk, dv
+
+
+def decode_workspace(B, N, Hq, Hkv, d, Bk_dec=64, device="cuda"):
+    n = load_library().mala_decode_workspace_size(B, N, Hq, Hkv, d, Bk_dec)
+    if n == 0:
+        raise MalaError("mala_decode_workspace_size", MALA_ERR_UNSUPPORTED, "unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, lse=None, kept_tiles=None, ws=None):
+    """Decode one token.  q [B,Hq,d] bf16 contiguous; caches [B,N,Hkv,d] bf16.
+    Returns (o [B,Hq,d] bf16, lse [B,Hq] fp32, kept_tiles [B,Hkv] int32)."""
+    _dev_check(q, kcache, vcache)
+    B, Hq, d = q.shape
+    N, Hkv = kcache.shape[1], kcache.shape[2]
+    if not q.is_contiguous() or q.dtype != torch.bfloat16:
+        raise ValueError("q must be a contiguous bf16 [B, Hq, d] tensor")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    kept_tiles = torch.empty((B, Hkv), dtype=torch.int32, device=q.device) if kept_tiles is None else kept_tiles
+    if ws is None:
+        ws = decode_workspace(B, N, Hq, Hkv, d, Bk_dec, q.device)
+    lib = load_library()
+    rc = lib.mala_decode(_ptr(q), _t4(kcache), _t4(vcache), B, N, Hq, Hkv, d, float(tau), Bk_dec,
+                         _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(ws), ws.numel(), _stream(q))
+    _check("mala_decode", rc)
+    return o, lse, kept_tiles
+
+
+class MalaAttention(torch.autograd.Function):
+    """Autograd wrapper: forward saves (q, k, v, o, lse) only -- no mask."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, tau, Bq, Bk):
+        o, lse = mala_fwd(q, k, v, tau, Bq, Bk)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (tau, Bq, Bk)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        tau, Bq, Bk = ctx.cfg
+        dq, dk, dv = mala_bwd(q, k, v, o, do.contiguous(), lse, tau, Bq, Bk)
+        return dq, dk, dv, None, None, None
+
+
+def mala_attention(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64):
+    return MalaAttention.apply(q, k, v, tau, Bq, Bk)

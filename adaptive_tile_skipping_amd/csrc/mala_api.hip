@@ -1,0 +1,213 @@
+// libmala C ABI: argument validation on the host, then kernel launches on the
+// caller's stream.  Nothing is enqueued when validation fails.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mala.h"
+#include "mala_internal.h"
+
+using namespace mala;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool t4_ok(const mala_t4& t, bool need) {
+    if (!t.ptr) return !need;
+    if (!aligned16(t.ptr)) return false;
+    if ((t.sb % 8) || (t.sl % 8) || (t.sh % 8)) return false;
+    if (t.sb < 0 || t.sl < 0 || t.sh < 0) return false;
+    return true;
+}
+
+bool tau_ok(float tau) { return isfinite(tau) && tau >= 0.f; }
+
+float log2_tau(float tau) { return tau == 0.f ? -INFINITY : (float)log2((double)tau); }
+
+bool fwd_shape_supported(int d, int Bq, int Bk) {
+    return (d == 128 && Bq == 128 && Bk == 64) || (d == 64 && Bq == 64 && Bk == 64);
+}
+
+bool dims_ok(int B, int L, int Hq, int Hkv, int d) {
+    if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return false;
+    if (Hq % Hkv) return false;
+    if ((int64_t)L * Hq * B > INT32_MAX / 2) return false;
+    return true;
+}
+
+// Workgroups per XCD run in groups of `chunk` consecutive units: one query
+// block of every q head of a KV head, twice, so that the heads sharing K/V
+// tiles sit on the same L2.
+int pick_chunk(int Hq, int Hkv) {
+    const int G = Hq / Hkv;
+    int c = 2 * G;
+    if (c < 4) c = 4;
+    if (c > 32) c = 32;
+    return c;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mala_status_string(mala_status s) {
+    switch (s) {
+        case MALA_OK: return "MALA_OK";
+        case MALA_ERR_INVALID_ARG: return "MALA_ERR_INVALID_ARG";
+        case MALA_ERR_UNSUPPORTED: return "MALA_ERR_UNSUPPORTED";
+        case MALA_ERR_WORKSPACE: return "MALA_ERR_WORKSPACE";
+        case MALA_ERR_HIP: return "MALA_ERR_HIP";
+    }
+    return "MALA_ERR_UNKNOWN";
+}
+
+const char* mala_version(void) { return "0.1.0 gfx950"; }
+
+mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int Hkv, int d,
+                     float tau, int Bq, int Bk, mala_t4 o, float* lse,
+                     const mala_tile_stats* stats, void* stream) {
+    if (!dims_ok(B, L, Hq, Hkv, d) || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
+    if (!t4_ok(q, true) || !t4_ok(k, true) || !t4_ok(v, true) || !t4_ok(o, true) || !lse)
+        return MALA_ERR_INVALID_ARG;
+    if (!fwd_shape_supported(d, Bq, Bk)) return MALA_ERR_UNSUPPORTED;
+    FwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = (const uint16_t*)q.ptr; p.k = (const uint16_t*)k.ptr; p.v = (const uint16_t*)v.ptr;
+    p.o = (uint16_t*)o.ptr; p.lse = lse;
+    p.q_sb = q.sb; p.q_sl = q.sl; p.q_sh = q.sh;
+    p.k_sb = k.sb; p.k_sl = k.sl; p.k_sh = k.sh;
+    p.v_sb = v.sb; p.v_sl = v.sl; p.v_sh = v.sh;
+    p.o_sb = o.sb; p.o_sl = o.sl; p.o_sh = o.sh;
+    p.B = B; p.L = L; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.nQB = (L + Bq - 1) / Bq; p.nKT = (L + Bk - 1) / Bk;
+    p.nunits = B * Hq * p.nQB;
+    p.chunk = pick_chunk(Hq, Hkv);
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    p.log2_tau = log2_tau(tau);
+    p.nwords = (p.nKT + 31) / 32;
+    bool st = false;
+    if (stats) {
+        p.kept_tiles = stats->kept_tiles;
+        p.kept_slots = stats->kept_slots;
+        p.omitted = stats->omitted_mass;
+        p.bits = stats->decision_bits;
+        st = stats->omitted_mass != nullptr;
+    }
+    hipError_t e = launch_fwd(p, d, Bq, Bk, st, (hipStream_t)stream);
+    return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
+}
+
+size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk) {
+    if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
+    const size_t rows = (size_t)B * Hq * L;
+    return align256(rows * d * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, const float* lse,
+                     int B, int L, int Hq, int Hkv, int d, float tau, int Bq, int Bk,
+                     mala_t4 dq, mala_t4 dk, mala_t4 dv, void* ws, size_t ws_bytes,
+                     const mala_tile_stats* bwd_stats, void* stream) {
+    if (!dims_ok(B, L, Hq, Hkv, d) || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
+    if (!t4_ok(q, true) || !t4_ok(k, true) || !t4_ok(v, true) || !t4_ok(o, true) || !t4_ok(dout, true) ||
+        !t4_ok(dq, true) || !t4_ok(dk, true) || !t4_ok(dv, true) || !lse)
+        return MALA_ERR_INVALID_ARG;
+    if (bwd_stats && bwd_stats->omitted_mass) return MALA_ERR_INVALID_ARG;
+    if (!fwd_shape_supported(d, Bq, Bk)) return MALA_ERR_UNSUPPORTED;
+    const size_t need = mala_bwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
+    BwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = (const uint16_t*)q.ptr; p.k = (const uint16_t*)k.ptr; p.v = (const uint16_t*)v.ptr;
+    p.o = (const uint16_t*)o.ptr; p.dout = (const uint16_t*)dout.ptr; p.lse = lse;
+    p.dq = (uint16_t*)dq.ptr; p.dk = (uint16_t*)dk.ptr; p.dv = (uint16_t*)dv.ptr;
+    const size_t rows = (size_t)B * Hq * L;
+    char* w = (char*)ws;
+    p.dq_acc = (float*)w; w += align256(rows * d * sizeof(float));
+    p.rowd = (float*)w; w += align256(rows * sizeof(float));
+    p.rowc = (float*)w;
+    p.q_sb = q.sb; p.q_sl = q.sl; p.q_sh = q.sh;
+    p.k_sb = k.sb; p.k_sl = k.sl; p.k_sh = k.sh;
+    p.v_sb = v.sb; p.v_sl = v.sl; p.v_sh = v.sh;
+    p.o_sb = o.sb; p.o_sl = o.sl; p.o_sh = o.sh;
+    p.do_sb = dout.sb; p.do_sl = dout.sl; p.do_sh = dout.sh;
+    p.dq_sb = dq.sb; p.dq_sl = dq.sl; p.dq_sh = dq.sh;
+    p.dk_sb = dk.sb; p.dk_sl = dk.sl; p.dk_sh = dk.sh;
+    p.dv_sb = dv.sb; p.dv_sl = dv.sl; p.dv_sh = dv.sh;
+    p.B = B; p.L = L; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.nQB = (L + Bq - 1) / Bq; p.nKT = (L + Bk - 1) / Bk;
+    p.nunits = B * Hkv * p.nKT;
+    p.chunk = 4;
+    p.scale = (float)(1.0 / sqrt((double)d));
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    p.log2_tau = log2_tau(tau);
+    p.nwords = (p.nKT + 31) / 32;
+    if (bwd_stats) {
+        p.kept_tiles = bwd_stats->kept_tiles;
+        p.kept_slots = bwd_stats->kept_slots;
+        p.bits = bwd_stats->decision_bits;
+    }
+    hipError_t e = launch_bwd(p, d, Bq, Bk, (hipStream_t)stream);
+    return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
+}
+
+size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_dec) {
+    if (!dims_ok(B, N, Hq, Hkv, d) || (d != 128 && d != 64) || Bk_dec != 64) return 0;
+    const int G = Hq / Hkv;
+    const size_t nT = (size_t)(N + Bk_dec - 1) / Bk_dec;
+    const size_t grp = (size_t)B * Hkv;
+    const size_t nsplit = 64;
+    size_t s = 0;
+    s += 2 * align256(grp * G * nT * sizeof(float));          // tmax, tsum
+    s += align256(grp * G * (size_t)N * sizeof(float));       // spill
+    s += align256(grp * nT * sizeof(int32_t));                // klist
+    s += align256(grp * sizeof(int32_t));                     // kcount
+    s += align256(grp * G * sizeof(float));                   // lse2
+    s += align256(grp * nsplit * G * d * sizeof(float));      // part_o
+    s += align256(grp * nsplit * G * 2 * sizeof(float));      // part_ml
+    return s;
+}
+
+mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
+                        int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
+                        void* ws, size_t ws_bytes, void* stream) {
+    if (!dims_ok(B, N, Hq, Hkv, d) || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
+    if (!q || !aligned16(q) || !o || !aligned16(o) || !lse) return MALA_ERR_INVALID_ARG;
+    if (!t4_ok(kcache, true) || !t4_ok(vcache, true)) return MALA_ERR_INVALID_ARG;
+    if ((d != 128 && d != 64) || Bk_dec != 64) return MALA_ERR_UNSUPPORTED;
+    const int G = Hq / Hkv;
+    if (G > 16) return MALA_ERR_UNSUPPORTED;
+    const size_t need = mala_decode_workspace_size(B, N, Hq, Hkv, d, Bk_dec);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
+    DecParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = (const uint16_t*)q; p.k = (const uint16_t*)kcache.ptr; p.v = (const uint16_t*)vcache.ptr;
+    p.o = (uint16_t*)o; p.lse = lse; p.kept_tiles = kept_tiles;
+    p.k_sb = kcache.sb; p.k_sl = kcache.sl; p.k_sh = kcache.sh;
+    p.v_sb = vcache.sb; p.v_sl = vcache.sl; p.v_sh = vcache.sh;
+    p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
+    p.nT = (N + Bk_dec - 1) / Bk_dec;
+    p.nsplit = 64;
+    if (p.nsplit > p.nT) p.nsplit = p.nT;
+    p.tiles_per_split = (p.nT + p.nsplit - 1) / p.nsplit;
+    p.nsplit = (p.nT + p.tiles_per_split - 1) / p.tiles_per_split;
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    p.log2_tau = log2_tau(tau);
+    p.log2_N = (float)log2((double)N);
+    const size_t nT = (size_t)p.nT, grp = (size_t)B * Hkv;
+    char* w = (char*)ws;
+    p.tmax = (float*)w; w += align256(grp * G * nT * sizeof(float));
+    p.tsum = (float*)w; w += align256(grp * G * nT * sizeof(float));
+    p.spill = (float*)w; w += align256(grp * G * (size_t)N * sizeof(float));
+    p.klist = (int32_t*)w; w += align256(grp * nT * sizeof(int32_t));
+    p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));
+    p.lse2 = (float*)w; w += align256(grp * G * sizeof(float));
+    p.part_o = (float*)w; w += align256(grp * 64 * G * d * sizeof(float));
+    p.part_ml = (float*)w;
+    hipError_t e = launch_decode(p, d, Bk_dec, tau == 0.f, (hipStream_t)stream);
+    return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
+}
+
+}  // extern "C"

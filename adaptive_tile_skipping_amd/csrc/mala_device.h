@@ -1,0 +1,85 @@
+// Device-side helpers shared by the libmala kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mala {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
+// Lane layouts (wave64): A[i][k] at lane i + 32*(k/8), element k%8;
+// B[k][j] at lane j + 32*(k/8), element k%8;
+// C[i][j] at lane j + 32*((i/4)%2), register (i/8)*4 + i%4.
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same shape and layouts with fp16 operands.
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).  A[i][k] at lane i + 16*(k/8), element k%8;
+// B[k][j] at lane j + 16*(k/8); C[i][j] at lane j + 16*(i/4), register i%4.
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Hardware base-2 exponential / logarithm (v_exp_f32, v_log_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+__device__ __forceinline__ _Float16 to_f16(float x) { return (_Float16)x; }
+
+// Two bf16 values (given as fp32 bit patterns) -> packed fp16.  Exact for
+// magnitudes in fp16's normal range; beyond +-65504 the value saturates
+// (round toward zero), below 2^-14 it becomes an fp16 subnormal.
+__device__ __forceinline__ uint32_t pack2_f16_from_f32bits(uint32_t lo, uint32_t hi) {
+    fp16x2 r = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(lo), __uint_as_float(hi));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {   // combine lane l with lane l^32
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum_pair(float x) {
+    return x + __shfl_xor(x, 32);
+}
+
+// Position of key kk (0..15 within a 16-key group) in the transposed-V LDS
+// rows: bits 2 and 3 swapped, so that the 8 consecutive positions a lane
+// feeds to the P.V contraction are exactly the 8 keys its score registers hold.
+__device__ __forceinline__ int vt_pos16(int kk) {
+    return (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+// Maps a linear workgroup id onto a work-unit id so that `chunk` consecutive
+// units run on the same XCD (workgroups are dealt round-robin to the 8 XCDs)
+// while each XCD still receives units in increasing order.  Returns an id in
+// [0, 8*chunk*ceil(n/(8*chunk))); ids >= n are padding and exit.
+__device__ __forceinline__ int xcd_unit(int bid, int chunk) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    return ((slot / chunk) * 8 + xcd) * chunk + slot % chunk;
+}
+
+}  // namespace mala

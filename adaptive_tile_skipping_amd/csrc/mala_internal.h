@@ -1,0 +1,77 @@
+// Host-side kernel parameter blocks and launchers of libmala (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mala {
+
+struct FwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    int64_t q_sb, q_sl, q_sh, k_sb, k_sl, k_sh, v_sb, v_sl, v_sh, o_sb, o_sl, o_sh;
+    int B, L, Hq, Hkv, G, nQB, nKT, nunits, chunk;
+    float scale_log2;   // log2(e) / sqrt(d): scores in base 2
+    float log2_tau;     // log2(tau); -inf for tau = 0
+    int32_t* kept_tiles;
+    int32_t* kept_slots;
+    float* omitted;
+    uint32_t* bits;
+    int nwords;
+};
+
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* dq_acc;      // [B, Hq, L, d] fp32 workspace
+    float* rowd;        // [B, Hq, L] fp32: D_i = dO_i . O_i
+    float* rowc;        // [B, Hq, L] fp32: LSE_i*log2(e) + log2(tau) - log2(i+1)
+    int64_t q_sb, q_sl, q_sh, k_sb, k_sl, k_sh, v_sb, v_sl, v_sh, o_sb, o_sl, o_sh;
+    int64_t do_sb, do_sl, do_sh, dq_sb, dq_sl, dq_sh, dk_sb, dk_sl, dk_sh, dv_sb, dv_sl, dv_sh;
+    int B, L, Hq, Hkv, G, nQB, nKT, nunits, chunk;
+    float scale;        // 1 / sqrt(d)
+    float scale_log2;   // log2(e) / sqrt(d)
+    float log2_tau;
+    int32_t* kept_tiles;
+    int32_t* kept_slots;
+    uint32_t* bits;
+    int nwords;
+};
+
+struct DecParams {
+    const uint16_t* q;      // [B, Hq, d]
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;            // [B, Hq, d]
+    float* lse;             // [B, Hq]
+    int32_t* kept_tiles;    // [B, Hkv] or null
+    int64_t k_sb, k_sl, k_sh, v_sb, v_sl, v_sh;
+    int B, N, Hq, Hkv, G, nT, nsplit, tiles_per_split;
+    float scale_log2;
+    float log2_tau;
+    float log2_N;
+    // workspace
+    float* tmax;            // [B, Hkv, G, nT]  tile row max (base 2)
+    float* tsum;            // [B, Hkv, G, nT]  sum 2^(s - tile max)
+    float* spill;           // [B, Hkv, G, N]   base-2 scores
+    int32_t* klist;         // [B, Hkv, nT]     retained tiles, newest first
+    int32_t* kcount;        // [B, Hkv]
+    float* lse2;            // [B, Hkv, G]      base-2 final log-normaliser
+    float* part_o;          // [B, Hkv, nsplit, G, d] partial outputs
+    float* part_ml;         // [B, Hkv, nsplit, G, 2] partial (max, sum) (dense path)
+};
+
+hipError_t launch_fwd(const FwdParams& p, int d, int Bq, int Bk, bool stats, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int d, int Bq, int Bk, hipStream_t s);
+hipError_t launch_decode(const DecParams& p, int d, int Bkd, bool dense, hipStream_t s);
+
+}  // namespace mala

@@ -1,0 +1,144 @@
+/*
+ * libmala -- MALA (MassAlloc Attention) fused causal attention for AMD MI355X
+ * (gfx950).  C ABI: plain pointers, sizes and element strides; no C++ or
+ * framework types cross it, no exception leaves it.
+ *
+ * The operation ("MassAlloc Attention: Let Attention Allocate Its Own
+ * Compute", arXiv 2609.32712; summary page agihunt.info, and review page
+ * jaehun.me, sections "One tolerance governs everything", "Forward: online
+ * sparse softmax", "Backward: offline sparse probabilities"):
+ *   causal softmax attention in which every legal query-key tile is scored,
+ *   but the post-score work of a tile (softmax update, V load, P.V) is skipped
+ *   when, for every row of the query block, exp(tile row max) divided by the
+ *   softmax mass retained so far is below tau / L_i, L_i = i + 1 being the
+ *   number of keys row i can see.  Tiles are visited from the diagonal toward
+ *   key 0, so the first legal tile of each row is always kept (its retained
+ *   mass is still empty).  The backward pass re-applies the test with the
+ *   final log-normaliser (LSE) saved by the forward, so its kept set is a
+ *   subset of the forward's; no mask is stored.  tau = 0 skips nothing and is
+ *   plain causal softmax attention.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are bf16 (IEEE bfloat16, round-to-nearest-even), described by
+ *     mala_t4: element pointer and element strides for dims [B, L, H, d]; the d
+ *     dimension is contiguous.  Pointers and the byte size of every stride must
+ *     be 16-byte aligned (strides multiples of 8 elements).
+ *   - Scale is 1/sqrt(d); LSE is the natural log of the retained normaliser of
+ *     the scaled scores.
+ *   - GQA: Hq must be a multiple of Hkv; q head h reads KV head h / (Hq/Hkv).
+ *   - The caller owns every buffer, including workspaces; the library
+ *     allocates no device memory and keeps no mutable global state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting.  Arguments are validated on the host
+ *     before anything is enqueued: an invalid call enqueues nothing.
+ *   - tau must be finite and >= 0.
+ *   - Arithmetic: scores, softmax state and accumulators in fp32; the P.V
+ *     contraction of the forward and decode runs in fp16 (P in [0, 1] rounded
+ *     to nearest; V converted exactly from bf16, so |v| must stay within
+ *     fp16's range, 65504, beyond which it saturates); the other contractions
+ *     take bf16 operands.
+ *   - Supported shapes: (d, Bq, Bk) = (128, 128, 64) or (64, 64, 64) for
+ *     mala_fwd / mala_bwd; decode takes d = 128 or 64 with Bk_dec = 64.
+ *     Anything else returns MALA_ERR_UNSUPPORTED.
+ */
+#ifndef MALA_H_
+#define MALA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MALA_OK = 0,
+    MALA_ERR_INVALID_ARG = 1,   /* null required pointer, bad shape/stride/alignment, bad tau */
+    MALA_ERR_UNSUPPORTED = 2,   /* (d, Bq, Bk) combination not built */
+    MALA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace_size query */
+    MALA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} mala_status;
+
+/* A bf16 tensor [B, L, H, d]; element strides; d stride is 1. */
+typedef struct {
+    void* ptr;
+    int64_t sb, sl, sh;
+} mala_t4;
+
+/* Optional per-call tile statistics (every pointer may be NULL).
+ *   kept_tiles    [B, Hq, nQB] int32: retained key tiles per query block.
+ *   kept_slots    [B, Hq, L]   int32: legal (causal) keys inside retained
+ *                 tiles, per row -- the post-score key slots of the row.
+ *   omitted_mass  [B, Hq, L]   fp32: probability mass of the skipped legal
+ *                 keys, Z_O / (Z_R + Z_O).  Non-NULL switches the kernel to
+ *                 a statistics mode that also exponentiates skipped tiles
+ *                 (slower; keep NULL in timed runs).  Forward only.
+ *   decision_bits [B, Hq, nQB, ceil(nKT/32)] uint32: bit (kt % 32) of word
+ *                 kt / 32 is 1 iff key tile kt was retained for the block;
+ *                 bits of tiles the block never visits are 0.
+ * nQB = ceil(L / Bq), nKT = ceil(L / Bk).  Every element is overwritten. */
+typedef struct {
+    int32_t* kept_tiles;
+    int32_t* kept_slots;
+    float* omitted_mass;
+    uint32_t* decision_bits;
+} mala_tile_stats;
+
+/* Forward (training forward or prefill), causal, Lq = Lk = L.
+ *   q [B, L, Hq, d], k, v [B, L, Hkv, d] bf16 in device memory.
+ *   o [B, L, Hq, d] bf16 output; lse [B, Hq, L] fp32 output (contiguous).
+ *   stats: NULL or per-call statistics (see mala_tile_stats).
+ * Decision rule: review page "Forward: online sparse softmax"; summary page,
+ * forward paragraph. */
+mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int Hkv, int d,
+                     float tau, int Bq, int Bk, mala_t4 o, float* lse,
+                     const mala_tile_stats* stats, void* stream);
+
+/* Bytes of device workspace mala_bwd needs (fp32 dQ accumulator, row terms). */
+size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk);
+
+/* Backward.  Inputs as saved by mala_fwd (q, k, v, o, lse) plus dout.
+ *   dq [B, L, Hq, d], dk, dv [B, L, Hkv, d] bf16 outputs (dk/dv summed over
+ *   the q heads of each KV head).  ws: device workspace of at least
+ *   mala_bwd_workspace_size(...) bytes, 256-byte aligned; it is cleared by the
+ *   call itself (on the stream) and may be reused between calls.
+ *   bwd_stats: NULL or statistics of the backward's own decisions
+ *   (kept_tiles, kept_slots, decision_bits; omitted_mass must be NULL).
+ * Decision rule: review page "Backward: offline sparse probabilities";
+ * summary page, backward paragraph.  The result is not the exact derivative
+ * of the forward for tau > 0 (the pages say so); it is the softmax-attention
+ * gradient restricted to the tiles the backward keeps. */
+mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, const float* lse,
+                     int B, int L, int Hq, int Hkv, int d, float tau, int Bq, int Bk,
+                     mala_t4 dq, mala_t4 dk, mala_t4 dv, void* ws, size_t ws_bytes,
+                     const mala_tile_stats* bwd_stats, void* stream);
+
+/* Bytes of device workspace mala_decode needs (tile statistics, score spill,
+ * retained-tile lists, partial outputs). */
+size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_dec);
+
+/* Decode: one new query token per sequence against a KV cache of N keys (the
+ * cache includes the new token's key and value).
+ *   q [B, Hq, d] bf16 contiguous; kcache, vcache [B, N, Hkv, d] bf16 (mala_t4
+ *   with L = N).  o [B, Hq, d] bf16 output; lse [B, Hq] fp32 output.
+ *   kept_tiles: NULL or [B, Hkv] int32 output, retained cache tiles per
+ *   (sequence, KV head).  ws: device workspace of at least
+ *   mala_decode_workspace_size(...) bytes, 256-byte aligned.
+ * The decision block is the group of Hq/Hkv q heads sharing a KV head, all
+ * with L_i = N; cache tiles of Bk_dec keys are visited newest first (same
+ * tau as training: summary page, forward paragraph; review page "One
+ * tolerance governs everything"). */
+mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
+                        int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* mala_status_string(mala_status s);
+
+/* Library version, e.g. "0.1.0 gfx950". */
+const char* mala_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MALA_H_ */

@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/mala.h, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import adaptive_tile_skipping_amd as mala
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mala.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mala_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
+              "mala_decode_workspace_size", "mala_status_string", "mala_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mala.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) <= set(mala.EXPORTS) | {"mala_version"}
+
+
+def test_status_strings_and_version():
+    lib = mala.load_library()
+    for code, name in enumerate(["MALA_OK", "MALA_ERR_INVALID_ARG", "MALA_ERR_UNSUPPORTED",
+                                 "MALA_ERR_WORKSPACE", "MALA_ERR_HIP"]):
+        assert lib.mala_status_string(code).decode() == name
+    assert b"gfx950" in lib.mala_version()
+
+
+def _t4(ptr=16 * 1024, sb=8 * 1024, sl=8 * 16, sh=128):
+    return mala.MalaT4(ptr, sb, sl, sh)
+
+
+def _fwd(**kw):
+    a = dict(q=_t4(), k=_t4(), v=_t4(), B=1, L=256, Hq=2, Hkv=1, d=128, tau=1.0, Bq=128, Bk=64,
+             o=_t4(), lse=ctypes.c_void_p(4096), stats=None)
+    a.update(kw)
+    lib = mala.load_library()
+    return lib.mala_fwd(a["q"], a["k"], a["v"], a["B"], a["L"], a["Hq"], a["Hkv"], a["d"], a["tau"],
+                        a["Bq"], a["Bk"], a["o"], a["lse"], a["stats"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=mala.MalaT4(None, 0, 0, 0)), mala.MALA_ERR_INVALID_ARG),
+    (dict(lse=None), mala.MALA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), mala.MALA_ERR_INVALID_ARG),
+    (dict(tau=-1.0), mala.MALA_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), mala.MALA_ERR_INVALID_ARG),
+    (dict(tau=float("inf")), mala.MALA_ERR_INVALID_ARG),
+    (dict(L=0), mala.MALA_ERR_INVALID_ARG),
+    (dict(B=-1), mala.MALA_ERR_INVALID_ARG),
+    (dict(q=_t4(ptr=16 * 1024 + 2)), mala.MALA_ERR_INVALID_ARG),    # misaligned pointer
+    (dict(k=_t4(sl=130)), mala.MALA_ERR_INVALID_ARG),               # stride not a multiple of 8
+    (dict(d=96), mala.MALA_ERR_UNSUPPORTED),
+    (dict(Bq=64), mala.MALA_ERR_UNSUPPORTED),
+    (dict(Bk=128), mala.MALA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_arguments(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_bwd_workspace_and_errors():
+    lib = mala.load_library()
+    n = lib.mala_bwd_workspace_size(1, 1000, 4, 2, 128, 128, 64)
+    assert n >= 4 * 1000 * 128 * 4
+    assert lib.mala_bwd_workspace_size(1, 1000, 4, 2, 96, 128, 64) == 0
+    t = _t4()
+    args = [t, t, t, t, t, ctypes.c_void_p(4096), 1, 1000, 4, 2, 128, 1.0, 128, 64, t, t, t]
+    # missing / small / misaligned workspace
+    assert lib.mala_bwd(*args, None, 0, None, None) == mala.MALA_ERR_WORKSPACE
+    assert lib.mala_bwd(*args, ctypes.c_void_p(1 << 20), n - 1, None, None) == mala.MALA_ERR_WORKSPACE
+    assert lib.mala_bwd(*args, ctypes.c_void_p((1 << 20) + 16), n, None, None) == mala.MALA_ERR_WORKSPACE
+    bad = list(args)
+    bad[11] = -0.5
+    assert lib.mala_bwd(*bad, ctypes.c_void_p(1 << 20), n, None, None) == mala.MALA_ERR_INVALID_ARG
+    st = mala.MalaTileStats(None, None, 4096, None)   # omitted mass is forward-only
+    assert lib.mala_bwd(*args, ctypes.c_void_p(1 << 20), n, ctypes.pointer(st), None) == mala.MALA_ERR_INVALID_ARG
+
+
+def test_decode_workspace_and_errors():
+    lib = mala.load_library()
+    n = lib.mala_decode_workspace_size(8, 131072, 5, 1, 128, 64)
+    assert n > 8 * 5 * 131072 * 4
+    assert lib.mala_decode_workspace_size(8, 131072, 5, 1, 128, 32) == 0
+    t = _t4()
+    q = ctypes.c_void_p(4096)
+    base = [q, t, t, 2, 1000, 4, 2, 128, 1.0, 64, ctypes.c_void_p(8192), ctypes.c_void_p(12288), None]
+    assert lib.mala_decode(*base, None, 0, None) == mala.MALA_ERR_WORKSPACE
+    bad = list(base)
+    bad[8] = float("nan")
+    assert lib.mala_decode(*bad, ctypes.c_void_p(1 << 20), 1 << 30, None) == mala.MALA_ERR_INVALID_ARG
+    bad = list(base)
+    bad[9] = 32
+    assert lib.mala_decode(*bad, ctypes.c_void_p(1 << 20), 1 << 30, None) == mala.MALA_ERR_UNSUPPORTED
+    bad = list(base)
+    bad[0] = ctypes.c_void_p(4098)
+    assert lib.mala_decode(*bad, ctypes.c_void_p(1 << 20), 1 << 30, None) == mala.MALA_ERR_INVALID_ARG
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 128, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="GPU only"):
+        mala.mala_fwd(x, x, x, 1.0)

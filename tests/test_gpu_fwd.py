@@ -1,0 +1,135 @@
+"""GPU parity of mala_fwd (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import adaptive_tile_skipping_amd as mala
+import mala_gen as G
+from oracle import oracle_fwd
+from parity import (bf16_tensor, compare_decisions, rel_l2_per_head, to_f64, unpack_bits)
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 2e-3       # max relative L2 error of O per (b, h) slice
+LSE_TOL = 1e-4     # |LSE_gpu - LSE_oracle| on rows of blocks without decision mismatch
+STAT_TOL = 0.01    # relative difference of means (kept slots, omitted mass)
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch.device("cuda:0")
+
+
+def run_fwd_case(inp, tau, Bq, Bk, blocks=None, stats_mode=True, label=""):
+    dev = _dev()
+    B, L, Hq, d = inp["q"].shape
+    Hkv = inp["k"].shape[2]
+    q, k, v = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v"))
+    st = mala.make_stats(B, Hq, L, Bq, Bk, dev, omitted=stats_mode)
+    print(f"[fwd] {label} B={B} L={L} Hq={Hq} Hkv={Hkv} d={d} tau={tau} Bq={Bq} Bk={Bk}", flush=True)
+    o, lse = mala.mala_fwd(q, k, v, tau, Bq, Bk, stats=st)
+    torch.cuda.synchronize()
+    qf, kf, vf = (G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v"))
+    ref = oracle_fwd(qf, kf, vf, tau, Bq, Bk, blocks=blocks)
+    nQB, nKT = -(-L // Bq), -(-L // Bk)
+    gkeep = unpack_bits(st["decision_bits"].cpu().numpy(), nKT)
+    rows = np.zeros((B, Hq, L), bool)
+    if blocks is None:
+        sel = np.ones((B, Hq, nQB), bool)
+    else:
+        sel = np.zeros((B * Hq * nQB,), bool)
+        sel[np.asarray(blocks)] = True
+        sel = sel.reshape(B, Hq, nQB)
+    for qb in range(nQB):
+        rows[:, :, qb * Bq:min(L, qb * Bq + Bq)] = sel[:, :, qb, None]
+    dec = compare_decisions(np.where(ref["keep"] == 255, 255, gkeep), ref["keep"], ref["margin"])
+    assert dec["nonexempt"] == 0, dec
+    # blocks with any mismatch are excluded from the tight row checks
+    bad = (np.where(ref["keep"] == 255, 0, gkeep) != np.where(ref["keep"] == 255, 0, ref["keep"])).any(-1)
+    clean_rows = rows.copy()
+    for qb in range(nQB):
+        clean_rows[:, :, qb * Bq:min(L, qb * Bq + Bq)] &= ~bad[:, :, qb, None]
+    o_g, lse_g = to_f64(o), lse.cpu().numpy().astype(np.float64)
+    # O: relative L2 per (b, h) over the selected rows
+    msk = np.moveaxis(rows, 2, 1)[..., None]  # [B, L, Hq, 1]
+    worst, glob = rel_l2_per_head(np.where(msk, o_g, 0.0), np.where(msk, ref["o"], 0.0))
+    assert worst <= O_TOL, (worst, glob)
+    lerr = np.abs(lse_g - ref["lse"])[clean_rows]
+    if lerr.size:
+        assert lerr.max() <= LSE_TOL + 1e-5 * np.abs(ref["lse"][clean_rows]).max(), lerr.max()
+    slots_g = st["kept_slots"].cpu().numpy()
+    assert np.array_equal(slots_g[clean_rows], ref["kept_slots"][clean_rows])
+    ms_g, ms_o = slots_g[rows].mean(), ref["kept_slots"][rows].mean()
+    assert abs(ms_g - ms_o) <= STAT_TOL * ms_o
+    kt_g = st["kept_tiles"].cpu().numpy()
+    kt_o = (ref["keep"] == 1).sum(-1)
+    assert np.array_equal(kt_g[sel & ~bad], kt_o[sel & ~bad])
+    if stats_mode:
+        om_g = st["omitted_mass"].cpu().numpy().astype(np.float64)
+        a, bb = om_g[rows].mean(), ref["omitted"][rows].mean()
+        assert abs(a - bb) <= STAT_TOL * bb + 1e-9, (a, bb)
+    return dict(dec=dec, o_worst=worst, o_global=glob, keep_frac=float((ref["keep"] == 1).sum() / max(1, (ref["keep"] != 255).sum())))
+
+
+@pytest.mark.parametrize("tau", [0.0, 1.0])
+def test_fwd_tiny_512(tau):
+    w = G.WORKLOADS["tiny_512"]
+    inp = G.workload_inputs("tiny_512")
+    r = run_fwd_case(inp, tau, w["Bq"], w["Bk"], label="tiny_512")
+    print(r)
+
+
+@pytest.mark.parametrize("L", [1, 77, 128, 129, 1000])
+@pytest.mark.parametrize("tau", [0.0, 0.25, 1.0, 4.0])
+def test_fwd_ragged_gqa(L, tau):
+    inp = G.attn_inputs(300 + L, 2, L, 6, 2, 128, 0.1, diffuse_kv_heads=(1,))
+    run_fwd_case(inp, tau, 128, 64, label=f"ragged L={L}")
+
+
+@pytest.mark.parametrize("L", [64, 65, 300])
+def test_fwd_d64_ragged(L):
+    inp = G.attn_inputs(400 + L, 1, L, 4, 1, 64, 0.2)
+    run_fwd_case(inp, 1.0, 64, 64, label=f"d64 L={L}")
+
+
+def test_fwd_strided_views():
+    """q/k/v as views into a packed [B, L, 3, H, d] buffer (non-contiguous heads)."""
+    dev = _dev()
+    inp = G.attn_inputs(500, 1, 520, 4, 4, 128, 0.1)
+    qkv = torch.stack([bf16_tensor(inp[x], dev) for x in ("q", "k", "v")], dim=2)  # [B, L, 3, H, d]
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    assert not q.is_contiguous()
+    o1, l1 = mala.mala_fwd(q, k, v, 1.0, 128, 64)
+    o2, l2 = mala.mala_fwd(q.contiguous(), k.contiguous(), v.contiguous(), 1.0, 128, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_gqa_8k():
+    w = G.WORKLOADS["gqa_8k"]
+    inp = G.workload_inputs("gqa_8k", with_dout=False)
+    r = run_fwd_case(inp, 1.0, w["Bq"], w["Bk"], label="gqa_8k")
+    print(r)
+
+
+def test_fwd_train_128k_sampled():
+    """Full-size launch (L = 131072, Hq = 5, Hkv = 1); the oracle checks sampled blocks."""
+    w = G.WORKLOADS["train_128k"]
+    inp = G.workload_inputs("train_128k", with_dout=False)
+    nQB = 131072 // 128
+    blocks = [h * nQB + qb for h, qb in ((0, 0), (1, 1), (2, 517), (3, nQB - 2), (4, nQB - 1), (0, nQB - 1))]
+    r = run_fwd_case(inp, 1.0, w["Bq"], w["Bk"], blocks=blocks, stats_mode=False, label="train_128k sampled")
+    print(r)
+
+
+def test_fwd_deterministic():
+    dev = _dev()
+    inp = G.attn_inputs(600, 1, 2048, 4, 2, 128, 0.1)
+    q, k, v = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v"))
+    s1 = mala.make_stats(1, 4, 2048, 128, 64, dev)
+    s2 = mala.make_stats(1, 4, 2048, 128, 64, dev)
+    o1, l1 = mala.mala_fwd(q, k, v, 1.0, stats=s1)
+    o2, l2 = mala.mala_fwd(q, k, v, 1.0, stats=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(s1["decision_bits"], s2["decision_bits"])
