@@ -103,7 +103,9 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
 size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk) {
     if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
     const size_t rows = (size_t)B * Hq * L;
-    return align256(rows * d * sizeof(float)) + 2 * align256(rows * sizeof(float));
+    const size_t Lpad = (size_t)((L + Bq - 1) / Bq) * Bq;
+    const size_t tr = (size_t)B * Hq * d * Lpad * 2;
+    return align256(rows * d * sizeof(float)) + 2 * align256(rows * sizeof(float)) + 2 * align256(tr);
 }
 
 mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, const float* lse,
@@ -127,7 +129,11 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     char* w = (char*)ws;
     p.dq_acc = (float*)w; w += align256(rows * d * sizeof(float));
     p.rowd = (float*)w; w += align256(rows * sizeof(float));
-    p.rowc = (float*)w;
+    p.rowc = (float*)w; w += align256(rows * sizeof(float));
+    p.Lpad = ((L + Bq - 1) / Bq) * Bq;
+    const size_t tr = (size_t)B * Hq * d * p.Lpad * 2;
+    p.qt = (uint16_t*)w; w += align256(tr);
+    p.dot = (uint16_t*)w;
     p.q_sb = q.sb; p.q_sl = q.sl; p.q_sh = q.sh;
     p.k_sb = k.sb; p.k_sl = k.sl; p.k_sh = k.sh;
     p.v_sb = v.sb; p.v_sl = v.sl; p.v_sh = v.sh;

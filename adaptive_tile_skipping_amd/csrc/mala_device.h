@@ -73,6 +73,21 @@ __device__ __forceinline__ int vt_pos16(int kk) {
     return (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
 }
 
+// 16-byte global -> LDS copy that bypasses registers (gfx950
+// global_load_lds_dwordx4).  Every lane supplies its own global address; the
+// wave's 64 chunks land contiguously at `lds_wave_base` (wave-uniform), lane
+// l at byte 16*l.
+__device__ __forceinline__ void load16_to_lds(const void* gptr, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait for every outstanding memory operation of this wave (including the
+// global -> LDS copies above), then a workgroup barrier.
+__device__ __forceinline__ void wait_all_then_barrier() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
 // Maps a linear workgroup id onto a work-unit id so that `chunk` consecutive
 // units run on the same XCD (workgroups are dealt round-robin to the 8 XCDs)
 // while each XCD still receives units in increasing order.  Returns an id in

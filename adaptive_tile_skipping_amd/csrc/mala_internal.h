@@ -34,7 +34,10 @@ struct BwdParams {
     uint16_t* dv;
     float* dq_acc;      // [B, Hq, L, d] fp32 workspace
     float* rowd;        // [B, Hq, L] fp32: D_i = dO_i . O_i
-    float* rowc;        // [B, Hq, L] fp32: LSE_i*log2(e) + log2(tau) - log2(i+1)
+    float* rowc;        // [B, Hq, L] fp32: LSE_i * log2(e)
+    uint16_t* qt;       // [B, Hq, d, Lpad] bf16: Q transposed, query positions permuted in 16-groups
+    uint16_t* dot;      // [B, Hq, d, Lpad] bf16: dO transposed, same permutation
+    int Lpad;           // nQB * Bq
     int64_t q_sb, q_sl, q_sh, k_sb, k_sl, k_sh, v_sb, v_sl, v_sh, o_sb, o_sl, o_sh;
     int64_t do_sb, do_sl, do_sh, dq_sb, dq_sl, dq_sh, dk_sb, dk_sl, dk_sh, dv_sb, dv_sl, dv_sh;
     int B, L, Hq, Hkv, G, nQB, nKT, nunits, chunk;

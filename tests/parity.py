@@ -70,14 +70,69 @@ def rel_l2(x: np.ndarray, y: np.ndarray) -> float:
     return float(np.linalg.norm(x - y) / n) if n > 0 else float(np.linalg.norm(x - y))
 
 
-def rel_l2_per_head(x, y, head_axis: int = 2):
-    """Max over (b, h) slices of the relative L2 error, and the global value."""
+def rel_l2_per_head(x, y, head_axis: int = 2, floor_frac: float = 0.0):
+    """Max over (b, h) slices of the relative L2 error, and the global value.
+
+    With floor_frac > 0 each slice's error is divided by
+    max(|y_slice|, floor_frac * max_slices |y_slice|): a slice whose exact value
+    is vanishingly small next to the others (a gradient that cancels to ~1e-7 of
+    its neighbours, below what fp32 arithmetic resolves) is measured against
+    that floor instead of its own norm."""
+    x = np.moveaxis(np.asarray(x, np.float64), head_axis, 1)
+    y = np.moveaxis(np.asarray(y, np.float64), head_axis, 1)
+    norms = np.array([[np.linalg.norm(y[b, h]) for h in range(y.shape[1])] for b in range(y.shape[0])])
+    floor = floor_frac * norms.max() if norms.size else 0.0
+    worst = 0.0
+    for b in range(x.shape[0]):
+        for h in range(x.shape[1]):
+            den = max(norms[b, h], floor)
+            err = np.linalg.norm(x[b, h] - y[b, h])
+            worst = max(worst, err / den if den > 0 else err)
+    return worst, rel_l2(x, y)
+
+
+FP32_CANCEL = 2.0 ** -11
+
+
+def grad_floors(name, q, k, v, dout, rowmask, scale):
+    """Per-slice noise floor of an fp32 evaluation of the attention gradient.
+
+    dS = P (dP - D) subtracts two dot products of magnitude |dO||v|; in fp32
+    each carries ~1e-6 of that magnitude, so rows whose exact dS cancels
+    (one-hot attention) have dq, dk far below what fp32 resolves.  The floor
+    of a dq slice (b, h) is FP32_CANCEL * scale * |dO rows| * max|v| * max|k|;
+    of a dk slice (b, kh) the same with the rows of every q head of the group
+    and max|q|.  dv needs none (it has no cancellation).
+    q, dout [B, L, Hq, d]; k, v [B, L, Hkv, d]; rowmask [B, L, Hq] rows compared.
+    Returns [B, H] floors."""
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    Gq = Hq // Hkv
+    vmax = np.linalg.norm(v, axis=-1).max(axis=1)          # [B, Hkv]
+    kmax = np.linalg.norm(k, axis=-1).max(axis=1)
+    qmax = np.linalg.norm(q, axis=-1).max(axis=1)           # [B, Hq]
+    dn = np.sqrt((np.where(rowmask[..., None], dout, 0.0) ** 2).sum(axis=(1, 3)))   # [B, Hq]
+    if name == "dq":
+        kh = np.arange(Hq) // Gq
+        return FP32_CANCEL * scale * dn * vmax[:, kh] * kmax[:, kh]
+    if name == "dk":
+        dng = np.sqrt((dn ** 2).reshape(B, Hkv, Gq).sum(-1))
+        qg = qmax.reshape(B, Hkv, Gq).max(-1)
+        return FP32_CANCEL * scale * dng * vmax * qg
+    return np.zeros((B, Hkv))
+
+
+def rel_l2_floored(x, y, floors, head_axis: int = 2):
+    """Max over (b, h) slices of |x - y| / max(|y|, floor[b, h]), and the global
+    relative error."""
     x = np.moveaxis(np.asarray(x, np.float64), head_axis, 1)
     y = np.moveaxis(np.asarray(y, np.float64), head_axis, 1)
     worst = 0.0
     for b in range(x.shape[0]):
         for h in range(x.shape[1]):
-            worst = max(worst, rel_l2(x[b, h], y[b, h]))
+            den = max(np.linalg.norm(y[b, h]), floors[b, h])
+            err = np.linalg.norm(x[b, h] - y[b, h])
+            worst = max(worst, err / den if den > 0 else err)
     return worst, rel_l2(x, y)
 
 

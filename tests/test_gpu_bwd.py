@@ -1,0 +1,204 @@
+"""GPU parity of mala_bwd (through the C ABI) against the fp64 oracle.
+
+The GPU backward consumes the GPU forward's O and LSE; the oracle backward
+consumes the oracle forward's own O and LSE, so no value from the HIP path
+reaches the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import adaptive_tile_skipping_amd as mala
+import mala_gen as G
+from oracle import oracle_bwd, oracle_fwd
+from parity import (bf16_tensor, compare_decisions, grad_floors, rel_l2_floored, rel_l2_per_head, to_f64,
+                    unpack_bits)
+
+pytestmark = pytest.mark.gpu
+
+GRAD_TOL = 1e-2
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch.device("cuda:0")
+
+
+def _rows_of_blocks(blocks, B, Hq, L, Bq):
+    nQB = -(-L // Bq)
+    m = np.zeros((B, Hq, L), bool)
+    for bid in blocks:
+        bh, qb = divmod(bid, nQB)
+        m[bh // Hq, bh % Hq, qb * Bq:min(L, qb * Bq + Bq)] = True
+    return m
+
+
+def run_bwd_case(inp, tau, Bq, Bk, qblocks=None, ktiles=None, label=""):
+    """mala_bwd as a function of its inputs: both sides get the same (q, k, v, o,
+    dout, lse), with o and lse taken from the oracle forward and rounded to the
+    types the API stores (bf16 O, fp32 LSE).  Where the oracle forward was not
+    run (sampled large cases), the GPU gets the GPU forward's O/LSE for rows no
+    checked gradient depends on."""
+    dev = _dev()
+    B, L, Hq, d = inp["q"].shape
+    Hkv = inp["k"].shape[2]
+    nQB, nKT = -(-L // Bq), -(-L // Bk)
+    q, k, v, do = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v", "dout"))
+    print(f"[bwd] {label} B={B} L={L} Hq={Hq} Hkv={Hkv} d={d} tau={tau}", flush=True)
+    f64 = {x: G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")}
+    fwd_blocks = None
+    if qblocks is not None or ktiles is not None:
+        need = set(qblocks or [])
+        Gq = Hq // Hkv
+        for kid in (ktiles or []):
+            bk, kt = divmod(kid, nKT)
+            b, kh = divmod(bk, Hkv)
+            for g in range(Gq):
+                for qb in range((kt * Bk) // Bq, nQB):
+                    need.add((b * Hq + kh * Gq + g) * nQB + qb)
+        fwd_blocks = sorted(need)
+    rf = oracle_fwd(f64["q"], f64["k"], f64["v"], tau, Bq, Bk, blocks=fwd_blocks)
+    o_bits = G.round_to_bf16_bits(np.nan_to_num(rf["o"]))
+    lse32 = rf["lse"].astype(np.float32)
+    o_in = bf16_tensor(o_bits, dev)
+    lse_in = torch.from_numpy(lse32).to(dev)
+    if fwd_blocks is not None:
+        og, lg = mala.mala_fwd(q, k, v, tau, Bq, Bk)
+        rows = torch.from_numpy(_rows_of_blocks(fwd_blocks, B, Hq, L, Bq)).to(dev)
+        lse_in = torch.where(rows, lse_in, lg)
+        o_in = torch.where(rows.permute(0, 2, 1)[..., None], o_in, og)
+    bst = mala.make_stats(B, Hq, L, Bq, Bk, dev)
+    dq, dk, dv = mala.mala_bwd(q, k, v, o_in, do, lse_in, tau, Bq, Bk, stats=bst)
+    torch.cuda.synchronize()
+    o_or = G.bf16_bits_to_f64(o_bits)
+    rb = oracle_bwd(f64["q"], f64["k"], f64["v"], o_or, f64["dout"], lse32.astype(np.float64), tau, Bq, Bk,
+                    qunits=qblocks, kunits=ktiles)
+    bkeep = unpack_bits(bst["decision_bits"].cpu().numpy(), nKT)
+    dec = compare_decisions(np.where(rb["keep"] == 255, 255, bkeep), rb["keep"], rb["margin"], descending=False)
+    assert dec["nonexempt"] == 0, dec
+    # rows touched by a (near-tie, exempt) decision mismatch are left out of the
+    # gradient comparison: query rows of the block, key rows of the tile
+    vis = rb["keep"] != 255
+    mism = vis & (np.where(vis, bkeep, 0) != np.where(vis, rb["keep"], 0))
+    qbad = np.zeros((B, L, Hq, 1), bool)
+    kbad = np.zeros((B, L, Hkv, 1), bool)
+    Gq = Hq // Hkv
+    for b_, h_, qb_, kt_ in zip(*np.nonzero(mism)):
+        qbad[b_, qb_ * Bq:(qb_ + 1) * Bq, h_] = True
+        kbad[b_, kt_ * Bk:(kt_ + 1) * Bk, h_ // Gq] = True
+    res = {}
+    scale = 1.0 / np.sqrt(d)
+    qrows = np.moveaxis(~np.isnan(rb["dq"][..., 0]) & ~qbad[..., 0], 1, 2)   # [B, Hq, L]
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        ref = rb[name]
+        got = to_f64(g)
+        m = ~np.isnan(ref) & ~(qbad if name == "dq" else kbad)
+        if name == "dq":
+            rowm = np.moveaxis(qrows, 1, 2)
+        else:   # rows that can see the compared keys: i >= the first compared key
+            jmin = int(np.nonzero(m.any(axis=(0, 2, 3)))[0].min()) if m.any() else 0
+            rowm = np.zeros((B, L, Hq), bool)
+            rowm[:, jmin:, :] = True
+        fl = grad_floors(name, f64["q"], f64["k"], f64["v"], f64["dout"], rowm, scale)
+        res[name] = rel_l2_floored(np.where(m, got, 0.0), np.where(m, ref, 0.0), fl)
+    print("grad errors", {n: res[n] for n in ("dq", "dk", "dv")}, flush=True)
+    for name in ("dq", "dk", "dv"):
+        assert res[name][0] <= GRAD_TOL, (name, res[name])
+    if qblocks is None:
+        kt_g = bst["kept_tiles"].cpu().numpy()
+        clean_blk = ~mism.any(-1)
+        assert np.array_equal(kt_g[clean_blk], (rb["keep"] == 1).sum(-1)[clean_blk])
+        ks_g = bst["kept_slots"].cpu().numpy()
+        ks_o = pins_keymask(rb["keep"], L, Bq, Bk).sum(-1)
+        clean_rows = ~np.moveaxis(qbad[..., 0], 1, 2)
+        assert np.array_equal(ks_g[clean_rows], ks_o[clean_rows])
+    res["bwd_keep_frac"] = float((bkeep == 1).sum() / max(1, (rb["keep"] != 255).sum()))
+    res["dec"] = dec
+    return res
+
+
+def pins_keymask(keep, L, Bq, Bk):
+    import pins
+    return pins.keep_to_keymask(keep, L, Bq, Bk)
+
+
+def test_bwd_chain_fwd_to_bwd_dv_and_nesting():
+    """GPU forward -> GPU backward against oracle forward -> oracle backward.
+    dV is well conditioned in O and is checked to the gradient tolerance; the
+    backward's decisions are checked with forward mismatches as cascades, and
+    the GPU's backward keeps no tile its own forward skipped."""
+    dev = _dev()
+    inp = G.attn_inputs(950, 1, 1100, 4, 2, 128, 0.1, diffuse_kv_heads=(1,))
+    B, L, Hq, d = inp["q"].shape
+    nKT = -(-L // 64)
+    q, k, v, do = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v", "dout"))
+    fst = mala.make_stats(B, Hq, L, 128, 64, dev)
+    o, lse = mala.mala_fwd(q, k, v, 1.0, stats=fst)
+    bst = mala.make_stats(B, Hq, L, 128, 64, dev)
+    dq, dk, dv = mala.mala_bwd(q, k, v, o, do, lse, 1.0, stats=bst)
+    torch.cuda.synchronize()
+    f64 = {x: G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")}
+    rf = oracle_fwd(f64["q"], f64["k"], f64["v"], 1.0, 128, 64)
+    rb = oracle_bwd(f64["q"], f64["k"], f64["v"], rf["o"], f64["dout"], rf["lse"], 1.0, 128, 64)
+    fkeep = unpack_bits(fst["decision_bits"].cpu().numpy(), nKT)
+    bkeep = unpack_bits(bst["decision_bits"].cpu().numpy(), nKT)
+    vis = rf["keep"] != 255
+    fbad = (np.where(vis, fkeep, 0) != np.where(vis, rf["keep"], 0)).any(-1)
+    dec = compare_decisions(np.where(vis, bkeep, 255), rb["keep"], rb["margin"], descending=False,
+                            cascade_prefix=fbad)
+    assert dec["nonexempt"] == 0, dec
+    assert not np.any((bkeep == 1) & (fkeep == 0) & vis)
+    worst, glob = rel_l2_per_head(to_f64(dv), rb["dv"])
+    assert worst <= GRAD_TOL, (worst, glob)
+    print("chain dq/dk errors (ill-conditioned in bf16 O):",
+          rel_l2_per_head(to_f64(dq), rb["dq"]), rel_l2_per_head(to_f64(dk), rb["dk"]))
+
+
+@pytest.mark.parametrize("tau", [0.0, 1.0])
+def test_bwd_tiny_512(tau):
+    w = G.WORKLOADS["tiny_512"]
+    print(run_bwd_case(G.workload_inputs("tiny_512"), tau, w["Bq"], w["Bk"], label="tiny_512"))
+
+
+@pytest.mark.parametrize("L", [1, 77, 129, 1000])
+@pytest.mark.parametrize("tau", [0.0, 0.25, 1.0, 4.0])
+def test_bwd_ragged_gqa(L, tau):
+    inp = G.attn_inputs(700 + L, 2, L, 6, 2, 128, 0.1, diffuse_kv_heads=(1,))
+    run_bwd_case(inp, tau, 128, 64, label=f"ragged L={L}")
+
+
+@pytest.mark.parametrize("L", [64, 200])
+def test_bwd_d64(L):
+    inp = G.attn_inputs(800 + L, 1, L, 4, 2, 64, 0.2)
+    run_bwd_case(inp, 1.0, 64, 64, label=f"d64 L={L}")
+
+
+def test_bwd_gqa_8k():
+    w = G.WORKLOADS["gqa_8k"]
+    print(run_bwd_case(G.workload_inputs("gqa_8k"), 1.0, w["Bq"], w["Bk"], label="gqa_8k"))
+
+
+def test_bwd_train_128k_sampled():
+    """Full-size launch; dq checked on sampled query blocks, dk/dv on the last key tiles."""
+    w = G.WORKLOADS["train_128k"]
+    inp = G.workload_inputs("train_128k")
+    nQB, nKT = 131072 // 128, 131072 // 64
+    qblocks = [h * nQB + qb for h, qb in ((0, nQB - 1), (2, nQB - 1), (4, nQB - 2), (1, 700))]
+    ktiles = [nKT - 1, nKT - 2, nKT - 3]
+    print(run_bwd_case(inp, 1.0, w["Bq"], w["Bk"], qblocks=qblocks, ktiles=ktiles, label="train_128k sampled"))
+
+
+def test_bwd_workspace_reuse_and_determinism_of_decisions():
+    dev = _dev()
+    inp = G.attn_inputs(900, 1, 1500, 4, 2, 128, 0.1)
+    q, k, v, do = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v", "dout"))
+    o, lse = mala.mala_fwd(q, k, v, 1.0)
+    ws = mala.bwd_workspace(1, 1500, 4, 2, 128, device=dev)
+    s1 = mala.make_stats(1, 4, 1500, 128, 64, dev)
+    s2 = mala.make_stats(1, 4, 1500, 128, 64, dev)
+    g1 = mala.mala_bwd(q, k, v, o, do, lse, 1.0, ws=ws, stats=s1)
+    g1 = [t.clone() for t in g1]
+    g2 = mala.mala_bwd(q, k, v, o, do, lse, 1.0, ws=ws, stats=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1["decision_bits"], s2["decision_bits"])
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])   # dk, dv: no atomics
+    assert (g1[0].float() - g2[0].float()).abs().max().item() <= 1e-2  # dq: atomic order
