@@ -64,7 +64,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mala_bwd.restype = I
     lib.mala_decode_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.mala_decode_workspace_size.restype = S
-    lib.mala_decode.argtypes = [P, MalaT4, MalaT4, I, I, I, I, I, F, I, P, P, P, P, S, P]
+    lib.mala_decode.argtypes = [P, MalaT4, MalaT4, I, I, I, I, I, F, I, P, P, P, P, P, S, P]
     lib.mala_decode.restype = I
     lib.mala_status_string.argtypes = [I]
     lib.mala_status_string.restype = ctypes.c_char_p
@@ -176,9 +176,12 @@ def decode_workspace(B, N, Hq, Hkv, d, Bk_dec=64, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, lse=None, kept_tiles=None, ws=None):
+def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, lse=None, kept_tiles=None, ws=None,
+                decision_bits=None):
     """Decode one token.  q [B,Hq,d] bf16 contiguous; caches [B,N,Hkv,d] bf16.
-    Returns (o [B,Hq,d] bf16, lse [B,Hq] fp32, kept_tiles [B,Hkv] int32)."""
+    Returns (o [B,Hq,d] bf16, lse [B,Hq] fp32, kept_tiles [B,Hkv] int32).
+    decision_bits: optional int32 tensor [B, Hkv, ceil(nT/32)] filled with the
+    per-tile keep bits."""
     _dev_check(q, kcache, vcache)
     B, Hq, d = q.shape
     N, Hkv = kcache.shape[1], kcache.shape[2]
@@ -191,7 +194,7 @@ def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, l
         ws = decode_workspace(B, N, Hq, Hkv, d, Bk_dec, q.device)
     lib = load_library()
     rc = lib.mala_decode(_ptr(q), _t4(kcache), _t4(vcache), B, N, Hq, Hkv, d, float(tau), Bk_dec,
-                         _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(ws), ws.numel(), _stream(q))
+                         _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits), _ptr(ws), ws.numel(), _stream(q))
     _check("mala_decode", rc)
     return o, lse, kept_tiles
 

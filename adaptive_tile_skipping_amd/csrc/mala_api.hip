@@ -49,6 +49,20 @@ int pick_chunk(int Hq, int Hkv) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Decode splits per (sequence, KV head): enough workgroups (~2048) to keep
+// many cache loads in flight, never more than the cache has tiles.
+void decode_split(int B, int Hkv, int nT, int* nsplit, int* tps) {
+    const int ngrp = B * Hkv;
+    int ns = (2048 + ngrp - 1) / ngrp;
+    if (ns > 512) ns = 512;
+    if (ns > nT) ns = nT;
+    if (ns < 1) ns = 1;
+    int t = (nT + ns - 1) / ns;
+    ns = (nT + t - 1) / t;
+    *nsplit = ns;
+    *tps = t;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,7 +178,9 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
     const int G = Hq / Hkv;
     const size_t nT = (size_t)(N + Bk_dec - 1) / Bk_dec;
     const size_t grp = (size_t)B * Hkv;
-    const size_t nsplit = 64;
+    int ns, tps;
+    decode_split(B, Hkv, (int)nT, &ns, &tps);
+    const size_t nsplit = (size_t)ns;
     size_t s = 0;
     s += 2 * align256(grp * G * nT * sizeof(float));          // tmax, tsum
     s += align256(grp * G * (size_t)N * sizeof(float));       // spill
@@ -178,7 +194,7 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
 
 mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
                         int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
-                        void* ws, size_t ws_bytes, void* stream) {
+                        uint32_t* decision_bits, void* ws, size_t ws_bytes, void* stream) {
     if (!dims_ok(B, N, Hq, Hkv, d) || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
     if (!q || !aligned16(q) || !o || !aligned16(o) || !lse) return MALA_ERR_INVALID_ARG;
     if (!t4_ok(kcache, true) || !t4_ok(vcache, true)) return MALA_ERR_INVALID_ARG;
@@ -190,15 +206,13 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
     DecParams p;
     memset(&p, 0, sizeof(p));
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)kcache.ptr; p.v = (const uint16_t*)vcache.ptr;
-    p.o = (uint16_t*)o; p.lse = lse; p.kept_tiles = kept_tiles;
+    p.o = (uint16_t*)o; p.lse = lse; p.kept_tiles = kept_tiles; p.bits = decision_bits;
     p.k_sb = kcache.sb; p.k_sl = kcache.sl; p.k_sh = kcache.sh;
     p.v_sb = vcache.sb; p.v_sl = vcache.sl; p.v_sh = vcache.sh;
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
     p.nT = (N + Bk_dec - 1) / Bk_dec;
-    p.nsplit = 64;
-    if (p.nsplit > p.nT) p.nsplit = p.nT;
-    p.tiles_per_split = (p.nT + p.nsplit - 1) / p.nsplit;
-    p.nsplit = (p.nT + p.tiles_per_split - 1) / p.tiles_per_split;
+    p.nwords = (p.nT + 31) / 32;
+    decode_split(B, Hkv, p.nT, &p.nsplit, &p.tiles_per_split);
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     p.log2_tau = log2_tau(tau);
     p.log2_N = (float)log2((double)N);
@@ -210,7 +224,7 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
     p.klist = (int32_t*)w; w += align256(grp * nT * sizeof(int32_t));
     p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));
     p.lse2 = (float*)w; w += align256(grp * G * sizeof(float));
-    p.part_o = (float*)w; w += align256(grp * 64 * G * d * sizeof(float));
+    p.part_o = (float*)w; w += align256(grp * (size_t)p.nsplit * G * d * sizeof(float));
     p.part_ml = (float*)w;
     hipError_t e = launch_decode(p, d, Bk_dec, tau == 0.f, (hipStream_t)stream);
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;

@@ -57,6 +57,8 @@ struct DecParams {
     uint16_t* o;            // [B, Hq, d]
     float* lse;             // [B, Hq]
     int32_t* kept_tiles;    // [B, Hkv] or null
+    uint32_t* bits;         // [B, Hkv, nwords] or null
+    int nwords;
     int64_t k_sb, k_sl, k_sh, v_sb, v_sl, v_sh;
     int B, N, Hq, Hkv, G, nT, nsplit, tiles_per_split;
     float scale_log2;

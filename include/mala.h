@@ -122,7 +122,9 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
  *   q [B, Hq, d] bf16 contiguous; kcache, vcache [B, N, Hkv, d] bf16 (mala_t4
  *   with L = N).  o [B, Hq, d] bf16 output; lse [B, Hq] fp32 output.
  *   kept_tiles: NULL or [B, Hkv] int32 output, retained cache tiles per
- *   (sequence, KV head).  ws: device workspace of at least
+ *   (sequence, KV head).  decision_bits: NULL or [B, Hkv, ceil(nT/32)] uint32
+ *   output, nT = ceil(N / Bk_dec): bit (t % 32) of word t / 32 is 1 iff cache
+ *   tile t was retained.  ws: device workspace of at least
  *   mala_decode_workspace_size(...) bytes, 256-byte aligned.
  * The decision block is the group of Hq/Hkv q heads sharing a KV head, all
  * with L_i = N; cache tiles of Bk_dec keys are visited newest first (same
@@ -130,7 +132,7 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
  * tolerance governs everything"). */
 mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
                         int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
-                        void* ws, size_t ws_bytes, void* stream);
+                        uint32_t* decision_bits, void* ws, size_t ws_bytes, void* stream);
 
 /* Static string naming a status code. */
 const char* mala_status_string(mala_status s);

@@ -96,7 +96,7 @@ def test_decode_workspace_and_errors():
     assert lib.mala_decode_workspace_size(8, 131072, 5, 1, 128, 32) == 0
     t = _t4()
     q = ctypes.c_void_p(4096)
-    base = [q, t, t, 2, 1000, 4, 2, 128, 1.0, 64, ctypes.c_void_p(8192), ctypes.c_void_p(12288), None]
+    base = [q, t, t, 2, 1000, 4, 2, 128, 1.0, 64, ctypes.c_void_p(8192), ctypes.c_void_p(12288), None, None]
     assert lib.mala_decode(*base, None, 0, None) == mala.MALA_ERR_WORKSPACE
     bad = list(base)
     bad[8] = float("nan")
