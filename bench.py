@@ -1,0 +1,252 @@
+"""Benchmark of the MALA hot path on one MI355X.
+
+One step = one pass of the whole path on synthetic inputs resident in HBM:
+  * training forward + backward at 128K tokens (B=1, Hq=5, Hkv=1, d=128 --
+    one GPU's share of a 40q/8kv-head model split 8 ways by heads), tau = 1,
+  * one decode step of 8 sequences against a 131072-token cache (Hq=5,
+    Hkv=1, d=128), tau = 1.
+`value` is the dense-equivalent throughput of the step: the FLOPs dense causal
+attention would execute for the same outputs (forward 4d per legal query-key
+pair, backward 10d, decode 4d per cached key and head) divided by the
+measured step time.  The same kernels at tau = 0 (the dense path) are timed in
+the same run for the speedups, the dominant kernel's roofline is measured live
+with HIP events on the launch stream, and the fp64 oracle is timed on a
+bounded sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tau0]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MALA fwd/bwd ms + effective TFLOP/s at 128K (1 GPU share), decode ms vs τ=0"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tau", type=float, default=1.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison")
+    ap.add_argument("--cpu-blocks", type=int, default=8, help="query blocks per head in the CPU sample")
+    return ap.parse_args()
+
+
+def legal_pairs_block(L, Bq, qb):
+    r0, r1 = qb * Bq, min(L, qb * Bq + Bq)
+    return sum(i + 1 for i in range(r0, r1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(the attention operator shards by heads with no communication; run one process per GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import adaptive_tile_skipping_amd as mala
+    import mala_gen as G
+
+    dev = torch.device("cuda:0")
+    torch.cuda.init()
+    tau = args.tau
+    W = G.WORKLOADS["train_128k"]
+    B, L, Hq, Hkv, d, Bq, Bk = W["B"], W["L"], W["Hq"], W["Hkv"], W["d"], W["Bq"], W["Bk"]
+    WD = G.WORKLOADS["decode_128k"]
+    DB, DN, DHq, DHkv, Dd = WD["B"], WD["N"], WD["Hq"], WD["Hkv"], WD["d"]
+
+    t_gen = time.time()
+    inp = G.workload_inputs("train_128k")
+    dinp = G.workload_inputs("decode_128k")
+
+    def tens(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (tens(inp[x]) for x in ("q", "k", "v", "dout"))
+    qd, kc, vc = (tens(dinp[x]) for x in ("q", "k", "v"))
+    t_gen = time.time() - t_gen
+
+    # preallocated outputs and workspaces: the timed step allocates nothing
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bws = mala.bwd_workspace(B, L, Hq, Hkv, d, Bq, Bk, dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((DB, DHq), dtype=torch.float32, device=dev)
+    keptd = torch.empty((DB, DHkv), dtype=torch.int32, device=dev)
+    dws = mala.decode_workspace(DB, DN, DHq, DHkv, Dd, 64, dev)
+
+    def fwd(t):
+        mala.mala_fwd(q, k, v, t, Bq, Bk, o=o, lse=lse)
+
+    def bwd(t):
+        mala.mala_bwd(q, k, v, o, do, lse, t, Bq, Bk, dq=dq, dk=dk, dv=dv, ws=bws)
+
+    def dec(t):
+        mala.mala_decode(qd, kc, vc, t, 64, o=od, lse=lsed, kept_tiles=keptd, ws=dws)
+
+    def timed_steps(t, steps, warmup):
+        for _ in range(warmup):
+            fwd(t); bwd(t); dec(t)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s in range(steps):
+            ev[s][0].record(); fwd(t)
+            ev[s][1].record(); bwd(t)
+            ev[s][2].record(); dec(t)
+            ev[s][3].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        dd = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+        return wall, f, b, dd
+
+    ms_step, fwd_ms, bwd_ms, dec_ms = timed_steps(tau, args.steps, args.warmup)
+    print(f"# tau={tau}: step {ms_step:.3f} ms (fwd {fwd_ms:.3f}, bwd {bwd_ms:.3f}, decode {dec_ms * 1e3:.1f} us)",
+          file=sys.stderr, flush=True)
+
+    # decode alone with the caches flushed from the 256 MB Infinity Cache
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+
+    def dec_flushed(t, n=10):
+        times = []
+        for _ in range(n + 2):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(); dec(t); e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times[2:]))
+
+    dec_us = dec_flushed(tau) * 1e3
+    res0 = None
+    if not args.no_tau0:
+        ms0, f0, b0, _ = timed_steps(0.0, max(2, min(args.steps, 3)), 1)
+        d0 = dec_flushed(0.0) * 1e3
+        res0 = dict(ms_per_step=ms0, fwd_ms=f0, bwd_ms=b0, decode_us=d0)
+        print(f"# tau=0: step {ms0:.3f} ms (fwd {f0:.3f}, bwd {b0:.3f}, decode {d0:.1f} us)",
+              file=sys.stderr, flush=True)
+
+    # ---- decision statistics of the benchmarked step (untimed)
+    fst = mala.make_stats(B, Hq, L, Bq, Bk, dev)
+    mala.mala_fwd(q, k, v, tau, Bq, Bk, o=o, lse=lse, stats=fst)
+    bst = mala.make_stats(B, Hq, L, Bq, Bk, dev)
+    mala.mala_bwd(q, k, v, o, do, lse, tau, Bq, Bk, dq=dq, dk=dk, dv=dv, ws=bws, stats=bst)
+    mala.mala_decode(qd, kc, vc, tau, 64, o=od, lse=lsed, kept_tiles=keptd, ws=dws)
+    torch.cuda.synchronize()
+    nQB, nKT = -(-L // Bq), -(-L // Bk)
+    visited = np.array([((min(L, qb * Bq + Bq) - 1) // Bk) + 1 for qb in range(nQB)], dtype=np.int64)
+    n_visit = int(visited.sum()) * B * Hq
+    kf = int(fst["kept_tiles"].sum().item())
+    kb = int(bst["kept_tiles"].sum().item())
+    slots_f = float(fst["kept_slots"].double().sum().item())
+    slots_b = float(bst["kept_slots"].double().sum().item())
+    pairs = B * Hq * L * (L + 1) // 2
+    tile_flop = 2.0 * Bq * Bk * d
+    dense_fwd = 4.0 * d * pairs
+    dense_bwd = 10.0 * d * pairs
+    dense_dec = 4.0 * Dd * DN * DHq * DB
+    # algorithmic work of each launch (legal slots only)
+    alg_fwd = 2.0 * d * pairs + 2.0 * d * slots_f
+    alg_bwd = 2.0 * d * pairs + 8.0 * d * slots_b
+    exec_fwd = tile_flop * (n_visit + kf)
+    exec_bwd = tile_flop * (n_visit + 4 * kb)
+    kept_dec = int(keptd.sum().item())
+    nT = -(-DN // 64)
+    dec_bytes = DB * DN * DHkv * Dd * 2 + kept_dec * 64 * Dd * 2      # all of K + the kept V tiles
+    dec_bytes0 = 2 * DB * DN * DHkv * Dd * 2
+
+    value = (dense_fwd + dense_bwd + dense_dec) / (ms_step * 1e-3) / 1e12
+
+    # ---- roofline of the dominant kernel (by measured time)
+    cand = {"mala_fwd_kernel": (fwd_ms, alg_fwd), "mala_bwd (pre+main+convert)": (bwd_ms, alg_bwd)}
+    dom = max(cand, key=lambda n: cand[n][0])
+    dms, dflop = cand[dom]
+    achieved = dflop / (dms * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_tflop_per_launch": round(dflop / 1e12, 3), "launch_ms": round(dms, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "train_128k fwd+bwd (B=1 L=131072 Hq=5 Hkv=1 d=128 Bq=128 Bk=64) + "
+                               "decode_128k (B=8 N=131072 Hq=5 Hkv=1 d=128 Bk_dec=64)",
+                   "tau": tau},
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "decode_us_in_step": round(dec_ms * 1e3, 2),
+        "decode_us": round(dec_us, 2),
+        "decode_tokens_per_s": round(DB / (dec_us * 1e-6), 1),
+        "decode_hbm_gbs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
+        "effective_tflops": {"fwd": round(dense_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+                             "bwd": round(dense_bwd / (bwd_ms * 1e-3) / 1e12, 2)},
+        "executed_tflops": {"fwd": round(exec_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+                            "bwd": round(exec_bwd / (bwd_ms * 1e-3) / 1e12, 2)},
+        "skip": {"fwd_kept_tile_frac": round(kf / n_visit, 4), "bwd_kept_tile_frac": round(kb / n_visit, 4),
+                 "decode_kept_tile_frac": round(kept_dec / (DB * DHkv * nT), 4)},
+        "slots_per_query": {"fwd": round(slots_f / (B * Hq * L), 1), "bwd": round(slots_b / (B * Hq * L), 1)},
+        "roofline": roofline,
+        "gen_s": round(t_gen, 1),
+    }
+    if res0 is not None:
+        out["tau0"] = {k2: round(v2, 4) for k2, v2 in res0.items()}
+        out["tau0"]["decode_hbm_gbs"] = round(dec_bytes0 / (res0["decode_us"] * 1e-6) / 1e9, 1)
+        out["speedup_vs_tau0"] = {"fwd": round(res0["fwd_ms"] / fwd_ms, 3), "bwd": round(res0["bwd_ms"] / bwd_ms, 3),
+                                  "decode": round(res0["decode_us"] / dec_us, 3),
+                                  "step": round(res0["ms_per_step"] / ms_step, 3)}
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
+    if not args.no_cpu:
+        from oracle import oracle_bwd, oracle_fwd, oracle_threads
+        f64 = {x: G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")}
+        nb = max(1, args.cpu_blocks)
+        qbs = [int((j + 0.5) * nQB / nb) for j in range(nb)]
+        blocks = [h * nQB + qb for h in range(Hq) for qb in qbs]
+        pairs_s = sum(legal_pairs_block(L, Bq, qb) for qb in qbs) * Hq
+        t0 = time.perf_counter()
+        rf = oracle_fwd(f64["q"], f64["k"], f64["v"], tau, Bq, Bk, blocks=blocks)
+        oracle_bwd(f64["q"], f64["k"], f64["v"], rf["o"], f64["dout"], rf["lse"], tau, Bq, Bk,
+                   qunits=blocks, do_dkdv=False)
+        tcpu = time.perf_counter() - t0
+        credited = (4.0 + 6.0) * d * pairs_s
+        out["cpu_baseline"] = {
+            "value": round(credited / tcpu / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle forward + backward dQ pass on {len(blocks)} query blocks of train_128k "
+                      f"({nb} evenly spaced blocks x {Hq} heads, tau={tau}); credited dense-equivalent "
+                      f"4d (forward) + 6d (S, dP, dQ) FLOPs per legal pair; {tcpu:.1f} s",
+            "seconds": round(tcpu, 2)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
