@@ -37,7 +37,7 @@ class MalaTileStats(ctypes.Structure):
                 ("omitted_mass", ctypes.c_void_p), ("decision_bits", ctypes.c_void_p)]
 
 
-EXPORTS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
+EXPORTS = ("mala_fwd", "mala_fwd_workspace_size", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
            "mala_decode_workspace_size", "mala_status_string", "mala_version")
 
 _lib = None
@@ -54,8 +54,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                            "(python -m adaptive_tile_skipping_amd._build or __graft_entry__.build())")
     lib = ctypes.CDLL(p)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mala_fwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.mala_fwd_workspace_size.restype = S
     lib.mala_fwd.argtypes = [MalaT4, MalaT4, MalaT4, I, I, I, I, I, F, I, I, MalaT4, P,
-                             ctypes.POINTER(MalaTileStats), P]
+                             ctypes.POINTER(MalaTileStats), P, S, P]
     lib.mala_fwd.restype = I
     lib.mala_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.mala_bwd_workspace_size.restype = S
@@ -121,7 +123,15 @@ def make_stats(B: int, Hq: int, L: int, Bq: int, Bk: int, device, omitted: bool 
     return st
 
 
-def mala_fwd(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64, o=None, lse=None, stats: dict | None = None):
+def fwd_workspace(B, L, Hq, Hkv, d, Bq=128, Bk=64, device="cuda"):
+    n = load_library().mala_fwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk)
+    if n == 0:
+        raise MalaError("mala_fwd_workspace_size", MALA_ERR_UNSUPPORTED, "unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mala_fwd(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64, o=None, lse=None, stats: dict | None = None,
+             ws=None):
     """Forward.  q [B,L,Hq,d], k/v [B,L,Hkv,d] bf16 on the GPU.
     Returns (o [B,L,Hq,d] bf16, lse [B,Hq,L] fp32)."""
     _dev_check(q, k, v)
@@ -135,9 +145,11 @@ def mala_fwd(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64, o=None, lse
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
     if not lse.is_contiguous() or lse.dtype != torch.float32:
         raise ValueError("lse must be a contiguous float32 [B, Hq, L] tensor")
+    if ws is None:
+        ws = fwd_workspace(B, L, Hq, Hkv, d, Bq, Bk, q.device)
     lib = load_library()
     rc = lib.mala_fwd(_t4(q), _t4(k), _t4(v), B, L, Hq, Hkv, d, float(tau), Bq, Bk, _t4(o),
-                      _ptr(lse), _stats_struct(stats), _stream(q))
+                      _ptr(lse), _stats_struct(stats), _ptr(ws), ws.numel(), _stream(q))
     _check("mala_fwd", rc)
     return o, lse
 

@@ -80,13 +80,21 @@ const char* mala_status_string(mala_status s) {
 
 const char* mala_version(void) { return "0.1.0 gfx950"; }
 
+size_t mala_fwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk) {
+    if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
+    const size_t Lpad = (size_t)((L + Bk - 1) / Bk) * Bk;
+    return align256((size_t)B * Hkv * Lpad * d * 2);
+}
+
 mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int Hkv, int d,
                      float tau, int Bq, int Bk, mala_t4 o, float* lse,
-                     const mala_tile_stats* stats, void* stream) {
+                     const mala_tile_stats* stats, void* ws, size_t ws_bytes, void* stream) {
     if (!dims_ok(B, L, Hq, Hkv, d) || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
     if (!t4_ok(q, true) || !t4_ok(k, true) || !t4_ok(v, true) || !t4_ok(o, true) || !lse)
         return MALA_ERR_INVALID_ARG;
     if (!fwd_shape_supported(d, Bq, Bk)) return MALA_ERR_UNSUPPORTED;
+    const size_t need = mala_fwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
     FwdParams p;
     memset(&p, 0, sizeof(p));
     p.q = (const uint16_t*)q.ptr; p.k = (const uint16_t*)k.ptr; p.v = (const uint16_t*)v.ptr;
@@ -102,6 +110,8 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     p.log2_tau = log2_tau(tau);
     p.nwords = (p.nKT + 31) / 32;
+    p.vh = (uint16_t*)ws;
+    p.Lpad = p.nKT * Bk;
     bool st = false;
     if (stats) {
         p.kept_tiles = stats->kept_tiles;
@@ -189,6 +199,8 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
     s += align256(grp * G * sizeof(float));                   // lse2
     s += align256(grp * nsplit * G * d * sizeof(float));      // part_o
     s += align256(grp * nsplit * G * 2 * sizeof(float));      // part_ml
+    s += align256(grp * G * d * sizeof(float));               // o_acc
+    s += align256(grp * sizeof(int32_t));                     // done
     return s;
 }
 
@@ -225,7 +237,9 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
     p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));
     p.lse2 = (float*)w; w += align256(grp * G * sizeof(float));
     p.part_o = (float*)w; w += align256(grp * (size_t)p.nsplit * G * d * sizeof(float));
-    p.part_ml = (float*)w;
+    p.part_ml = (float*)w; w += align256(grp * (size_t)p.nsplit * G * 2 * sizeof(float));
+    p.o_acc = (float*)w; w += align256(grp * G * d * sizeof(float));
+    p.done = (int32_t*)w;
     hipError_t e = launch_decode(p, d, Bk_dec, tau == 0.f, (hipStream_t)stream);
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
 }

@@ -10,19 +10,28 @@
 // skipped tile gets no V load and no P.V.
 //
 // Kernels (tau > 0):
-//   mala_dec_score   one wave per (sequence, KV head, tile): S^T = K q^T with
-//                    32x32x16 bf16 MFMAs (the G rows padded to 32 columns),
-//                    per-row tile max and shifted sum, base-2 scores spilled
-//                    to the workspace.  Reads every K byte once: this is the
-//                    HBM-bound score discovery.
-//   mala_dec_decide  one wave per (sequence, KV head): the sequential scan.
-//                    The row state only grows, so a tile that votes skip under
-//                    the current state is skipped; the scan evaluates 64 tiles
-//                    per ballot and jumps to the first keeping lane, costing one
-//                    step per kept tile plus one per 64 tiles.
-//   mala_dec_pv      kept tiles only, split over workgroups: P = 2^(s - lse)
-//                    from the spill, V tile loads, fp32 accumulation.
-//   mala_dec_combine sums the split partials, writes o (bf16) and LSE.
+//   mala_dec_score   one wave per (sequence, KV head, tile).  The K tile is
+//                    copied global -> LDS (every load instruction covers whole
+//                    cache lines; XOR-swizzled 16-byte chunks keep the MFMA
+//                    fragment reads conflict-free), then S^T = K q^T with
+//                    32x32x16 bf16 MFMAs (the G rows padded to 32 columns).
+//                    Writes per-row tile max and shifted sum and the base-2
+//                    scores (spill).  Reads every K byte once: the HBM-bound
+//                    score discovery.
+//   mala_dec_decide  one wave per (sequence, KV head): the sequential rule,
+//                    evaluated 64 tiles per round.  The candidate set is every
+//                    tile that votes keep under the state at the start of the
+//                    round; an exact log-sum-exp prefix scan gives each tile the
+//                    retained mass it would see if all earlier candidates are
+//                    kept.  Candidates that still vote keep up to the first one
+//                    that flips to skip are final (their prefixes were exact);
+//                    the flipped tile is skipped and the next round starts after
+//                    it.  A tile that votes skip under a smaller retained mass
+//                    can never turn to keep, so non-candidates are final too.
+//   mala_dec_pv      kept tiles only, 4 per round per workgroup: P = 2^(s - lse)
+//                    from the spill, V tile loads issued before P is ready,
+//                    fp32 accumulation, atomics into an fp32 output; the last
+//                    workgroup of a (sequence, KV head) writes o in bf16.
 // tau = 0 keeps every tile, so the scan is elided: mala_dec_dense is a fused
 // split-K decode (scores, online softmax and P.V per split) and
 // mala_dec_dense_combine merges the splits.
@@ -33,46 +42,66 @@ namespace mala {
 
 namespace {
 constexpr int BKD = 64;
-constexpr int GMAX = 16;
+
+// (max, shifted sum) log-sum-exp pairs in base 2: combine is associative.
+__device__ __forceinline__ void lse_combine(float& m, float& l, float m2, float l2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == kNegInf) return;                 // both empty
+    l = l * fast_exp2(m - mn) + l2 * fast_exp2(m2 - mn);
+    m = mn;
+}
 }  // namespace
 
-// q fragments for S^T = K q^T: B operand column = row g (lanes g < G), d in a
-// permuted order: lane half hi, step st covers d = (D/2)*hi + 8*st .. +8, which
-// lets each lane read one contiguous run of its key row.
+// Stages one 64-key tile into this wave's LDS slice [64][D] with 16-byte chunk
+// c of row r stored at chunk c ^ (r % (D/8)).  Rows past N repeat row N-1.
+template <int D>
+__device__ __forceinline__ void stage_k_tile(const DecParams& p, int b, int kh, int t, uint16_t* slice) {
+    constexpr int QCH = D / 8;
+    const int lane = threadIdx.x & 63;
+    const uint16_t* kb = p.k + b * p.k_sb + kh * p.k_sh;
+#pragma unroll
+    for (int n = 0; n < QCH; ++n) {
+        const int slot = 64 * n + lane;
+        const int r = slot / QCH, pc = slot % QCH;
+        const int c = pc ^ (r % QCH);
+        int j = t * BKD + r;
+        j = j < p.N ? j : p.N - 1;
+        load16_to_lds(kb + (int64_t)j * p.k_sl + 8 * c, reinterpret_cast<unsigned char*>(slice) + 1024 * n);
+    }
+}
+
+// q fragments (B operand: column g = lane%32 for g < G, d = 16 st + 8 hi ..).
 template <int D>
 __device__ __forceinline__ void load_q_frags(const DecParams& p, int b, int kh, bf16x8* qf) {
-    constexpr int ST = D / 16;
     const int lane = threadIdx.x & 63;
     const int g = lane & 31, hi = lane >> 5;
     const bool ok = g < p.G;
-    const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + kh * p.G + (ok ? g : 0)) * D + (D / 2) * hi;
+    const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + kh * p.G + (ok ? g : 0)) * D;
 #pragma unroll
-    for (int st = 0; st < ST; ++st) {
-        const u32x4 x = ok ? *(const u32x4*)(qrow + 8 * st) : u32x4{0, 0, 0, 0};
+    for (int st = 0; st < D / 16; ++st) {
+        const u32x4 x = ok ? *(const u32x4*)(qrow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
         qf[st] = __builtin_bit_cast(bf16x8, x);
     }
 }
 
-// Scores of one 64-key tile for the wave: s[sub][r] is row g = lane%32, key
-// 32*sub + 8(r/4) + 4*hi + r%4, base 2, -inf past N.
+// Scores of the staged tile: s[sub][r] is row g = lane%32, key
+// 32 sub + 8(r/4) + 4 hi + r%4, base 2, -inf past N.
 template <int D>
-__device__ __forceinline__ void tile_scores(const DecParams& p, int b, int kh, int t, const bf16x8* qf,
+__device__ __forceinline__ void tile_scores(const DecParams& p, int t, const uint16_t* slice, const bf16x8* qf,
                                             f32x16* s) {
-    constexpr int ST = D / 16;
+    constexpr int QCH = D / 8;
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, hi = lane >> 5;
-    const uint16_t* kb = p.k + b * p.k_sb + kh * p.k_sh;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-        int j = t * BKD + 32 * sub + l32;
-        j = j < p.N ? j : p.N - 1;
-        const uint16_t* kr = kb + (int64_t)j * p.k_sl + (D / 2) * hi;
-        u32x4 kx[ST];
-#pragma unroll
-        for (int st = 0; st < ST; ++st) kx[st] = *(const u32x4*)(kr + 8 * st);
+        const int row = 32 * sub + l32;
         s[sub] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < ST; ++st) s[sub] = mfma32x32x16(__builtin_bit_cast(bf16x8, kx[st]), qf[st], s[sub]);
+        for (int st = 0; st < D / 16; ++st) {
+            const int pc = (2 * st + hi) ^ (row % QCH);
+            const bf16x8 a = *(const bf16x8*)(slice + row * D + 8 * pc);
+            s[sub] = mfma32x32x16(a, qf[st], s[sub]);
+        }
     }
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -85,18 +114,26 @@ __device__ __forceinline__ void tile_scores(const DecParams& p, int b, int kh, i
 
 template <int D>
 __global__ __launch_bounds__(256) void mala_dec_score(const DecParams p) {
-    const int lane = threadIdx.x & 63;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[4][BKD * D];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (task >= p.B * p.Hkv * p.nT) return;
+    const int task = blockIdx.x * 4 + w;
+    if (task >= p.B * p.Hkv * p.nT) return;       // no barriers in this kernel
     const int grp = task / p.nT;
     const int t = task % p.nT;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
+    stage_k_tile<D>(p, b, kh, t, sK[w]);
+    // per-call resets owned by this tile
     if (p.bits && lane == 0 && (t % 32) == 0) p.bits[(int64_t)grp * p.nwords + t / 32] = 0u;
+    if (t == 0) {
+        for (int e = lane; e < p.G * D; e += 64) p.o_acc[(int64_t)grp * p.G * D + e] = 0.f;
+        if (lane == 0) p.done[grp] = 0;
+    }
     bf16x8 qf[D / 16];
     load_q_frags<D>(p, b, kh, qf);
+    __builtin_amdgcn_s_waitcnt(0);                // this wave's tile is in LDS
     f32x16 s[2];
-    tile_scores<D>(p, b, kh, t, qf, s);
+    tile_scores<D>(p, t, sK[w], qf, s);
     float M = kNegInf;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
@@ -133,23 +170,25 @@ __global__ __launch_bounds__(256) void mala_dec_score(const DecParams p) {
     }
 }
 
+template <int GP>
 __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     const int grp = blockIdx.x;
     const int lane = threadIdx.x;
     const int G = p.G;
     const float theta = p.log2_tau - p.log2_N;
-    float m[GMAX], l[GMAX], thr[GMAX];
+    float m[GP], l[GP], thr[GP];          // retained state (identical in all lanes)
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) { m[g] = kNegInf; l[g] = 0.f; thr[g] = kNegInf; }
+    for (int g = 0; g < GP; ++g) { m[g] = kNegInf; l[g] = 0.f; thr[g] = kNegInf; }
     int kept = 0;
     int32_t* klist = p.klist + (int64_t)grp * p.nT;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int nchunk = (p.nT + 63) / 64;
     for (int c = 0; c < nchunk; ++c) {
         const int t = p.nT - 1 - (c * 64 + lane);        // newest first
         const bool valid = t >= 0;
-        float Mg[GMAX], Sg[GMAX];
+        float Mg[GP], Sg[GP];
 #pragma unroll
-        for (int g = 0; g < GMAX; ++g) {
+        for (int g = 0; g < GP; ++g) {
             Mg[g] = kNegInf;
             Sg[g] = 0.f;
             if (g < G && valid) {
@@ -159,34 +198,72 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
         }
         int pos = 0;
         while (pos < 64) {
-            bool vote = false;
-            if (valid && lane >= pos) {
+            const bool active = valid && lane >= pos;
+            bool v0 = false;
 #pragma unroll
-                for (int g = 0; g < GMAX; ++g)
-                    if (g < G) vote |= (l[g] == 0.f) || (Mg[g] >= thr[g]);
-            }
-            const uint64_t mask = __ballot(vote);
-            if (mask == 0ull) break;
-            const int f = __builtin_ctzll(mask);
+            for (int g = 0; g < GP; ++g)
+                if (g < G) v0 |= (l[g] == 0.f) || (Mg[g] >= thr[g]);
+            v0 = v0 && active;
+            const uint64_t K0 = __ballot(v0);
+            if (K0 == 0ull) break;                        // the rest of the chunk is skipped
+            // exclusive prefix (over candidates) of the tile masses, per row
+            float em[GP], el[GP], im[GP], il[GP];
+            bool v1 = false;
 #pragma unroll
-            for (int g = 0; g < GMAX; ++g) {
-                if (g < G) {
-                    const float Mf = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Mg[g]), f));
-                    const float Sf = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, Sg[g]), f));
-                    const float mn = fmaxf(m[g], Mf);
-                    const float a = (m[g] == kNegInf) ? 0.f : fast_exp2(m[g] - mn);
-                    l[g] = l[g] * a + Sf * fast_exp2(Mf - mn);
-                    m[g] = mn;
-                    thr[g] = m[g] + fast_log2(l[g]) + theta;
+            for (int g = 0; g < GP; ++g) {
+                if (g >= G) continue;
+                float xm = v0 ? Mg[g] : kNegInf, xl = v0 ? Sg[g] : 0.f;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const float ym = __shfl_up(xm, off), yl = __shfl_up(xl, off);
+                    if (lane >= off) {
+                        float tm = ym, tl = yl;
+                        lse_combine(tm, tl, xm, xl);
+                        xm = tm; xl = tl;
+                    }
                 }
+                im[g] = xm; il[g] = xl;                    // inclusive
+                float pm = __shfl_up(xm, 1), pl = __shfl_up(xl, 1);
+                if (lane == 0) { pm = kNegInf; pl = 0.f; }
+                em[g] = pm; el[g] = pl;                    // exclusive
+                // retained mass this tile would see: state (+) earlier candidates
+                float zm = m[g], zl = l[g];
+                lse_combine(zm, zl, pm, pl);
+                v1 |= (zl == 0.f) || (Mg[g] - zm - fast_log2(zl) >= theta);
             }
-            if (lane == 0) {
-                const int tk = p.nT - 1 - (c * 64 + f);
-                klist[kept] = tk;
-                if (p.bits) atomicOr(p.bits + (int64_t)grp * p.nwords + tk / 32, 1u << (tk % 32));
+            v1 = v1 && v0;
+            const uint64_t flips = __ballot(v0 && !v1);
+            uint64_t acc;
+            int fsrc;                                      // lane whose prefix is the new state
+            bool exclusive;
+            if (flips == 0ull) {
+                acc = K0;
+                fsrc = 63;
+                exclusive = false;
+            } else {
+                const int f = __builtin_ctzll(flips);
+                acc = K0 & ((f == 0) ? 0ull : (~0ull >> (64 - f)));
+                fsrc = f;
+                exclusive = true;
+                pos = f + 1;
             }
-            ++kept;
-            pos = f + 1;
+            if ((acc >> lane) & 1ull) {
+                const int rank = __builtin_popcountll(acc & lt_mask);
+                klist[kept + rank] = t;
+                if (p.bits) atomicOr(p.bits + (int64_t)grp * p.nwords + t / 32, 1u << (t % 32));
+            }
+            kept += __builtin_popcountll(acc);
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                if (g >= G) continue;
+                const float sm = exclusive ? em[g] : im[g];
+                const float sl = exclusive ? el[g] : il[g];
+                const float nm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sm), fsrc));
+                const float nl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sl), fsrc));
+                lse_combine(m[g], l[g], nm, nl);
+                thr[g] = (l[g] > 0.f) ? m[g] + fast_log2(l[g]) + theta : kNegInf;
+            }
+            if (flips == 0ull) break;
         }
     }
     if (lane == 0) {
@@ -196,7 +273,7 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     if (lane < G) {
         float mm = kNegInf, ll = 0.f;
 #pragma unroll
-        for (int g = 0; g < GMAX; ++g)
+        for (int g = 0; g < GP; ++g)
             if (g == lane) { mm = m[g]; ll = l[g]; }
         const float lz2 = mm + fast_log2(ll);
         p.lse2[(int64_t)grp * G + lane] = lz2;
@@ -205,15 +282,16 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     }
 }
 
-// Thread layout of the P.V phase: dc = tid % (D/8) owns d = 8 dc .. 8 dc + 7,
-// kg = tid / (D/8) owns keys kg*KPT .. of each tile.
-template <int D>
+// P.V thread layout: dc = tid % (D/8) owns d = 8 dc .. 8 dc + 7; kg = tid / (D/8)
+// owns KPT consecutive keys of each round's 256 keys (4 tiles).
+template <int D, int GP>
 __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
     constexpr int DC = D / 8;
-    constexpr int NKG = 256 / DC;          // key groups
-    constexpr int KPT = BKD / NKG;         // keys per thread per tile
-    __shared__ float sP[GMAX][BKD];
+    constexpr int NKG = 256 / DC;
+    constexpr int KPT = 4 * BKD / NKG;
+    __shared__ float sP[GP][4 * BKD];
     __shared__ float sRed[NKG][D];
+    __shared__ int sLast;
     const int tid = threadIdx.x;
     const int s = blockIdx.x, grp = blockIdx.y;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
@@ -223,39 +301,52 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
     const int i0 = s * per;
     const int i1 = (i0 + per < cnt) ? i0 + per : cnt;
     const int dc = tid % DC, kg = tid / DC;
-    float acc[GMAX][8];
+    float acc[GP][8];
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g)
+    for (int g = 0; g < GP; ++g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     const uint16_t* vb = p.v + b * p.v_sb + kh * p.v_sh + 8 * dc;
-    for (int idx = i0; idx < i1; ++idx) {
-        const int t = p.klist[(int64_t)grp * p.nT + idx];
-        for (int e = tid; e < G * BKD; e += 256) {
-            const int g = e / BKD, j = e % BKD;
-            const int key = t * BKD + j;
+    for (int base = i0; base < i1; base += 4) {
+        // V rows first (independent of P), then P for the round's 4 tiles
+        u32x4 vx[KPT];
+        int keys[KPT];
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int jj = kg * KPT + r;                  // 0 .. 255: tile jj/64 of the round
+            const int idx = base + jj / BKD;
+            int key = -1;
+            if (idx < i1) key = p.klist[(int64_t)grp * p.nT + idx] * BKD + jj % BKD;
+            keys[r] = key;
+            const int kk = (key >= 0 && key < p.N) ? key : 0;
+            vx[r] = *(const u32x4*)(vb + (int64_t)kk * p.v_sl);
+        }
+        for (int e = tid; e < G * 4 * BKD; e += 256) {
+            const int g = e / (4 * BKD), jj = e % (4 * BKD);
+            const int idx = base + jj / BKD;
             float pr = 0.f;
-            if (key < p.N)
-                pr = fast_exp2(p.spill[((int64_t)grp * G + g) * p.N + key] - p.lse2[(int64_t)grp * G + g]);
-            sP[g][j] = pr;
+            if (idx < i1) {
+                const int key = p.klist[(int64_t)grp * p.nT + idx] * BKD + jj % BKD;
+                if (key < p.N)
+                    pr = fast_exp2(p.spill[((int64_t)grp * G + g) * p.N + key] - p.lse2[(int64_t)grp * G + g]);
+            }
+            sP[g][jj] = pr;
         }
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            const int j = kg * KPT + r;
-            int key = t * BKD + j;
-            key = key < p.N ? key : p.N - 1;      // P is 0 past N
-            const u32x4 x = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
+            if (keys[r] < 0 || keys[r] >= p.N) continue;
+            const int jj = kg * KPT + r;
             float vv[8];
 #pragma unroll
             for (int m2 = 0; m2 < 4; ++m2) {
-                vv[2 * m2] = __uint_as_float(x[m2] << 16);
-                vv[2 * m2 + 1] = __uint_as_float(x[m2] & 0xFFFF0000u);
+                vv[2 * m2] = __uint_as_float(vx[r][m2] << 16);
+                vv[2 * m2 + 1] = __uint_as_float(vx[r][m2] & 0xFFFF0000u);
             }
 #pragma unroll
-            for (int g = 0; g < GMAX; ++g) {
+            for (int g = 0; g < GP; ++g) {
                 if (g < G) {
-                    const float pr = sP[g][j];
+                    const float pr = sP[g][jj];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc[g][e] += pr * vv[e];
                 }
@@ -263,49 +354,53 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
         }
         __syncthreads();
     }
-    // reduce over key groups, one row at a time
-    float* po = p.part_o + (((int64_t)grp * p.nsplit + s) * G) * D;
-    for (int g = 0; g < G; ++g) {
+    // reduce over key groups, add into the fp32 output accumulator
+    float* oacc = p.o_acc + (int64_t)grp * G * D;
+    if (i0 < i1) {
+        for (int g = 0; g < G; ++g) {
 #pragma unroll
-        for (int gg = 0; gg < GMAX; ++gg)
-            if (gg == g)
+            for (int gg = 0; gg < GP; ++gg)
+                if (gg == g)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sRed[kg][8 * dc + e] = acc[gg][e];
-        __syncthreads();
-        if (tid < D) {
-            float sum = 0.f;
+                    for (int e = 0; e < 8; ++e) sRed[kg][8 * dc + e] = acc[gg][e];
+            __syncthreads();
+            if (tid < D) {
+                float sum = 0.f;
 #pragma unroll
-            for (int k2 = 0; k2 < NKG; ++k2) sum += sRed[k2][tid];
-            po[(int64_t)g * D + tid] = sum;
+                for (int k2 = 0; k2 < NKG; ++k2) sum += sRed[k2][tid];
+                unsafeAtomicAdd(oacc + (int64_t)g * D + tid, sum);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void mala_dec_combine(const DecParams p) {
-    const int grp = blockIdx.x;
-    const int G = p.G;
-    const int b = grp / p.Hkv, kh = grp % p.Hkv;
-    for (int e = threadIdx.x; e < G * D; e += 256) {
-        const int g = e / D, d = e % D;
-        float sum = 0.f;
-        for (int s = 0; s < p.nsplit; ++s) sum += p.part_o[(((int64_t)grp * p.nsplit + s) * G + g) * D + d];
-        p.o[((int64_t)b * p.Hq + kh * G + g) * D + d] = (uint16_t)float_to_bf16_bits(sum);
+    // the last workgroup of the group converts the accumulator to bf16
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sLast = (atomicAdd(p.done + grp, 1) == p.nsplit - 1) ? 1 : 0;
+    __syncthreads();
+    if (sLast) {
+        __threadfence();
+        for (int e = tid; e < G * D; e += 256) {
+            const float x = __hip_atomic_load(oacc + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int g = e / D, d = e % D;
+            p.o[((int64_t)b * p.Hq + kh * G + g) * D + d] = (uint16_t)float_to_bf16_bits(x);
+        }
     }
 }
 
 // tau = 0: fused split-K decode.  Each workgroup owns tiles_per_split tiles of
-// one (sequence, KV head); its 4 waves score 4 tiles at a time, then the whole
-// workgroup runs the online-softmax update and P.V for those 256 keys.
-template <int D>
+// one (sequence, KV head); per round its 4 waves stage and score 4 tiles while
+// every thread's V rows for those tiles are already in flight; then the
+// online-softmax update and P.V for the 256 keys.
+template <int D, int GP>
 __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
     constexpr int DC = D / 8;
     constexpr int NKG = 256 / DC;
-    constexpr int KPT = 4 * BKD / NKG;     // keys per thread per group of 4 tiles
-    __shared__ float sS[GMAX][4 * BKD];
-    __shared__ float sAlpha[GMAX];
-    __shared__ float sState[GMAX][2];      // running max, sum
+    constexpr int KPT = 4 * BKD / NKG;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[4][BKD * D];
+    __shared__ float sS[GP][4 * BKD];
+    __shared__ float sAlpha[GP];
+    __shared__ float sState[GP][2];      // running max, sum (base 2)
     __shared__ float sRed[NKG][D];
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -317,22 +412,30 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
     const int t1 = (t0 + p.tiles_per_split < p.nT) ? t0 + p.tiles_per_split : p.nT;
     bf16x8 qf[D / 16];
     load_q_frags<D>(p, b, kh, qf);
-    if (tid < GMAX) { sState[tid][0] = kNegInf; sState[tid][1] = 0.f; }
+    if (tid < GP) { sState[tid][0] = kNegInf; sState[tid][1] = 0.f; }
     const int dc = tid % DC, kg = tid / DC;
-    float acc[GMAX][8];
+    float acc[GP][8];
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g)
+    for (int g = 0; g < GP; ++g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
     const uint16_t* vb = p.v + b * p.v_sb + kh * p.v_sh + 8 * dc;
     __syncthreads();
     for (int tb = t0; tb < t1; tb += 4) {
-        // ---- scores of tiles tb .. tb+3 (wave w: tile tb + w)
+        const int t = tb + w;
+        if (t < t1) stage_k_tile<D>(p, b, kh, t, sK[w]);
+        u32x4 vx[KPT];
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            int key = tb * BKD + kg * KPT + r;
+            key = (key < t1 * BKD && key < p.N) ? key : 0;
+            vx[r] = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
+        }
         {
-            const int t = tb + w;
             f32x16 sc[2];
             if (t < t1) {
-                tile_scores<D>(p, b, kh, t, qf, sc);
+                __builtin_amdgcn_s_waitcnt(0);
+                tile_scores<D>(p, t, sK[w], qf, sc);
             } else {
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
@@ -348,7 +451,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
             }
         }
         __syncthreads();
-        // ---- online softmax over the 256 new scores: 16 threads per row
+        // online softmax over the 256 new scores: 16 threads per row
         {
             const int g = tid >> 4, part = tid & 15;
             float mx = kNegInf;
@@ -378,28 +481,27 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
             }
         }
         __syncthreads();
-        // ---- P.V over the 4 tiles' keys
 #pragma unroll
-        for (int g = 0; g < GMAX; ++g) {
+        for (int g = 0; g < GP; ++g) {
             if (g < G) {
                 const float a = sAlpha[g];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[g][e] *= a;
             }
         }
+#pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            const int jj = kg * KPT + r;                 // 0 .. 255 within the 4 tiles
-            int key = tb * BKD + jj;
+            const int jj = kg * KPT + r;
+            const int key = tb * BKD + jj;
             if (key >= t1 * BKD || key >= p.N) continue;
-            const u32x4 x = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
             float vv[8];
 #pragma unroll
             for (int m2 = 0; m2 < 4; ++m2) {
-                vv[2 * m2] = __uint_as_float(x[m2] << 16);
-                vv[2 * m2 + 1] = __uint_as_float(x[m2] & 0xFFFF0000u);
+                vv[2 * m2] = __uint_as_float(vx[r][m2] << 16);
+                vv[2 * m2 + 1] = __uint_as_float(vx[r][m2] & 0xFFFF0000u);
             }
 #pragma unroll
-            for (int g = 0; g < GMAX; ++g) {
+            for (int g = 0; g < GP; ++g) {
                 if (g < G) {
                     const float pr = sS[g][jj];
 #pragma unroll
@@ -412,7 +514,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
     float* po = p.part_o + (((int64_t)grp * p.nsplit + s) * G) * D;
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-        for (int gg = 0; gg < GMAX; ++gg)
+        for (int gg = 0; gg < GP; ++gg)
             if (gg == g)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sRed[kg][8 * dc + e] = acc[gg][e];
@@ -431,55 +533,85 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
     }
 }
 
+// One workgroup per (group, row, 32-wide d slice): 8 split classes x 32 d.
 template <int D>
 __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p) {
-    const int grp = blockIdx.x;
+    __shared__ float sM[256];
+    __shared__ float sO[8][32];
+    __shared__ float sL[8];
+    const int tid = threadIdx.x;
+    const int grp = blockIdx.x, g = blockIdx.y, dq = blockIdx.z;
     const int G = p.G;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
-    for (int e = threadIdx.x; e < G * D; e += 256) {
-        const int g = e / D, d = e % D;
-        float M = kNegInf;
-        for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, p.part_ml[(((int64_t)grp * p.nsplit + s) * G + g) * 2]);
-        float lsum = 0.f, osum = 0.f;
-        for (int s = 0; s < p.nsplit; ++s) {
-            const int64_t ix = ((int64_t)grp * p.nsplit + s) * G + g;
-            const float ms = p.part_ml[ix * 2];
-            if (ms == kNegInf) continue;
-            const float a = fast_exp2(ms - M);
-            lsum += p.part_ml[ix * 2 + 1] * a;
-            osum += p.part_o[ix * D + d] * a;
-        }
-        p.o[((int64_t)b * p.Hq + kh * G + g) * D + d] = (uint16_t)float_to_bf16_bits(osum / lsum);
-        if (d == 0) p.lse[(int64_t)b * p.Hq + kh * G + g] = (M + fast_log2(lsum)) * kLn2;
+    const int64_t base = (int64_t)grp * p.nsplit;
+    // global max over splits
+    float mx = kNegInf;
+    for (int s = tid; s < p.nsplit; s += 256) mx = fmaxf(mx, p.part_ml[((base + s) * G + g) * 2]);
+    sM[tid] = mx;
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if (tid < off) sM[tid] = fmaxf(sM[tid], sM[tid + off]);
+        __syncthreads();
     }
-    if (threadIdx.x == 0 && p.kept_tiles) p.kept_tiles[grp] = p.nT;
-    if (p.bits)
-        for (int wd = threadIdx.x; wd < p.nwords; wd += 256) {
-            const int rem = p.nT - 32 * wd;
-            p.bits[(int64_t)grp * p.nwords + wd] = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
-        }
+    const float M = sM[0];
+    const int d = 32 * dq + (tid & 31), cls = tid >> 5;
+    float osum = 0.f, lsum = 0.f;
+#pragma unroll 4
+    for (int s = cls; s < p.nsplit; s += 8) {
+        const int64_t ix = (base + s) * G + g;
+        const float ms = p.part_ml[ix * 2];
+        const float a = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+        osum += p.part_o[ix * D + d] * a;
+        lsum += p.part_ml[ix * 2 + 1] * a;
+    }
+    sO[cls][tid & 31] = osum;
+    if ((tid & 31) == 0) sL[cls] = lsum;
+    __syncthreads();
+    if (tid < 32) {
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { o += sO[c][tid]; l += sL[c]; }
+        p.o[((int64_t)b * p.Hq + kh * G + g) * D + 32 * dq + tid] = (uint16_t)float_to_bf16_bits(o / l);
+        if (dq == 0 && tid == 0) p.lse[(int64_t)b * p.Hq + kh * G + g] = (M + fast_log2(l)) * kLn2;
+    }
+    if (dq == 0 && g == 0) {
+        if (tid == 0 && p.kept_tiles) p.kept_tiles[grp] = p.nT;
+        if (p.bits)
+            for (int wd = tid; wd < p.nwords; wd += 256) {
+                const int rem = p.nT - 32 * wd;
+                p.bits[(int64_t)grp * p.nwords + wd] = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
+            }
+    }
 }
 
-template <int D>
+template <int D, int GP>
 static hipError_t launch_decode_t(const DecParams& p, bool dense, hipStream_t s) {
     const int ngrp = p.B * p.Hkv;
     if (dense) {
-        hipLaunchKernelGGL((mala_dec_dense<D>), dim3(p.nsplit, ngrp), dim3(256), 0, s, p);
-        hipLaunchKernelGGL((mala_dec_dense_combine<D>), dim3(ngrp), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_dense<D, GP>), dim3(p.nsplit, ngrp), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_dense_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     } else {
         const int tasks = ngrp * p.nT;
         hipLaunchKernelGGL((mala_dec_score<D>), dim3((tasks + 3) / 4), dim3(256), 0, s, p);
-        hipLaunchKernelGGL(mala_dec_decide, dim3(ngrp), dim3(64), 0, s, p);
-        hipLaunchKernelGGL((mala_dec_pv<D>), dim3(p.nsplit, ngrp), dim3(256), 0, s, p);
-        hipLaunchKernelGGL((mala_dec_combine<D>), dim3(ngrp), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3(p.nsplit, ngrp), dim3(256), 0, s, p);
     }
     return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_decode_d(const DecParams& p, bool dense, hipStream_t s) {
+    if (p.G <= 1) return launch_decode_t<D, 1>(p, dense, s);
+    if (p.G <= 2) return launch_decode_t<D, 2>(p, dense, s);
+    if (p.G <= 4) return launch_decode_t<D, 4>(p, dense, s);
+    if (p.G <= 8) return launch_decode_t<D, 8>(p, dense, s);
+    return launch_decode_t<D, 16>(p, dense, s);
+}
+
 hipError_t launch_decode(const DecParams& p, int d, int Bkd, bool dense, hipStream_t s) {
-    if (Bkd != BKD || p.G > GMAX) return hipErrorInvalidValue;
-    if (d == 128) return launch_decode_t<128>(p, dense, s);
-    if (d == 64) return launch_decode_t<64>(p, dense, s);
+    if (Bkd != BKD || p.G > 16) return hipErrorInvalidValue;
+    if (d == 128) return launch_decode_d<128>(p, dense, s);
+    if (d == 64) return launch_decode_d<64>(p, dense, s);
     return hipErrorInvalidValue;
 }
 

@@ -81,6 +81,19 @@ __device__ __forceinline__ void load16_to_lds(const void* gptr, void* lds_wave_b
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
+// LDS transposing read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte chunks addressed by lanes
+// 4k + i/4, k = 0..3.  So when lane j of a group addresses row r0 + j/4,
+// columns c0 + 4 (j % 4) .. +3 of a 16-bit matrix, lane i receives rows
+// r0..r0+3 of column c0 + i: four consecutive rows of one column.
+// The result is returned as two dwords (elements 0-1, 2-3).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_elem) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) const uint16_t*)lds_elem));
+    return __builtin_bit_cast(u32x2, x);
+}
+
 // Wait for every outstanding memory operation of this wave (including the
 // global -> LDS copies above), then a workgroup barrier.
 __device__ __forceinline__ void wait_all_then_barrier() {

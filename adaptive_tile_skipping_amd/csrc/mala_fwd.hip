@@ -16,37 +16,67 @@
 // lane holds all scores of one query (16 keys per 32-key subtile, the other 16
 // in lane l^32).  Row reductions are therefore in-lane plus one swap, the
 // block decision is a wave ballot plus an LDS OR, and P^T feeds the next
-// contraction O^T += V^T P^T directly from the score registers.
+// contraction O^T += V^T P^T straight from the score registers.
 //   - Q fragments live in registers for the whole loop.
-//   - K tiles are double-buffered in LDS; the next tile's global loads are
-//     issued before the current tile's MFMAs.
-//   - V tiles are fetched only after the keep decision, transposed on the way
-//     into LDS (positions inside each 16-key group permuted to match the
-//     score-register order) and converted to fp16, exactly for |v| <= 65504.
-//   - P.V runs as an fp16 contraction: P in [0, 1] rounded to nearest fp16
-//     keeps the relative weight error near 3e-4 (bf16 P would cost ~1e-3 on
-//     diffuse rows, as much as the bf16 rounding of O itself).
+//   - K and V tiles move global -> LDS with direct copies (no registers),
+//     16-byte chunks XOR-swizzled per row so the MFMA reads are conflict-free.
+//   - V is read from an fp16 copy made once per call (exact for |v| <= 65504);
+//     its MFMA operand (8 consecutive keys per lane for one d) comes from the
+//     LDS transposing read ds_read_b64_tr_b16.  P.V is an fp16 contraction: P
+//     in [0, 1] rounded to nearest fp16 keeps the relative weight error near
+//     3e-4 (bf16 P would cost ~1e-3 on diffuse rows, as much as the bf16
+//     rounding of O itself).
+//   - Software pipeline: the keep decision of tile t needs only the row
+//     statistics (m, l), not the accumulator, so the P.V of tile t runs one
+//     iteration later; the V copy of tile t therefore overlaps the score MFMAs
+//     of tile t-1, and K(t-2) is fetched while tile t-1 is scored.
+//   - Causal masking only on diagonal (or ragged) tiles; the 1/sqrt(d) scale
+//     is folded into the exponent's FMA; the accumulator is rescaled only when
+//     some row's running max moved.
 #include "mala_device.h"
 #include "mala_internal.h"
 
 namespace mala {
 
+namespace {
+// V copy: bf16 [B, L, Hkv, D] -> fp16 [B, Hkv, Lpad, D], zero rows past L.
+template <int D>
+__global__ __launch_bounds__(256) void mala_v_to_f16(const FwdParams p) {
+    constexpr int CH = D / 8;
+    const int64_t n = (int64_t)p.B * p.Hkv * p.Lpad * CH;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
+        const int c = (int)(idx % CH);
+        const int64_t row = idx / CH;
+        const int j = (int)(row % p.Lpad);
+        const int64_t bk = row / p.Lpad;
+        const int kh = (int)(bk % p.Hkv), b = (int)(bk / p.Hkv);
+        u32x4 o = {0, 0, 0, 0};
+        if (j < p.L) {
+            const u32x4 x = *(const u32x4*)(p.v + b * p.v_sb + (int64_t)j * p.v_sl + kh * p.v_sh + 8 * c);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) o[m] = pack2_f16_from_f32bits(x[m] << 16, x[m] & 0xFFFF0000u);
+        }
+        *(u32x4*)(p.vh + row * D + 8 * c) = o;
+    }
+}
+}  // namespace
+
 template <int D, int BQ, int BK, bool STATS>
-__global__ __launch_bounds__(BQ / 32 * 64) void mala_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(BQ / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mala_fwd_kernel(const FwdParams p) {
     constexpr int NW = BQ / 32;
-    constexpr int NT = NW * 64;
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
-    constexpr int KROW = D + 8;          // padded LDS row of a K tile (elements)
-    constexpr int VROW = BK + 8;         // padded LDS row of a transposed V tile
-    constexpr int KCH = D / 8;           // 16-byte chunks per key row
-    constexpr int KPASS = BK * KCH / NT;
-    constexpr int VPASS = (BK / 4) * KCH / NT;
+    constexpr int QCH = D / 8;                   // 16-byte chunks per row
+    constexpr int TILE_SLOTS = BK * QCH;         // 16-byte chunks per tile
+    constexpr int INST = TILE_SLOTS / (NW * 64); // copies per lane per tile
     static_assert(BK == 64, "tile width");
-    static_assert(KPASS * NT == BK * KCH && VPASS * NT == (BK / 4) * KCH, "load split");
+    static_assert(INST * NW * 64 == TILE_SLOTS, "copy split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
+    // K: [2][BK][D] bf16, chunk c of row r at c ^ (r % QCH)
+    // V: [2][BK][D] fp16, chunk c of row r at c ^ (4 (r % 4)) % QCH
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][BK * D];
     __shared__ int sFlag[2][NW];
 
     const int tid = threadIdx.x;
@@ -70,9 +100,10 @@ __global__ __launch_bounds__(BQ / 32 * 64) void mala_fwd_kernel(const FwdParams 
     const bool valid = i < L;
     const int rend = (i0 + BQ < L) ? i0 + BQ : L;
     const int kt_first = (rend - 1) / BK;
+    const bool ragged = (i0 + BQ > L);
 
     const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh;
-    const uint16_t* vbase = p.v + b * p.v_sb + kh * p.v_sh;
+    const uint16_t* vhbase = p.vh + ((int64_t)b * p.Hkv + kh) * p.Lpad * D;
 
     // ---- Q fragments (B operand: column = query, 8 consecutive d per lane)
     bf16x8 qf[KSTEPS];
@@ -85,57 +116,89 @@ __global__ __launch_bounds__(BQ / 32 * 64) void mala_fwd_kernel(const FwdParams 
         }
     }
 
-    u32x4 kreg[KPASS];
-    auto load_k = [&](int kt) {
+    auto copy_k = [&](int kt, int buf) {
 #pragma unroll
-        for (int ps = 0; ps < KPASS; ++ps) {
-            const int idx = tid + ps * NT;
-            const int r = idx / KCH, c = idx % KCH;
-            const int j = kt * BK + r;
-            kreg[ps] = (j < L) ? *(const u32x4*)(kbase + (int64_t)j * p.k_sl + 8 * c) : u32x4{0, 0, 0, 0};
+        for (int n = 0; n < INST; ++n) {
+            const int slot0 = (n * NW + w) * 64;
+            const int sl = slot0 + lane;
+            const int r = sl / QCH, pc = sl % QCH;
+            const int c = pc ^ (r % QCH);
+            int j = kt * BK + r;
+            j = j < L ? j : L - 1;               // rows past L are masked by causality
+            load16_to_lds(kbase + (int64_t)j * p.k_sl + 8 * c, reinterpret_cast<unsigned char*>(sK[buf]) + slot0 * 16);
         }
     };
-    auto store_k = [&](int buf) {
+    auto copy_v = [&](int kt, int buf) {
 #pragma unroll
-        for (int ps = 0; ps < KPASS; ++ps) {
-            const int idx = tid + ps * NT;
-            const int r = idx / KCH, c = idx % KCH;
-            *(u32x4*)(&sK[buf][r * KROW + 8 * c]) = kreg[ps];
+        for (int n = 0; n < INST; ++n) {
+            const int slot0 = (n * NW + w) * 64;
+            const int sl = slot0 + lane;
+            const int r = sl / QCH, pc = sl % QCH;
+            const int c = pc ^ ((4 * (r & 3)) % QCH);
+            load16_to_lds(vhbase + (int64_t)(kt * BK + r) * D + 8 * c,
+                          reinterpret_cast<unsigned char*>(sV[buf]) + slot0 * 16);
         }
     };
-    u32x4 vreg[VPASS][4];
-    auto load_v = [&](int kt) {
+    // S^T = K Q^T for the tile in sK[buf]; raw (unscaled) scores
+    auto scores = [&](int buf, f32x16* s) {
 #pragma unroll
-        for (int ps = 0; ps < VPASS; ++ps) {
-            const int idx = tid + ps * NT;
-            const int kq = idx % (BK / 4), dc = idx / (BK / 4);
+        for (int sub = 0; sub < 2; ++sub) {
+            const int row = 32 * sub + l32;
+            s[sub] = f32x16{};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = kt * BK + 4 * kq + r;
-                vreg[ps][r] = (j < L) ? *(const u32x4*)(vbase + (int64_t)j * p.v_sl + 8 * dc) : u32x4{0, 0, 0, 0};
+            for (int st = 0; st < KSTEPS; ++st) {
+                const int pc = (2 * st + hi) ^ (row % QCH);
+                const bf16x8 a = *(const bf16x8*)(&sK[buf][row * D + 8 * pc]);
+                s[sub] = mfma32x32x16(a, qf[st], s[sub]);
             }
         }
     };
-    auto store_vt = [&]() {
+    // causal mask (diagonal / ragged tiles) and raw row max
+    auto mask_max = [&](int kt, f32x16* s) -> float {
+        float M = kNegInf;
+        const bool need = ragged || (kt * BK + BK - 1 > i0);
+        if (need) {
+            const int lim = valid ? (i - kt * BK) : -1;
 #pragma unroll
-        for (int ps = 0; ps < VPASS; ++ps) {
-            const int idx = tid + ps * NT;
-            const int kq = idx % (BK / 4), dc = idx / (BK / 4);
-            const int pos = 16 * (kq >> 2) + vt_pos16(4 * (kq & 3));
+            for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t a0 = vreg[ps][0][m], a1 = vreg[ps][1][m];
-                const uint32_t a2 = vreg[ps][2][m], a3 = vreg[ps][3][m];
-                u32x2 lo = {pack2_f16_from_f32bits(a0 << 16, a1 << 16), pack2_f16_from_f32bits(a2 << 16, a3 << 16)};
-                u32x2 hv = {pack2_f16_from_f32bits(a0 & 0xFFFF0000u, a1 & 0xFFFF0000u),
-                            pack2_f16_from_f32bits(a2 & 0xFFFF0000u, a3 & 0xFFFF0000u)};
-                *(u32x2*)(&sV[(8 * dc + 2 * m) * VROW + pos]) = lo;
-                *(u32x2*)(&sV[(8 * dc + 2 * m + 1) * VROW + pos]) = hv;
+                for (int r = 0; r < 16; ++r) {
+                    const int jj = 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    s[sub][r] = (jj <= lim) ? s[sub][r] : kNegInf;
+                }
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) M = fmaxf(M, s[sub][r]);
+        return wave_max_pair(M);
+    };
+    // O^T += V^T P^T with V^T fragments from the transposing LDS read
+    auto pv = [&](int buf, const f16x8* pb, f32x16* acc) {
+        const int j16 = lane & 15;
+        const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x2 half2x[2];
+#pragma unroll
+                for (int rd = 0; rd < 2; ++rd) {
+                    const int row = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
+                    const int col = 32 * dt + dsel;
+                    const int phys = ((col >> 3) ^ ((4 * (row & 3)) % QCH)) * 8 + (col & 7);
+                    half2x[rd] = lds_read_tr16(&sV[buf][0] + row * D + phys);
+                }
+                // whole-dword assembly of the operand (element-wise 16-bit inserts
+                // of the transposed results are not reliable with this compiler)
+                const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
+                acc[dt] = mfma32x32x16_f16(__builtin_bit_cast(f16x8, w4), pb[ks], acc[dt]);
             }
         }
     };
 
     // ---- per-row state (this lane's query; lanes l and l^32 hold identical copies)
+    const float c2 = p.scale_log2;
     float m2 = kNegInf;          // running max of retained base-2 scores
     float lsum = 0.f;            // retained sum, shifted by m2
     float thr = kNegInf;         // cached keep threshold m2 + log2(lsum) + theta
@@ -154,87 +217,71 @@ __global__ __launch_bounds__(BQ / 32 * 64) void mala_fwd_kernel(const FwdParams 
         for (int wd = kt_first / 32 + 1; wd < p.nwords; ++wd) bitrow[wd] = 0u;
     }
 
-    load_k(kt_first);
-    store_k(0);
-    __syncthreads();
+    // ---- prologue
+    copy_k(kt_first, kt_first & 1);
+    if (kt_first >= 1) copy_k(kt_first - 1, (kt_first - 1) & 1);
+    wait_all_then_barrier();
+    f32x16 scur[2];
+    scores(kt_first & 1, scur);
+    float Mraw = mask_max(kt_first, scur);
 
-    for (int it = 0; it <= kt_first; ++it) {
-        const int kt = kt_first - it;
-        const int buf = it & 1;
-        if (kt > 0) load_k(kt - 1);
+    bool pending = false;
+    int pend_buf = 0;
+    float pend_alpha = 1.f;
+    f16x8 pend_p[4];
 
-        // ---- score discovery: S^T = K Q^T for the two 32-key subtiles
-        f32x16 s[2];
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            s[sub] = f32x16{};
-#pragma unroll
-            for (int st = 0; st < KSTEPS; ++st) {
-                const bf16x8 a = *(const bf16x8*)(&sK[buf][(32 * sub + l32) * KROW + 16 * st + 8 * hi]);
-                s[sub] = mfma32x32x16(a, qf[st], s[sub]);
-            }
-        }
-        // scale to base 2 and mask illegal keys (j > i, or invalid row)
-        const int lim = valid ? (i - kt * BK) : -1;   // last legal key offset in the tile
-        float M = kNegInf;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int jj = 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                float x = s[sub][r] * p.scale_log2;
-                x = (jj <= lim) ? x : kNegInf;
-                s[sub][r] = x;
-                M = fmaxf(M, x);
-            }
-        }
-        M = wave_max_pair(M);
-
-        // ---- keep decision
-        const bool has = M > kNegInf;
+    for (int kt = kt_first; kt >= 0; --kt) {
+        const int buf = kt & 1;
+        // ---- keep decision for tile kt (state holds every kept tile > kt)
+        const float M = Mraw * c2;
+        const bool has = Mraw > kNegInf;
         const bool vote = has && (lsum == 0.f || M >= thr);
         const bool wave_any = __ballot(vote) != 0ull;
         if (lane == 0) sFlag[buf][w] = wave_any ? 1 : 0;
-        if (kt > 0) store_k(buf ^ 1);
-        __syncthreads();
+        wait_all_then_barrier();                 // K(kt-1) and V of the pending tile have landed
         bool keep = false;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) keep |= (sFlag[buf][ww] != 0);
 
+        if (keep) copy_v(kt, buf);
+        if (kt >= 2) copy_k(kt - 2, buf);
+
+        f32x16 snext[2];
+        if (kt >= 1) scores(buf ^ 1, snext);
+
+        if (pending) {
+            if (__ballot(pend_alpha != 1.f) != 0ull) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
+            }
+            pv(pend_buf, pend_p, acc);
+        }
+        pending = false;
         if (keep) {
-            load_v(kt);
-            // online-softmax update of this row
+            // online-softmax statistics of this row for tile kt; P for the next iteration
             const float mn = fmaxf(m2, M);
             const float muse = (mn == kNegInf) ? 0.f : mn;
             const float alpha = fast_exp2(m2 - muse);
             float psum = 0.f;
-            f16x8 pb[4];
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(s[sub][r] - muse);
+                    const float e = fast_exp2(__builtin_fmaf(scur[sub][r], c2, -muse));
                     psum += e;
-                    pb[2 * sub + (r >> 3)][r & 7] = to_f16(e);
+                    pend_p[2 * sub + (r >> 3)][r & 7] = to_f16(e);
                 }
             }
             psum = wave_sum_pair(psum);
             lsum = lsum * alpha + psum;
             m2 = mn;
             thr = (lsum > 0.f) ? m2 + fast_log2(lsum) + theta : kNegInf;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-            if (lim >= 0) slots += (lim < BK - 1 ? lim : BK - 1) + 1;
-            store_vt();
-            __syncthreads();
-            // O^T += V^T P^T
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const f16x8 a = *(const f16x8*)(&sV[(32 * dt + l32) * VROW + 16 * ks + 8 * hi]);
-                    acc[dt] = mfma32x32x16_f16(a, pb[ks], acc[dt]);
-                }
+            pend_alpha = alpha;
+            pend_buf = buf;
+            pending = true;
+            if (valid) {
+                const int lim = i - kt * BK;
+                if (lim >= 0) slots += (lim < BK - 1 ? lim : BK - 1) + 1;
             }
             ++kept_count;
             bitword |= 1u << (kt & 31);
@@ -245,7 +292,7 @@ __global__ __launch_bounds__(BQ / 32 * 64) void mala_fwd_kernel(const FwdParams 
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) osum += fast_exp2(s[sub][r] - mn);
+                    for (int r = 0; r < 16; ++r) osum += fast_exp2(__builtin_fmaf(scur[sub][r], c2, -mn));
                 osum = wave_sum_pair(osum);
                 ol = ol * fast_exp2(om - mn) + osum;
                 om = mn;
@@ -255,6 +302,19 @@ __global__ __launch_bounds__(BQ / 32 * 64) void mala_fwd_kernel(const FwdParams 
             bitrow[kt >> 5] = bitword;
             bitword = 0;
         }
+        if (kt >= 1) {
+            scur[0] = snext[0];
+            scur[1] = snext[1];
+            Mraw = mask_max(kt - 1, scur);
+        }
+    }
+    if (pending) {
+        wait_all_then_barrier();
+        if (__ballot(pend_alpha != 1.f) != 0ull) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
+        }
+        pv(pend_buf, pend_p, acc);
     }
 
     // ---- epilogue: O = acc / l, LSE = (m2 + log2 l) ln 2
@@ -290,6 +350,12 @@ __global__ __launch_bounds__(BQ / 32 * 64) void mala_fwd_kernel(const FwdParams 
 template <int D, int BQ, int BK>
 static hipError_t launch_fwd_t(const FwdParams& p, bool stats, hipStream_t s) {
     constexpr int NT = BQ / 32 * 64;
+    {
+        const int64_t n = (int64_t)p.B * p.Hkv * p.Lpad * (D / 8);
+        int g = (int)((n + 255) / 256);
+        if (g > 16384) g = 16384;
+        hipLaunchKernelGGL((mala_v_to_f16<D>), dim3(g), dim3(256), 0, s, p);
+    }
     const int per = 8 * p.chunk;
     const int grid = (p.nunits + per - 1) / per * per;
     if (stats)

@@ -86,6 +86,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fws = mala.fwd_workspace(B, L, Hq, Hkv, d, Bq, Bk, dev)
     bws = mala.bwd_workspace(B, L, Hq, Hkv, d, Bq, Bk, dev)
     od = torch.empty_like(qd)
     lsed = torch.empty((DB, DHq), dtype=torch.float32, device=dev)
@@ -93,7 +94,7 @@ def main():
     dws = mala.decode_workspace(DB, DN, DHq, DHkv, Dd, 64, dev)
 
     def fwd(t):
-        mala.mala_fwd(q, k, v, t, Bq, Bk, o=o, lse=lse)
+        mala.mala_fwd(q, k, v, t, Bq, Bk, o=o, lse=lse, ws=fws)
 
     def bwd(t):
         mala.mala_bwd(q, k, v, o, do, lse, t, Bq, Bk, dq=dq, dk=dk, dv=dv, ws=bws)
@@ -147,7 +148,7 @@ def main():
 
     # ---- decision statistics of the benchmarked step (untimed)
     fst = mala.make_stats(B, Hq, L, Bq, Bk, dev)
-    mala.mala_fwd(q, k, v, tau, Bq, Bk, o=o, lse=lse, stats=fst)
+    mala.mala_fwd(q, k, v, tau, Bq, Bk, o=o, lse=lse, stats=fst, ws=fws)
     bst = mala.make_stats(B, Hq, L, Bq, Bk, dev)
     mala.mala_bwd(q, k, v, o, do, lse, tau, Bq, Bk, dq=dq, dk=dk, dv=dv, ws=bws, stats=bst)
     mala.mala_decode(qd, kc, vc, tau, 64, o=od, lse=lsed, kept_tiles=keptd, ws=dws)

@@ -84,15 +84,20 @@ typedef struct {
     uint32_t* decision_bits;
 } mala_tile_stats;
 
+/* Bytes of device workspace mala_fwd needs (an fp16 copy of V). */
+size_t mala_fwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk);
+
 /* Forward (training forward or prefill), causal, Lq = Lk = L.
  *   q [B, L, Hq, d], k, v [B, L, Hkv, d] bf16 in device memory.
  *   o [B, L, Hq, d] bf16 output; lse [B, Hq, L] fp32 output (contiguous).
  *   stats: NULL or per-call statistics (see mala_tile_stats).
+ *   ws: device workspace of at least mala_fwd_workspace_size(...) bytes,
+ *   256-byte aligned; overwritten by the call.
  * Decision rule: review page "Forward: online sparse softmax"; summary page,
  * forward paragraph. */
 mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int Hkv, int d,
                      float tau, int Bq, int Bk, mala_t4 o, float* lse,
-                     const mala_tile_stats* stats, void* stream);
+                     const mala_tile_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of device workspace mala_bwd needs (fp32 dQ accumulator, row terms). */
 size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk);

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
+    for n in ("mala_fwd", "mala_fwd_workspace_size", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
               "mala_decode_workspace_size", "mala_status_string", "mala_version"):
         assert n in names
 
@@ -49,7 +49,8 @@ def _fwd(**kw):
     a.update(kw)
     lib = mala.load_library()
     return lib.mala_fwd(a["q"], a["k"], a["v"], a["B"], a["L"], a["Hq"], a["Hkv"], a["d"], a["tau"],
-                        a["Bq"], a["Bk"], a["o"], a["lse"], a["stats"], None)
+                        a["Bq"], a["Bk"], a["o"], a["lse"], a["stats"], a.get("ws", ctypes.c_void_p(1 << 20)),
+                        a.get("ws_bytes", 1 << 30), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -66,6 +67,9 @@ def _fwd(**kw):
     (dict(d=96), mala.MALA_ERR_UNSUPPORTED),
     (dict(Bq=64), mala.MALA_ERR_UNSUPPORTED),
     (dict(Bk=128), mala.MALA_ERR_UNSUPPORTED),
+    (dict(ws=None), mala.MALA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), mala.MALA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 64)), mala.MALA_ERR_WORKSPACE),
 ])
 def test_fwd_rejects_bad_arguments(kw, code):
     assert _fwd(**kw) == code
