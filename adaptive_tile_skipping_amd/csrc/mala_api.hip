@@ -128,8 +128,9 @@ size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int
     if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
     const size_t rows = (size_t)B * Hq * L;
     const size_t Lpad = (size_t)((L + Bq - 1) / Bq) * Bq;
+    const size_t prow = (size_t)B * Hq * Lpad;
     const size_t tr = (size_t)B * Hq * d * Lpad * 2;
-    return align256(rows * d * sizeof(float)) + 2 * align256(rows * sizeof(float)) + 2 * align256(tr);
+    return align256(rows * d * sizeof(float)) + 3 * align256(prow * sizeof(float)) + 2 * align256(tr);
 }
 
 mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, const float* lse,
@@ -142,6 +143,8 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
         return MALA_ERR_INVALID_ARG;
     if (bwd_stats && bwd_stats->omitted_mass) return MALA_ERR_INVALID_ARG;
     if (!fwd_shape_supported(d, Bq, Bk)) return MALA_ERR_UNSUPPORTED;
+    // a query block is read through one buffer resource (32-bit byte range)
+    if (((int64_t)Bq * q.sl + d) * 2 > INT32_MAX) return MALA_ERR_UNSUPPORTED;
     const size_t need = mala_bwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk);
     if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
     BwdParams p;
@@ -152,9 +155,11 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     const size_t rows = (size_t)B * Hq * L;
     char* w = (char*)ws;
     p.dq_acc = (float*)w; w += align256(rows * d * sizeof(float));
-    p.rowd = (float*)w; w += align256(rows * sizeof(float));
-    p.rowc = (float*)w; w += align256(rows * sizeof(float));
     p.Lpad = ((L + Bq - 1) / Bq) * Bq;
+    const size_t prow = (size_t)B * Hq * p.Lpad;
+    p.rowd = (float*)w; w += align256(prow * sizeof(float));
+    p.rowc = (float*)w; w += align256(prow * sizeof(float));
+    p.rowt = (float*)w; w += align256(prow * sizeof(float));
     const size_t tr = (size_t)B * Hq * d * p.Lpad * 2;
     p.qt = (uint16_t*)w; w += align256(tr);
     p.dot = (uint16_t*)w;

@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
     const int r0 = rb * PRE_ROWS;
     const int L = p.L;
     const int64_t bh = (int64_t)b * p.Hq + h;
-    // D_i = dO_i . O_i and LSE in base 2 (4 threads per row)
+    // D_i = dO_i . O_i, LSE in base 2 and minus the keep threshold on raw scores
+    // (4 threads per row).  Rows past L get D = 0, LSE = 0 and -inf, so their
+    // scores never vote; with tau = 0 every legal tile is kept and the term is 0.
     {
         const int r = tid >> 2, part = tid & 3;
         const int i = r0 + r;
@@ -72,10 +74,21 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
-        if (part == 0 && i < L) {
-            p.rowd[bh * L + i] = acc;
-            p.rowc[bh * L + i] = p.lse[bh * L + i] * kLog2e;
-            if (p.kept_slots) p.kept_slots[bh * L + i] = 0;
+        if (part == 0) {
+            const int64_t ri = bh * p.Lpad + i;
+            if (i < L) {
+                const float l2 = p.lse[bh * L + i] * kLog2e;
+                p.rowd[ri] = acc;
+                p.rowc[ri] = l2;
+                p.rowt[ri] = (p.log2_tau == kNegInf)
+                                 ? 0.f
+                                 : -(l2 + (p.log2_tau - fast_log2((float)(i + 1)))) / p.scale_log2;
+                if (p.kept_slots) p.kept_slots[bh * L + i] = 0;
+            } else {
+                p.rowd[ri] = 0.f;
+                p.rowc[ri] = 0.f;
+                p.rowt[ri] = kNegInf;
+            }
         }
     }
     // stage Q and dO rows (zeros past L)
@@ -134,16 +147,18 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     constexpr int SROW = BK + 8;         // LDS row of dS [query][key] and K^T [d][key]
     constexpr int QSLOTS = BQ * QCH;     // 16-byte chunks per Q block
     constexpr int QINST = QSLOTS / 256;  // global->LDS copies per lane per block
-    constexpr int QBYTES = 2 * BQ * D * 2;
+    constexpr int NBUF = 3;              // Q blocks in flight: current + two prefetched
+    constexpr int QBYTES = NBUF * BQ * D * 2;
     constexpr int RBYTES = 2 * 2 * DT * 16 * 64 * 4;     // epilogue reduction
     constexpr int UBYTES = QBYTES > RBYTES ? QBYTES : RBYTES;
     static_assert(QINST * 256 == QSLOTS && WSUB >= 1, "shape");
 
-    // Q blocks: [2][BQ][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r % QCH)
+    // Q blocks: [NBUF][BQ][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r % QCH)
     __shared__ __attribute__((aligned(16))) unsigned char sU[UBYTES];
     __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SROW];
     __shared__ __attribute__((aligned(16))) uint16_t sdS[BQ * SROW];
-    __shared__ __attribute__((aligned(16))) float sRow[2][3][BQ];   // [buf][c | lse2 | D][query]
+    // [buf][keep threshold on raw scores | lse2 | D][query]
+    __shared__ __attribute__((aligned(16))) float sRow[NBUF][3][BQ];
     __shared__ int sFlag[2][4];
     uint16_t* sQ = reinterpret_cast<uint16_t*>(sU);
 
@@ -164,6 +179,8 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int L = p.L;
     const int j0 = kt * BK;
     const int G = p.G;
+    const float c2 = p.scale_log2;
+    const bool keep_all = p.log2_tau == kNegInf;   // tau = 0: dense backward
 
     // ---- resident K and V fragments (B operands: column = key, 8 consecutive d)
     const int jme = j0 + 32 * kw + l32;
@@ -200,196 +217,209 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int qb_lo = j0 / BQ;
     const int nqb = p.nQB - qb_lo;
     const int nsteps = G * nqb;
-    const float log2_tau = p.log2_tau;
 
-    float rreg[3] = {0.f, 0.f, 0.f};
-    auto step_of = [&](int s, int& h, int& qb) {
-        h = kh * G + s / nqb;
-        qb = p.nQB - 1 - s % nqb;           // newest block first
-    };
-    // issue the global -> LDS copies of step s's Q block and load its row terms
-    auto fetch = [&](int s, int buf) {
-        int h, qb;
-        step_of(s, h, qb);
-        const int64_t bh = (int64_t)b * p.Hq + h;
-        const uint16_t* qbase = p.q + b * p.q_sb + h * p.q_sh;
+    // Step s covers q head kh*G + s / nqb and query block nQB-1 - s % nqb
+    // (newest block first, so workgroups that start together read the same Q).
+    // Per-lane byte offsets of this lane's 16-byte chunks inside a Q block
+    // (row r, logical chunk c stored at physical chunk c ^ (r % QCH)).
+    uint32_t qoff[QINST];
+#pragma unroll
+    for (int n = 0; n < QINST; ++n) {
+        const int sl = (n * 4 + w) * 64 + lane;
+        const int r = sl / QCH, pc = sl % QCH;
+        const int c = pc ^ (r % QCH);
+        qoff[n] = (uint32_t)((r * p.q_sl + 8 * c) * 2);
+    }
+    int f_h = kh * G, f_qb = p.nQB - 1;     // the step being fetched
+    // issue the copies of one step's Q block and row terms into buffer `buf`
+    auto fetch_advance = [&](int buf) {
+        const int64_t bh = (int64_t)b * p.Hq + f_h;
+        const int row0 = f_qb * BQ;
+        const int nrow = (L - row0 < BQ) ? L - row0 : BQ;
+        // row terms: waves 0..2 copy threshold / lse2 / D (BQ floats each)
+        if (w < 3 && lane * 4 < BQ) {
+            const float* src = (w == 0 ? p.rowt : (w == 1 ? p.rowc : p.rowd)) + bh * p.Lpad + row0;
+            load16_to_lds(src + 4 * lane, &sRow[buf][w][0]);
+        }
+        // the block's rows through a buffer resource ending at row L-1, so the
+        // rows past L read as zero without per-lane clamps
+        const uint16_t* qblk = p.q + b * p.q_sb + (int64_t)row0 * p.q_sl + f_h * p.q_sh;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qblk, (uint32_t)(((nrow - 1) * p.q_sl + D) * 2));
         unsigned char* dst = sU + buf * (BQ * D * 2);
 #pragma unroll
-        for (int n = 0; n < QINST; ++n) {
-            const int slot0 = (n * 4 + w) * 64;
-            const int sl = slot0 + lane;
-            const int r = sl / QCH, pc = sl % QCH;
-            const int c = pc ^ (r % QCH);
-            int i = qb * BQ + r;
-            i = i < L ? i : L - 1;          // rows past L are masked; keep the read in bounds
-            load16_to_lds(qbase + (int64_t)i * p.q_sl + 8 * c, dst + slot0 * 16);
-        }
-        if (tid < BQ) {
-            const int i = qb * BQ + tid;
-            if (i < L) {
-                const float l2 = p.rowc[bh * L + i];
-                rreg[0] = l2 + (log2_tau - fast_log2((float)(i + 1)));
-                rreg[1] = l2;
-                rreg[2] = p.rowd[bh * L + i];
-            } else {
-                rreg[0] = __builtin_inff();   // rows past L never vote
-                rreg[1] = 0.f;
-                rreg[2] = 0.f;
-            }
-        }
-    };
-    auto store_rows = [&](int buf) {
-        if (tid < BQ) {
-            sRow[buf][0][tid] = rreg[0];
-            sRow[buf][1][tid] = rreg[1];
-            sRow[buf][2][tid] = rreg[2];
-        }
+        for (int n = 0; n < QINST; ++n) buffer16_to_lds(rq, qoff[n], dst + (n * 4 + w) * 64 * 16);
+        if (--f_qb < qb_lo) { f_qb = p.nQB - 1; ++f_h; }
     };
 
-    if (nsteps > 0) {
-        fetch(0, 0);
-        store_rows(0);
-    }
+    if (nsteps > 0) fetch_advance(0);
+    if (nsteps > 1) fetch_advance(1);
     wait_all_then_barrier();
 
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        int h, qb;
-        step_of(s, h, qb);
+    int h = kh * G, qb = p.nQB - 1;         // the step being computed
+    int s = 0;
+    f32x16 sc[WSUB];
+    while (s < nsteps) {
+        // ---- inner loop over steps whose tile is skipped: score recompute and
+        // predicate only, nothing else live (the accumulators stay untouched)
+        bool keep = false;
+        int buf = 0;
+        bool diag = false;
+        for (;;) {
+            buf = s % NBUF;
+            const bool prefetch = s + 2 < nsteps;
+            if (prefetch) fetch_advance((s + 2) % NBUF);
+            const uint16_t* sQb = sQ + buf * BQ * D;
+            diag = (qb == qb_lo);
+            // S' = Q K^T - threshold for the wave's query subtiles x 32 keys: the
+            // accumulator starts at minus each row's threshold (row terms in LDS)
+#pragma unroll
+            for (int t = 0; t < WSUB; ++t) {
+                const int qsub = WSUB * qh + t;
+                const int row = 32 * qsub + l32;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 tv = *(const f32x4*)(&sRow[buf][0][32 * qsub + 8 * g4 + 4 * hi]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sc[t][4 * g4 + e] = tv[e];
+                }
+#pragma unroll
+                for (int st = 0; st < KSTEPS; ++st) {
+                    const int pc = (2 * st + hi) ^ (row % QCH);
+                    const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
+                    sc[t] = mfma32x32x16(a, kf[st], sc[t]);
+                }
+            }
+            // nested predicate: keep iff some legal (i, j) has S'_ij >= 0
+            float mx = kNegInf;
+            if (diag) {
+#pragma unroll
+                for (int t = 0; t < WSUB; ++t) {
+                    const int qsub = WSUB * qh + t;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int ig = qb * BQ + 32 * qsub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        mx = fmaxf(mx, (jme <= ig) ? sc[t][r] : kNegInf);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < WSUB; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
+            }
+            const bool vote = keep_all || mx >= 0.f;
+            const bool wave_any = __ballot(vote) != 0ull;
+            if (lane == 0) sFlag[s & 1][w] = wave_any ? 1 : 0;
+            // the block of step s+1 (copied during step s-1) must have landed; the
+            // copies of step s+2 (QINST, plus one row-term copy on waves 0..2)
+            // may stay in flight
+            if (!prefetch) wait_vmcnt<0>();
+            else if (w < 3) wait_vmcnt<QINST + 1>();
+            else wait_vmcnt<QINST>();
+            __syncthreads();
+            keep = (sFlag[s & 1][0] | sFlag[s & 1][1] | sFlag[s & 1][2] | sFlag[s & 1][3]) != 0;
+            if (keep) break;
+            if (--qb < qb_lo) { qb = p.nQB - 1; ++h; }
+            if (++s >= nsteps) break;
+        }
+        if (!keep) break;
         const int64_t bh = (int64_t)b * p.Hq + h;
-        if (s + 1 < nsteps) fetch(s + 1, buf ^ 1);
-        const uint16_t* sQb = sQ + buf * BQ * D;
-
-        // ---- score recompute: S = Q K^T for the wave's query subtiles x 32 keys
-        f32x16 sc[WSUB];
-#pragma unroll
-        for (int t = 0; t < WSUB; ++t) {
-            const int qsub = WSUB * qh + t;
-            const int row = 32 * qsub + l32;
-            sc[t] = f32x16{};
-#pragma unroll
-            for (int st = 0; st < KSTEPS; ++st) {
-                const int pc = (2 * st + hi) ^ (row % QCH);
-                const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
-                sc[t] = mfma32x32x16(a, kf[st], sc[t]);
-            }
-        }
-        // ---- nested predicate: keep iff some legal (i, j) has s2_ij >= lse2_i + theta_i
-        bool vote = false;
-#pragma unroll
-        for (int t = 0; t < WSUB; ++t) {
-            const int qsub = WSUB * qh + t;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int ql = 32 * qsub + 8 * g4 + 4 * hi;
-                const f32x4 cv = *(const f32x4*)(&sRow[buf][0][ql]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ig = qb * BQ + ql + e;
-                    const float x = sc[t][4 * g4 + e] * p.scale_log2;
-                    sc[t][4 * g4 + e] = x;
-                    vote |= (jme <= ig) && (x >= cv[e]);
-                }
-            }
-        }
-        const bool wave_any = __ballot(vote) != 0ull;
-        if (lane == 0) sFlag[buf][w] = wave_any ? 1 : 0;
-        if (s + 1 < nsteps) store_rows(buf ^ 1);
-        wait_all_then_barrier();
-        const bool keep = (sFlag[buf][0] | sFlag[buf][1] | sFlag[buf][2] | sFlag[buf][3]) != 0;
-        if (!keep) continue;
-
-        // ---- dP = dO V^T (A operand rows straight from global dO)
-        f32x16 dp[WSUB];
-#pragma unroll
-        for (int t = 0; t < WSUB; ++t) {
-            const int qsub = WSUB * qh + t;
-            const int i = qb * BQ + 32 * qsub + l32;
-            const bool ok = i < L;
-            const uint16_t* grow = p.dout + b * p.do_sb + (int64_t)(ok ? i : 0) * p.do_sl + h * p.do_sh;
-            dp[t] = f32x16{};
-#pragma unroll
-            for (int st = 0; st < KSTEPS; ++st) {
-                const u32x4 x = ok ? *(const u32x4*)(grow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
-                dp[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, x), vf[st], dp[t]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- P, dS; A operands (key rows x 8 permuted query positions) for dV, dK
-        bf16x8 pa[2 * WSUB], da[2 * WSUB];
-#pragma unroll
-        for (int t = 0; t < WSUB; ++t) {
-            const int qsub = WSUB * qh + t;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int ql = 32 * qsub + 8 * g4 + 4 * hi;
-                const f32x4 lv = *(const f32x4*)(&sRow[buf][1][ql]);
-                const f32x4 dd = *(const f32x4*)(&sRow[buf][2][ql]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g4 + e;
-                    const int ig = qb * BQ + ql + e;
-                    const bool legal = (jme <= ig) && (ig < L);
-                    const float pr = legal ? fast_exp2(sc[t][r] - lv[e]) : 0.f;
-                    const float ds = pr * (dp[t][r] - dd[e]);
-                    pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
-                    const __bf16 dsb = to_bf16(ds);
-                    da[2 * t + (r >> 3)][r & 7] = dsb;
-                    sdS[(ql + e) * SROW + 32 * kw + l32] = __builtin_bit_cast(uint16_t, dsb);
-                }
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- dV += P^T dO, dK += dS^T Q  (B operands from the transposed copies)
-        const int64_t tbase = (int64_t)bh * D * p.Lpad + qb * BQ + (BQ / 2) * qh + 8 * hi;
-#pragma unroll
-        for (int ks = 0; ks < 2 * WSUB; ++ks) {
-            bf16x8 bg[DT], bq[DT];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int64_t off = tbase + (int64_t)(32 * dt + l32) * p.Lpad + 16 * ks;
-                bg[dt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.dot + off));
-                bq[dt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.qt + off));
-            }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                dv[dt] = mfma32x32x16(pa[ks], bg[dt], dv[dt]);
-                dk[dt] = mfma32x32x16(da[ks], bq[dt], dk[dt]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __syncthreads();   // dS complete in LDS
-        // ---- dQ += scale dS K, work items (query subtile, d tile) spread over the waves
         {
-            float* dqblk = p.dq_acc + (bh * L + qb * BQ) * D;
-            for (int item = w; item < NQS * DT; item += 4) {
-                const int qsub = item / DT, dt = item % DT;
-                f32x16 acc = f32x16{};
+            // ---- dP = dO V^T (A operand rows straight from global dO)
+            f32x16 dp[WSUB];
 #pragma unroll
-                for (int ks = 0; ks < BK / 16; ++ks) {
-                    const bf16x8 a = *(const bf16x8*)(&sdS[(32 * qsub + l32) * SROW + 16 * ks + 8 * hi]);
-                    const bf16x8 bb = *(const bf16x8*)(&sKt[(32 * dt + l32) * SROW + 16 * ks + 8 * hi]);
-                    acc = mfma32x32x16(a, bb, acc);
+            for (int t = 0; t < WSUB; ++t) {
+                const int qsub = WSUB * qh + t;
+                const int i = qb * BQ + 32 * qsub + l32;
+                const bool ok = i < L;
+                const uint16_t* grow = p.dout + b * p.do_sb + (int64_t)(ok ? i : 0) * p.do_sl + h * p.do_sh;
+                dp[t] = f32x16{};
+#pragma unroll
+                for (int st = 0; st < KSTEPS; ++st) {
+                    const u32x4 x = ok ? *(const u32x4*)(grow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
+                    dp[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, x), vf[st], dp[t]);
                 }
-                // C[i = query][j = d]: lane = d, registers = queries
-                float* col = dqblk + 32 * dt + l32;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // ---- P, dS; A operands (key rows x 8 permuted query positions) for dV, dK
+            bf16x8 pa[2 * WSUB], da[2 * WSUB];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qq = 32 * qsub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (qb * BQ + qq < L) unsafeAtomicAdd(col + (int64_t)qq * D, acc[r] * p.scale);
+            for (int t = 0; t < WSUB; ++t) {
+                const int qsub = WSUB * qh + t;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ql = 32 * qsub + 8 * g4 + 4 * hi;
+                    const f32x4 tv = *(const f32x4*)(&sRow[buf][0][ql]);
+                    const f32x4 lv = *(const f32x4*)(&sRow[buf][1][ql]);
+                    const f32x4 dd = *(const f32x4*)(&sRow[buf][2][ql]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g4 + e;
+                        const int ig = qb * BQ + ql + e;
+                        const bool legal = (jme <= ig) && (ig < L);
+                        const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r] - tv[e], c2, -lv[e])) : 0.f;
+                        const float ds = pr * (dp[t][r] - dd[e]);
+                        pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
+                        const __bf16 dsb = to_bf16(ds);
+                        da[2 * t + (r >> 3)][r & 7] = dsb;
+                        sdS[(ql + e) * SROW + 32 * kw + l32] = __builtin_bit_cast(uint16_t, dsb);
+                    }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- dV += P^T dO, dK += dS^T Q  (B operands from the transposed copies)
+            const int64_t tbase = (int64_t)bh * D * p.Lpad + qb * BQ + (BQ / 2) * qh + 8 * hi;
+#pragma unroll
+            for (int ks = 0; ks < 2 * WSUB; ++ks) {
+                bf16x8 bg[DT], bq[DT];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int64_t off = tbase + (int64_t)(32 * dt + l32) * p.Lpad + 16 * ks;
+                    bg[dt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.dot + off));
+                    bq[dt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.qt + off));
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    dv[dt] = mfma32x32x16(pa[ks], bg[dt], dv[dt]);
+                    dk[dt] = mfma32x32x16(da[ks], bq[dt], dk[dt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __syncthreads();   // dS complete in LDS
+            // ---- dQ += scale dS K, work items (query subtile, d tile) spread over the waves
+            {
+                float* dqblk = p.dq_acc + (bh * L + qb * BQ) * D;
+                for (int item = w; item < NQS * DT; item += 4) {
+                    const int qsub = item / DT, dt = item % DT;
+                    f32x16 acc = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < BK / 16; ++ks) {
+                        const bf16x8 a = *(const bf16x8*)(&sdS[(32 * qsub + l32) * SROW + 16 * ks + 8 * hi]);
+                        const bf16x8 bb = *(const bf16x8*)(&sKt[(32 * dt + l32) * SROW + 16 * ks + 8 * hi]);
+                        acc = mfma32x32x16(a, bb, acc);
+                    }
+                    // C[i = query][j = d]: lane = d, registers = queries
+                    float* col = dqblk + 32 * dt + l32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qq = 32 * qsub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        if (qb * BQ + qq < L) unsafeAtomicAdd(col + (int64_t)qq * D, acc[r] * p.scale);
+                    }
+                }
+            }
+            // ---- statistics of the backward's own decisions
+            if (tid == 0) {
+                if (p.kept_tiles) atomicAdd(p.kept_tiles + bh * p.nQB + qb, 1);
+                if (p.bits) atomicOr(p.bits + (bh * p.nQB + qb) * p.nwords + (kt >> 5), 1u << (kt & 31));
+            }
+            if (p.kept_slots && tid < BQ) {
+                const int i = qb * BQ + tid;
+                const int last = i - j0;
+                if (i < L && last >= 0) atomicAdd(p.kept_slots + bh * L + i, (last < BK - 1 ? last : BK - 1) + 1);
+            }
         }
-        // ---- statistics of the backward's own decisions
-        if (tid == 0) {
-            if (p.kept_tiles) atomicAdd(p.kept_tiles + bh * p.nQB + qb, 1);
-            if (p.bits) atomicOr(p.bits + (bh * p.nQB + qb) * p.nwords + (kt >> 5), 1u << (kt & 31));
-        }
-        if (p.kept_slots && tid < BQ) {
-            const int i = qb * BQ + tid;
-            const int last = i - j0;
-            if (i < L && last >= 0) atomicAdd(p.kept_slots + bh * L + i, (last < BK - 1 ? last : BK - 1) + 1);
-        }
+        if (--qb < qb_lo) { qb = p.nQB - 1; ++h; }
+        ++s;
     }
 
     // ---- epilogue: combine the two query halves, write dK (scaled) and dV

@@ -94,11 +94,31 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_elem) {
     return __builtin_bit_cast(u32x2, x);
 }
 
+// Raw buffer resource over `nbytes` bytes at `base` (reads past the end
+// return zero, dword by dword), and the matching 16-byte global -> LDS copy
+// at byte offset voffset (per lane) + soffset (uniform).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                            (int)voffset, 0, 0, 0);
+}
+
 // Wait for every outstanding memory operation of this wave (including the
 // global -> LDS copies above), then a workgroup barrier.
 __device__ __forceinline__ void wait_all_then_barrier() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+}
+
+// Wait until at most N vector-memory operations of this wave (loads, stores,
+// global -> LDS copies; they retire in issue order) are outstanding.
+// gfx9 s_waitcnt encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Maps a linear workgroup id onto a work-unit id so that `chunk` consecutive

@@ -35,8 +35,9 @@ struct BwdParams {
     uint16_t* dk;
     uint16_t* dv;
     float* dq_acc;      // [B, Hq, L, d] fp32 workspace
-    float* rowd;        // [B, Hq, L] fp32: D_i = dO_i . O_i
-    float* rowc;        // [B, Hq, L] fp32: LSE_i * log2(e)
+    float* rowd;        // [B, Hq, Lpad] fp32: D_i = dO_i . O_i (0 past L)
+    float* rowc;        // [B, Hq, Lpad] fp32: LSE_i * log2(e) (0 past L)
+    float* rowt;        // [B, Hq, Lpad] fp32: minus the keep threshold on raw scores (-inf past L)
     uint16_t* qt;       // [B, Hq, d, Lpad] bf16: Q transposed, query positions permuted in 16-groups
     uint16_t* dot;      // [B, Hq, d, Lpad] bf16: dO transposed, same permutation
     int Lpad;           // nQB * Bq

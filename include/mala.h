@@ -39,6 +39,8 @@
  *     take bf16 operands.
  *   - Supported shapes: (d, Bq, Bk) = (128, 128, 64) or (64, 64, 64) for
  *     mala_fwd / mala_bwd; decode takes d = 128 or 64 with Bk_dec = 64.
+ *     mala_bwd also needs (Bq * q's L stride + d) * 2 bytes <= INT32_MAX (one
+ *     query block is addressed through a 32-bit buffer range).
  *     Anything else returns MALA_ERR_UNSUPPORTED.
  */
 #ifndef MALA_H_
@@ -54,7 +56,7 @@ extern "C" {
 typedef enum {
     MALA_OK = 0,
     MALA_ERR_INVALID_ARG = 1,   /* null required pointer, bad shape/stride/alignment, bad tau */
-    MALA_ERR_UNSUPPORTED = 2,   /* (d, Bq, Bk) combination not built */
+    MALA_ERR_UNSUPPORTED = 2,   /* (d, Bq, Bk) combination not built, or a stride beyond a kernel's range */
     MALA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace_size query */
     MALA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
 } mala_status;
