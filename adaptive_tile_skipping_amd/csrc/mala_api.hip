@@ -130,7 +130,11 @@ size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int
     const size_t Lpad = (size_t)((L + Bq - 1) / Bq) * Bq;
     const size_t prow = (size_t)B * Hq * Lpad;
     const size_t tr = (size_t)B * Hq * d * Lpad * 2;
-    return align256(rows * d * sizeof(float)) + 3 * align256(prow * sizeof(float)) + 2 * align256(tr);
+    const size_t nQB = Lpad / Bq, nKT = (size_t)(L + Bk - 1) / Bk;
+    const size_t nwT = ((size_t)(Hq / Hkv) * nQB + 31) / 32;
+    const size_t tb = (size_t)B * Hkv * nKT * nwT * sizeof(uint32_t);
+    return align256(rows * d * sizeof(float)) + 2 * align256(prow * sizeof(float)) + 2 * align256(tr) +
+           align256(tb);
 }
 
 mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, const float* lse,
@@ -144,7 +148,8 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     if (bwd_stats && bwd_stats->omitted_mass) return MALA_ERR_INVALID_ARG;
     if (!fwd_shape_supported(d, Bq, Bk)) return MALA_ERR_UNSUPPORTED;
     // a query block is read through one buffer resource (32-bit byte range)
-    if (((int64_t)Bq * q.sl + d) * 2 > INT32_MAX) return MALA_ERR_UNSUPPORTED;
+    if (((int64_t)Bq * q.sl + d) * 2 > INT32_MAX || ((int64_t)Bk * k.sl + d) * 2 > INT32_MAX)
+        return MALA_ERR_UNSUPPORTED;
     const size_t need = mala_bwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk);
     if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
     BwdParams p;
@@ -159,10 +164,10 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     const size_t prow = (size_t)B * Hq * p.Lpad;
     p.rowd = (float*)w; w += align256(prow * sizeof(float));
     p.rowc = (float*)w; w += align256(prow * sizeof(float));
-    p.rowt = (float*)w; w += align256(prow * sizeof(float));
     const size_t tr = (size_t)B * Hq * d * p.Lpad * 2;
     p.qt = (uint16_t*)w; w += align256(tr);
-    p.dot = (uint16_t*)w;
+    p.dot = (uint16_t*)w; w += align256(tr);
+    p.tbits = (uint32_t*)w;
     p.q_sb = q.sb; p.q_sl = q.sl; p.q_sh = q.sh;
     p.k_sb = k.sb; p.k_sl = k.sl; p.k_sh = k.sh;
     p.v_sb = v.sb; p.v_sl = v.sl; p.v_sh = v.sh;
@@ -175,6 +180,10 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     p.nQB = (L + Bq - 1) / Bq; p.nKT = (L + Bk - 1) / Bk;
     p.nunits = B * Hkv * p.nKT;
     p.chunk = 4;
+    p.nwT = (p.G * p.nQB + 31) / 32;
+    p.nslab = (L + 255) / 256;
+    p.nunits_scan = p.nslab * B * Hq;
+    p.chunk_scan = pick_chunk(Hq, Hkv);
     p.scale = (float)(1.0 / sqrt((double)d));
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     p.log2_tau = log2_tau(tau);

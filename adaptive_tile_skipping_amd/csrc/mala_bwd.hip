@@ -16,18 +16,28 @@
 // Kernels:
 //   mala_bwd_pre    D_i, LSE_i in base 2, transposed copies of Q and dO (query
 //                   positions permuted inside each 16-group to match the MFMA
-//                   register order), zeroed dQ accumulator and statistics.
-//   mala_bwd_kernel one workgroup per (batch, KV head, key tile of 64 keys),
-//                   4 waves.  K and V fragments stay in registers; the kernel
-//                   streams the query blocks of every q head of the group,
-//                   newest block first, through a double-buffered LDS tile and
-//                   recomputes S = Q K^T for each (every legal tile is scored).
-//                   Wave w owns keys 32(w&1).. and half (w>>1) of the block's
-//                   queries.  S is laid out with one key per lane and the
-//                   block's queries in registers, so P^T and dS^T feed the dV
-//                   and dK contractions straight from registers; dS also goes
-//                   to LDS (query-major) for dQ = dS K.  dK/dV accumulate in
-//                   registers over heads and blocks; dQ goes to an fp32
+//                   register order), zeroed dQ accumulator, tile bits and
+//                   statistics.
+//   mala_bwd_scan   the decision pass (tau > 0): one workgroup per (batch, q
+//                   head, 256-query slab), 4 waves of 64 queries.  Q and each
+//                   row's threshold stay in registers; key tiles stream from
+//                   the slab's diagonal to key 0 through a triple-buffered LDS
+//                   tile.  The score accumulator starts at minus the row's
+//                   threshold, so a tile is kept iff the masked maximum of the
+//                   accumulator is >= 0.  A kept tile sets one bit of its key
+//                   tile's word row (q head, query block); nothing else is
+//                   written, so skipped tiles cost only the score MFMAs.
+//   mala_bwd_kernel the gradient pass: one workgroup per (batch, KV head, key
+//                   tile of 64 keys), 4 waves, visiting only the kept (q head,
+//                   query block) steps of its key tile (all legal steps when
+//                   tau = 0).  K and V fragments stay in registers; each step's
+//                   Q block streams through a triple-buffered LDS tile and
+//                   S = Q K^T is recomputed.  Wave w owns keys 32(w&1).. and half
+//                   (w>>1) of the block's queries.  S is laid out with one key
+//                   per lane and the block's queries in registers, so P^T and
+//                   dS^T feed the dV and dK contractions straight from
+//                   registers; dS also goes to LDS (query-major) for dQ = dS K.
+//                   dK/dV accumulate in registers over steps; dQ goes to an fp32
 //                   accumulator with atomics.
 //   mala_dq_convert fp32 dQ accumulator -> bf16 dQ.
 #include "mala_device.h"
@@ -52,9 +62,7 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
     const int r0 = rb * PRE_ROWS;
     const int L = p.L;
     const int64_t bh = (int64_t)b * p.Hq + h;
-    // D_i = dO_i . O_i, LSE in base 2 and minus the keep threshold on raw scores
-    // (4 threads per row).  Rows past L get D = 0, LSE = 0 and -inf, so their
-    // scores never vote; with tau = 0 every legal tile is kept and the term is 0.
+    // D_i = dO_i . O_i and LSE in base 2 (4 threads per row; 0 past L)
     {
         const int r = tid >> 2, part = tid & 3;
         const int i = r0 + r;
@@ -76,20 +84,17 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
         acc += __shfl_xor(acc, 2);
         if (part == 0) {
             const int64_t ri = bh * p.Lpad + i;
-            if (i < L) {
-                const float l2 = p.lse[bh * L + i] * kLog2e;
-                p.rowd[ri] = acc;
-                p.rowc[ri] = l2;
-                p.rowt[ri] = (p.log2_tau == kNegInf)
-                                 ? 0.f
-                                 : -(l2 + (p.log2_tau - fast_log2((float)(i + 1)))) / p.scale_log2;
-                if (p.kept_slots) p.kept_slots[bh * L + i] = 0;
-            } else {
-                p.rowd[ri] = 0.f;
-                p.rowc[ri] = 0.f;
-                p.rowt[ri] = kNegInf;
-            }
+            p.rowd[ri] = (i < L) ? acc : 0.f;
+            p.rowc[ri] = (i < L) ? p.lse[bh * L + i] * kLog2e : 0.f;
+            if (p.kept_slots && i < L) p.kept_slots[bh * L + i] = 0;
         }
+    }
+    // zero the kept-tile bits (the scan only sets bits)
+    if (p.log2_tau != kNegInf) {
+        const int64_t nblk = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+        const int64_t fb = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+        const int64_t nw = (int64_t)p.B * p.Hkv * p.nKT * p.nwT;
+        for (int64_t idx = fb * 256 + tid; idx < nw; idx += nblk * 256) p.tbits[idx] = 0u;
     }
     // stage Q and dO rows (zeros past L)
     constexpr int CH = D / 8;
@@ -137,6 +142,191 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
     }
 }
 
+// Decision pass of the backward (tau > 0).  See the file comment.
+template <int D, int BQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mala_bwd_scan(
+    const BwdParams p) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int QCH = D / 8;             // 16-byte chunks per row
+    constexpr int KINST = BK * QCH / 256;  // global->LDS copies per lane per key tile
+    constexpr int NB = 3;                  // key tiles in flight: current + two prefetched
+    static_assert(KINST * 256 == BK * QCH, "shape");
+    // key tiles [NB][BK][D] bf16, chunk c of row r stored at chunk c ^ (r % QCH)
+    __shared__ __attribute__((aligned(16))) uint16_t sK[NB][BK * D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int u = xcd_unit(blockIdx.x, p.chunk_scan);
+    if (u >= p.nunits_scan) return;
+    const int BH = p.B * p.Hq;
+    const int slab = p.nslab - 1 - u / BH;   // longest slabs first
+    const int b = (u % BH) / p.Hq;
+    const int h = (u % BH) % p.Hq;
+    const int kh = h / p.G;
+    const int L = p.L;
+    const int R0 = slab * 256;
+    const int rw0 = R0 + 64 * w;             // the wave's 64 queries
+    const int last = (R0 + 255 < L - 1) ? R0 + 255 : L - 1;
+    const int kt_hi = last / BK;
+    const int kt_w = rw0 / BK;               // the wave's diagonal key tile
+    const bool live = rw0 < L;
+    const float c2 = p.scale_log2;
+    const int64_t bh = (int64_t)b * p.Hq + h;
+
+    // ---- Q fragments (A operands: row = query, 8 consecutive d) and the seeds:
+    // minus each row's threshold on raw scores, -inf past L
+    bf16x8 qa[2][KSTEPS];
+    f32x16 seed[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int i = rw0 + 32 * t + l32;
+        const bool ok = i < L;
+        const uint16_t* qr = p.q + b * p.q_sb + (int64_t)(ok ? i : 0) * p.q_sl + h * p.q_sh;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+            const u32x4 x = ok ? *(const u32x4*)(qr + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
+            qa[t][st] = __builtin_bit_cast(bf16x8, x);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ir = rw0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+            seed[t][r] = (ir < L) ? -(p.lse[bh * L + ir] * kLog2e + (p.log2_tau - fast_log2((float)(ir + 1)))) / c2
+                                  : kNegInf;
+        }
+    }
+
+    // ---- key tile copies through a buffer resource ending at key L-1
+    uint32_t koff[KINST];
+#pragma unroll
+    for (int n = 0; n < KINST; ++n) {
+        const int sl = (n * 4 + w) * 64 + lane;
+        const int r = sl / QCH, pc = sl % QCH;
+        koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
+    }
+    const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh;
+    auto copy_tile = [&](int kt, int buf) {
+        const int j0 = kt * BK;
+        const int nrow = (L - j0 < BK) ? L - j0 : BK;
+        const __amdgpu_buffer_rsrc_t rk =
+            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((nrow - 1) * p.k_sl + D) * 2));
+        unsigned char* dst = reinterpret_cast<unsigned char*>(sK[buf]);
+#pragma unroll
+        for (int n = 0; n < KINST; ++n) buffer16_to_lds(rk, koff[n], dst + (n * 4 + w) * 64 * 16);
+    };
+
+    const int nt = kt_hi + 1;
+    copy_tile(kt_hi, 0);
+    if (nt > 1) copy_tile(kt_hi - 1, 1);
+    wait_all_then_barrier();
+
+    uint32_t* bitrow = p.tbits + (int64_t)(b * p.Hkv + kh) * p.nKT * p.nwT;
+    const int bit = (h % p.G) * p.nQB + rw0 / BQ;
+
+    for (int it = 0; it < nt; ++it) {
+        const int kt = kt_hi - it;
+        const int buf = it % NB;
+        const bool prefetch = it + 2 < nt;
+        if (prefetch) copy_tile(kt - 2, (it + 2) % NB);
+        if (live && kt <= kt_w) {
+            const uint16_t* sKb = sK[buf];
+            f32x16 acc[2][2];
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) {
+                bf16x8 kb[2];
+#pragma unroll
+                for (int uu = 0; uu < 2; ++uu) {
+                    const int row = 32 * uu + l32;
+                    kb[uu] = *(const bf16x8*)(&sKb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int uu = 0; uu < 2; ++uu)
+                        acc[t][uu] = mfma32x32x16(qa[t][st], kb[uu], st == 0 ? seed[t] : acc[t][uu]);
+            }
+            // C[i = query][j = key]: lane = key 32uu + l32, register r = query
+            // 32t + 8(r/4) + 4hi + r%4.  Keep iff a legal entry is >= 0.
+            float mx = kNegInf;
+            if (kt == kt_w) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int uu = 0; uu <= t; ++uu)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int iq = 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+                            const bool legal = (uu < t) || (l32 <= iq);
+                            mx = fmaxf(mx, legal ? acc[t][uu][r] : kNegInf);
+                        }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][uu][r]);
+            }
+            if (__ballot(mx >= 0.f) != 0ull && lane == 0)
+                atomicOr(bitrow + (int64_t)kt * p.nwT + (bit >> 5), 1u << (bit & 31));
+        }
+        // tile kt-1 (copied during the previous iteration) must have landed
+        if (prefetch) wait_vmcnt<KINST>(); else wait_vmcnt<0>();
+        __syncthreads();
+    }
+}
+
+// Enumerates the steps of one key tile as hl * nQB + qb (hl = q head within
+// the KV group).  Dense (tau = 0): every q head, query blocks newest first down
+// to the block holding the tile.  Sparse: the set bits of the tile's word row
+// in increasing order, read 64 words (one per lane) at a time.  All state but
+// `my` is wave-uniform.
+struct StepCursor {
+    const uint32_t* words;
+    int nw, wb, wi;
+    uint32_t my, cur;
+    uint64_t mask;
+    bool dense;
+    int hl, qb, qb_lo, nQB, G;
+
+    __device__ void init(bool dense_, const uint32_t* words_, int nw_, int qb_lo_, int nQB_, int G_) {
+        dense = dense_; words = words_; nw = nw_;
+        wb = -64; wi = -65; my = 0u; cur = 0u; mask = 0ull;
+        hl = 0; qb = nQB_ - 1; qb_lo = qb_lo_; nQB = nQB_; G = G_;
+    }
+    __device__ int next(int lane) {
+        if (dense) {
+            if (hl >= G) return -1;
+            const int idx = hl * nQB + qb;
+            if (--qb < qb_lo) { qb = nQB - 1; ++hl; }
+            return idx;
+        }
+        for (;;) {
+            if (cur) {
+                const int bpos = __builtin_ctz(cur);
+                cur &= cur - 1u;
+                return wi * 32 + bpos;
+            }
+            const int off = wi - wb;   // -1 .. 63
+            const uint64_t m = (off >= 63) ? 0ull : (mask & (~0ull << (off + 1)));
+            if (m == 0ull) {
+                wb += 64;
+                if (wb >= nw) return -1;
+                my = (wb + lane < nw) ? words[wb + lane] : 0u;
+                mask = __ballot(my != 0u);
+                wi = wb - 1;
+                continue;
+            }
+            const int o = __builtin_ctzll(m);
+            wi = wb + o;
+            cur = (uint32_t)__builtin_amdgcn_readlane((int)my, o);
+        }
+    }
+};
+
 template <int D, int BQ>
 __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     constexpr int KSTEPS = D / 16;
@@ -157,9 +347,8 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char sU[UBYTES];
     __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SROW];
     __shared__ __attribute__((aligned(16))) uint16_t sdS[BQ * SROW];
-    // [buf][keep threshold on raw scores | lse2 | D][query]
-    __shared__ __attribute__((aligned(16))) float sRow[NBUF][3][BQ];
-    __shared__ int sFlag[2][4];
+    // [buf][lse2 | D][query]
+    __shared__ __attribute__((aligned(16))) float sRow[NBUF][2][BQ];
     uint16_t* sQ = reinterpret_cast<uint16_t*>(sU);
 
     const int tid = threadIdx.x;
@@ -180,7 +369,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int j0 = kt * BK;
     const int G = p.G;
     const float c2 = p.scale_log2;
-    const bool keep_all = p.log2_tau == kNegInf;   // tau = 0: dense backward
 
     // ---- resident K and V fragments (B operands: column = key, 8 consecutive d)
     const int jme = j0 + 32 * kw + l32;
@@ -215,11 +403,9 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     for (int dt = 0; dt < DT; ++dt) { dv[dt] = f32x16{}; dk[dt] = f32x16{}; }
 
     const int qb_lo = j0 / BQ;
-    const int nqb = p.nQB - qb_lo;
-    const int nsteps = G * nqb;
+    const bool dense = p.log2_tau == kNegInf;   // tau = 0: every legal step is kept
+    const uint32_t* trow = p.tbits + ((int64_t)(b * p.Hkv + kh) * p.nKT + kt) * p.nwT;
 
-    // Step s covers q head kh*G + s / nqb and query block nQB-1 - s % nqb
-    // (newest block first, so workgroups that start together read the same Q).
     // Per-lane byte offsets of this lane's 16-byte chunks inside a Q block
     // (row r, logical chunk c stored at physical chunk c ^ (r % QCH)).
     uint32_t qoff[QINST];
@@ -230,99 +416,65 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         const int c = pc ^ (r % QCH);
         qoff[n] = (uint32_t)((r * p.q_sl + 8 * c) * 2);
     }
-    int f_h = kh * G, f_qb = p.nQB - 1;     // the step being fetched
-    // issue the copies of one step's Q block and row terms into buffer `buf`
-    auto fetch_advance = [&](int buf) {
-        const int64_t bh = (int64_t)b * p.Hq + f_h;
+    // issue the copies of step `idx` (q head kh*G + idx / nQB, query block
+    // idx % nQB): its row terms and Q block, into buffer `buf`
+    auto fetch = [&](int idx, int buf) {
+        const int f_h = kh * G + idx / p.nQB, f_qb = idx % p.nQB;
+        const int64_t fbh = (int64_t)b * p.Hq + f_h;
         const int row0 = f_qb * BQ;
-        const int nrow = (L - row0 < BQ) ? L - row0 : BQ;
-        // row terms: waves 0..2 copy threshold / lse2 / D (BQ floats each)
-        if (w < 3 && lane * 4 < BQ) {
-            const float* src = (w == 0 ? p.rowt : (w == 1 ? p.rowc : p.rowd)) + bh * p.Lpad + row0;
+        // row terms: waves 0..1 copy lse2 / D (BQ floats each)
+        if (w < 2 && lane * 4 < BQ) {
+            const float* src = (w == 0 ? p.rowc : p.rowd) + fbh * p.Lpad + row0;
             load16_to_lds(src + 4 * lane, &sRow[buf][w][0]);
         }
         // the block's rows through a buffer resource ending at row L-1, so the
         // rows past L read as zero without per-lane clamps
+        const int nrow = (L - row0 < BQ) ? L - row0 : BQ;
         const uint16_t* qblk = p.q + b * p.q_sb + (int64_t)row0 * p.q_sl + f_h * p.q_sh;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qblk, (uint32_t)(((nrow - 1) * p.q_sl + D) * 2));
         unsigned char* dst = sU + buf * (BQ * D * 2);
 #pragma unroll
         for (int n = 0; n < QINST; ++n) buffer16_to_lds(rq, qoff[n], dst + (n * 4 + w) * 64 * 16);
-        if (--f_qb < qb_lo) { f_qb = p.nQB - 1; ++f_h; }
     };
 
-    if (nsteps > 0) fetch_advance(0);
-    if (nsteps > 1) fetch_advance(1);
+    StepCursor fc, cc;   // fetch cursor (two steps ahead) and compute cursor
+    fc.init(dense, trow, p.nwT, qb_lo, p.nQB, G);
+    cc.init(dense, trow, p.nwT, qb_lo, p.nQB, G);
+    int nx = fc.next(lane);
+    if (nx >= 0) {
+        fetch(nx, 0);
+        nx = fc.next(lane);
+        if (nx >= 0) {
+            fetch(nx, 1);
+            nx = fc.next(lane);
+        }
+    }
     wait_all_then_barrier();
 
-    int h = kh * G, qb = p.nQB - 1;         // the step being computed
-    int s = 0;
     f32x16 sc[WSUB];
-    while (s < nsteps) {
-        // ---- inner loop over steps whose tile is skipped: score recompute and
-        // predicate only, nothing else live (the accumulators stay untouched)
-        bool keep = false;
-        int buf = 0;
-        bool diag = false;
-        for (;;) {
-            buf = s % NBUF;
-            const bool prefetch = s + 2 < nsteps;
-            if (prefetch) fetch_advance((s + 2) % NBUF);
-            const uint16_t* sQb = sQ + buf * BQ * D;
-            diag = (qb == qb_lo);
-            // S' = Q K^T - threshold for the wave's query subtiles x 32 keys: the
-            // accumulator starts at minus each row's threshold (row terms in LDS)
-#pragma unroll
-            for (int t = 0; t < WSUB; ++t) {
-                const int qsub = WSUB * qh + t;
-                const int row = 32 * qsub + l32;
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const f32x4 tv = *(const f32x4*)(&sRow[buf][0][32 * qsub + 8 * g4 + 4 * hi]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sc[t][4 * g4 + e] = tv[e];
-                }
-#pragma unroll
-                for (int st = 0; st < KSTEPS; ++st) {
-                    const int pc = (2 * st + hi) ^ (row % QCH);
-                    const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
-                    sc[t] = mfma32x32x16(a, kf[st], sc[t]);
-                }
-            }
-            // nested predicate: keep iff some legal (i, j) has S'_ij >= 0
-            float mx = kNegInf;
-            if (diag) {
-#pragma unroll
-                for (int t = 0; t < WSUB; ++t) {
-                    const int qsub = WSUB * qh + t;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int ig = qb * BQ + 32 * qsub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        mx = fmaxf(mx, (jme <= ig) ? sc[t][r] : kNegInf);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < WSUB; ++t)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
-            }
-            const bool vote = keep_all || mx >= 0.f;
-            const bool wave_any = __ballot(vote) != 0ull;
-            if (lane == 0) sFlag[s & 1][w] = wave_any ? 1 : 0;
-            // the block of step s+1 (copied during step s-1) must have landed; the
-            // copies of step s+2 (QINST, plus one row-term copy on waves 0..2)
-            // may stay in flight
-            if (!prefetch) wait_vmcnt<0>();
-            else if (w < 3) wait_vmcnt<QINST + 1>();
-            else wait_vmcnt<QINST>();
-            __syncthreads();
-            keep = (sFlag[s & 1][0] | sFlag[s & 1][1] | sFlag[s & 1][2] | sFlag[s & 1][3]) != 0;
-            if (keep) break;
-            if (--qb < qb_lo) { qb = p.nQB - 1; ++h; }
-            if (++s >= nsteps) break;
+    int s = 0;
+    for (int cur = cc.next(lane); cur >= 0; cur = cc.next(lane), ++s) {
+        const int buf = s % NBUF;
+        const bool prefetch = nx >= 0;
+        if (prefetch) {
+            fetch(nx, (s + 2) % NBUF);
+            nx = fc.next(lane);
         }
-        if (!keep) break;
+        const int h = kh * G + cur / p.nQB;
+        const int qb = cur % p.nQB;
+        const uint16_t* sQb = sQ + buf * BQ * D;
+        // ---- S = Q K^T for the wave's query subtiles x 32 keys (raw scores)
+#pragma unroll
+        for (int t = 0; t < WSUB; ++t) {
+            const int row = 32 * (WSUB * qh + t) + l32;
+            sc[t] = f32x16{};
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) {
+                const int pc = (2 * st + hi) ^ (row % QCH);
+                const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
+                sc[t] = mfma32x32x16(a, kf[st], sc[t]);
+            }
+        }
         const int64_t bh = (int64_t)b * p.Hq + h;
         {
             // ---- dP = dO V^T (A operand rows straight from global dO)
@@ -349,15 +501,14 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int ql = 32 * qsub + 8 * g4 + 4 * hi;
-                    const f32x4 tv = *(const f32x4*)(&sRow[buf][0][ql]);
-                    const f32x4 lv = *(const f32x4*)(&sRow[buf][1][ql]);
-                    const f32x4 dd = *(const f32x4*)(&sRow[buf][2][ql]);
+                    const f32x4 lv = *(const f32x4*)(&sRow[buf][0][ql]);
+                    const f32x4 dd = *(const f32x4*)(&sRow[buf][1][ql]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * g4 + e;
                         const int ig = qb * BQ + ql + e;
                         const bool legal = (jme <= ig) && (ig < L);
-                        const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r] - tv[e], c2, -lv[e])) : 0.f;
+                        const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e])) : 0.f;
                         const float ds = pr * (dp[t][r] - dd[e]);
                         pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
                         const __bf16 dsb = to_bf16(ds);
@@ -418,8 +569,13 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                 if (i < L && last >= 0) atomicAdd(p.kept_slots + bh * L + i, (last < BK - 1 ? last : BK - 1) + 1);
             }
         }
-        if (--qb < qb_lo) { qb = p.nQB - 1; ++h; }
-        ++s;
+        // the block of step s+1 (copied during step s-1) must have landed; the
+        // copies of step s+2 (QINST, plus one row-term copy on waves 0..1)
+        // may stay in flight
+        if (!prefetch) wait_vmcnt<0>();
+        else if (w < 2) wait_vmcnt<QINST + 1>();
+        else wait_vmcnt<QINST>();
+        __syncthreads();
     }
 
     // ---- epilogue: combine the two query halves, write dK (scaled) and dV
@@ -483,6 +639,11 @@ __global__ __launch_bounds__(256) void mala_dq_convert(const BwdParams p) {
 template <int D, int BQ>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
     hipLaunchKernelGGL((mala_bwd_pre<D, BQ>), dim3(p.Lpad / PRE_ROWS, p.Hq, p.B), dim3(256), 0, s, p);
+    if (p.log2_tau != -INFINITY) {
+        const int per_s = 8 * p.chunk_scan;
+        const int grid_s = (p.nunits_scan + per_s - 1) / per_s * per_s;
+        hipLaunchKernelGGL((mala_bwd_scan<D, BQ>), dim3(grid_s), dim3(256), 0, s, p);
+    }
     const int per = 8 * p.chunk;
     const int grid = (p.nunits + per - 1) / per * per;
     hipLaunchKernelGGL((mala_bwd_kernel<D, BQ>), dim3(grid), dim3(256), 0, s, p);

@@ -39,8 +39,9 @@
  *     take bf16 operands.
  *   - Supported shapes: (d, Bq, Bk) = (128, 128, 64) or (64, 64, 64) for
  *     mala_fwd / mala_bwd; decode takes d = 128 or 64 with Bk_dec = 64.
- *     mala_bwd also needs (Bq * q's L stride + d) * 2 bytes <= INT32_MAX (one
- *     query block is addressed through a 32-bit buffer range).
+ *     mala_bwd also needs (Bq * q's L stride + d) * 2 and (Bk * k's L stride +
+ *     d) * 2 bytes <= INT32_MAX (a query block or key tile is addressed
+ *     through a 32-bit buffer range).
  *     Anything else returns MALA_ERR_UNSUPPORTED.
  */
 #ifndef MALA_H_
