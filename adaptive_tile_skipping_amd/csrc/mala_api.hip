@@ -213,8 +213,6 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
     s += align256(grp * G * sizeof(float));                   // lse2
     s += align256(grp * nsplit * G * d * sizeof(float));      // part_o
     s += align256(grp * nsplit * G * 2 * sizeof(float));      // part_ml
-    s += align256(grp * G * d * sizeof(float));               // o_acc
-    s += align256(grp * sizeof(int32_t));                     // done
     return s;
 }
 
@@ -251,9 +249,7 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
     p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));
     p.lse2 = (float*)w; w += align256(grp * G * sizeof(float));
     p.part_o = (float*)w; w += align256(grp * (size_t)p.nsplit * G * d * sizeof(float));
-    p.part_ml = (float*)w; w += align256(grp * (size_t)p.nsplit * G * 2 * sizeof(float));
-    p.o_acc = (float*)w; w += align256(grp * G * d * sizeof(float));
-    p.done = (int32_t*)w;
+    p.part_ml = (float*)w;
     hipError_t e = launch_decode(p, d, Bk_dec, tau == 0.f, (hipStream_t)stream);
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
 }

@@ -30,8 +30,8 @@
 //                    can never turn to keep, so non-candidates are final too.
 //   mala_dec_pv      kept tiles only, 4 per round per workgroup: P = 2^(s - lse)
 //                    from the spill, V tile loads issued before P is ready,
-//                    fp32 accumulation, atomics into an fp32 output; the last
-//                    workgroup of a (sequence, KV head) writes o in bf16.
+//                    fp32 accumulation into one partial output per split.
+//   mala_dec_sum_combine  sums the partials (already normalised) -> bf16 o.
 // tau = 0 keeps every tile, so the scan is elided: mala_dec_dense is a fused
 // split-K decode (scores, online softmax and P.V per split) and
 // mala_dec_dense_combine merges the splits.
@@ -114,89 +114,252 @@ __device__ __forceinline__ void tile_scores(const DecParams& p, int t, const uin
 
 template <int D>
 __global__ __launch_bounds__(256) void mala_dec_score(const DecParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[4][BKD * D];
+    constexpr int QCH = D / 8;                     // copies per lane per tile
+    __shared__ __attribute__((aligned(16))) uint16_t sK[4][2][BKD * D];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    const int task = blockIdx.x * 4 + w;
-    if (task >= p.B * p.Hkv * p.nT) return;       // no barriers in this kernel
-    const int grp = task / p.nT;
-    const int t = task % p.nT;
-    const int b = grp / p.Hkv, kh = grp % p.Hkv;
-    stage_k_tile<D>(p, b, kh, t, sK[w]);
-    // per-call resets owned by this tile
-    if (p.bits && lane == 0 && (t % 32) == 0) p.bits[(int64_t)grp * p.nwords + t / 32] = 0u;
-    if (t == 0) {
-        for (int e = lane; e < p.G * D; e += 64) p.o_acc[(int64_t)grp * p.G * D + e] = 0.f;
-        if (lane == 0) p.done[grp] = 0;
+    // each wave streams a contiguous run of tiles, the next one in flight
+    // while the current one is scored (no barriers in this kernel)
+    const int ntask = p.B * p.Hkv * p.nT;
+    const int nwave = gridDim.x * 4;
+    const int per = (ntask + nwave - 1) / nwave;
+    const int gw = w * gridDim.x + blockIdx.x;     // neighbouring runs on different CUs
+    int task = gw * per;
+    const int tend = (task + per < ntask) ? task + per : ntask;
+    if (task >= tend) return;
+    {
+        const int g0 = task / p.nT;
+        stage_k_tile<D>(p, g0 / p.Hkv, g0 % p.Hkv, task % p.nT, sK[w][0]);
     }
+    int qgrp = -1;
     bf16x8 qf[D / 16];
-    load_q_frags<D>(p, b, kh, qf);
-    __builtin_amdgcn_s_waitcnt(0);                // this wave's tile is in LDS
-    f32x16 s[2];
-    tile_scores<D>(p, t, sK[w], qf, s);
-    float M = kNegInf;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) M = fmaxf(M, s[sub][r]);
-    M = wave_max_pair(M);
-    float sum = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum += fast_exp2(s[sub][r] - M);
-    sum = wave_sum_pair(sum);
-    const int g = l32;
-    if (g < p.G) {
-        float* sp = p.spill + ((int64_t)grp * p.G + g) * p.N + (int64_t)t * BKD;
-        const bool full = (t + 1) * BKD <= p.N;
+    for (int k = 0; task < tend; ++k, ++task) {
+        const int grp = task / p.nT;
+        const int t = task % p.nT;
+        const int b = grp / p.Hkv, kh = grp % p.Hkv;
+        const bool more = task + 1 < tend;
+        if (grp != qgrp) {
+            load_q_frags<D>(p, b, kh, qf);
+            qgrp = grp;
+        }
+        if (more) {
+            const int g2 = (task + 1) / p.nT;
+            stage_k_tile<D>(p, g2 / p.Hkv, g2 % p.Hkv, (task + 1) % p.nT, sK[w][(k + 1) & 1]);
+        }
+        // per-call reset owned by this tile
+        if (p.bits && lane == 0 && (t % 32) == 0) p.bits[(int64_t)grp * p.nwords + t / 32] = 0u;
+        if (more) wait_vmcnt<QCH>(); else wait_vmcnt<0>();   // this tile is in LDS
+        f32x16 sv[2];
+        tile_scores<D>(p, t, sK[w][k & 1], qf, sv);
+        float M = kNegInf;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int j0 = 32 * sub + 8 * q4 + 4 * hi;
-                if (full) {
-                    *(f32x4*)(sp + j0) = f32x4{s[sub][4 * q4], s[sub][4 * q4 + 1], s[sub][4 * q4 + 2], s[sub][4 * q4 + 3]};
-                } else {
+            for (int r = 0; r < 16; ++r) M = fmaxf(M, sv[sub][r]);
+        M = wave_max_pair(M);
+        float sum = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (t * BKD + j0 + e < p.N) sp[j0 + e] = s[sub][4 * q4 + e];
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += fast_exp2(sv[sub][r] - M);
+        sum = wave_sum_pair(sum);
+        const int g = l32;
+        if (g < p.G) {
+            float* sp = p.spill + ((int64_t)grp * p.G + g) * p.N + (int64_t)t * BKD;
+            const bool full = (t + 1) * BKD <= p.N;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int j0 = 32 * sub + 8 * q4 + 4 * hi;
+                    if (full) {
+                        *(f32x4*)(sp + j0) =
+                            f32x4{sv[sub][4 * q4], sv[sub][4 * q4 + 1], sv[sub][4 * q4 + 2], sv[sub][4 * q4 + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (t * BKD + j0 + e < p.N) sp[j0 + e] = sv[sub][4 * q4 + e];
+                    }
                 }
+            if (hi == 0) {
+                p.tmax[((int64_t)grp * p.nT + t) * p.G + g] = M;
+                p.tsum[((int64_t)grp * p.nT + t) * p.G + g] = sum;
             }
-        if (hi == 0) {
-            p.tmax[((int64_t)grp * p.nT + t) * p.G + g] = M;
-            p.tsum[((int64_t)grp * p.nT + t) * p.G + g] = sum;
         }
     }
 }
 
+// wave64 prefix sums and reductions built on DPP lane moves: row shifts inside
+// 16-lane rows, then row broadcasts of lanes 15 and 31 (lanes whose source is
+// out of range add 0).
+template <int CTRL, int ROWMASK, bool BOUND0>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, BOUND0));
+}
+__device__ __forceinline__ float wave_incl_sum(float x) {
+    x += dpp_f<0x111, 0xF, true>(x);    // row_shr:1
+    x += dpp_f<0x112, 0xF, true>(x);    // row_shr:2
+    x += dpp_f<0x114, 0xF, true>(x);    // row_shr:4
+    x += dpp_f<0x118, 0xF, true>(x);    // row_shr:8
+    x += dpp_f<0x142, 0xA, false>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_f<0x143, 0xC, false>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+__device__ __forceinline__ float wave_max_all(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+__device__ __forceinline__ float wave_min_all(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fminf(x, __shfl_xor(x, off));
+    return x;
+}
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// The sequential decode rule, one wave per (sequence, KV head), 64 tiles per
+// chunk (lane = tile, newest first).  State: the retained mass of each row,
+// as a reference exponent m and a mass l relative to it (l = 0: nothing
+// retained yet, so the next tile is kept).
+//
+// Each round takes as candidates the active tiles that vote keep under the
+// state at the round start (a tile that votes skip under a smaller retained
+// mass can never turn to keep, so non-candidates are final), adds to each
+// candidate's test the mass of the earlier candidates (an exclusive prefix
+// sum), and accepts the candidates up to the first one that then votes skip:
+// their prefixes were exact.  That tile is skipped and the next round starts
+// after it.
+//
+// Fast path (linear masses): per chunk the reference is the running maximum
+// over every tile seen, a_t = 2^(M_t - ref), x_t = tile sum * a_t, and row g
+// votes keep iff a_t >= (tau/N) * (retained + earlier candidates).  Taken when
+// no value can leave fp32's normal range (state and tile maxima within 96 of
+// the reference, tau/N within 2^+-120); otherwise the chunk runs the same
+// rounds with log-sum-exp pairs.
 template <int GP>
 __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     const int grp = blockIdx.x;
     const int lane = threadIdx.x;
     const int G = p.G;
     const float theta = p.log2_tau - p.log2_N;
-    float m[GP], l[GP], thr[GP];          // retained state (identical in all lanes)
+    const bool lin_ok = theta >= -120.f && theta <= 120.f;
+    const float cthr = fast_exp2(theta);
+    float m[GP], l[GP];                   // retained state (identical in all lanes)
 #pragma unroll
-    for (int g = 0; g < GP; ++g) { m[g] = kNegInf; l[g] = 0.f; thr[g] = kNegInf; }
+    for (int g = 0; g < GP; ++g) { m[g] = kNegInf; l[g] = 0.f; }
     int kept = 0;
     int32_t* klist = p.klist + (int64_t)grp * p.nT;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int nchunk = (p.nT + 63) / 64;
+    const float* tmax = p.tmax + (int64_t)grp * p.nT * G;
+    const float* tsum = p.tsum + (int64_t)grp * p.nT * G;
+
+    // accepted tiles of a round: list, bits, count
+    auto accept = [&](uint64_t acc, int t) {
+        if ((acc >> lane) & 1ull) {
+            klist[kept + __builtin_popcountll(acc & lt_mask)] = t;
+            if (p.bits) atomicOr(p.bits + (int64_t)grp * p.nwords + t / 32, 1u << (t % 32));
+        }
+        kept += __builtin_popcountll(acc);
+    };
+
+    float Mn[GP], Sn[GP];                 // next chunk's tile statistics (prefetched)
+    auto load_chunk = [&](int c) {
+        const int t = p.nT - 1 - (c * 64 + lane);
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            Mn[g] = kNegInf;
+            Sn[g] = 0.f;
+            if (g < G && t >= 0 && c < nchunk) {
+                Mn[g] = tmax[(int64_t)t * G + g];
+                Sn[g] = tsum[(int64_t)t * G + g];
+            }
+        }
+    };
+    load_chunk(0);
     for (int c = 0; c < nchunk; ++c) {
-        const int t = p.nT - 1 - (c * 64 + lane);        // newest first
+        const int t = p.nT - 1 - (c * 64 + lane);
         const bool valid = t >= 0;
         float Mg[GP], Sg[GP];
 #pragma unroll
+        for (int g = 0; g < GP; ++g) { Mg[g] = Mn[g]; Sg[g] = Sn[g]; }
+        load_chunk(c + 1);
+        const bool empty0 = l[0] == 0.f;
+        // reference exponents and the range check of the fast path
+        float ref[GP];
+        bool fast = lin_ok;
+#pragma unroll
         for (int g = 0; g < GP; ++g) {
-            Mg[g] = kNegInf;
-            Sg[g] = 0.f;
-            if (g < G && valid) {
-                Mg[g] = p.tmax[((int64_t)grp * p.nT + t) * G + g];
-                Sg[g] = p.tsum[((int64_t)grp * p.nT + t) * G + g];
-            }
+            ref[g] = 0.f;
+            if (g >= G) continue;
+            ref[g] = fmaxf(m[g], wave_max_all(Mg[g]));
+            const float lo = wave_min_all(valid ? Mg[g] : ref[g]);
+            fast = fast && (lo >= ref[g] - 96.f) && (empty0 || m[g] >= ref[g] - 96.f);
         }
         int pos = 0;
+        if (fast) {
+            float a[GP], x[GP], Z[GP];
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                a[g] = 0.f; x[g] = 0.f; Z[g] = 0.f;
+                if (g >= G) continue;
+                a[g] = valid ? fast_exp2(Mg[g] - ref[g]) : 0.f;
+                x[g] = Sg[g] * a[g];
+                Z[g] = empty0 ? 0.f : l[g] * fast_exp2(m[g] - ref[g]);
+            }
+            bool empty = empty0;
+            while (pos < 64) {
+                const bool active = valid && lane >= pos;
+                bool v0 = empty;
+#pragma unroll
+                for (int g = 0; g < GP; ++g)
+                    if (g < G) v0 = v0 || (a[g] >= cthr * Z[g]);
+                v0 = v0 && active;
+                const uint64_t K0 = __ballot(v0);
+                if (K0 == 0ull) break;                    // the rest of the chunk is skipped
+                const int first = __builtin_ctzll(K0);
+                float inc[GP], exc[GP];
+                bool v1 = empty && lane == first;         // nothing retained before it
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    inc[g] = 0.f; exc[g] = 0.f;
+                    if (g >= G) continue;
+                    const float xv = v0 ? x[g] : 0.f;
+                    inc[g] = wave_incl_sum(xv);
+                    exc[g] = inc[g] - xv;
+                    v1 = v1 || (a[g] >= cthr * (Z[g] + exc[g]));
+                }
+                v1 = v1 && v0;
+                const uint64_t flips = __ballot(v0 && !v1);
+                uint64_t acc;
+                int src;
+                bool use_exc;
+                if (flips == 0ull) {
+                    acc = K0; src = 63; use_exc = false;
+                } else {
+                    const int f = __builtin_ctzll(flips);
+                    acc = K0 & ((f == 0) ? 0ull : (~0ull >> (64 - f)));
+                    src = f; use_exc = true;
+                    pos = f + 1;
+                }
+                accept(acc, t);
+                if (acc) empty = false;
+#pragma unroll
+                for (int g = 0; g < GP; ++g)
+                    if (g < G) Z[g] += readlane_f(use_exc ? exc[g] : inc[g], src);
+                if (flips == 0ull) break;
+            }
+#pragma unroll
+            for (int g = 0; g < GP; ++g)
+                if (g < G && !empty) { m[g] = ref[g]; l[g] = Z[g]; }
+            continue;
+        }
+        // ---- log-domain rounds (same structure) for chunks outside the fast range
+        float thr[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) thr[g] = (l[g] > 0.f) ? m[g] + fast_log2(l[g]) + theta : kNegInf;
         while (pos < 64) {
             const bool active = valid && lane >= pos;
             bool v0 = false;
@@ -205,12 +368,12 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
                 if (g < G) v0 |= (l[g] == 0.f) || (Mg[g] >= thr[g]);
             v0 = v0 && active;
             const uint64_t K0 = __ballot(v0);
-            if (K0 == 0ull) break;                        // the rest of the chunk is skipped
-            // exclusive prefix (over candidates) of the tile masses, per row
+            if (K0 == 0ull) break;
             float em[GP], el[GP], im[GP], il[GP];
             bool v1 = false;
 #pragma unroll
             for (int g = 0; g < GP; ++g) {
+                em[g] = kNegInf; el[g] = 0.f; im[g] = kNegInf; il[g] = 0.f;
                 if (g >= G) continue;
                 float xm = v0 ? Mg[g] : kNegInf, xl = v0 ? Sg[g] : 0.f;
 #pragma unroll
@@ -222,11 +385,10 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
                         xm = tm; xl = tl;
                     }
                 }
-                im[g] = xm; il[g] = xl;                    // inclusive
+                im[g] = xm; il[g] = xl;
                 float pm = __shfl_up(xm, 1), pl = __shfl_up(xl, 1);
                 if (lane == 0) { pm = kNegInf; pl = 0.f; }
-                em[g] = pm; el[g] = pl;                    // exclusive
-                // retained mass this tile would see: state (+) earlier candidates
+                em[g] = pm; el[g] = pl;
                 float zm = m[g], zl = l[g];
                 lse_combine(zm, zl, pm, pl);
                 v1 |= (zl == 0.f) || (Mg[g] - zm - fast_log2(zl) >= theta);
@@ -234,32 +396,22 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
             v1 = v1 && v0;
             const uint64_t flips = __ballot(v0 && !v1);
             uint64_t acc;
-            int fsrc;                                      // lane whose prefix is the new state
-            bool exclusive;
+            int src;
+            bool use_exc;
             if (flips == 0ull) {
-                acc = K0;
-                fsrc = 63;
-                exclusive = false;
+                acc = K0; src = 63; use_exc = false;
             } else {
                 const int f = __builtin_ctzll(flips);
                 acc = K0 & ((f == 0) ? 0ull : (~0ull >> (64 - f)));
-                fsrc = f;
-                exclusive = true;
+                src = f; use_exc = true;
                 pos = f + 1;
             }
-            if ((acc >> lane) & 1ull) {
-                const int rank = __builtin_popcountll(acc & lt_mask);
-                klist[kept + rank] = t;
-                if (p.bits) atomicOr(p.bits + (int64_t)grp * p.nwords + t / 32, 1u << (t % 32));
-            }
-            kept += __builtin_popcountll(acc);
+            accept(acc, t);
 #pragma unroll
             for (int g = 0; g < GP; ++g) {
                 if (g >= G) continue;
-                const float sm = exclusive ? em[g] : im[g];
-                const float sl = exclusive ? el[g] : il[g];
-                const float nm = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sm), fsrc));
-                const float nl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sl), fsrc));
+                const float nm = readlane_f(use_exc ? em[g] : im[g], src);
+                const float nl = readlane_f(use_exc ? el[g] : il[g], src);
                 lse_combine(m[g], l[g], nm, nl);
                 thr[g] = (l[g] > 0.f) ? m[g] + fast_log2(l[g]) + theta : kNegInf;
             }
@@ -291,7 +443,6 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
     constexpr int KPT = 4 * BKD / NKG;
     __shared__ float sP[GP][4 * BKD];
     __shared__ float sRed[NKG][D];
-    __shared__ int sLast;
     const int tid = threadIdx.x;
     const int s = blockIdx.x, grp = blockIdx.y;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
@@ -354,37 +505,47 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
         }
         __syncthreads();
     }
-    // reduce over key groups, add into the fp32 output accumulator
-    float* oacc = p.o_acc + (int64_t)grp * G * D;
-    if (i0 < i1) {
-        for (int g = 0; g < G; ++g) {
+    // reduce over key groups into this split's partial output (zeros when the
+    // split has no retained tile)
+    float* po = p.part_o + (((int64_t)grp * p.nsplit + s) * G) * D;
+    for (int g = 0; g < G; ++g) {
 #pragma unroll
-            for (int gg = 0; gg < GP; ++gg)
-                if (gg == g)
+        for (int gg = 0; gg < GP; ++gg)
+            if (gg == g)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) sRed[kg][8 * dc + e] = acc[gg][e];
-            __syncthreads();
-            if (tid < D) {
-                float sum = 0.f;
+                for (int e = 0; e < 8; ++e) sRed[kg][8 * dc + e] = acc[gg][e];
+        __syncthreads();
+        if (tid < D) {
+            float sum = 0.f;
 #pragma unroll
-                for (int k2 = 0; k2 < NKG; ++k2) sum += sRed[k2][tid];
-                unsafeAtomicAdd(oacc + (int64_t)g * D + tid, sum);
-            }
-            __syncthreads();
+            for (int k2 = 0; k2 < NKG; ++k2) sum += sRed[k2][tid];
+            po[(int64_t)g * D + tid] = sum;
         }
+        __syncthreads();
     }
-    // the last workgroup of the group converts the accumulator to bf16
-    __threadfence();
+}
+
+// Sum of the split partials (already normalised by the final LSE) -> bf16 o.
+// One workgroup per (group, row, 32-wide d slice): 8 split classes x 32 d.
+template <int D>
+__global__ __launch_bounds__(256) void mala_dec_sum_combine(const DecParams p) {
+    __shared__ float sO[8][32];
+    const int tid = threadIdx.x;
+    const int grp = blockIdx.x, g = blockIdx.y, dq = blockIdx.z;
+    const int G = p.G;
+    const int b = grp / p.Hkv, kh = grp % p.Hkv;
+    const int64_t base = (int64_t)grp * p.nsplit;
+    const int d = 32 * dq + (tid & 31), cls = tid >> 5;
+    float osum = 0.f;
+#pragma unroll 4
+    for (int s = cls; s < p.nsplit; s += 8) osum += p.part_o[((base + s) * G + g) * D + d];
+    sO[cls][tid & 31] = osum;
     __syncthreads();
-    if (tid == 0) sLast = (atomicAdd(p.done + grp, 1) == p.nsplit - 1) ? 1 : 0;
-    __syncthreads();
-    if (sLast) {
-        __threadfence();
-        for (int e = tid; e < G * D; e += 256) {
-            const float x = __hip_atomic_load(oacc + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int g = e / D, d = e % D;
-            p.o[((int64_t)b * p.Hq + kh * G + g) * D + d] = (uint16_t)float_to_bf16_bits(x);
-        }
+    if (tid < 32) {
+        float o = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o += sO[c][tid];
+        p.o[((int64_t)b * p.Hq + kh * G + g) * D + 32 * dq + tid] = (uint16_t)float_to_bf16_bits(o);
     }
 }
 
@@ -592,9 +753,12 @@ static hipError_t launch_decode_t(const DecParams& p, bool dense, hipStream_t s)
         hipLaunchKernelGGL((mala_dec_dense_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     } else {
         const int tasks = ngrp * p.nT;
-        hipLaunchKernelGGL((mala_dec_score<D>), dim3((tasks + 3) / 4), dim3(256), 0, s, p);
+        int nwg = (tasks + 3) / 4;
+        if (nwg > 256) nwg = 256;        // one workgroup (128 KB of K in flight) per CU
+        hipLaunchKernelGGL((mala_dec_score<D>), dim3(nwg), dim3(256), 0, s, p);
         hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(64), 0, s, p);
         hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3(p.nsplit, ngrp), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_sum_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     }
     return hipGetLastError();
 }

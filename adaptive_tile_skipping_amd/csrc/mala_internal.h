@@ -78,8 +78,6 @@ struct DecParams {
     float* lse2;            // [B, Hkv, G]      base-2 final log-normaliser
     float* part_o;          // [B, Hkv, nsplit, G, d] partial outputs
     float* part_ml;         // [B, Hkv, nsplit, G, 2] partial (max, sum) (dense path)
-    float* o_acc;           // [B, Hkv, G, d] fp32 output accumulator (kept-tile path)
-    int32_t* done;          // [B, Hkv] finished P.V workgroups (kept-tile path)
 };
 
 hipError_t launch_fwd(const FwdParams& p, int d, int Bq, int Bk, bool stats, hipStream_t s);
