@@ -205,15 +205,20 @@ __device__ __forceinline__ float wave_incl_sum(float x) {
     x += dpp_f<0x143, 0xC, false>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
-__device__ __forceinline__ float wave_max_all(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
+// Maximum over the wave (lanes whose source is out of range keep -inf).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_max_step(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(kNegInf), __float_as_int(v), CTRL,
+                                                                ROWMASK, 0xF, false)));
 }
-__device__ __forceinline__ float wave_min_all(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fminf(x, __shfl_xor(x, off));
-    return x;
+__device__ __forceinline__ float wave_max_all(float x) {
+    x = dpp_max_step<0x111, 0xF>(x);
+    x = dpp_max_step<0x112, 0xF>(x);
+    x = dpp_max_step<0x114, 0xF>(x);
+    x = dpp_max_step<0x118, 0xF>(x);
+    x = dpp_max_step<0x142, 0xA>(x);
+    x = dpp_max_step<0x143, 0xC>(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 __device__ __forceinline__ float readlane_f(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
@@ -265,57 +270,79 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
         kept += __builtin_popcountll(acc);
     };
 
-    float Mn[GP], Sn[GP];                 // next chunk's tile statistics (prefetched)
-    auto load_chunk = [&](int c) {
-        const int t = p.nT - 1 - (c * 64 + lane);
+    // Tile statistics stream through an LDS ring of RING chunk slots, DEPTH
+    // chunks ahead, with buffer-resource copies (reads before tile 0 return 0).
+    // Slot layout: [max | sum][64 * GP] floats, tile t_lo + i at entry i * G + g.
+    constexpr int DEPTH = (63 / (2 * GP)) < 7 ? ((63 / (2 * GP)) < 1 ? 1 : 63 / (2 * GP)) : 7;
+    constexpr int RING = DEPTH + 1;
+    __shared__ float sStat[RING][2][64 * GP];
+    const __amdgpu_buffer_rsrc_t rmax = make_rsrc(tmax, (uint32_t)(p.nT * G * 4));
+    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(tsum, (uint32_t)(p.nT * G * 4));
+    auto issue_chunk = [&](int c) {
+        const int t_lo = p.nT - 64 * (c + 1);          // may be negative
+        const uint32_t base = (uint32_t)(t_lo * G * 4);
+        float* dm = sStat[c % RING][0];
+        float* ds = sStat[c % RING][1];
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            Mn[g] = kNegInf;
-            Sn[g] = 0.f;
-            if (g < G && t >= 0 && c < nchunk) {
-                Mn[g] = tmax[(int64_t)t * G + g];
-                Sn[g] = tsum[(int64_t)t * G + g];
-            }
+        for (int i = 0; i < GP; ++i) {
+            const uint32_t off = base + (uint32_t)((64 * i + lane) * 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rmax, (__attribute__((address_space(3))) void*)(dm + 64 * i), 4,
+                                                    (int)off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsum, (__attribute__((address_space(3))) void*)(ds + 64 * i), 4,
+                                                    (int)off, 0, 0, 0);
         }
     };
-    load_chunk(0);
+    for (int c = 0; c < DEPTH; ++c)
+        if (c < nchunk) issue_chunk(c);
     for (int c = 0; c < nchunk; ++c) {
         const int t = p.nT - 1 - (c * 64 + lane);
         const bool valid = t >= 0;
+        if (c + DEPTH < nchunk) {
+            issue_chunk(c + DEPTH);
+            wait_vmcnt<DEPTH * 2 * GP>();
+        } else {
+            wait_vmcnt<0>();
+        }
         float Mg[GP], Sg[GP];
+        {
+            const float* sm = sStat[c % RING][0];
+            const float* ss = sStat[c % RING][1];
+            const int i = 63 - lane;                   // t - t_lo
 #pragma unroll
-        for (int g = 0; g < GP; ++g) { Mg[g] = Mn[g]; Sg[g] = Sn[g]; }
-        load_chunk(c + 1);
+            for (int g = 0; g < GP; ++g) {
+                Mg[g] = (g < G && valid) ? sm[i * G + g] : kNegInf;
+                Sg[g] = (g < G && valid) ? ss[i * G + g] : 0.f;
+            }
+        }
         const bool empty0 = l[0] == 0.f;
-        // reference exponents and the range check of the fast path
+        // reference exponents and the range check of the fast path; every loop
+        // over rows runs all GP slots branch-free (rows >= G are inert)
         float ref[GP];
-        bool fast = lin_ok;
+        bool fast = lin_ok, lane_ok = true;
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-            ref[g] = 0.f;
-            if (g >= G) continue;
-            ref[g] = fmaxf(m[g], wave_max_all(Mg[g]));
-            const float lo = wave_min_all(valid ? Mg[g] : ref[g]);
-            fast = fast && (lo >= ref[g] - 96.f) && (empty0 || m[g] >= ref[g] - 96.f);
+            const bool row = g < G;
+            ref[g] = row ? fmaxf(m[g], wave_max_all(Mg[g])) : 0.f;
+            lane_ok = lane_ok && (!row || !valid || Mg[g] >= ref[g] - 96.f);
+            fast = fast && (!row || empty0 || m[g] >= ref[g] - 96.f);
         }
+        fast = fast && (__ballot(!lane_ok) == 0ull);
         int pos = 0;
         if (fast) {
             float a[GP], x[GP], Z[GP];
 #pragma unroll
             for (int g = 0; g < GP; ++g) {
-                a[g] = 0.f; x[g] = 0.f; Z[g] = 0.f;
-                if (g >= G) continue;
-                a[g] = valid ? fast_exp2(Mg[g] - ref[g]) : 0.f;
+                const bool row = g < G;
+                a[g] = (row && valid) ? fast_exp2(Mg[g] - ref[g]) : 0.f;
                 x[g] = Sg[g] * a[g];
-                Z[g] = empty0 ? 0.f : l[g] * fast_exp2(m[g] - ref[g]);
+                Z[g] = !row ? 1.f : (empty0 ? 0.f : l[g] * fast_exp2(m[g] - ref[g]));
             }
             bool empty = empty0;
             while (pos < 64) {
                 const bool active = valid && lane >= pos;
                 bool v0 = empty;
 #pragma unroll
-                for (int g = 0; g < GP; ++g)
-                    if (g < G) v0 = v0 || (a[g] >= cthr * Z[g]);
+                for (int g = 0; g < GP; ++g) v0 = v0 || (a[g] >= cthr * Z[g]);
                 v0 = v0 && active;
                 const uint64_t K0 = __ballot(v0);
                 if (K0 == 0ull) break;                    // the rest of the chunk is skipped
@@ -324,8 +351,6 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
                 bool v1 = empty && lane == first;         // nothing retained before it
 #pragma unroll
                 for (int g = 0; g < GP; ++g) {
-                    inc[g] = 0.f; exc[g] = 0.f;
-                    if (g >= G) continue;
                     const float xv = v0 ? x[g] : 0.f;
                     inc[g] = wave_incl_sum(xv);
                     exc[g] = inc[g] - xv;
@@ -347,13 +372,14 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
                 accept(acc, t);
                 if (acc) empty = false;
 #pragma unroll
-                for (int g = 0; g < GP; ++g)
-                    if (g < G) Z[g] += readlane_f(use_exc ? exc[g] : inc[g], src);
+                for (int g = 0; g < GP; ++g) Z[g] += readlane_f(use_exc ? exc[g] : inc[g], src);
                 if (flips == 0ull) break;
             }
+            if (!empty) {
 #pragma unroll
-            for (int g = 0; g < GP; ++g)
-                if (g < G && !empty) { m[g] = ref[g]; l[g] = Z[g]; }
+                for (int g = 0; g < GP; ++g)
+                    if (g < G) { m[g] = ref[g]; l[g] = Z[g]; }
+            }
             continue;
         }
         // ---- log-domain rounds (same structure) for chunks outside the fast range
@@ -768,6 +794,7 @@ static hipError_t launch_decode_d(const DecParams& p, bool dense, hipStream_t s)
     if (p.G <= 1) return launch_decode_t<D, 1>(p, dense, s);
     if (p.G <= 2) return launch_decode_t<D, 2>(p, dense, s);
     if (p.G <= 4) return launch_decode_t<D, 4>(p, dense, s);
+    if (p.G == 5) return launch_decode_t<D, 5>(p, dense, s);    // 40q / 8kv head models
     if (p.G <= 8) return launch_decode_t<D, 8>(p, dense, s);
     return launch_decode_t<D, 16>(p, dense, s);
 }
