@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--tau", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison")
-    ap.add_argument("--cpu-blocks", type=int, default=8, help="query blocks per head in the CPU sample")
+    ap.add_argument("--cpu-blocks", type=int, default=48, help="query blocks per head in the CPU sample")
     return ap.parse_args()
 
 
