@@ -93,6 +93,9 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
     if (!t4_ok(q, true) || !t4_ok(k, true) || !t4_ok(v, true) || !t4_ok(o, true) || !lse)
         return MALA_ERR_INVALID_ARG;
     if (!fwd_shape_supported(d, Bq, Bk)) return MALA_ERR_UNSUPPORTED;
+    // one KV head's keys and its fp16 V copy are addressed through 32-bit buffer ranges
+    if (((int64_t)(L - 1) * k.sl + d) * 2 > INT32_MAX || (int64_t)(L + Bq) * d * 2 > INT32_MAX)
+        return MALA_ERR_UNSUPPORTED;
     const size_t need = mala_fwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk);
     if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
     FwdParams p;

@@ -94,15 +94,24 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_elem) {
     return __builtin_bit_cast(u32x2, x);
 }
 
-// Raw buffer resource over `nbytes` bytes at `base` (reads past the end
-// return zero, dword by dword), and the matching 16-byte global -> LDS copy
-// at byte offset voffset (per lane) + soffset (uniform).
+// Raw buffer resource over `nbytes` bytes at `base`, and the matching 16-byte
+// global -> LDS copy at per-lane byte offset voffset.  The range check covers
+// the per-lane offset: lanes whose 16 bytes lie past `nbytes` read zero, dword
+// by dword.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
 __device__ __forceinline__ void buffer16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset, void* lds_wave_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
                                             (int)voffset, 0, 0, 0);
+}
+// Same with a wave-uniform byte offset added from a scalar register.  The
+// scalar offset is not part of the range check, so use this form only where
+// every access is known to stay inside the resource.
+__device__ __forceinline__ void buffer16_to_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
+                                                  void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                            (int)voffset, (int)soffset, 0, 0);
 }
 
 // Wait for every outstanding memory operation of this wave (including the

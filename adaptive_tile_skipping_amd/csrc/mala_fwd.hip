@@ -116,28 +116,33 @@ void mala_fwd_kernel(const FwdParams p) {
         }
     }
 
-    auto copy_k = [&](int kt, int buf) {
+    // K and V tiles move global -> LDS through buffer resources with fixed
+    // per-lane byte offsets.  K: one resource per tile, starting at the tile and
+    // ending at key L-1, so rows past L read as zero (they are masked by
+    // causality).  V: one resource over the padded fp16 copy, the tile offset
+    // in a scalar (every access stays inside the copy).
+    uint32_t koff[INST], voff[INST];
 #pragma unroll
-        for (int n = 0; n < INST; ++n) {
-            const int slot0 = (n * NW + w) * 64;
-            const int sl = slot0 + lane;
-            const int r = sl / QCH, pc = sl % QCH;
-            const int c = pc ^ (r % QCH);
-            int j = kt * BK + r;
-            j = j < L ? j : L - 1;               // rows past L are masked by causality
-            load16_to_lds(kbase + (int64_t)j * p.k_sl + 8 * c, reinterpret_cast<unsigned char*>(sK[buf]) + slot0 * 16);
-        }
+    for (int n = 0; n < INST; ++n) {
+        const int sl = (n * NW + w) * 64 + lane;
+        const int r = sl / QCH, pc = sl % QCH;
+        koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
+        voff[n] = (uint32_t)((r * D + 8 * (pc ^ ((4 * (r & 3)) % QCH))) * 2);
+    }
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhbase, (uint32_t)((int64_t)p.Lpad * D * 2));
+    auto copy_k = [&](int kt, int buf) {
+        const int j0 = kt * BK;
+        const __amdgpu_buffer_rsrc_t krs =
+            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(L - 1 - j0) * p.k_sl + D) * 2));
+#pragma unroll
+        for (int n = 0; n < INST; ++n)
+            buffer16_to_lds(krs, koff[n], reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
     };
     auto copy_v = [&](int kt, int buf) {
+        const uint32_t so = (uint32_t)(kt * BK * D * 2);
 #pragma unroll
-        for (int n = 0; n < INST; ++n) {
-            const int slot0 = (n * NW + w) * 64;
-            const int sl = slot0 + lane;
-            const int r = sl / QCH, pc = sl % QCH;
-            const int c = pc ^ ((4 * (r & 3)) % QCH);
-            load16_to_lds(vhbase + (int64_t)(kt * BK + r) * D + 8 * c,
-                          reinterpret_cast<unsigned char*>(sV[buf]) + slot0 * 16);
-        }
+        for (int n = 0; n < INST; ++n)
+            buffer16_to_lds_s(vrs, voff[n], so, reinterpret_cast<unsigned char*>(sV[buf]) + (n * NW + w) * 64 * 16);
     };
     // S^T = K Q^T for the tile in sK[buf]; raw (unscaled) scores
     auto scores = [&](int buf, f32x16* s) {

@@ -39,9 +39,10 @@
  *     take bf16 operands.
  *   - Supported shapes: (d, Bq, Bk) = (128, 128, 64) or (64, 64, 64) for
  *     mala_fwd / mala_bwd; decode takes d = 128 or 64 with Bk_dec = 64.
- *     mala_bwd also needs (Bq * q's L stride + d) * 2 and (Bk * k's L stride +
- *     d) * 2 bytes <= INT32_MAX (a query block or key tile is addressed
- *     through a 32-bit buffer range).
+ *     Byte ranges addressed through 32-bit buffer resources must stay within
+ *     INT32_MAX: mala_fwd needs ((L-1) * k's L stride + d) * 2 and
+ *     (L + Bq) * d * 2; mala_bwd needs (Bq * q's L stride + d) * 2 and
+ *     (Bk * k's L stride + d) * 2.
  *     Anything else returns MALA_ERR_UNSUPPORTED.
  */
 #ifndef MALA_H_
