@@ -33,6 +33,8 @@
 //   - Causal masking only on diagonal (or ragged) tiles; the 1/sqrt(d) scale
 //     is folded into the exponent's FMA; the accumulator is rescaled only when
 //     some row's running max moved.
+#include <type_traits>
+
 #include "mala_device.h"
 #include "mala_internal.h"
 
@@ -226,58 +228,121 @@ void mala_fwd_kernel(const FwdParams p) {
     copy_k(kt_first, kt_first & 1);
     if (kt_first >= 1) copy_k(kt_first - 1, (kt_first - 1) & 1);
     wait_all_then_barrier();
-    f32x16 scur[2];
-    scores(kt_first & 1, scur);
-    float Mraw = mask_max(kt_first, scur);
+    f32x16 sA[2], sB[2];         // scores: of the tile being decided / of the next tile
+    f16x8 pp[4];                 // P of the pending tile, then of the tile being kept
+    scores(kt_first & 1, sA);
+    float Mraw = mask_max(kt_first, sA);
 
-    bool pending = false;
+    bool pending = false;        // P.V of the last kept tile not yet accumulated
     int pend_buf = 0;
     float pend_alpha = 1.f;
-    f16x8 pend_p[4];
 
-    for (int kt = kt_first; kt >= 0; --kt) {
+    // One tile: decide tile kt from (m, l); then, in one straight-line block per
+    // (keep, pending) case, issue the P.V MFMAs of the pending tile, then the
+    // score MFMAs of tile kt-1 interleaved with the softmax of tile kt (whose P
+    // reuses the registers the P.V just consumed).  scur/snext swap roles from
+    // one tile to the next (the loop is unrolled by two), so no copies.
+    auto tile = [&](int kt, f32x16* scur, f32x16* snext) {
         const int buf = kt & 1;
-        // ---- keep decision for tile kt (state holds every kept tile > kt)
         const float M = Mraw * c2;
         const bool has = Mraw > kNegInf;
         const bool vote = has && (lsum == 0.f || M >= thr);
         const bool wave_any = __ballot(vote) != 0ull;
         if (lane == 0) sFlag[buf][w] = wave_any ? 1 : 0;
         wait_all_then_barrier();                 // K(kt-1) and V of the pending tile have landed
-        bool keep = false;
+        int kflag = 0;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) keep |= (sFlag[buf][ww] != 0);
+        for (int ww = 0; ww < NW; ++ww) kflag |= sFlag[buf][ww];
+        // identical in every lane: make the branches below scalar
+        const bool keep = __builtin_amdgcn_readfirstlane(kflag) != 0;
 
         if (keep) copy_v(kt, buf);
         if (kt >= 2) copy_k(kt - 2, buf);
-
-        f32x16 snext[2];
-        if (kt >= 1) scores(buf ^ 1, snext);
-
-        if (pending) {
-            if (__ballot(pend_alpha != 1.f) != 0ull) {
+        if (pending && __ballot(pend_alpha != 1.f) != 0ull) {
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
-            }
-            pv(pend_buf, pend_p, acc);
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
         }
+        float mn = m2, muse = 0.f, alpha = 1.f;
+        if (keep) {
+            mn = fmaxf(m2, M);
+            muse = (mn == kNegInf) ? 0.f : mn;
+            alpha = fast_exp2(m2 - muse);
+        }
+        float ps0 = 0.f, ps1 = 0.f;
+        const uint16_t* kb = sK[buf ^ 1];        // K(kt-1); stale but harmless when kt == 0
+        const uint16_t* vb = sV[pend_buf];
+        // P.V of the pending tile (MFMA and LDS only).  Operand reads run two
+        // MFMAs ahead through small register rings, and a scheduling barrier
+        // closes every step, so the compiler keeps this order instead of
+        // hoisting every LDS read.
+        if (pending) {
+            constexpr int NPV = 4 * DT;
+            const int j16 = lane & 15;
+            const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+            auto vread = [&](int s2) -> f16x8 {
+                const int dt = s2 % DT, ks = s2 / DT;
+                u32x2 half2x[2];
+#pragma unroll
+                for (int rd = 0; rd < 2; ++rd) {
+                    const int vrow = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
+                    const int col = 32 * dt + dsel;
+                    const int phys = ((col >> 3) ^ ((4 * (vrow & 3)) % QCH)) * 8 + (col & 7);
+                    half2x[rd] = lds_read_tr16(vb + vrow * D + phys);
+                }
+                // whole-dword assembly of the operand (element-wise 16-bit inserts
+                // of the transposed results are not reliable with this compiler)
+                const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
+                return __builtin_bit_cast(f16x8, w4);
+            };
+            f16x8 vq[3];
+            vq[0] = vread(0);
+            vq[1] = vread(1);
+#pragma unroll
+            for (int s2 = 0; s2 < NPV; ++s2) {
+                if (s2 + 2 < NPV) vq[(s2 + 2) % 3] = vread(s2 + 2);
+                const int dt = s2 % DT, ks = s2 / DT;
+                acc[dt] = mfma32x32x16_f16(vq[s2 % 3], pp[ks], acc[dt]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // Scores of tile kt-1, with the softmax of tile kt (when kept) spread
+        // over the MFMA steps; its P reuses the registers the P.V consumed.
+        auto body = [&](auto keep_c) {
+            constexpr bool KEEP = decltype(keep_c)::value;
+            constexpr int NS = 2 * KSTEPS;       // score MFMAs of one tile
+            constexpr int EPS = 32 / NS;         // softmax elements per score MFMA
+            auto kread = [&](int s2) -> bf16x8 {
+                const int sub = s2 & 1, st = s2 >> 1;
+                const int row = 32 * sub + l32;
+                return *(const bf16x8*)(&kb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
+            };
+            bf16x8 kq[3];
+            kq[0] = kread(0);
+            kq[1] = kread(1);
+#pragma unroll
+            for (int s2 = 0; s2 < NS; ++s2) {
+                if (s2 + 2 < NS) kq[(s2 + 2) % 3] = kread(s2 + 2);
+                const int sub = s2 & 1, st = s2 >> 1;
+                snext[sub] = mfma32x32x16(kq[s2 % 3], qf[st], st == 0 ? f32x16{} : snext[sub]);
+                if (KEEP) {
+#pragma unroll
+                    for (int e2 = 0; e2 < EPS; ++e2) {
+                        const int e = s2 * EPS + e2;
+                        const int sx = e >> 4, r = e & 15;
+                        const float ex = fast_exp2(__builtin_fmaf(scur[sx][r], c2, -muse));
+                        if (e2 & 1) ps1 += ex; else ps0 += ex;
+                        pp[2 * sx + (r >> 3)][r & 7] = to_f16(ex);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (keep) body(std::true_type{});
+        else body(std::false_type{});
+
         pending = false;
         if (keep) {
-            // online-softmax statistics of this row for tile kt; P for the next iteration
-            const float mn = fmaxf(m2, M);
-            const float muse = (mn == kNegInf) ? 0.f : mn;
-            const float alpha = fast_exp2(m2 - muse);
-            float psum = 0.f;
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(__builtin_fmaf(scur[sub][r], c2, -muse));
-                    psum += e;
-                    pend_p[2 * sub + (r >> 3)][r & 7] = to_f16(e);
-                }
-            }
-            psum = wave_sum_pair(psum);
+            const float psum = wave_sum_pair(ps0 + ps1);
             lsum = lsum * alpha + psum;
             m2 = mn;
             thr = (lsum > 0.f) ? m2 + fast_log2(lsum) + theta : kNegInf;
@@ -292,26 +357,28 @@ void mala_fwd_kernel(const FwdParams p) {
             bitword |= 1u << (kt & 31);
         } else if (STATS) {
             if (has) {
-                const float mn = fmaxf(om, M);
+                const float on = fmaxf(om, M);
                 float osum = 0.f;
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) osum += fast_exp2(__builtin_fmaf(scur[sub][r], c2, -mn));
+                    for (int r = 0; r < 16; ++r) osum += fast_exp2(__builtin_fmaf(scur[sub][r], c2, -on));
                 osum = wave_sum_pair(osum);
-                ol = ol * fast_exp2(om - mn) + osum;
-                om = mn;
+                ol = ol * fast_exp2(om - on) + osum;
+                om = on;
             }
         }
         if (want_bits && tid == 0 && ((kt & 31) == 0)) {
             bitrow[kt >> 5] = bitword;
             bitword = 0;
         }
-        if (kt >= 1) {
-            scur[0] = snext[0];
-            scur[1] = snext[1];
-            Mraw = mask_max(kt - 1, scur);
-        }
+        if (kt >= 1) Mraw = mask_max(kt - 1, snext);
+    };
+
+    for (int kt = kt_first; kt >= 0; --kt) {
+        tile(kt, sA, sB);
+        sA[0] = sB[0];
+        sA[1] = sB[1];
     }
     if (pending) {
         wait_all_then_barrier();
@@ -319,7 +386,7 @@ void mala_fwd_kernel(const FwdParams p) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
         }
-        pv(pend_buf, pend_p, acc);
+        pv(pend_buf, pp, acc);
     }
 
     // ---- epilogue: O = acc / l, LSE = (m2 + log2 l) ln 2
