@@ -41,7 +41,49 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison")
     ap.add_argument("--cpu-blocks", type=int, default=48, help="query blocks per head in the CPU sample")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run two forward launches and a plain 1 GiB device copy, then exit (for PMC passes)")
     return ap.parse_args()
+
+
+# The forward kernel's HBM traffic comes from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) over `bench.py --traffic-probe`, calibrated against
+# the plain copy kernel the probe runs; the summary records the figures and a
+# hash of the kernel sources they were taken with.  A source change voids them.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mala_fwd_kernel_train_128k_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "adaptive_tile_skipping_amd", "csrc", f)
+                  for f in ("mala_fwd.hip", "mala_device.h", "mala_internal.h", "mala_api.hip")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per forward launch from the committed PMC summary, or None when
+    the summary is missing or was taken with other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`")
+        if ":" in line:
+            k, _, v = line.partition(":")
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def legal_pairs_block(L, Bq, qb):
@@ -101,6 +143,19 @@ def main():
 
     def dec(t):
         mala.mala_decode(qd, kc, vc, t, 64, o=od, lse=lsed, kept_tiles=keptd, ws=dws)
+
+    if args.traffic_probe:
+        fwd(tau)
+        torch.cuda.synchronize()
+        fwd(tau)
+        torch.cuda.synchronize()
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": "2 x mala_fwd (train_128k, tau=%g) + 1 GiB device copy" % tau,
+                          "copy_bytes": src.numel() * 4}), flush=True)
+        return
 
     def timed_steps(t, steps, warmup):
         for _ in range(warmup):
@@ -178,12 +233,13 @@ def main():
     value = (dense_fwd + dense_bwd + dense_dec) / (ms_step * 1e-3) / 1e12
 
     # ---- roofline of the dominant kernel (by measured time)
-    cand = {"mala_fwd_kernel": (fwd_ms, alg_fwd), "mala_bwd (pre+main+convert)": (bwd_ms, alg_bwd)}
+    cand = {"mala_fwd_kernel": (fwd_ms, alg_fwd), "mala_bwd (pre+scan+gradient+convert)": (bwd_ms, alg_bwd)}
     dom = max(cand, key=lambda n: cand[n][0])
     dms, dflop = cand[dom]
     achieved = dflop / (dms * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic() if dom == "mala_fwd_kernel" else None,
                 "algorithmic_tflop_per_launch": round(dflop / 1e12, 3), "launch_ms": round(dms, 4)}
 
     out = {
