@@ -129,15 +129,14 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
 
 size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk) {
     if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
-    const size_t rows = (size_t)B * Hq * L;
     const size_t Lpad = (size_t)((L + Bq - 1) / Bq) * Bq;
     const size_t prow = (size_t)B * Hq * Lpad;
     const size_t tr = (size_t)B * Hq * d * Lpad * 2;
     const size_t nQB = Lpad / Bq, nKT = (size_t)(L + Bk - 1) / Bk;
     const size_t nwT = ((size_t)(Hq / Hkv) * nQB + 31) / 32;
     const size_t tb = (size_t)B * Hkv * nKT * nwT * sizeof(uint32_t);
-    return align256(rows * d * sizeof(float)) + 2 * align256(prow * sizeof(float)) + 2 * align256(tr) +
-           align256(tb);
+    const size_t qbb = (size_t)B * Hq * nQB * ((nKT + 31) / 32) * sizeof(uint32_t);
+    return 2 * align256(prow * sizeof(float)) + 2 * align256(tr) + align256(tb) + align256(qbb);
 }
 
 mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, const float* lse,
@@ -151,7 +150,8 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     if (bwd_stats && bwd_stats->omitted_mass) return MALA_ERR_INVALID_ARG;
     if (!fwd_shape_supported(d, Bq, Bk)) return MALA_ERR_UNSUPPORTED;
     // a query block is read through one buffer resource (32-bit byte range)
-    if (((int64_t)Bq * q.sl + d) * 2 > INT32_MAX || ((int64_t)Bk * k.sl + d) * 2 > INT32_MAX)
+    if (((int64_t)Bq * q.sl + d) * 2 > INT32_MAX || ((int64_t)(L - 1) * k.sl + d) * 2 > INT32_MAX ||
+        ((int64_t)(L - 1) * v.sl + d) * 2 > INT32_MAX)
         return MALA_ERR_UNSUPPORTED;
     const size_t need = mala_bwd_workspace_size(B, L, Hq, Hkv, d, Bq, Bk);
     if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
@@ -160,9 +160,7 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     p.q = (const uint16_t*)q.ptr; p.k = (const uint16_t*)k.ptr; p.v = (const uint16_t*)v.ptr;
     p.o = (const uint16_t*)o.ptr; p.dout = (const uint16_t*)dout.ptr; p.lse = lse;
     p.dq = (uint16_t*)dq.ptr; p.dk = (uint16_t*)dk.ptr; p.dv = (uint16_t*)dv.ptr;
-    const size_t rows = (size_t)B * Hq * L;
     char* w = (char*)ws;
-    p.dq_acc = (float*)w; w += align256(rows * d * sizeof(float));
     p.Lpad = ((L + Bq - 1) / Bq) * Bq;
     const size_t prow = (size_t)B * Hq * p.Lpad;
     p.rowd = (float*)w; w += align256(prow * sizeof(float));
@@ -171,6 +169,12 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     p.qt = (uint16_t*)w; w += align256(tr);
     p.dot = (uint16_t*)w; w += align256(tr);
     p.tbits = (uint32_t*)w;
+    {
+        const size_t nQB_ = (size_t)((L + Bq - 1) / Bq), nKT_ = (size_t)((L + Bk - 1) / Bk);
+        const size_t nwT_ = ((size_t)(Hq / Hkv) * nQB_ + 31) / 32;
+        w += align256((size_t)B * Hkv * nKT_ * nwT_ * sizeof(uint32_t));
+    }
+    p.qbits = (uint32_t*)w;
     p.q_sb = q.sb; p.q_sl = q.sl; p.q_sh = q.sh;
     p.k_sb = k.sb; p.k_sl = k.sl; p.k_sh = k.sh;
     p.v_sb = v.sb; p.v_sl = v.sl; p.v_sh = v.sh;
@@ -187,6 +191,8 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     p.nslab = (L + 255) / 256;
     p.nunits_scan = p.nslab * B * Hq;
     p.chunk_scan = pick_chunk(Hq, Hkv);
+    p.nunits_dq = B * Hq * p.nQB;
+    p.chunk_dq = pick_chunk(Hq, Hkv);
     p.scale = (float)(1.0 / sqrt((double)d));
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     p.log2_tau = log2_tau(tau);

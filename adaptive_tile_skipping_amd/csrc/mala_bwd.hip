@@ -16,18 +16,18 @@
 // Kernels:
 //   mala_bwd_pre    D_i, LSE_i in base 2, transposed copies of Q and dO (query
 //                   positions permuted inside each 16-group to match the MFMA
-//                   register order), zeroed dQ accumulator, tile bits and
-//                   statistics.
+//                   register order), zeroed tile bits and statistics.
 //   mala_bwd_scan   the decision pass (tau > 0): one workgroup per (batch, q
 //                   head, 256-query slab), 4 waves of 64 queries.  Q and each
 //                   row's threshold stay in registers; key tiles stream from
 //                   the slab's diagonal to key 0 through a triple-buffered LDS
 //                   tile.  The score accumulator starts at minus the row's
 //                   threshold, so a tile is kept iff the masked maximum of the
-//                   accumulator is >= 0.  A kept tile sets one bit of its key
-//                   tile's word row (q head, query block); nothing else is
-//                   written, so skipped tiles cost only the score MFMAs.
-//   mala_bwd_kernel the gradient pass: one workgroup per (batch, KV head, key
+//                   accumulator is >= 0.  A kept tile sets its bit in the key
+//                   tile's word row (q head, query block) and in the query
+//                   block's word row (key tile); nothing else is written, so
+//                   skipped tiles cost only the score MFMAs.
+//   mala_bwd_kernel the dK/dV pass: one workgroup per (batch, KV head, key
 //                   tile of 64 keys), 4 waves, visiting only the kept (q head,
 //                   query block) steps of its key tile (all legal steps when
 //                   tau = 0).  K and V fragments stay in registers; each step's
@@ -36,10 +36,13 @@
 //                   (w>>1) of the block's queries.  S is laid out with one key
 //                   per lane and the block's queries in registers, so P^T and
 //                   dS^T feed the dV and dK contractions straight from
-//                   registers; dS also goes to LDS (query-major) for dQ = dS K.
-//                   dK/dV accumulate in registers over steps; dQ goes to an fp32
-//                   accumulator with atomics.
-//   mala_dq_convert fp32 dQ accumulator -> bf16 dQ.
+//                   registers; dK/dV accumulate in registers over steps.
+//   mala_bwd_dq     the dQ pass: one workgroup per (batch, q head, query
+//                   block), waves of 32 queries, visiting the block's kept key
+//                   tiles (all legal tiles when tau = 0) with K and V tiles
+//                   double-buffered in LDS: S^T = K Q^T and dP^T = V dO^T, then
+//                   dQ^T += K^T dS^T with K^T from LDS transposing reads.  dQ is
+//                   accumulated in registers and written once: no atomics.
 #include "mala_device.h"
 #include "mala_internal.h"
 
@@ -95,6 +98,8 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
         const int64_t fb = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
         const int64_t nw = (int64_t)p.B * p.Hkv * p.nKT * p.nwT;
         for (int64_t idx = fb * 256 + tid; idx < nw; idx += nblk * 256) p.tbits[idx] = 0u;
+        const int64_t nq = (int64_t)p.B * p.Hq * p.nQB * p.nwords;
+        for (int64_t idx = fb * 256 + tid; idx < nq; idx += nblk * 256) p.qbits[idx] = 0u;
     }
     // stage Q and dO rows (zeros past L)
     constexpr int CH = D / 8;
@@ -108,12 +113,6 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
         }
         *(u32x4*)(&sQ[r * TROW + 8 * c]) = xq;
         *(u32x4*)(&sD[r * TROW + 8 * c]) = xg;
-    }
-    // zero the fp32 dQ accumulator rows [B][Hq][L][D]
-    for (int idx = tid; idx < PRE_ROWS * D / 4; idx += 256) {
-        const int r = idx / (D / 4), c = idx % (D / 4);
-        const int i = r0 + r;
-        if (i < L) *(f32x4*)(p.dq_acc + (bh * L + i) * D + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // statistics owned by the query block starting in these rows
     if ((r0 % BQ) == 0) {
@@ -225,6 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     uint32_t* bitrow = p.tbits + (int64_t)(b * p.Hkv + kh) * p.nKT * p.nwT;
     const int bit = (h % p.G) * p.nQB + rw0 / BQ;
+    uint32_t* qrow = p.qbits + (bh * p.nQB + rw0 / BQ) * p.nwords;
 
     for (int it = 0; it < nt; ++it) {
         const int kt = kt_hi - it;
@@ -270,8 +270,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][uu][r]);
             }
-            if (__ballot(mx >= 0.f) != 0ull && lane == 0)
+            if (__ballot(mx >= 0.f) != 0ull && lane == 0) {
                 atomicOr(bitrow + (int64_t)kt * p.nwT + (bit >> 5), 1u << (bit & 31));
+                atomicOr(qrow + (kt >> 5), 1u << (kt & 31));
+            }
         }
         // tile kt-1 (copied during the previous iteration) must have landed
         if (prefetch) wait_vmcnt<KINST>(); else wait_vmcnt<0>();
@@ -334,7 +336,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     constexpr int NQS = BQ / 32;         // query subtiles of the block
     constexpr int WSUB = NQS / 2;        // query subtiles per wave
     constexpr int QCH = D / 8;           // 16-byte chunks per Q row
-    constexpr int SROW = BK + 8;         // LDS row of dS [query][key] and K^T [d][key]
     constexpr int QSLOTS = BQ * QCH;     // 16-byte chunks per Q block
     constexpr int QINST = QSLOTS / 256;  // global->LDS copies per lane per block
     constexpr int NBUF = 3;              // Q blocks in flight: current + two prefetched
@@ -345,8 +346,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
 
     // Q blocks: [NBUF][BQ][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r % QCH)
     __shared__ __attribute__((aligned(16))) unsigned char sU[UBYTES];
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sdS[BQ * SROW];
     // [buf][lse2 | D][query]
     __shared__ __attribute__((aligned(16))) float sRow[NBUF][2][BQ];
     uint16_t* sQ = reinterpret_cast<uint16_t*>(sU);
@@ -385,19 +384,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
             vf[st] = __builtin_bit_cast(bf16x8, c);
         }
     }
-    // ---- K^T into LDS for the dQ contraction (natural key order)
-    for (int idx = tid; idx < BK * QCH; idx += 256) {
-        const int r = idx / QCH, c = idx % QCH;
-        const int j = j0 + r;
-        const u32x4 x = (j < L) ? *(const u32x4*)(p.k + b * p.k_sb + (int64_t)j * p.k_sl + kh * p.k_sh + 8 * c)
-                                : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            sKt[(8 * c + 2 * m) * SROW + r] = (uint16_t)(x[m] & 0xFFFFu);
-            sKt[(8 * c + 2 * m + 1) * SROW + r] = (uint16_t)(x[m] >> 16);
-        }
-    }
-
     f32x16 dv[DT], dk[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) { dv[dt] = f32x16{}; dk[dt] = f32x16{}; }
@@ -511,9 +497,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                         const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e])) : 0.f;
                         const float ds = pr * (dp[t][r] - dd[e]);
                         pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
-                        const __bf16 dsb = to_bf16(ds);
-                        da[2 * t + (r >> 3)][r & 7] = dsb;
-                        sdS[(ql + e) * SROW + 32 * kw + l32] = __builtin_bit_cast(uint16_t, dsb);
+                        da[2 * t + (r >> 3)][r & 7] = to_bf16(ds);
                     }
                 }
             }
@@ -535,28 +519,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                     dk[dt] = mfma32x32x16(da[ks], bq[dt], dk[dt]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
-            __syncthreads();   // dS complete in LDS
-            // ---- dQ += scale dS K, work items (query subtile, d tile) spread over the waves
-            {
-                float* dqblk = p.dq_acc + (bh * L + qb * BQ) * D;
-                for (int item = w; item < NQS * DT; item += 4) {
-                    const int qsub = item / DT, dt = item % DT;
-                    f32x16 acc = f32x16{};
-#pragma unroll
-                    for (int ks = 0; ks < BK / 16; ++ks) {
-                        const bf16x8 a = *(const bf16x8*)(&sdS[(32 * qsub + l32) * SROW + 16 * ks + 8 * hi]);
-                        const bf16x8 bb = *(const bf16x8*)(&sKt[(32 * dt + l32) * SROW + 16 * ks + 8 * hi]);
-                        acc = mfma32x32x16(a, bb, acc);
-                    }
-                    // C[i = query][j = d]: lane = d, registers = queries
-                    float* col = dqblk + 32 * dt + l32;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int qq = 32 * qsub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (qb * BQ + qq < L) unsafeAtomicAdd(col + (int64_t)qq * D, acc[r] * p.scale);
-                    }
-                }
             }
             // ---- statistics of the backward's own decisions
             if (tid == 0) {
@@ -616,23 +578,199 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void mala_dq_convert(const BwdParams p) {
-    const int64_t n = (int64_t)p.B * p.Hq * p.L * (D / 8);
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
-        const int c = (int)(idx % (D / 8));
-        const int64_t row = idx / (D / 8);
-        const int i = (int)(row % p.L);
-        const int64_t bh = row / p.L;
-        const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-        const float* src = p.dq_acc + row * D + 8 * c;
-        const f32x4 a = *(const f32x4*)src, bb = *(const f32x4*)(src + 4);
-        u32x4 o;
-        o[0] = float_to_bf16_bits(a[0]) | (float_to_bf16_bits(a[1]) << 16);
-        o[1] = float_to_bf16_bits(a[2]) | (float_to_bf16_bits(a[3]) << 16);
-        o[2] = float_to_bf16_bits(bb[0]) | (float_to_bf16_bits(bb[1]) << 16);
-        o[3] = float_to_bf16_bits(bb[2]) | (float_to_bf16_bits(bb[3]) << 16);
-        *(u32x4*)(p.dq + b * p.dq_sb + (int64_t)i * p.dq_sl + h * p.dq_sh + 8 * c) = o;
+// K row swizzle of the dQ pass: 16-byte chunk c of row r lives at chunk
+// c ^ kswz(r).  kswz permutes 0..15 over 16 consecutive rows (row-wise 16-byte
+// reads of the score contraction are conflict-free) and gives the four rows of
+// a transposing read four different chunk pairs (the K^T reads of the dQ
+// contraction are conflict-free too).  For d = 64 (8 chunks) only the second
+// property holds.
+template <int QCH>
+__device__ __forceinline__ int kswz(int r) {
+    return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) % QCH;
+}
+
+// dQ pass: see the file comment.  dQ_i = scale * sum over kept tiles of
+// dS_ij k_j, with dS = P (dP - D), P = exp(S - LSE).
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mala_bwd_dq(const BwdParams p) {
+    constexpr int NW = BQ / 32;
+    constexpr int KSTEPS = D / 16;
+    constexpr int DT = D / 32;
+    constexpr int QCH = D / 8;
+    constexpr int INST = BK * QCH / (NW * 64);   // copies per lane per tile (each of K, V)
+    static_assert(INST * NW * 64 == BK * QCH, "shape");
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * D];   // chunk c of row r at c ^ kswz(r)
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][BK * D];   // chunk c of row r at c ^ (r % QCH)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+
+    const int u = xcd_unit(blockIdx.x, p.chunk_dq);
+    if (u >= p.nunits_dq) return;
+    const int nbh = p.B * p.Hq;
+    const int qb = p.nQB - 1 - u / nbh;          // longest blocks first
+    const int64_t bh = u % nbh;
+    const int b = (int)(bh / p.Hq);
+    const int h = (int)(bh % p.Hq);
+    const int kh = h / p.G;
+    const int L = p.L;
+    const int i = qb * BQ + 32 * w + l32;         // this lane's query row
+    const bool valid = i < L;
+    const int rend = (qb * BQ + BQ < L) ? qb * BQ + BQ : L;
+    const int kt_first = (rend - 1) / BK;
+    const float c2 = p.scale_log2;
+
+    // ---- Q and dO fragments (B operands: column = query, 8 consecutive d)
+    bf16x8 qf[KSTEPS], gf[KSTEPS];
+    {
+        const uint16_t* qr = p.q + b * p.q_sb + (int64_t)(valid ? i : 0) * p.q_sl + h * p.q_sh;
+        const uint16_t* gr = p.dout + b * p.do_sb + (int64_t)(valid ? i : 0) * p.do_sl + h * p.do_sh;
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+            const u32x4 x = valid ? *(const u32x4*)(qr + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
+            const u32x4 y = valid ? *(const u32x4*)(gr + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
+            qf[st] = __builtin_bit_cast(bf16x8, x);
+            gf[st] = __builtin_bit_cast(bf16x8, y);
+        }
+    }
+    const float lse2 = valid ? p.rowc[bh * p.Lpad + i] : 0.f;
+    const float dval = valid ? p.rowd[bh * p.Lpad + i] : 0.f;
+
+    // ---- tile copies: buffer resources from the tile to key L-1 (rows past L read zero)
+    uint32_t koff[INST], voff[INST];
+#pragma unroll
+    for (int n = 0; n < INST; ++n) {
+        const int sl = (n * NW + w) * 64 + lane;
+        const int r = sl / QCH, pc = sl % QCH;
+        koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ kswz<QCH>(r))) * 2);
+        voff[n] = (uint32_t)((r * p.v_sl + 8 * (pc ^ (r % QCH))) * 2);
+    }
+    const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh;
+    const uint16_t* vbase = p.v + b * p.v_sb + kh * p.v_sh;
+    auto fetch = [&](int kt, int buf) {
+        const int j0 = kt * BK;
+        const __amdgpu_buffer_rsrc_t kr =
+            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(L - 1 - j0) * p.k_sl + D) * 2));
+        const __amdgpu_buffer_rsrc_t vr =
+            make_rsrc(vbase + (int64_t)j0 * p.v_sl, (uint32_t)(((int64_t)(L - 1 - j0) * p.v_sl + D) * 2));
+#pragma unroll
+        for (int n = 0; n < INST; ++n) {
+            buffer16_to_lds(kr, koff[n], reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
+            buffer16_to_lds(vr, voff[n], reinterpret_cast<unsigned char*>(sV[buf]) + (n * NW + w) * 64 * 16);
+        }
+    };
+
+    // ---- kept key tiles of this block, newest first: all legal tiles at tau = 0,
+    // else the set bits of the block's word row
+    const bool dense = p.log2_tau == kNegInf;
+    const uint32_t* qrow = p.qbits + (bh * p.nQB + qb) * p.nwords;
+    int cwi = kt_first >> 5;                     // sparse cursor: word index and remaining bits
+    uint32_t cword = dense ? 0u : (qrow[cwi] & (kt_first % 32 == 31 ? ~0u : ((2u << (kt_first % 32)) - 1u)));
+    int dnext = kt_first;
+    auto next_tile = [&]() -> int {
+        if (dense) return dnext >= 0 ? dnext-- : -1;
+        while (cword == 0u) {
+            if (--cwi < 0) return -1;
+            cword = qrow[cwi];
+        }
+        const int bpos = 31 - __builtin_clz(cword);
+        cword &= ~(1u << bpos);
+        return cwi * 32 + bpos;
+    };
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+    const int j16 = lane & 15;
+    const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+
+    int tcur = next_tile();
+    int tnext = -1;
+    if (tcur >= 0) {
+        fetch(tcur, 0);
+        tnext = next_tile();
+        if (tnext >= 0) fetch(tnext, 1);
+        if (tnext >= 0) wait_vmcnt<2 * INST>(); else wait_vmcnt<0>();
+        __syncthreads();
+    }
+    for (int s = 0; tcur >= 0; ++s) {
+        const int buf = s & 1;
+        const uint16_t* kb = sK[buf];
+        const uint16_t* vb = sV[buf];
+        // S^T = K Q^T and dP^T = V dO^T (one key per register row, this lane's query)
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int row = 32 * sub + l32;
+            sc[sub] = f32x16{};
+            dp[sub] = f32x16{};
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) {
+                const bf16x8 a = *(const bf16x8*)(&kb[row * D + 8 * ((2 * st + hi) ^ kswz<QCH>(row))]);
+                const bf16x8 vv = *(const bf16x8*)(&vb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
+                sc[sub] = mfma32x32x16(a, qf[st], sc[sub]);
+                dp[sub] = mfma32x32x16(vv, gf[st], dp[sub]);
+            }
+        }
+        // P and dS on legal (causal) entries; dS^T as the B operand of dQ^T
+        bf16x8 dsf[4];
+        const int j0 = tcur * BK;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = j0 + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const bool legal = valid && j <= i;
+                const float pr = legal ? fast_exp2(__builtin_fmaf(sc[sub][r], c2, -lse2)) : 0.f;
+                dsf[2 * sub + (r >> 3)][r & 7] = to_bf16(pr * (dp[sub][r] - dval));
+            }
+        // dQ^T += K^T dS^T, K^T fragments (8 keys of one d per lane) by transposing reads
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                u32x2 half2x[2];
+#pragma unroll
+                for (int rd = 0; rd < 2; ++rd) {
+                    const int krow = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
+                    const int col = 32 * dt + dsel;
+                    const int phys = ((col >> 3) ^ kswz<QCH>(krow)) * 8 + (col & 7);
+                    half2x[rd] = lds_read_tr16(kb + krow * D + phys);
+                }
+                // whole-dword assembly of the operand
+                const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
+                acc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, w4), dsf[ks], acc[dt]);
+            }
+        __syncthreads();                         // every wave is done with buffer `buf`
+        const int tn2 = (tnext >= 0) ? next_tile() : -1;
+        if (tn2 >= 0) fetch(tn2, buf);
+        // the tile in the other buffer (copied one step ago) must have landed
+        if (tn2 >= 0) wait_vmcnt<2 * INST>(); else wait_vmcnt<0>();
+        __syncthreads();
+        tcur = tnext;
+        tnext = tn2;
+    }
+
+    // ---- dQ = scale * acc, C[i = d][j = query]: registers = 4 consecutive d
+    if (valid) {
+        uint16_t* orow = p.dq + b * p.dq_sb + (int64_t)i * p.dq_sl + h * p.dq_sh;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * dt + 8 * g + 4 * hi;
+                u32x2 pk;
+                pk[0] = float_to_bf16_bits(acc[dt][4 * g + 0] * p.scale) |
+                        (float_to_bf16_bits(acc[dt][4 * g + 1] * p.scale) << 16);
+                pk[1] = float_to_bf16_bits(acc[dt][4 * g + 2] * p.scale) |
+                        (float_to_bf16_bits(acc[dt][4 * g + 3] * p.scale) << 16);
+                *(u32x2*)(orow + d0) = pk;
+            }
+        }
     }
 }
 
@@ -647,10 +785,9 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
     const int per = 8 * p.chunk;
     const int grid = (p.nunits + per - 1) / per * per;
     hipLaunchKernelGGL((mala_bwd_kernel<D, BQ>), dim3(grid), dim3(256), 0, s, p);
-    const int64_t n = (int64_t)p.B * p.Hq * p.L * (D / 8);
-    int cg = (int)((n + 255) / 256);
-    if (cg > 8192) cg = 8192;
-    hipLaunchKernelGGL((mala_dq_convert<D>), dim3(cg), dim3(256), 0, s, p);
+    const int per_q = 8 * p.chunk_dq;
+    const int grid_q = (p.nunits_dq + per_q - 1) / per_q * per_q;
+    hipLaunchKernelGGL((mala_bwd_dq<D, BQ>), dim3(grid_q), dim3(BQ / 32 * 64), 0, s, p);
     return hipGetLastError();
 }
 

@@ -34,10 +34,10 @@ struct BwdParams {
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
-    float* dq_acc;      // [B, Hq, L, d] fp32 workspace
     float* rowd;        // [B, Hq, Lpad] fp32: D_i = dO_i . O_i (0 past L)
     float* rowc;        // [B, Hq, Lpad] fp32: LSE_i * log2(e) (0 past L)
     uint32_t* tbits;    // [B, Hkv, nKT, nwT] bit (h % G) * nQB + qb: tile (qb, kt) of q head h kept
+    uint32_t* qbits;    // [B, Hq, nQB, nwords] bit kt: the same tile, query-major
     uint16_t* qt;       // [B, Hq, d, Lpad] bf16: Q transposed, query positions permuted in 16-groups
     uint16_t* dot;      // [B, Hq, d, Lpad] bf16: dO transposed, same permutation
     int Lpad;           // nQB * Bq
@@ -46,6 +46,7 @@ struct BwdParams {
     int B, L, Hq, Hkv, G, nQB, nKT, nunits, chunk;
     int nwT;            // ceil(G * nQB / 32)
     int nslab, nunits_scan, chunk_scan;   // scan kernel: 256-query slabs, work units
+    int nunits_dq, chunk_dq;              // dQ pass: (batch, q head, query block) units
     float scale;        // 1 / sqrt(d)
     float scale_log2;   // log2(e) / sqrt(d)
     float log2_tau;
