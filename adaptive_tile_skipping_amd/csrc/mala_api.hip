@@ -131,12 +131,11 @@ size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int
     if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
     const size_t Lpad = (size_t)((L + Bq - 1) / Bq) * Bq;
     const size_t prow = (size_t)B * Hq * Lpad;
-    const size_t tr = (size_t)B * Hq * d * Lpad * 2;
     const size_t nQB = Lpad / Bq, nKT = (size_t)(L + Bk - 1) / Bk;
     const size_t nwT = ((size_t)(Hq / Hkv) * nQB + 31) / 32;
     const size_t tb = (size_t)B * Hkv * nKT * nwT * sizeof(uint32_t);
     const size_t qbb = (size_t)B * Hq * nQB * ((nKT + 31) / 32) * sizeof(uint32_t);
-    return 2 * align256(prow * sizeof(float)) + 2 * align256(tr) + align256(tb) + align256(qbb);
+    return 2 * align256(prow * sizeof(float)) + align256(tb) + align256(qbb);
 }
 
 mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, const float* lse,
@@ -165,9 +164,6 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     const size_t prow = (size_t)B * Hq * p.Lpad;
     p.rowd = (float*)w; w += align256(prow * sizeof(float));
     p.rowc = (float*)w; w += align256(prow * sizeof(float));
-    const size_t tr = (size_t)B * Hq * d * p.Lpad * 2;
-    p.qt = (uint16_t*)w; w += align256(tr);
-    p.dot = (uint16_t*)w; w += align256(tr);
     p.tbits = (uint32_t*)w;
     {
         const size_t nQB_ = (size_t)((L + Bq - 1) / Bq), nKT_ = (size_t)((L + Bk - 1) / Bk);

@@ -14,9 +14,8 @@
 //     dK += scale dS^T Q, dQ += scale dS K,   D_i = dO_i . O_i.
 //
 // Kernels:
-//   mala_bwd_pre    D_i, LSE_i in base 2, transposed copies of Q and dO (query
-//                   positions permuted inside each 16-group to match the MFMA
-//                   register order), zeroed tile bits and statistics.
+//   mala_bwd_pre    D_i and LSE_i in base 2 per row, zeroed tile bits and
+//                   statistics.
 //   mala_bwd_scan   the decision pass (tau > 0): one workgroup per (batch, q
 //                   head, 256-query slab), 4 waves of 64 queries.  Q and each
 //                   row's threshold stay in registers; key tiles stream from
@@ -31,12 +30,13 @@
 //                   tile of 64 keys), 4 waves, visiting only the kept (q head,
 //                   query block) steps of its key tile (all legal steps when
 //                   tau = 0).  K and V fragments stay in registers; each step's
-//                   Q block streams through a triple-buffered LDS tile and
-//                   S = Q K^T is recomputed.  Wave w owns keys 32(w&1).. and half
-//                   (w>>1) of the block's queries.  S is laid out with one key
-//                   per lane and the block's queries in registers, so P^T and
-//                   dS^T feed the dV and dK contractions straight from
-//                   registers; dK/dV accumulate in registers over steps.
+//                   Q and dO blocks stream through double-buffered LDS tiles and
+//                   S = Q K^T, dP = dO V^T are recomputed.  Wave w owns keys
+//                   32(w&1).. and half (w>>1) of the block's queries.  S is laid
+//                   out with one key per lane and the block's queries in
+//                   registers, so P^T and dS^T feed the dV and dK contractions
+//                   straight from registers, with dO^T and Q^T from transposing
+//                   LDS reads; dK/dV accumulate in registers over steps.
 //   mala_bwd_dq     the dQ pass: one workgroup per (batch, q head, query
 //                   block), waves of 32 queries, visiting the block's kept key
 //                   tiles (all legal tiles when tau = 0) with K and V tiles
@@ -52,14 +52,10 @@ namespace {
 constexpr int BK = 64;
 constexpr int PRE_ROWS = 64;
 
-__device__ __forceinline__ int qpos(int i) { return (i & ~15) | vt_pos16(i & 15); }
 }  // namespace
 
 template <int D, int BQ>
 __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
-    constexpr int TROW = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[PRE_ROWS * TROW];
-    __shared__ __attribute__((aligned(16))) uint16_t sD[PRE_ROWS * TROW];
     const int tid = threadIdx.x;
     const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int r0 = rb * PRE_ROWS;
@@ -101,19 +97,6 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
         const int64_t nq = (int64_t)p.B * p.Hq * p.nQB * p.nwords;
         for (int64_t idx = fb * 256 + tid; idx < nq; idx += nblk * 256) p.qbits[idx] = 0u;
     }
-    // stage Q and dO rows (zeros past L)
-    constexpr int CH = D / 8;
-    for (int idx = tid; idx < PRE_ROWS * CH; idx += 256) {
-        const int r = idx / CH, c = idx % CH;
-        const int i = r0 + r;
-        u32x4 xq = {0, 0, 0, 0}, xg = {0, 0, 0, 0};
-        if (i < L) {
-            xq = *(const u32x4*)(p.q + b * p.q_sb + (int64_t)i * p.q_sl + h * p.q_sh + 8 * c);
-            xg = *(const u32x4*)(p.dout + b * p.do_sb + (int64_t)i * p.do_sl + h * p.do_sh + 8 * c);
-        }
-        *(u32x4*)(&sQ[r * TROW + 8 * c]) = xq;
-        *(u32x4*)(&sD[r * TROW + 8 * c]) = xg;
-    }
     // statistics owned by the query block starting in these rows
     if ((r0 % BQ) == 0) {
         const int qb = r0 / BQ;
@@ -122,22 +105,6 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
             if (p.bits)
                 for (int wd = tid; wd < p.nwords; wd += 256) p.bits[(bh * p.nQB + qb) * p.nwords + wd] = 0u;
         }
-    }
-    __syncthreads();
-    // transposed writes: thread -> (d row, 8 consecutive positions)
-    for (int idx = tid; idx < D * (PRE_ROWS / 8); idx += 256) {
-        const int d = idx / (PRE_ROWS / 8), pg = idx % (PRE_ROWS / 8);
-        uint32_t wq[4], wg[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int p0 = 8 * pg + 2 * e;
-            const int ra = qpos(p0), rb2 = qpos(p0 + 1);   // involution on 0..63
-            wq[e] = (uint32_t)sQ[ra * TROW + d] | ((uint32_t)sQ[rb2 * TROW + d] << 16);
-            wg[e] = (uint32_t)sD[ra * TROW + d] | ((uint32_t)sD[rb2 * TROW + d] << 16);
-        }
-        const int64_t off = (bh * D + d) * p.Lpad + r0 + 8 * pg;
-        *(u32x4*)(p.qt + off) = u32x4{wq[0], wq[1], wq[2], wq[3]};
-        *(u32x4*)(p.dot + off) = u32x4{wg[0], wg[1], wg[2], wg[3]};
     }
 }
 
@@ -329,26 +296,37 @@ struct StepCursor {
     }
 };
 
+// LDS row swizzle for tiles read both row-wise (16-byte MFMA operand reads)
+// and transposed (ds_read_b64_tr_b16): 16-byte chunk c of row r lives at chunk
+// c ^ kswz(r).  kswz permutes 0..15 over 16 consecutive rows (row-wise reads
+// are conflict-free) and gives the four rows of a transposing read four
+// different chunk pairs (transposed reads are conflict-free too).  For d = 64
+// (8 chunks) only the second property holds.
+template <int QCH>
+__device__ __forceinline__ int kswz(int r) {
+    return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) % QCH;
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
     constexpr int NQS = BQ / 32;         // query subtiles of the block
     constexpr int WSUB = NQS / 2;        // query subtiles per wave
-    constexpr int QCH = D / 8;           // 16-byte chunks per Q row
-    constexpr int QSLOTS = BQ * QCH;     // 16-byte chunks per Q block
-    constexpr int QINST = QSLOTS / 256;  // global->LDS copies per lane per block
-    constexpr int NBUF = 3;              // Q blocks in flight: current + two prefetched
-    constexpr int QBYTES = NBUF * BQ * D * 2;
+    constexpr int QCH = D / 8;           // 16-byte chunks per row
+    constexpr int QSLOTS = BQ * QCH;     // 16-byte chunks per block (each of Q, dO)
+    constexpr int QINST = QSLOTS / 256;  // global->LDS copies per lane per block and tensor
+    constexpr int BLK = BQ * D;          // elements of one block
+    constexpr int QBYTES = 2 * 2 * BLK * 2;               // [buf][Q | dO] blocks
     constexpr int RBYTES = 2 * 2 * DT * 16 * 64 * 4;     // epilogue reduction
     constexpr int UBYTES = QBYTES > RBYTES ? QBYTES : RBYTES;
     static_assert(QINST * 256 == QSLOTS && WSUB >= 1, "shape");
 
-    // Q blocks: [NBUF][BQ][D] bf16, 16-byte chunk c of row r stored at chunk c ^ (r % QCH)
+    // [buf][Q | dO][BQ][D] bf16, 16-byte chunk c of row r stored at chunk c ^ kswz(r)
     __shared__ __attribute__((aligned(16))) unsigned char sU[UBYTES];
     // [buf][lse2 | D][query]
-    __shared__ __attribute__((aligned(16))) float sRow[NBUF][2][BQ];
-    uint16_t* sQ = reinterpret_cast<uint16_t*>(sU);
+    __shared__ __attribute__((aligned(16))) float sRow[2][2][BQ];
+    uint16_t* sQD = reinterpret_cast<uint16_t*>(sU);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -392,18 +370,18 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const bool dense = p.log2_tau == kNegInf;   // tau = 0: every legal step is kept
     const uint32_t* trow = p.tbits + ((int64_t)(b * p.Hkv + kh) * p.nKT + kt) * p.nwT;
 
-    // Per-lane byte offsets of this lane's 16-byte chunks inside a Q block
-    // (row r, logical chunk c stored at physical chunk c ^ (r % QCH)).
-    uint32_t qoff[QINST];
+    // Per-lane byte offsets of this lane's 16-byte chunks inside a Q / dO block
+    uint32_t qoff[QINST], goff[QINST];
 #pragma unroll
     for (int n = 0; n < QINST; ++n) {
         const int sl = (n * 4 + w) * 64 + lane;
         const int r = sl / QCH, pc = sl % QCH;
-        const int c = pc ^ (r % QCH);
+        const int c = pc ^ kswz<QCH>(r);
         qoff[n] = (uint32_t)((r * p.q_sl + 8 * c) * 2);
+        goff[n] = (uint32_t)((r * p.do_sl + 8 * c) * 2);
     }
     // issue the copies of step `idx` (q head kh*G + idx / nQB, query block
-    // idx % nQB): its row terms and Q block, into buffer `buf`
+    // idx % nQB): its row terms, Q block and dO block, into buffer `buf`
     auto fetch = [&](int idx, int buf) {
         const int f_h = kh * G + idx / p.nQB, f_qb = idx % p.nQB;
         const int64_t fbh = (int64_t)b * p.Hq + f_h;
@@ -413,131 +391,130 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
             const float* src = (w == 0 ? p.rowc : p.rowd) + fbh * p.Lpad + row0;
             load16_to_lds(src + 4 * lane, &sRow[buf][w][0]);
         }
-        // the block's rows through a buffer resource ending at row L-1, so the
+        // the blocks' rows through buffer resources ending at row L-1, so the
         // rows past L read as zero without per-lane clamps
         const int nrow = (L - row0 < BQ) ? L - row0 : BQ;
         const uint16_t* qblk = p.q + b * p.q_sb + (int64_t)row0 * p.q_sl + f_h * p.q_sh;
+        const uint16_t* gblk = p.dout + b * p.do_sb + (int64_t)row0 * p.do_sl + f_h * p.do_sh;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qblk, (uint32_t)(((nrow - 1) * p.q_sl + D) * 2));
-        unsigned char* dst = sU + buf * (BQ * D * 2);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gblk, (uint32_t)(((nrow - 1) * p.do_sl + D) * 2));
+        unsigned char* dq_ = sU + buf * (2 * BLK * 2);
+        unsigned char* dg_ = dq_ + BLK * 2;
 #pragma unroll
-        for (int n = 0; n < QINST; ++n) buffer16_to_lds(rq, qoff[n], dst + (n * 4 + w) * 64 * 16);
+        for (int n = 0; n < QINST; ++n) {
+            buffer16_to_lds(rq, qoff[n], dq_ + (n * 4 + w) * 64 * 16);
+            buffer16_to_lds(rg, goff[n], dg_ + (n * 4 + w) * 64 * 16);
+        }
+    };
+    // every copy of the step fetched last may stay in flight
+    auto wait_prev = [&](bool more) {
+        if (!more) wait_vmcnt<0>();
+        else if (w < 2) wait_vmcnt<2 * QINST + 1>();
+        else wait_vmcnt<2 * QINST>();
     };
 
-    StepCursor fc, cc;   // fetch cursor (two steps ahead) and compute cursor
-    fc.init(dense, trow, p.nwT, qb_lo, p.nQB, G);
-    cc.init(dense, trow, p.nwT, qb_lo, p.nQB, G);
-    int nx = fc.next(lane);
-    if (nx >= 0) {
-        fetch(nx, 0);
-        nx = fc.next(lane);
-        if (nx >= 0) {
-            fetch(nx, 1);
-            nx = fc.next(lane);
+    const int j16 = lane & 15;
+    const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+    // B operand of dV / dK: 8 queries (in the score registers' order) of one d,
+    // by transposing reads of a row-major block
+    auto tread = [&](const uint16_t* blk, int qrow0, int dt) -> bf16x8 {
+        u32x2 half2x[2];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int row = qrow0 + 8 * rd + 4 * hi + (j16 >> 2);
+            const int col = 32 * dt + dsel;
+            const int phys = ((col >> 3) ^ kswz<QCH>(row)) * 8 + (col & 7);
+            half2x[rd] = lds_read_tr16(blk + row * D + phys);
         }
+        const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
+        return __builtin_bit_cast(bf16x8, w4);
+    };
+
+    StepCursor cc;
+    cc.init(dense, trow, p.nwT, qb_lo, p.nQB, G);
+    int cur = cc.next(lane), nxt = -1;
+    if (cur >= 0) {
+        fetch(cur, 0);
+        nxt = cc.next(lane);
+        if (nxt >= 0) fetch(nxt, 1);
+        wait_prev(nxt >= 0);
+        __syncthreads();
     }
-    wait_all_then_barrier();
 
     f32x16 sc[WSUB];
-    int s = 0;
-    for (int cur = cc.next(lane); cur >= 0; cur = cc.next(lane), ++s) {
-        const int buf = s % NBUF;
-        const bool prefetch = nx >= 0;
-        if (prefetch) {
-            fetch(nx, (s + 2) % NBUF);
-            nx = fc.next(lane);
-        }
+    for (int s = 0; cur >= 0; ++s) {
+        const int buf = s & 1;
         const int h = kh * G + cur / p.nQB;
         const int qb = cur % p.nQB;
-        const uint16_t* sQb = sQ + buf * BQ * D;
-        // ---- S = Q K^T for the wave's query subtiles x 32 keys (raw scores)
+        const uint16_t* sQb = sQD + buf * 2 * BLK;
+        const uint16_t* sGb = sQb + BLK;
+        const int64_t bh = (int64_t)b * p.Hq + h;
+        // ---- S = Q K^T and dP = dO V^T for the wave's query subtiles x 32 keys
+        f32x16 dp[WSUB];
 #pragma unroll
         for (int t = 0; t < WSUB; ++t) {
             const int row = 32 * (WSUB * qh + t) + l32;
             sc[t] = f32x16{};
+            dp[t] = f32x16{};
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) {
-                const int pc = (2 * st + hi) ^ (row % QCH);
+                const int pc = (2 * st + hi) ^ kswz<QCH>(row);
                 const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
+                const bf16x8 g = *(const bf16x8*)(&sGb[row * D + 8 * pc]);
                 sc[t] = mfma32x32x16(a, kf[st], sc[t]);
+                dp[t] = mfma32x32x16(g, vf[st], dp[t]);
             }
         }
-        const int64_t bh = (int64_t)b * p.Hq + h;
-        {
-            // ---- dP = dO V^T (A operand rows straight from global dO)
-            f32x16 dp[WSUB];
+        // ---- P, dS; A operands (key rows x 8 permuted query positions) for dV, dK
+        bf16x8 pa[2 * WSUB], da[2 * WSUB];
 #pragma unroll
-            for (int t = 0; t < WSUB; ++t) {
-                const int qsub = WSUB * qh + t;
-                const int i = qb * BQ + 32 * qsub + l32;
-                const bool ok = i < L;
-                const uint16_t* grow = p.dout + b * p.do_sb + (int64_t)(ok ? i : 0) * p.do_sl + h * p.do_sh;
-                dp[t] = f32x16{};
+        for (int t = 0; t < WSUB; ++t) {
+            const int qsub = WSUB * qh + t;
 #pragma unroll
-                for (int st = 0; st < KSTEPS; ++st) {
-                    const u32x4 x = ok ? *(const u32x4*)(grow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
-                    dp[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, x), vf[st], dp[t]);
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int ql = 32 * qsub + 8 * g4 + 4 * hi;
+                const f32x4 lv = *(const f32x4*)(&sRow[buf][0][ql]);
+                const f32x4 dd = *(const f32x4*)(&sRow[buf][1][ql]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    const int ig = qb * BQ + ql + e;
+                    const bool legal = (jme <= ig) && (ig < L);
+                    const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e])) : 0.f;
+                    const float ds = pr * (dp[t][r] - dd[e]);
+                    pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
+                    da[2 * t + (r >> 3)][r & 7] = to_bf16(ds);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // ---- P, dS; A operands (key rows x 8 permuted query positions) for dV, dK
-            bf16x8 pa[2 * WSUB], da[2 * WSUB];
-#pragma unroll
-            for (int t = 0; t < WSUB; ++t) {
-                const int qsub = WSUB * qh + t;
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int ql = 32 * qsub + 8 * g4 + 4 * hi;
-                    const f32x4 lv = *(const f32x4*)(&sRow[buf][0][ql]);
-                    const f32x4 dd = *(const f32x4*)(&sRow[buf][1][ql]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g4 + e;
-                        const int ig = qb * BQ + ql + e;
-                        const bool legal = (jme <= ig) && (ig < L);
-                        const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e])) : 0.f;
-                        const float ds = pr * (dp[t][r] - dd[e]);
-                        pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
-                        da[2 * t + (r >> 3)][r & 7] = to_bf16(ds);
-                    }
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- dV += P^T dO, dK += dS^T Q  (B operands from the transposed copies)
-            const int64_t tbase = (int64_t)bh * D * p.Lpad + qb * BQ + (BQ / 2) * qh + 8 * hi;
-#pragma unroll
-            for (int ks = 0; ks < 2 * WSUB; ++ks) {
-                bf16x8 bg[DT], bq[DT];
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int64_t off = tbase + (int64_t)(32 * dt + l32) * p.Lpad + 16 * ks;
-                    bg[dt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.dot + off));
-                    bq[dt] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.qt + off));
-                }
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    dv[dt] = mfma32x32x16(pa[ks], bg[dt], dv[dt]);
-                    dk[dt] = mfma32x32x16(da[ks], bq[dt], dk[dt]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // ---- statistics of the backward's own decisions
-            if (tid == 0) {
-                if (p.kept_tiles) atomicAdd(p.kept_tiles + bh * p.nQB + qb, 1);
-                if (p.bits) atomicOr(p.bits + (bh * p.nQB + qb) * p.nwords + (kt >> 5), 1u << (kt & 31));
-            }
-            if (p.kept_slots && tid < BQ) {
-                const int i = qb * BQ + tid;
-                const int last = i - j0;
-                if (i < L && last >= 0) atomicAdd(p.kept_slots + bh * L + i, (last < BK - 1 ? last : BK - 1) + 1);
             }
         }
-        // the block of step s+1 (copied during step s-1) must have landed; the
-        // copies of step s+2 (QINST, plus one row-term copy on waves 0..1)
-        // may stay in flight
-        if (!prefetch) wait_vmcnt<0>();
-        else if (w < 2) wait_vmcnt<QINST + 1>();
-        else wait_vmcnt<QINST>();
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- dV += P^T dO, dK += dS^T Q  (B operands by transposing reads)
+#pragma unroll
+        for (int ks = 0; ks < 2 * WSUB; ++ks) {
+            const int qrow0 = (BQ / 2) * qh + 16 * ks;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                dv[dt] = mfma32x32x16(pa[ks], tread(sGb, qrow0, dt), dv[dt]);
+                dk[dt] = mfma32x32x16(da[ks], tread(sQb, qrow0, dt), dk[dt]);
+            }
+        }
+        // ---- statistics of the backward's own decisions
+        if (tid == 0) {
+            if (p.kept_tiles) atomicAdd(p.kept_tiles + bh * p.nQB + qb, 1);
+            if (p.bits) atomicOr(p.bits + (bh * p.nQB + qb) * p.nwords + (kt >> 5), 1u << (kt & 31));
+        }
+        if (p.kept_slots && tid < BQ) {
+            const int i = qb * BQ + tid;
+            const int last = i - j0;
+            if (i < L && last >= 0) atomicAdd(p.kept_slots + bh * L + i, (last < BK - 1 ? last : BK - 1) + 1);
+        }
+        __syncthreads();                         // every wave is done with buffer `buf`
+        const int n2 = (nxt >= 0) ? cc.next(lane) : -1;
+        if (n2 >= 0) fetch(n2, buf);
+        wait_prev(n2 >= 0);                      // the next step's blocks have landed
         __syncthreads();
+        cur = nxt;
+        nxt = n2;
     }
 
     // ---- epilogue: combine the two query halves, write dK (scaled) and dV
@@ -576,17 +553,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                 }
             }
     }
-}
-
-// K row swizzle of the dQ pass: 16-byte chunk c of row r lives at chunk
-// c ^ kswz(r).  kswz permutes 0..15 over 16 consecutive rows (row-wise 16-byte
-// reads of the score contraction are conflict-free) and gives the four rows of
-// a transposing read four different chunk pairs (the K^T reads of the dQ
-// contraction are conflict-free too).  For d = 64 (8 chunks) only the second
-// property holds.
-template <int QCH>
-__device__ __forceinline__ int kswz(int r) {
-    return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) % QCH;
 }
 
 // dQ pass: see the file comment.  dQ_i = scale * sum over kept tiles of

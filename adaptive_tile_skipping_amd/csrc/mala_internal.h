@@ -38,8 +38,6 @@ struct BwdParams {
     float* rowc;        // [B, Hq, Lpad] fp32: LSE_i * log2(e) (0 past L)
     uint32_t* tbits;    // [B, Hkv, nKT, nwT] bit (h % G) * nQB + qb: tile (qb, kt) of q head h kept
     uint32_t* qbits;    // [B, Hq, nQB, nwords] bit kt: the same tile, query-major
-    uint16_t* qt;       // [B, Hq, d, Lpad] bf16: Q transposed, query positions permuted in 16-groups
-    uint16_t* dot;      // [B, Hq, d, Lpad] bf16: dO transposed, same permutation
     int Lpad;           // nQB * Bq
     int64_t q_sb, q_sl, q_sh, k_sb, k_sl, k_sh, v_sb, v_sl, v_sh, o_sb, o_sl, o_sh;
     int64_t do_sb, do_sl, do_sh, dq_sb, dq_sl, dq_sh, dk_sb, dk_sl, dk_sh, dv_sb, dv_sl, dv_sh;

@@ -103,7 +103,7 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
                      float tau, int Bq, int Bk, mala_t4 o, float* lse,
                      const mala_tile_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
-/* Bytes of device workspace mala_bwd needs (row terms, transposed Q and dO, kept-tile bits). */
+/* Bytes of device workspace mala_bwd needs (row terms and kept-tile bits). */
 size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk);
 
 /* Backward.  Inputs as saved by mala_fwd (q, k, v, o, lse) plus dout.
