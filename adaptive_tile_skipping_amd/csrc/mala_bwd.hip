@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int KSTEPS = D / 16;
     constexpr int QCH = D / 8;             // 16-byte chunks per row
     constexpr int KINST = BK * QCH / 256;  // global->LDS copies per lane per key tile
-    constexpr int NB = 3;                  // key tiles in flight: current + two prefetched
+    constexpr int NB = 4;                  // two pairs of key tiles: the current pair and the next
     static_assert(KINST * 256 == BK * QCH, "shape");
     // key tiles [NB][BK][D] bf16, chunk c of row r stored at chunk c ^ (r % QCH)
     __shared__ __attribute__((aligned(16))) uint16_t sK[NB][BK * D];
@@ -184,36 +184,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int n = 0; n < KINST; ++n) buffer16_to_lds(rk, koff[n], dst + (n * 4 + w) * 64 * 16);
     };
 
+    // Key tiles are processed in pairs, one barrier per pair: pair q holds tiles
+    // kt_hi - 2q and kt_hi - 2q - 1 in slots 2(q & 1) and 2(q & 1) + 1.
     const int nt = kt_hi + 1;
-    copy_tile(kt_hi, 0);
-    if (nt > 1) copy_tile(kt_hi - 1, 1);
-    wait_all_then_barrier();
+    const int npair = (nt + 1) / 2;
+    auto copy_pair = [&](int q) {
+        const int kt = kt_hi - 2 * q;
+        copy_tile(kt, 2 * (q & 1));
+        if (kt >= 1) copy_tile(kt - 1, 2 * (q & 1) + 1);
+    };
+    copy_pair(0);
 
     uint32_t* bitrow = p.tbits + (int64_t)(b * p.Hkv + kh) * p.nKT * p.nwT;
     const int bit = (h % p.G) * p.nQB + rw0 / BQ;
     uint32_t* qrow = p.qbits + (bh * p.nQB + rw0 / BQ) * p.nwords;
 
-    for (int it = 0; it < nt; ++it) {
-        const int kt = kt_hi - it;
-        const int buf = it % NB;
-        const bool prefetch = it + 2 < nt;
-        if (prefetch) copy_tile(kt - 2, (it + 2) % NB);
-        if (live && kt <= kt_w) {
+    for (int q = 0; q < npair; ++q) {
+        // pair q has landed, and every wave is done with pair q - 1, whose
+        // slots take pair q + 1
+        wait_all_then_barrier();
+        if (q + 1 < npair) copy_pair(q + 1);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+        const int kt = kt_hi - 2 * q - half;
+        const int buf = 2 * (q & 1) + half;
+        if (kt >= 0 && live && kt <= kt_w) {
             const uint16_t* sKb = sK[buf];
             f32x16 acc[2][2];
+            // K fragments are read one k-step ahead (a two-slot ring); a
+            // scheduling barrier closes every step to keep that order
+            auto kread = [&](int st, int uu) -> bf16x8 {
+                const int row = 32 * uu + l32;
+                return *(const bf16x8*)(&sKb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
+            };
+            bf16x8 kb[2][2];
+            kb[0][0] = kread(0, 0);
+            kb[0][1] = kread(0, 1);
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) {
-                bf16x8 kb[2];
-#pragma unroll
-                for (int uu = 0; uu < 2; ++uu) {
-                    const int row = 32 * uu + l32;
-                    kb[uu] = *(const bf16x8*)(&sKb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
+                if (st + 1 < KSTEPS) {
+                    kb[(st + 1) & 1][0] = kread(st + 1, 0);
+                    kb[(st + 1) & 1][1] = kread(st + 1, 1);
                 }
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int uu = 0; uu < 2; ++uu)
-                        acc[t][uu] = mfma32x32x16(qa[t][st], kb[uu], st == 0 ? seed[t] : acc[t][uu]);
+                        acc[t][uu] = mfma32x32x16(qa[t][st], kb[st & 1][uu], st == 0 ? seed[t] : acc[t][uu]);
+                __builtin_amdgcn_sched_barrier(0);
             }
             // C[i = query][j = key]: lane = key 32uu + l32, register r = query
             // 32t + 8(r/4) + 4hi + r%4.  Keep iff a legal entry is >= 0.
@@ -230,21 +248,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                             mx = fmaxf(mx, legal ? acc[t][uu][r] : kNegInf);
                         }
             } else {
+                // four independent chains, then combined
+                float m4[4];
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int c = 0; c < 4; ++c) {
+                    m4[c] = acc[c >> 1][c & 1][0];
 #pragma unroll
-                    for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[t][uu][r]);
+                    for (int r = 1; r < 16; ++r) m4[c] = fmaxf(m4[c], acc[c >> 1][c & 1][r]);
+                }
+                mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
             }
             if (__ballot(mx >= 0.f) != 0ull && lane == 0) {
                 atomicOr(bitrow + (int64_t)kt * p.nwT + (bit >> 5), 1u << (bit & 31));
                 atomicOr(qrow + (kt >> 5), 1u << (kt & 31));
             }
         }
-        // tile kt-1 (copied during the previous iteration) must have landed
-        if (prefetch) wait_vmcnt<KINST>(); else wait_vmcnt<0>();
-        __syncthreads();
+        }
     }
 }
 
