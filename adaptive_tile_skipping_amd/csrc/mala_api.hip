@@ -210,13 +210,14 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
     int ns, tps;
     decode_split(B, Hkv, (int)nT, &ns, &tps);
     const size_t nsplit = (size_t)ns;
+    const size_t npart = nsplit > (nT + 3) / 4 ? nsplit : (nT + 3) / 4;
     size_t s = 0;
     s += 2 * align256(grp * G * nT * sizeof(float));          // tmax, tsum
     s += align256(grp * G * (size_t)N * sizeof(float));       // spill
     s += align256(grp * nT * sizeof(int32_t));                // klist
     s += align256(grp * sizeof(int32_t));                     // kcount
     s += align256(grp * G * sizeof(float));                   // lse2
-    s += align256(grp * nsplit * G * d * sizeof(float));      // part_o
+    s += align256(grp * npart * G * d * sizeof(float));       // part_o
     s += align256(grp * nsplit * G * 2 * sizeof(float));      // part_ml
     return s;
 }
@@ -253,7 +254,8 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
     p.klist = (int32_t*)w; w += align256(grp * nT * sizeof(int32_t));
     p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));
     p.lse2 = (float*)w; w += align256(grp * G * sizeof(float));
-    p.part_o = (float*)w; w += align256(grp * (size_t)p.nsplit * G * d * sizeof(float));
+    p.npart = p.nsplit > (p.nT + 3) / 4 ? p.nsplit : (p.nT + 3) / 4;
+    p.part_o = (float*)w; w += align256(grp * (size_t)p.npart * G * d * sizeof(float));
     p.part_ml = (float*)w;
     hipError_t e = launch_decode(p, d, Bk_dec, tau == 0.f, (hipStream_t)stream);
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;

@@ -10,14 +10,13 @@
 // skipped tile gets no V load and no P.V.
 //
 // Kernels (tau > 0):
-//   mala_dec_score   one wave per (sequence, KV head, tile).  The K tile is
-//                    copied global -> LDS (every load instruction covers whole
-//                    cache lines; XOR-swizzled 16-byte chunks keep the MFMA
-//                    fragment reads conflict-free), then S^T = K q^T with
-//                    32x32x16 bf16 MFMAs (the G rows padded to 32 columns).
-//                    Writes per-row tile max and shifted sum and the base-2
-//                    scores (spill).  Reads every K byte once: the HBM-bound
-//                    score discovery.
+//   mala_dec_score   persistent waves, each streaming a contiguous run of
+//                    tiles with the next tile's K fragments loaded into
+//                    registers while the current tile is scored: S^T = K q^T
+//                    with 32x32x16 bf16 MFMAs (the G rows padded to 32
+//                    columns).  Writes per-row tile max and shifted sum and the
+//                    base-2 scores (spill).  Reads every K byte once: the
+//                    HBM-bound score discovery.
 //   mala_dec_decide  one wave per (sequence, KV head): the sequential rule,
 //                    evaluated 64 tiles per round.  The candidate set is every
 //                    tile that votes keep under the state at the start of the
@@ -28,9 +27,9 @@
 //                    the flipped tile is skipped and the next round starts after
 //                    it.  A tile that votes skip under a smaller retained mass
 //                    can never turn to keep, so non-candidates are final too.
-//   mala_dec_pv      kept tiles only, 4 per round per workgroup: P = 2^(s - lse)
-//                    from the spill, V tile loads issued before P is ready,
-//                    fp32 accumulation into one partial output per split.
+//   mala_dec_pv      kept tiles only, one wave per tile: P = 2^(s - lse) from
+//                    the spill, V rows loaded at once, fp32 accumulation, one
+//                    partial output per workgroup of four tiles.
 //   mala_dec_sum_combine  sums the partials (already normalised) -> bf16 o.
 // tau = 0 keeps every tile, so the scan is elided: mala_dec_dense is a fused
 // split-K decode (scores, online softmax and P.V per split) and
@@ -113,13 +112,14 @@ __device__ __forceinline__ void tile_scores(const DecParams& p, int t, const uin
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void mala_dec_score(const DecParams p) {
-    constexpr int QCH = D / 8;                     // copies per lane per tile
-    __shared__ __attribute__((aligned(16))) uint16_t sK[4][2][BKD * D];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mala_dec_score(const DecParams p) {
+    constexpr int KSTEPS = D / 16;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    // each wave streams a contiguous run of tiles, the next one in flight
-    // while the current one is scored (no barriers in this kernel)
+    // Each wave streams a contiguous run of tiles.  K fragments (A operands:
+    // row = key, 8 consecutive d) are loaded straight into registers, the next
+    // tile's loads in flight while the current tile is scored; no LDS.
     const int ntask = p.B * p.Hkv * p.nT;
     const int nwave = gridDim.x * 4;
     const int per = (ntask + nwave - 1) / nwave;
@@ -127,30 +127,45 @@ __global__ __launch_bounds__(256) void mala_dec_score(const DecParams p) {
     int task = gw * per;
     const int tend = (task + per < ntask) ? task + per : ntask;
     if (task >= tend) return;
-    {
-        const int g0 = task / p.nT;
-        stage_k_tile<D>(p, g0 / p.Hkv, g0 % p.Hkv, task % p.nT, sK[w][0]);
-    }
+
+    auto load_tile = [&](int tk, bf16x8 (&kf)[2][KSTEPS]) {
+        const int grp = tk / p.nT, t = tk % p.nT;
+        const int b = grp / p.Hkv, kh = grp % p.Hkv;
+        const uint16_t* kb = p.k + b * p.k_sb + kh * p.k_sh;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            int j = t * BKD + 32 * sub + l32;
+            j = j < p.N ? j : p.N - 1;                 // rows past N are masked below
+            const uint16_t* row = kb + (int64_t)j * p.k_sl + 8 * hi;
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) kf[sub][st] = *(const bf16x8*)(row + 16 * st);
+        }
+    };
     int qgrp = -1;
     bf16x8 qf[D / 16];
-    for (int k = 0; task < tend; ++k, ++task) {
-        const int grp = task / p.nT;
-        const int t = task % p.nT;
-        const int b = grp / p.Hkv, kh = grp % p.Hkv;
-        const bool more = task + 1 < tend;
+    auto score_tile = [&](int tk, const bf16x8 (&kf)[2][KSTEPS]) {
+        const int grp = tk / p.nT;
+        const int t = tk % p.nT;
         if (grp != qgrp) {
-            load_q_frags<D>(p, b, kh, qf);
+            load_q_frags<D>(p, grp / p.Hkv, grp % p.Hkv, qf);
             qgrp = grp;
-        }
-        if (more) {
-            const int g2 = (task + 1) / p.nT;
-            stage_k_tile<D>(p, g2 / p.Hkv, g2 % p.Hkv, (task + 1) % p.nT, sK[w][(k + 1) & 1]);
         }
         // per-call reset owned by this tile
         if (p.bits && lane == 0 && (t % 32) == 0) p.bits[(int64_t)grp * p.nwords + t / 32] = 0u;
-        if (more) wait_vmcnt<QCH>(); else wait_vmcnt<0>();   // this tile is in LDS
         f32x16 sv[2];
-        tile_scores<D>(p, t, sK[w][k & 1], qf, sv);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            sv[sub] = f32x16{};
+#pragma unroll
+            for (int st = 0; st < KSTEPS; ++st) sv[sub] = mfma32x32x16(kf[sub][st], qf[st], sv[sub]);
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = t * BKD + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                sv[sub][r] = (j < p.N) ? sv[sub][r] * p.scale_log2 : kNegInf;
+            }
         float M = kNegInf;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -185,6 +200,17 @@ __global__ __launch_bounds__(256) void mala_dec_score(const DecParams p) {
                 p.tmax[((int64_t)grp * p.nT + t) * p.G + g] = M;
                 p.tsum[((int64_t)grp * p.nT + t) * p.G + g] = sum;
             }
+        }
+    };
+
+    bf16x8 ka[2][KSTEPS], kb[2][KSTEPS];
+    load_tile(task, ka);
+    for (; task < tend; task += 2) {
+        if (task + 1 < tend) load_tile(task + 1, kb);
+        score_tile(task, ka);
+        if (task + 1 < tend) {
+            if (task + 2 < tend) load_tile(task + 2, ka);
+            score_tile(task + 1, kb);
         }
     }
 }
@@ -460,98 +486,92 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     }
 }
 
-// P.V thread layout: dc = tid % (D/8) owns d = 8 dc .. 8 dc + 7; kg = tid / (D/8)
-// owns KPT consecutive keys of each round's 256 keys (4 tiles).
+// P.V over the kept tiles: one wave per kept tile, four per workgroup, every
+// load issued at once (the tile index, then its V rows and spilled scores).
+// Lane (dc, kg) owns d = 8 dc .. 8 dc + 7 of KPL consecutive keys; the wave's
+// partial output is reduced across kg with lane shuffles, the workgroup's
+// across its waves in LDS, and written as one partial per workgroup.
 template <int D, int GP>
 __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
-    constexpr int DC = D / 8;
-    constexpr int NKG = 256 / DC;
-    constexpr int KPT = 4 * BKD / NKG;
-    __shared__ float sP[GP][4 * BKD];
-    __shared__ float sRed[NKG][D];
+    constexpr int DC = D / 8;            // 16-byte chunks per V row
+    constexpr int KG = 64 / DC;          // key groups per wave
+    constexpr int KPL = BKD / KG;        // keys per lane
+    __shared__ float sP[4][GP][BKD];
+    __shared__ float sRed[4][GP][D];
     const int tid = threadIdx.x;
-    const int s = blockIdx.x, grp = blockIdx.y;
+    const int lane = tid & 63, w = tid >> 6;
+    const int grp = blockIdx.y;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
     const int G = p.G;
     const int cnt = p.kcount[grp];
-    const int per = (cnt + p.nsplit - 1) / p.nsplit;
-    const int i0 = s * per;
-    const int i1 = (i0 + per < cnt) ? i0 + per : cnt;
-    const int dc = tid % DC, kg = tid / DC;
+    if (blockIdx.x * 4 >= cnt) return;          // the whole workgroup: no partial is read
+    const int idx = blockIdx.x * 4 + w;
+    const bool has = idx < cnt;
+    const int t = has ? p.klist[(int64_t)grp * p.nT + idx] : 0;
+    const int dc = lane % DC, kg = lane / DC;
+    // V rows of this lane's keys (16-byte chunk dc)
+    u32x4 vx[KPL];
+    const uint16_t* vb = p.v + b * p.v_sb + kh * p.v_sh + 8 * dc;
+#pragma unroll
+    for (int r = 0; r < KPL; ++r) {
+        int key = t * BKD + kg * KPL + r;
+        key = key < p.N ? key : p.N - 1;
+        vx[r] = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
+    }
+    // P of the tile: lane = key, one value per row
+    {
+        const int key = t * BKD + lane;
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            float pr = 0.f;
+            if (has && g < G && key < p.N)
+                pr = fast_exp2(p.spill[((int64_t)grp * G + g) * p.N + key] - p.lse2[(int64_t)grp * G + g]);
+            sP[w][g][lane] = pr;
+        }
+    }
+    __syncthreads();
     float acc[GP][8];
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-    const uint16_t* vb = p.v + b * p.v_sb + kh * p.v_sh + 8 * dc;
-    for (int base = i0; base < i1; base += 4) {
-        // V rows first (independent of P), then P for the round's 4 tiles
-        u32x4 vx[KPT];
-        int keys[KPT];
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const int jj = kg * KPT + r;                  // 0 .. 255: tile jj/64 of the round
-            const int idx = base + jj / BKD;
-            int key = -1;
-            if (idx < i1) key = p.klist[(int64_t)grp * p.nT + idx] * BKD + jj % BKD;
-            keys[r] = key;
-            const int kk = (key >= 0 && key < p.N) ? key : 0;
-            vx[r] = *(const u32x4*)(vb + (int64_t)kk * p.v_sl);
+    for (int r = 0; r < KPL; ++r) {
+        float vv[8];
+#pragma unroll
+        for (int m2 = 0; m2 < 4; ++m2) {
+            vv[2 * m2] = __uint_as_float(vx[r][m2] << 16);
+            vv[2 * m2 + 1] = __uint_as_float(vx[r][m2] & 0xFFFF0000u);
         }
-        for (int e = tid; e < G * 4 * BKD; e += 256) {
-            const int g = e / (4 * BKD), jj = e % (4 * BKD);
-            const int idx = base + jj / BKD;
-            float pr = 0.f;
-            if (idx < i1) {
-                const int key = p.klist[(int64_t)grp * p.nT + idx] * BKD + jj % BKD;
-                if (key < p.N)
-                    pr = fast_exp2(p.spill[((int64_t)grp * G + g) * p.N + key] - p.lse2[(int64_t)grp * G + g]);
-            }
-            sP[g][jj] = pr;
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            const float pr = sP[w][g][kg * KPL + r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[g][e] += pr * vv[e];
         }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            if (keys[r] < 0 || keys[r] >= p.N) continue;
-            const int jj = kg * KPT + r;
-            float vv[8];
-#pragma unroll
-            for (int m2 = 0; m2 < 4; ++m2) {
-                vv[2 * m2] = __uint_as_float(vx[r][m2] << 16);
-                vv[2 * m2 + 1] = __uint_as_float(vx[r][m2] & 0xFFFF0000u);
-            }
-#pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                if (g < G) {
-                    const float pr = sP[g][jj];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[g][e] += pr * vv[e];
-                }
-            }
-        }
-        __syncthreads();
     }
-    // reduce over key groups into this split's partial output (zeros when the
-    // split has no retained tile)
-    float* po = p.part_o + (((int64_t)grp * p.nsplit + s) * G) * D;
-    for (int g = 0; g < G; ++g) {
+    // reduce over the key groups of the wave (lanes dc + DC * kg)
 #pragma unroll
-        for (int gg = 0; gg < GP; ++gg)
-            if (gg == g)
+    for (int off = DC; off < 64; off <<= 1)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sRed[kg][8 * dc + e] = acc[gg][e];
-        __syncthreads();
-        if (tid < D) {
-            float sum = 0.f;
+        for (int g = 0; g < GP; ++g)
 #pragma unroll
-            for (int k2 = 0; k2 < NKG; ++k2) sum += sRed[k2][tid];
-            po[(int64_t)g * D + tid] = sum;
-        }
-        __syncthreads();
+            for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+    if (kg == 0) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sRed[w][g][8 * dc + e] = acc[g][e];
+    }
+    __syncthreads();
+    float* po = p.part_o + (((int64_t)grp * p.npart + blockIdx.x) * G) * D;
+    for (int e = tid; e < G * D; e += 256) {
+        const int g = e / D, d = e % D;
+        po[e] = sRed[0][g][d] + sRed[1][g][d] + sRed[2][g][d] + sRed[3][g][d];
     }
 }
 
-// Sum of the split partials (already normalised by the final LSE) -> bf16 o.
+// Sum of the P.V partials (already normalised by the final LSE) -> bf16 o.
 // One workgroup per (group, row, 32-wide d slice): 8 split classes x 32 d.
 template <int D>
 __global__ __launch_bounds__(256) void mala_dec_sum_combine(const DecParams p) {
@@ -560,11 +580,12 @@ __global__ __launch_bounds__(256) void mala_dec_sum_combine(const DecParams p) {
     const int grp = blockIdx.x, g = blockIdx.y, dq = blockIdx.z;
     const int G = p.G;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
-    const int64_t base = (int64_t)grp * p.nsplit;
+    const int64_t base = (int64_t)grp * p.npart;
     const int d = 32 * dq + (tid & 31), cls = tid >> 5;
+    const int nused = (p.kcount[grp] + 3) / 4;   // P.V workgroups that wrote a partial
     float osum = 0.f;
 #pragma unroll 4
-    for (int s = cls; s < p.nsplit; s += 8) osum += p.part_o[((base + s) * G + g) * D + d];
+    for (int s = cls; s < nused; s += 8) osum += p.part_o[((base + s) * G + g) * D + d];
     sO[cls][tid & 31] = osum;
     __syncthreads();
     if (tid < 32) {
@@ -698,7 +719,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
         }
         __syncthreads();
     }
-    float* po = p.part_o + (((int64_t)grp * p.nsplit + s) * G) * D;
+    float* po = p.part_o + (((int64_t)grp * p.npart + s) * G) * D;
     for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int gg = 0; gg < GP; ++gg)
@@ -748,7 +769,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p)
         const int64_t ix = (base + s) * G + g;
         const float ms = p.part_ml[ix * 2];
         const float a = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
-        osum += p.part_o[ix * D + d] * a;
+        osum += p.part_o[(((int64_t)grp * p.npart + s) * G + g) * D + d] * a;
         lsum += p.part_ml[ix * 2 + 1] * a;
     }
     sO[cls][tid & 31] = osum;
@@ -780,10 +801,10 @@ static hipError_t launch_decode_t(const DecParams& p, bool dense, hipStream_t s)
     } else {
         const int tasks = ngrp * p.nT;
         int nwg = (tasks + 3) / 4;
-        if (nwg > 256) nwg = 256;        // one workgroup (128 KB of K in flight) per CU
+        if (nwg > 512) nwg = 512;        // two workgroups (8 waves) per CU
         hipLaunchKernelGGL((mala_dec_score<D>), dim3(nwg), dim3(256), 0, s, p);
         hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(64), 0, s, p);
-        hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3(p.nsplit, ngrp), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3((p.nT + 3) / 4, ngrp), dim3(256), 0, s, p);
         hipLaunchKernelGGL((mala_dec_sum_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     }
     return hipGetLastError();

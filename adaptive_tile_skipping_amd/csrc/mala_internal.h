@@ -65,6 +65,7 @@ struct DecParams {
     int nwords;
     int64_t k_sb, k_sl, k_sh, v_sb, v_sl, v_sh;
     int B, N, Hq, Hkv, G, nT, nsplit, tiles_per_split;
+    int npart;              // max(nsplit, ceil(nT / 4)): partial outputs per (sequence, KV head)
     float scale_log2;
     float log2_tau;
     float log2_N;
@@ -75,7 +76,7 @@ struct DecParams {
     int32_t* klist;         // [B, Hkv, nT]     retained tiles, newest first
     int32_t* kcount;        // [B, Hkv]
     float* lse2;            // [B, Hkv, G]      base-2 final log-normaliser
-    float* part_o;          // [B, Hkv, nsplit, G, d] partial outputs
+    float* part_o;          // [B, Hkv, npart, G, d] partial outputs (dense splits or P.V workgroups)
     float* part_ml;         // [B, Hkv, nsplit, G, 2] partial (max, sum) (dense path)
 };
 
