@@ -287,6 +287,37 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     const float* tmax = p.tmax + (int64_t)grp * p.nT * G;
     const float* tsum = p.tsum + (int64_t)grp * p.nT * G;
 
+    // Group reference: the largest tile max of each row.  When every tile max
+    // lies within 96 of it and tau/N within 2^+-120, linear masses relative to
+    // it stay inside fp32's normal range for the whole scan, and the rounds run
+    // with one fixed reference (no per-chunk reference or rescaling).
+    float gref[GP];
+    bool linear = lin_ok;
+    {
+        float mx[GP], mn[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) { mx[g] = kNegInf; mn[g] = __builtin_inff(); }
+        // the flat [tile][row] array in 64-lane strides, eight loads in flight per lane
+        const int ntot = p.nT * G;
+#pragma unroll 8
+        for (int e = lane; e < ntot; e += 64) {
+            const float v = tmax[e];
+            const int g = e % G;
+#pragma unroll
+            for (int gg = 0; gg < GP; ++gg)
+                if (gg == g) {
+                    mx[gg] = fmaxf(mx[gg], v);
+                    mn[gg] = fminf(mn[gg], v);
+                }
+        }
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            gref[g] = (g < G) ? wave_max_all(mx[g]) : 0.f;
+            const float lo = (g < G) ? -wave_max_all(-mn[g]) : 0.f;
+            linear = linear && (g >= G || lo >= gref[g] - 96.f);
+        }
+    }
+
     // accepted tiles of a round: list, bits, count
     auto accept = [&](uint64_t acc, int t) {
         if ((acc >> lane) & 1ull) {
@@ -341,28 +372,44 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
             }
         }
         const bool empty0 = l[0] == 0.f;
-        // reference exponents and the range check of the fast path; every loop
-        // over rows runs all GP slots branch-free (rows >= G are inert)
-        float ref[GP];
-        bool fast = lin_ok, lane_ok = true;
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            const bool row = g < G;
-            ref[g] = row ? fmaxf(m[g], wave_max_all(Mg[g])) : 0.f;
-            lane_ok = lane_ok && (!row || !valid || Mg[g] >= ref[g] - 96.f);
-            fast = fast && (!row || empty0 || m[g] >= ref[g] - 96.f);
-        }
-        fast = fast && (__ballot(!lane_ok) == 0ull);
-        int pos = 0;
-        if (fast) {
-            float a[GP], x[GP], Z[GP];
+        float ref[GP], a[GP], x[GP], Z[GP];
+        bool fast;
+        if (linear) {
+            // the state holds the retained mass relative to gref
+            fast = true;
 #pragma unroll
             for (int g = 0; g < GP; ++g) {
                 const bool row = g < G;
-                a[g] = (row && valid) ? fast_exp2(Mg[g] - ref[g]) : 0.f;
+                ref[g] = gref[g];
+                a[g] = (row && valid) ? fast_exp2(Mg[g] - gref[g]) : 0.f;
                 x[g] = Sg[g] * a[g];
-                Z[g] = !row ? 1.f : (empty0 ? 0.f : l[g] * fast_exp2(m[g] - ref[g]));
+                Z[g] = !row ? 1.f : l[g];
             }
+        } else {
+            // reference exponents and the range check of the fast path; every
+            // loop over rows runs all GP slots branch-free (rows >= G are inert)
+            fast = lin_ok;
+            bool lane_ok = true;
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                const bool row = g < G;
+                ref[g] = row ? fmaxf(m[g], wave_max_all(Mg[g])) : 0.f;
+                lane_ok = lane_ok && (!row || !valid || Mg[g] >= ref[g] - 96.f);
+                fast = fast && (!row || empty0 || m[g] >= ref[g] - 96.f);
+            }
+            fast = fast && (__ballot(!lane_ok) == 0ull);
+            if (fast) {
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    const bool row = g < G;
+                    a[g] = (row && valid) ? fast_exp2(Mg[g] - ref[g]) : 0.f;
+                    x[g] = Sg[g] * a[g];
+                    Z[g] = !row ? 1.f : (empty0 ? 0.f : l[g] * fast_exp2(m[g] - ref[g]));
+                }
+            }
+        }
+        int pos = 0;
+        if (fast) {
             bool empty = empty0;
             while (pos < 64) {
                 const bool active = valid && lane >= pos;
@@ -404,7 +451,10 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
             if (!empty) {
 #pragma unroll
                 for (int g = 0; g < GP; ++g)
-                    if (g < G) { m[g] = ref[g]; l[g] = Z[g]; }
+                    if (g < G) {
+                        if (!linear) m[g] = ref[g];
+                        l[g] = Z[g];
+                    }
             }
             continue;
         }
@@ -473,6 +523,11 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     if (lane == 0) {
         p.kcount[grp] = kept;
         if (p.kept_tiles) p.kept_tiles[grp] = kept;
+    }
+    if (linear) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+            if (g < G) m[g] = gref[g];
     }
     if (lane < G) {
         float mm = kNegInf, ll = 0.f;
