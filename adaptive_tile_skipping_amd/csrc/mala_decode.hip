@@ -231,6 +231,8 @@ __device__ __forceinline__ float wave_incl_sum(float x) {
     x += dpp_f<0x143, 0xC, false>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
+// The value of lane - 1 (0 in lane 0): DPP wave_shr:1.
+__device__ __forceinline__ float wave_shr1(float x) { return dpp_f<0x138, 0xF, true>(x); }
 // Maximum over the wave (lanes whose source is out of range keep -inf).
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ float dpp_max_step(float v) {
@@ -426,7 +428,9 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
                 for (int g = 0; g < GP; ++g) {
                     const float xv = v0 ? x[g] : 0.f;
                     inc[g] = wave_incl_sum(xv);
-                    exc[g] = inc[g] - xv;
+                    // the previous lane's inclusive sum (inc - xv would cancel
+                    // when this tile's mass dwarfs the earlier ones)
+                    exc[g] = wave_shr1(inc[g]);
                     v1 = v1 || (a[g] >= cthr * (Z[g] + exc[g]));
                 }
                 v1 = v1 && v0;
