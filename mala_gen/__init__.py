@@ -131,6 +131,40 @@ def attn_inputs(tag: int, B: int, L: int, Hq: int, Hkv: int, d: int, p: float,
             "B": B, "L": L, "Hq": Hq, "Hkv": Hkv, "d": d}
 
 
+def varlen_inputs(tag: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, p: float,
+                  diffuse_kv_heads=()) -> dict:
+    """Packed bf16 bit patterns for a batch of sequences whose Lq queries are
+    the last Lq positions of their Lk keys: q [sum Lq, Hq, d], k/v
+    [sum Lk, Hkv, d], cu_q/cu_k int32 [B+1].  Sequence s of length Lk is drawn
+    exactly as attn_inputs draws batch entry s of a length-Lk sequence, so a
+    chunk's rows are the last rows of that full sequence."""
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    lens_q, lens_k = [int(x) for x in lens_q], [int(x) for x in lens_k]
+    if len(lens_q) != len(lens_k) or any(lq < 0 or lk < lq for lq, lk in zip(lens_q, lens_k)):
+        raise ValueError("need 0 <= Lq <= Lk per sequence")
+    G = Hq // Hkv
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    q = np.zeros((int(cu_q[-1]), Hq, d), np.uint16)
+    k = np.zeros((int(cu_k[-1]), Hkv, d), np.uint16)
+    v = np.zeros((int(cu_k[-1]), Hkv, d), np.uint16)
+    diffuse = set(diffuse_kv_heads)
+    for s, (lq, lk) in enumerate(zip(lens_q, lens_k)):
+        if lk == 0:
+            continue
+        for kh in range(Hkv):
+            rng = _rng(tag, s, kh)
+            if kh in diffuse:
+                Q, K, V, _ = _diffuse_head(rng, lk, G, d)
+            else:
+                Q, K, V, _ = _local_retrieval_head(rng, lk, G, d, p)
+            q[cu_q[s]:cu_q[s + 1], kh * G:(kh + 1) * G, :] = round_to_bf16_bits(Q[lk - lq:])
+            k[cu_k[s]:cu_k[s + 1], kh, :] = round_to_bf16_bits(K)
+            v[cu_k[s]:cu_k[s + 1], kh, :] = round_to_bf16_bits(V)
+    return {"q": q, "k": k, "v": v, "cu_q": cu_q, "cu_k": cu_k, "Hq": Hq, "Hkv": Hkv, "d": d}
+
+
 def decode_inputs(tag: int, B: int, N: int, Hq: int, Hkv: int, d: int) -> dict:
     """bf16 bit patterns: q [B, Hq, d], kcache/vcache [B, N, Hkv, d]."""
     if Hq % Hkv:
@@ -172,11 +206,20 @@ WORKLOADS = {
                   Ls=(1024, 2048, 4096, 8192, 16384, 32768), taus=(0.0, 0.25, 1.0, 4.0)),
     "train_128k": dict(tag=3, B=1, L=131072, Hq=5, Hkv=1, d=128, p=0.02, diffuse=(), Bq=128, Bk=64, taus=(1.0, 0.0)),
     "decode_128k": dict(tag=4, B=8, N=131072, Hq=5, Hkv=1, d=128, Bk_dec=64, taus=(1.0, 0.0)),
+    # the last 16K queries of the 128K training sequence, prefilled onto the
+    # cache of the 112K keys before them (same seeds as train_128k)
+    "prefill_128k": dict(tag=3, lens_q=(16384,), lens_k=(131072,), Hq=5, Hkv=1, d=128, p=0.02, diffuse=(),
+                         Bq=128, Bk=64, taus=(1.0, 0.0)),
+    # a ragged batch: fresh prompts (Lq = Lk), chunks onto caches, single tokens
+    "varlen_mix": dict(tag=5, lens_q=(1000, 333, 1, 4096, 0, 700), lens_k=(1000, 2900, 5000, 6000, 77, 700),
+                       Hq=8, Hkv=2, d=128, p=0.1, diffuse=(1,), Bq=128, Bk=64, taus=(0.0, 0.25, 1.0, 4.0)),
 }
 
 
 def workload_inputs(name: str, L: int | None = None, with_dout: bool = True) -> dict:
     w = WORKLOADS[name]
+    if "lens_q" in w:
+        return varlen_inputs(w["tag"], w["lens_q"], w["lens_k"], w["Hq"], w["Hkv"], w["d"], w["p"], w["diffuse"])
     if name == "decode_128k":
         return decode_inputs(w["tag"], w["B"], w["N"] if L is None else L, w["Hq"], w["Hkv"], w["d"])
     LL = w.get("L") if L is None else L

@@ -46,9 +46,11 @@ def _load():
                                     P, P, P, P, P, P, i32]
     lib.mala_oracle_bwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, f64, i32, i32,
                                     P, i32, P, i32, P, P, P, P, P, i32]
+    lib.mala_oracle_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, i32,
+                                           P, P, P, P, P, P, i32]
     lib.mala_oracle_decode.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32,
                                        P, P, P, P, P, P, i32]
-    for f in (lib.mala_oracle_fwd, lib.mala_oracle_bwd, lib.mala_oracle_decode):
+    for f in (lib.mala_oracle_fwd, lib.mala_oracle_fwd_varlen, lib.mala_oracle_bwd, lib.mala_oracle_decode):
         f.restype = ctypes.c_int
     lib.mala_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -90,6 +92,39 @@ def oracle_fwd(q, k, v, tau: float, Bq: int, Bk: int, blocks=None, nthreads: int
                                  int(nthreads))
     if rc:
         raise ValueError(f"oracle_fwd failed with code {rc}")
+    return {"o": o, "lse": lse, "keep": keep, "margin": margin, "kept_slots": slots, "omitted": omitted}
+
+
+def oracle_fwd_varlen(q, k, v, cu_q, cu_k, tau: float, Bq: int, Bk: int, blocks=None, nthreads: int = 0):
+    """Variable-length forward (queries at the end of their keys, Lq <= Lk).
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d]; cu_q/cu_k [B+1] cumulative
+    lengths.  Returns dict(o, lse [Hq, total_q], keep/margin [B, Hq, nQB, nKT],
+    kept_slots, omitted) with nQB, nKT from the longest sequence; `blocks` as
+    in oracle_fwd with that nQB.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq = np.ascontiguousarray(cu_q, dtype=np.int32)
+    ck = np.ascontiguousarray(cu_k, dtype=np.int32)
+    B = len(cq) - 1
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    maxq = int(np.max(np.diff(cq))) if B > 0 else 0
+    maxk = int(np.max(np.diff(ck))) if B > 0 else 0
+    nQB, nKT = max(1, -(-maxq // Bq)), max(1, -(-maxk // Bk))
+    o = np.full(q.shape, np.nan)
+    lse = np.full((Hq, Tq), np.nan)
+    keep = np.full((B, Hq, nQB, nKT), KEEP_UNVISITED, np.uint8)
+    margin = np.full((B, Hq, nQB, nKT), np.nan)
+    slots = np.full((Hq, Tq), -1, np.int32)
+    omitted = np.full((Hq, Tq), np.nan)
+    bl = None if blocks is None else np.ascontiguousarray(blocks, dtype=np.int32)
+    rc = _load().mala_oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), B, Hq, Hkv, d,
+                                        float(tau), Bq, Bk, _ptr(bl), 0 if bl is None else len(bl),
+                                        _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(slots),
+                                        _ptr(omitted), int(nthreads))
+    if rc:
+        raise ValueError(f"oracle_fwd_varlen failed with code {rc}")
     return {"o": o, "lse": lse, "keep": keep, "margin": margin, "kept_slots": slots, "omitted": omitted}
 
 

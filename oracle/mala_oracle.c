@@ -41,10 +41,19 @@
  *   - decode applies the forward rule to the block of the G q heads sharing a
  *     KV head, with L_i = N (the cache includes the new token), tiles of the
  *     cache visited newest first ([P2] "One tolerance": one tau for decoding).
+ *   - prefill onto an existing cache (Lq <= Lk; [P1] names prefill as a mode
+ *     under the same tau): the Lq queries are the last Lq positions of the
+ *     sequence, so query row i (0-indexed in the chunk) sees keys
+ *     j <= Lk - Lq + i and L_i = Lk - Lq + i + 1.  Key tiles stay aligned to
+ *     key 0 and query blocks start at the chunk's first row, so a chunk that
+ *     starts at a multiple of Bq reproduces the rows of the full forward.
  *
  * Layouts: q, o, dout, dq: [B][L][Hq][d]; k, v, dk, dv: [B][L][Hkv][d];
  * lse: [B][Hq][L]; per-tile arrays keep/margin: [B][Hq][nQB][nKT] with
- * nQB = ceil(L/Bq), nKT = ceil(L/Bk).  keep holds 1 (kept) or 0 (skipped) for
+ * nQB = ceil(L/Bq), nKT = ceil(L/Bk).  The variable-length forward packs the
+ * sequences instead: q, o [total_q][Hq][d]; k, v [total_k][Hkv][d]; lse,
+ * kept_slots, omitted [Hq][total_q]; keep/margin [B][Hq][nQB][nKT] with nQB,
+ * nKT taken from the longest query and key lengths.  keep holds 1 (kept) or 0 (skipped) for
  * every visited tile; entries of tiles never visited are not written.
  * margin holds the decision's log-margin
  *     forward:  max over voting rows of (M_i - m_i - ln l_i - theta_i)
@@ -99,7 +108,12 @@ int mala_oracle_max_threads(void) {
 /* ------------------------------------------------------------------------ */
 typedef struct {
     const double *q, *k, *v;
-    int B, L, Hq, Hkv, d, Bq, Bk, nQB, nKT;
+    int B, Hq, Hkv, d, Bq, Bk, nQB, nKT;
+    /* per sequence: first packed row of its queries and of its keys, query
+     * and key counts, and the base of its [Hq] row-statistics rows */
+    const long *qoff, *koff, *lseoff;
+    const int *lq, *lk;
+    long lse_hstride;   /* distance between heads in lse / kept_slots / omitted */
     double tau, scale;
     double *o, *lse, *margin, *omitted;
     uint8_t* keep;
@@ -107,11 +121,19 @@ typedef struct {
 } fwd_ctx;
 
 static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
-    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, L = c->L, Bk = c->Bk;
+    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, Bk = c->Bk;
+    const int Lq = c->lq[b], Lk = c->lk[b];
+    const int off = Lk - Lq;          /* keys before the first query of the chunk */
     const int kh = h / (Hq / Hkv);
     const int r0 = qb * c->Bq;
-    const int r1 = (r0 + c->Bq < L) ? r0 + c->Bq : L;
+    if (r0 >= Lq) return OR_OK;       /* past this sequence's queries: not visited */
+    const int r1 = (r0 + c->Bq < Lq) ? r0 + c->Bq : Lq;
     const int nr = r1 - r0;
+    const double* qs = c->q + (size_t)c->qoff[b] * Hq * d;
+    const double* ks = c->k + (size_t)c->koff[b] * Hkv * d;
+    const double* vs = c->v + (size_t)c->koff[b] * Hkv * d;
+    double* os = c->o + (size_t)c->qoff[b] * Hq * d;
+    const size_t srow = (size_t)c->lseoff[b] + (size_t)h * c->lse_hstride;
     double* buf = (double*)malloc(sizeof(double) * ((size_t)nr * (8 + d) + (size_t)nr * Bk));
     int32_t* slots = (int32_t*)calloc((size_t)nr, sizeof(int32_t));
     if (!buf || !slots) { free(buf); free(slots); return OR_ENOMEM; }
@@ -126,23 +148,24 @@ static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
     double* S = acc + (size_t)nr * d;       /* [nr][Bk] tile scores          */
     for (int r = 0; r < nr; ++r) {
         m[r] = -INFINITY; l[r] = 0.0; om[r] = -INFINITY; ol[r] = 0.0;
-        th[r] = log_threshold(c->tau, (double)(r0 + r + 1));
+        th[r] = log_threshold(c->tau, (double)(off + r0 + r + 1));   /* L_i = visible keys */
     }
     memset(acc, 0, sizeof(double) * (size_t)nr * d);
 
-    const int kt_first = (r1 - 1) / Bk;  /* tile holding the diagonal of the last row */
+    /* tile holding the last legal key of the block's last row */
+    const int kt_first = (off + r1 - 1) / Bk;
     for (int kt = kt_first; kt >= 0; --kt) {          /* diagonal -> earlier keys */
         const int j0 = kt * Bk;
-        const int j1 = (j0 + Bk < L) ? j0 + Bk : L;
+        const int j1 = (j0 + Bk < Lk) ? j0 + Bk : Lk;
         /* score discovery: every legal key of the tile is scored */
         for (int r = 0; r < nr; ++r) {
-            const int i = r0 + r;
-            const double* qi = c->q + (((size_t)b * L + i) * Hq + h) * d;
+            const int jl = off + r0 + r;              /* last key row r may see */
+            const double* qi = qs + ((size_t)(r0 + r) * Hq + h) * d;
             double mx = -INFINITY;
             for (int j = j0; j < j1; ++j) {
                 double s = -INFINITY;
-                if (j <= i) {
-                    const double* kj = c->k + (((size_t)b * L + j) * Hkv + kh) * d;
+                if (j <= jl) {
+                    const double* kj = ks + ((size_t)j * Hkv + kh) * d;
                     s = dot(qi, kj, d) * c->scale;
                     if (s > mx) mx = s;
                 }
@@ -166,8 +189,8 @@ static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
 
         for (int r = 0; r < nr; ++r) {
             if (M[r] == -INFINITY) continue;
-            const int i = r0 + r;
-            const int nleg = ((i < j1 - 1) ? i : j1 - 1) - j0 + 1;
+            const int jl = off + r0 + r;
+            const int nleg = ((jl < j1 - 1) ? jl : j1 - 1) - j0 + 1;
             if (keep) {
                 /* standard online-softmax update with the tile's legal keys */
                 const double mn = (M[r] > m[r]) ? M[r] : m[r];
@@ -175,10 +198,10 @@ static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
                 double* ar = acc + (size_t)r * d;
                 for (int cc = 0; cc < d; ++cc) ar[cc] *= alpha;
                 double lsum = l[r] * alpha;
-                for (int j = j0; j <= i && j < j1; ++j) {
+                for (int j = j0; j <= jl && j < j1; ++j) {
                     const double p = exp(S[(size_t)r * Bk + (j - j0)] - mn);
                     lsum += p;
-                    const double* vj = c->v + (((size_t)b * L + j) * Hkv + kh) * d;
+                    const double* vj = vs + ((size_t)j * Hkv + kh) * d;
                     for (int cc = 0; cc < d; ++cc) ar[cc] += p * vj[cc];
                 }
                 l[r] = lsum;
@@ -188,7 +211,7 @@ static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
                 /* bookkeeping only: mass of the omitted legal keys */
                 const double mn = (M[r] > om[r]) ? M[r] : om[r];
                 double osum = (om[r] == -INFINITY) ? 0.0 : ol[r] * exp(om[r] - mn);
-                for (int j = j0; j <= i && j < j1; ++j) osum += exp(S[(size_t)r * Bk + (j - j0)] - mn);
+                for (int j = j0; j <= jl && j < j1; ++j) osum += exp(S[(size_t)r * Bk + (j - j0)] - mn);
                 ol[r] = osum;
                 om[r] = mn;
             }
@@ -196,20 +219,45 @@ static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
     }
     for (int r = 0; r < nr; ++r) {
         const int i = r0 + r;
-        const size_t orow = (((size_t)b * L + i) * Hq + h) * d;
-        for (int cc = 0; cc < d; ++cc) c->o[orow + cc] = acc[(size_t)r * d + cc] / l[r];
+        const size_t orow = ((size_t)i * Hq + h) * d;
+        for (int cc = 0; cc < d; ++cc) os[orow + cc] = acc[(size_t)r * d + cc] / l[r];
         const double lz = m[r] + log(l[r]);
-        c->lse[((size_t)b * Hq + h) * L + i] = lz;
-        if (c->kept_slots) c->kept_slots[((size_t)b * Hq + h) * L + i] = slots[r];
+        c->lse[srow + i] = lz;
+        if (c->kept_slots) c->kept_slots[srow + i] = slots[r];
         if (c->omitted) {
             double w = 0.0;
             if (ol[r] > 0.0) w = 1.0 / (1.0 + exp(lz - (om[r] + log(ol[r]))));
-            c->omitted[((size_t)b * Hq + h) * L + i] = w;
+            c->omitted[srow + i] = w;
         }
     }
     free(buf);
     free(slots);
     return OR_OK;
+}
+
+/* Runs the listed blocks (ids (b*Hq + h)*nQB + qb), or all of them longest
+ * first when blocks is NULL. */
+static int fwd_run(const fwd_ctx* c, const int32_t* blocks, int nblocks, int nthreads) {
+    const int B = c->B, Hq = c->Hq;
+    const long total = (long)B * Hq * c->nQB;
+    const long n = blocks ? nblocks : total;
+    int err = OR_OK;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < n; ++u) {
+        long id = blocks ? (long)blocks[u] : u;
+        if (id < 0 || id >= total) { err = OR_EINVAL; continue; }
+        if (!blocks) {
+            const long bh = id % ((long)B * Hq);
+            const long qb = c->nQB - 1 - id / ((long)B * Hq);
+            id = bh * c->nQB + qb;
+        }
+        const int qb = (int)(id % c->nQB);
+        const int bh = (int)(id / c->nQB);
+        int e = fwd_block(c, bh / Hq, bh % Hq, qb);
+        if (e) err = e;
+    }
+    return err;
 }
 
 int mala_oracle_fwd(const double* q, const double* k, const double* v,
@@ -220,30 +268,70 @@ int mala_oracle_fwd(const double* q, const double* k, const double* v,
     if (!q || !k || !v || !o || !lse) return OR_EINVAL;
     if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return OR_EINVAL;
     if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
+    long* offs = (long*)malloc(sizeof(long) * 3 * (size_t)B);
+    int* lens = (int*)malloc(sizeof(int) * (size_t)B);
+    if (!offs || !lens) { free(offs); free(lens); return OR_ENOMEM; }
+    for (int b = 0; b < B; ++b) {
+        offs[b] = (long)b * L;                     /* q and k rows */
+        offs[B + b] = (long)b * Hq * L;            /* lse [B][Hq][L] */
+        lens[b] = L;
+    }
     fwd_ctx c;
-    c.q = q; c.k = k; c.v = v; c.B = B; c.L = L; c.Hq = Hq; c.Hkv = Hkv; c.d = d;
+    c.q = q; c.k = k; c.v = v; c.B = B; c.Hq = Hq; c.Hkv = Hkv; c.d = d;
     c.Bq = Bq; c.Bk = Bk; c.nQB = (L + Bq - 1) / Bq; c.nKT = (L + Bk - 1) / Bk;
+    c.qoff = offs; c.koff = offs; c.lseoff = offs + B; c.lq = lens; c.lk = lens;
+    c.lse_hstride = L;
     c.tau = tau; c.scale = 1.0 / sqrt((double)d);
     c.o = o; c.lse = lse; c.keep = keep; c.margin = margin; c.kept_slots = kept_slots; c.omitted = omitted;
-    const long total = (long)B * Hq * c.nQB;
-    const long n = blocks ? nblocks : total;
-    int err = OR_OK;
-    set_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
-    for (long u = 0; u < n; ++u) {
-        long id = blocks ? (long)blocks[u] : u;
-        if (id < 0 || id >= total) { err = OR_EINVAL; continue; }
-        /* longest blocks first when running all of them */
-        if (!blocks) {
-            const long bh = id % ((long)B * Hq);
-            const long qb = c.nQB - 1 - id / ((long)B * Hq);
-            id = bh * c.nQB + qb;
-        }
-        const int qb = (int)(id % c.nQB);
-        const int bh = (int)(id / c.nQB);
-        int e = fwd_block(&c, bh / Hq, bh % Hq, qb);
-        if (e) err = e;
+    const int err = fwd_run(&c, blocks, nblocks, nthreads);
+    free(offs);
+    free(lens);
+    return err;
+}
+
+/* Variable-length forward: sequence b has queries cu_q[b] .. cu_q[b+1]-1 and
+ * keys cu_k[b] .. cu_k[b+1]-1 of the packed arrays, with its queries at the
+ * end of its keys (0 <= Lq <= Lk).  Layouts in the header comment; nQB and
+ * nKT from the longest query and key lengths. */
+int mala_oracle_fwd_varlen(const double* q, const double* k, const double* v,
+                           const int32_t* cu_q, const int32_t* cu_k,
+                           int B, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
+                           const int32_t* blocks, int nblocks,
+                           double* o, double* lse, uint8_t* keep, double* margin,
+                           int32_t* kept_slots, double* omitted, int nthreads) {
+    if (!q || !k || !v || !o || !lse || !cu_q || !cu_k) return OR_EINVAL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return OR_EINVAL;
+    if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
+    if (cu_q[0] != 0 || cu_k[0] != 0) return OR_EINVAL;
+    int maxq = 0, maxk = 0;
+    for (int b = 0; b < B; ++b) {
+        const int lq = cu_q[b + 1] - cu_q[b], lk = cu_k[b + 1] - cu_k[b];
+        if (lq < 0 || lk < lq) return OR_EINVAL;
+        if (lq > maxq) maxq = lq;
+        if (lk > maxk) maxk = lk;
     }
+    long* offs = (long*)malloc(sizeof(long) * 3 * (size_t)B);
+    int* lens = (int*)malloc(sizeof(int) * 2 * (size_t)B);
+    if (!offs || !lens) { free(offs); free(lens); return OR_ENOMEM; }
+    for (int b = 0; b < B; ++b) {
+        offs[b] = cu_q[b];
+        offs[B + b] = cu_k[b];
+        offs[2 * B + b] = cu_q[b];                 /* lse [Hq][total_q] */
+        lens[b] = cu_q[b + 1] - cu_q[b];
+        lens[B + b] = cu_k[b + 1] - cu_k[b];
+    }
+    fwd_ctx c;
+    c.q = q; c.k = k; c.v = v; c.B = B; c.Hq = Hq; c.Hkv = Hkv; c.d = d;
+    c.Bq = Bq; c.Bk = Bk;
+    c.nQB = maxq > 0 ? (maxq + Bq - 1) / Bq : 1;
+    c.nKT = maxk > 0 ? (maxk + Bk - 1) / Bk : 1;
+    c.qoff = offs; c.koff = offs + B; c.lseoff = offs + 2 * B; c.lq = lens; c.lk = lens + B;
+    c.lse_hstride = cu_q[B];
+    c.tau = tau; c.scale = 1.0 / sqrt((double)d);
+    c.o = o; c.lse = lse; c.keep = keep; c.margin = margin; c.kept_slots = kept_slots; c.omitted = omitted;
+    const int err = fwd_run(&c, blocks, nblocks, nthreads);
+    free(offs);
+    free(lens);
     return err;
 }
 

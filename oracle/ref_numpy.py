@@ -95,6 +95,42 @@ def fwd(q, k, v, tau, Bq, Bk):
     return {"o": o, "lse": lse, "keep": keep, "kept_slots": slots, "omitted": omitted}
 
 
+def fwd_varlen(q, k, v, cu_q, cu_k, tau, Bq, Bk):
+    """Packed sequences with the queries at the end of their keys: row i of a
+    chunk of Lq queries over Lk keys sees keys j <= Lk - Lq + i, L_i = that
+    count.  Key tiles start at key 0; query blocks at the chunk's first row.
+    Returns o [Tq,Hq,d], lse [Hq,Tq], keep [B,Hq,nQB,nKT] (255 = not visited)."""
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    B = len(cu_q) - 1
+    lqs = [cu_q[b + 1] - cu_q[b] for b in range(B)]
+    lks = [cu_k[b + 1] - cu_k[b] for b in range(B)]
+    nQB, nKT = max(1, -(-max(lqs) // Bq)), max(1, -(-max(lks) // Bk))
+    o = np.zeros_like(q)
+    lse = np.zeros((Hq, Tq))
+    keep = np.full((B, Hq, nQB, nKT), 255, np.uint8)
+    for b in range(B):
+        Lq, Lk = lqs[b], lks[b]
+        off = Lk - Lq
+        qs, ks = cu_q[b], cu_k[b]
+        vis = np.arange(Lk)[None, :] <= (off + np.arange(Lq))[:, None]     # [Lq, Lk]
+        for h in range(Hq):
+            kh = h // G
+            S = (q[qs:qs + Lq, h, :] @ k[ks:ks + Lk, kh, :].T) / np.sqrt(d)
+            for qb in range(-(-Lq // Bq)):
+                r0, r1 = qb * Bq, min(Lq, (qb + 1) * Bq)
+                first = (off + r1 - 1) // Bk
+                tiles = [(kt * Bk, min(Lk, (kt + 1) * Bk)) for kt in range(first, -1, -1)]
+                kept, m, l, dec, _ = rule_block(S[r0:r1], vis[r0:r1], off + np.arange(r0, r1) + 1, tau, tiles)
+                for t, kp in zip(range(first, -1, -1), dec):
+                    keep[b, h, qb, t] = kp
+                w = np.where(kept, np.exp(S[r0:r1] - m[:, None]), 0.0)
+                o[qs + r0:qs + r1, h, :] = (w @ v[ks:ks + Lk, kh, :]) / l[:, None]
+                lse[h, qs + r0:qs + r1] = m + np.log(l)
+    return {"o": o, "lse": lse, "keep": keep}
+
+
 def bwd(q, k, v, o, dout, lse, tau, Bq, Bk):
     """Offline backward rule.  Returns dq, dk, dv, keep [B,Hq,nQB,nKT]."""
     B, L, Hq, d = q.shape

@@ -1,0 +1,161 @@
+"""Pins of the variable-length / prefill forward of the fp64 oracle.
+
+Reading (the summary page names prefill as a mode under the same tau; the
+review page's "One tolerance governs everything" normalises by the row's
+visible-key count): a chunk of Lq queries over Lk >= Lq keys holds the last Lq
+positions of its sequence, so chunk row i sees keys j <= Lk - Lq + i and
+L_i = Lk - Lq + i + 1.  Key tiles are aligned to key 0, query blocks to the
+chunk's first row.
+"""
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import mala_gen as G
+from oracle import oracle_decode, oracle_fwd, oracle_fwd_varlen
+from oracle import ref_numpy as R
+
+
+def _f64(inp):
+    return [G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v")]
+
+
+def _bottom_right_softmax(q, k, v, cu_q, cu_k):
+    """Dense softmax attention with the bottom-right causal mask, in fp64."""
+    Tq, Hq, d = q.shape
+    Gq = Hq // k.shape[1]
+    o = np.full(q.shape, np.nan)
+    lse = np.full((Hq, Tq), np.nan)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        Lq, Lk = qe - qs, ke - ks
+        vis = np.arange(Lk)[None, :] <= (Lk - Lq + np.arange(Lq))[:, None]
+        for h in range(Hq):
+            S = q[qs:qe, h] @ k[ks:ke, h // Gq].T / np.sqrt(d)
+            S = np.where(vis, S, -np.inf)
+            mx = S.max(-1, keepdims=True)
+            w = np.exp(S - mx)
+            o[qs:qe, h] = (w @ v[ks:ke, h // Gq]) / w.sum(-1, keepdims=True)
+            lse[h, qs:qe] = mx[:, 0] + np.log(w.sum(-1))
+    return o, lse
+
+
+lens = st.lists(st.tuples(st.integers(0, 150), st.integers(0, 150)), min_size=1, max_size=4)
+
+
+@settings(max_examples=50, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(lens, st.sampled_from([1, 8, 32, 64]), st.sampled_from([1, 16, 64]),
+       st.sampled_from([0.0, 0.25, 1.0, 4.0]), st.integers(1, 2), st.integers(0, 10_000))
+def test_varlen_c_oracle_matches_numpy(pairs, Bq, Bk, tau, Gq, seed):
+    lq = [min(a, b) for a, b in pairs]
+    lk = [max(a, b) for a, b in pairs]
+    inp = G.varlen_inputs(300 + seed, lq, lk, 2 * Gq, 2, 8, 0.3, diffuse_kv_heads=(1,))
+    q, k, v = _f64(inp)
+    a = oracle_fwd_varlen(q, k, v, inp["cu_q"], inp["cu_k"], tau, Bq, Bk)
+    b = R.fwd_varlen(q, k, v, inp["cu_q"], inp["cu_k"], tau, Bq, Bk)
+    assert (a["keep"] == b["keep"]).all()
+    if q.shape[0]:
+        assert np.abs(a["o"] - b["o"]).max() <= 1e-11
+        assert np.abs(a["lse"] - b["lse"]).max() <= 1e-11
+
+
+@pytest.mark.parametrize("tiles", [(64, 64), (128, 64), (16, 32), (1, 1)])
+def test_varlen_tau0_is_bottom_right_softmax(tiles):
+    """tau = 0 keeps every tile: plain softmax attention with the queries at the
+    end of their keys."""
+    inp = G.varlen_inputs(310, [200, 1, 0, 77, 130], [200, 300, 50, 260, 131], 4, 2, 16, 0.2)
+    q, k, v = _f64(inp)
+    f = oracle_fwd_varlen(q, k, v, inp["cu_q"], inp["cu_k"], 0.0, *tiles)
+    o, lse = _bottom_right_softmax(q, k, v, inp["cu_q"], inp["cu_k"])
+    assert np.abs(f["o"] - o).max() <= 1e-12 * np.abs(o).max()
+    assert np.abs(f["lse"] - lse).max() <= 1e-12 * np.abs(lse).max()
+    vis = f["keep"] != 255
+    assert (f["keep"][vis] == 1).all()
+    # every legal tile of every block is visited, nothing else
+    cu_q, cu_k = inp["cu_q"], inp["cu_k"]
+    Bq, Bk = tiles
+    for b in range(len(cu_q) - 1):
+        Lq, Lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for qb in range(vis.shape[2]):
+            r1 = min(Lq, (qb + 1) * Bq)
+            n = (Lk - Lq + r1 - 1) // Bk + 1 if qb * Bq < Lq else 0
+            assert vis[b, 0, qb].sum() == n
+
+
+@settings(max_examples=30, deadline=None)
+@given(st.integers(1, 40), st.integers(0, 60), st.sampled_from([0.25, 1.0, 4.0]), st.integers(0, 999))
+def test_varlen_unit_tiles_match_key_by_key_statement(Lq, extra, tau, seed):
+    """Bq = Bk = 1: each chunk row is decided alone, key by key from its newest
+    visible key (Lk - Lq + i) down to key 0, with L = that row's key count."""
+    Lk = Lq + extra
+    inp = G.varlen_inputs(320 + seed, [Lq], [Lk], 1, 1, 8, 0.2)
+    q, k, v = _f64(inp)
+    f = oracle_fwd_varlen(q, k, v, inp["cu_q"], inp["cu_k"], tau, 1, 1)
+    S = (q[:, 0, :] @ k[:, 0, :].T) / np.sqrt(8)
+    for i in range(Lq):
+        jl = Lk - Lq + i
+        s = S[i, : jl + 1]
+        kept, Z, _ = R.per_key_row(np.exp(s - s.max()), tau)
+        got = np.nonzero(f["keep"][0, 0, i, : jl + 1] == 1)[0].tolist()
+        assert sorted(kept) == got
+        assert (f["keep"][0, 0, i, jl + 1:] == 255).all()
+        assert abs(f["lse"][0, i] - (np.log(Z) + s.max())) <= 1e-12 * max(1, abs(s.max()))
+
+
+@pytest.mark.parametrize("tau", [0.25, 1.0, 4.0])
+@pytest.mark.parametrize("tiles,start", [((64, 64), 128), ((128, 64), 256), ((32, 16), 96)])
+def test_chunk_at_block_boundary_reproduces_full_forward(tau, tiles, start):
+    """A chunk whose first query sits at a multiple of Bq meets the same blocks,
+    tiles and L_i as the full forward over the whole sequence, so its rows
+    equal the full forward's rows from that position on."""
+    L = 420
+    Bq, Bk = tiles
+    full = G.attn_inputs(330, 1, L, 4, 2, 16, 0.2, diffuse_kv_heads=(1,))
+    fq, fk, fv = [G.bf16_bits_to_f64(full[x]) for x in ("q", "k", "v")]
+    fr = oracle_fwd(fq, fk, fv, tau, Bq, Bk)
+    cu_q = np.array([0, L - start], np.int32)
+    cu_k = np.array([0, L], np.int32)
+    cr = oracle_fwd_varlen(fq[0, start:], fk[0], fv[0], cu_q, cu_k, tau, Bq, Bk)
+    assert np.array_equal(cr["o"], fr["o"][0, start:])
+    assert np.array_equal(cr["lse"], fr["lse"][0][:, start:])
+    nqb = cr["keep"].shape[2]
+    assert np.array_equal(cr["keep"][0], fr["keep"][0][:, start // Bq:start // Bq + nqb])
+    assert np.array_equal(cr["kept_slots"], fr["kept_slots"][0][:, start:])
+    # and the generator draws the chunk as the tail of the same sequence
+    ch = G.varlen_inputs(330, [L - start], [L], 4, 2, 16, 0.2, diffuse_kv_heads=(1,))
+    assert np.array_equal(ch["q"], full["q"][0, start:]) and np.array_equal(ch["k"], full["k"][0])
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.25, 1.0, 4.0])
+def test_single_query_chunks_match_decode(tau):
+    """Lq = 1 over an N-key cache with one q head per KV head (G = 1) is the
+    decode rule: the same tiles newest first, L_i = N."""
+    N, B, H, d = 700, 3, 2, 32
+    di = G.decode_inputs(340, B, N, H, H, d)
+    q, kc, vc = [G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")]
+    r = oracle_decode(q, kc, vc, tau, 64)
+    cu_q = np.arange(B + 1, dtype=np.int32)
+    cu_k = (np.arange(B + 1) * N).astype(np.int32)
+    f = oracle_fwd_varlen(q, kc.reshape(B * N, H, d), vc.reshape(B * N, H, d), cu_q, cu_k, tau, 16, 64)
+    assert np.array_equal(f["keep"][:, :, 0, :], r["keep"])
+    assert np.abs(f["o"] - r["o"]).max() <= 1e-13 * np.abs(r["o"]).max()
+    assert np.abs(f["lse"].T - r["lse"]).max() <= 1e-13 * np.abs(r["lse"]).max()
+    assert np.abs(f["omitted"].T - r["omitted"]).max() <= 1e-12
+
+
+@pytest.mark.parametrize("tau", [0.25, 1.0, 4.0])
+def test_varlen_prop1_bound_and_first_tile(tau):
+    """Omitted mass < tau / (1 + tau) per row, and each block keeps the tile of
+    its rows' newest keys."""
+    lq, lk = [300, 64, 1, 129], [300, 400, 999, 700]
+    inp = G.varlen_inputs(350, lq, lk, 4, 2, 32, 0.3)
+    q, k, v = _f64(inp)
+    Bq, Bk = 64, 64
+    f = oracle_fwd_varlen(q, k, v, inp["cu_q"], inp["cu_k"], tau, Bq, Bk)
+    assert (f["omitted"] < tau / (1 + tau)).all()
+    for b in range(len(lq)):
+        for i in range(lq[b]):
+            assert (f["keep"][b, :, i // Bq, (lk[b] - lq[b] + i) // Bk] == 1).all()
+    # unvisited blocks of short sequences stay unvisited
+    assert (f["keep"][2, :, 1:] == 255).all()
