@@ -6,7 +6,7 @@ PyTorch supplies device memory and the current HIP stream.  There is no CPU
 fallback: if the library is missing or the tensors are not on a HIP device,
 the calls raise.
 
-Names follow the C ABI: mala_fwd, mala_bwd, mala_decode, plus the autograd
+Names follow the C ABI: mala_fwd, mala_fwd_varlen, mala_bwd, mala_decode, plus the autograd
 wrapper `mala_attention` (saves only q, k, v, o and lse for the backward).
 """
 from __future__ import annotations
@@ -32,13 +32,18 @@ class MalaT4(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sl", ctypes.c_int64), ("sh", ctypes.c_int64)]
 
 
+class MalaT3(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("sl", ctypes.c_int64), ("sh", ctypes.c_int64)]
+
+
 class MalaTileStats(ctypes.Structure):
     _fields_ = [("kept_tiles", ctypes.c_void_p), ("kept_slots", ctypes.c_void_p),
                 ("omitted_mass", ctypes.c_void_p), ("decision_bits", ctypes.c_void_p)]
 
 
-EXPORTS = ("mala_fwd", "mala_fwd_workspace_size", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
-           "mala_decode_workspace_size", "mala_status_string", "mala_version")
+EXPORTS = ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
+           "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
+           "mala_status_string", "mala_version")
 
 _lib = None
 
@@ -59,6 +64,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mala_fwd.argtypes = [MalaT4, MalaT4, MalaT4, I, I, I, I, I, F, I, I, MalaT4, P,
                              ctypes.POINTER(MalaTileStats), P, S, P]
     lib.mala_fwd.restype = I
+    lib.mala_fwd_varlen_workspace_size.argtypes = [I, I, I, I, I, I]
+    lib.mala_fwd_varlen_workspace_size.restype = S
+    lib.mala_fwd_varlen.argtypes = [MalaT3, MalaT3, MalaT3, P, P, I, I, I, I, I, I, I, I, F, I, I, MalaT3, P,
+                                    ctypes.POINTER(MalaTileStats), P, S, P]
+    lib.mala_fwd_varlen.restype = I
     lib.mala_bwd_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.mala_bwd_workspace_size.restype = S
     lib.mala_bwd.argtypes = [MalaT4, MalaT4, MalaT4, MalaT4, MalaT4, P, I, I, I, I, I, F, I, I,
@@ -89,6 +99,16 @@ def _t4(t: torch.Tensor) -> MalaT4:
     if t.stride(3) != 1:
         raise ValueError("the d dimension must be contiguous")
     return MalaT4(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _t3(t: torch.Tensor) -> MalaT3:
+    if t.dim() != 3:
+        raise ValueError("expected a packed [total, H, d] tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError("libmala takes bfloat16 tensors")
+    if t.stride(2) != 1:
+        raise ValueError("the d dimension must be contiguous")
+    return MalaT3(t.data_ptr(), t.stride(0), t.stride(1))
 
 
 def _dev_check(*ts):
@@ -151,6 +171,58 @@ def mala_fwd(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64, o=None, lse
     rc = lib.mala_fwd(_t4(q), _t4(k), _t4(v), B, L, Hq, Hkv, d, float(tau), Bq, Bk, _t4(o),
                       _ptr(lse), _stats_struct(stats), _ptr(ws), ws.numel(), _stream(q))
     _check("mala_fwd", rc)
+    return o, lse
+
+
+def make_varlen_stats(B: int, Hq: int, total_q: int, max_q: int, max_k: int, Bq: int, Bk: int, device,
+                      omitted: bool = False) -> dict:
+    """Allocate the optional statistics outputs of mala_fwd_varlen."""
+    nQB, nKT = max(1, -(-max_q // Bq)), max(1, -(-max_k // Bk))
+    st = {"kept_tiles": torch.empty((B, Hq, nQB), dtype=torch.int32, device=device),
+          "kept_slots": torch.empty((Hq, total_q), dtype=torch.int32, device=device),
+          "decision_bits": torch.empty((B, Hq, nQB, -(-nKT // 32)), dtype=torch.int32, device=device)}
+    if omitted:
+        st["omitted_mass"] = torch.empty((Hq, total_q), dtype=torch.float32, device=device)
+    return st
+
+
+def fwd_varlen_workspace(B, total_k, Hkv, d, Bq=128, Bk=64, device="cuda"):
+    n = load_library().mala_fwd_varlen_workspace_size(B, total_k, Hkv, d, Bq, Bk)
+    if n == 0:
+        raise MalaError("mala_fwd_varlen_workspace_size", MALA_ERR_UNSUPPORTED, "unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mala_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, tau: float = 1.0,
+                    Bq: int = 128, Bk: int = 64, o=None, lse=None, stats: dict | None = None, ws=None):
+    """Forward over packed variable-length sequences whose queries are the last
+    Lq of their Lk keys (prefill, chunked prefill onto a cache, mixed batches).
+    q [total_q,Hq,d], k/v [total_k,Hkv,d] bf16; cu_seqlens_* int32 [B+1] on the
+    same device.  Returns (o [total_q,Hq,d] bf16, lse [Hq,total_q] fp32)."""
+    _dev_check(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if k.shape != (Tk, Hkv, d) or v.shape != k.shape:
+        raise ValueError("q, k, v shapes disagree")
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or not c.is_contiguous() or c.dim() != 1:
+            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] tensors")
+    B = cu_seqlens_q.numel() - 1
+    if B < 1 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 entries")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    if ws is None:
+        ws = fwd_varlen_workspace(B, Tk, Hkv, d, Bq, Bk, q.device)
+    lib = load_library()
+    rc = lib.mala_fwd_varlen(_t3(q), _t3(k), _t3(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Tq, Tk,
+                             int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d, float(tau), Bq, Bk, _t3(o),
+                             _ptr(lse), _stats_struct(stats), _ptr(ws), ws.numel(), _stream(q))
+    _check("mala_fwd_varlen", rc)
     return o, lse
 
 

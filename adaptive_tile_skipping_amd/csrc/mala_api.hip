@@ -127,6 +127,61 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
 }
 
+size_t mala_fwd_varlen_workspace_size(int B, int total_k, int Hkv, int d, int Bq, int Bk) {
+    if (B <= 0 || total_k < 0 || Hkv <= 0 || !fwd_shape_supported(d, Bq, Bk)) return 0;
+    return align256(((size_t)total_k + (size_t)B * Bk) * Hkv * d * 2);
+}
+
+mala_status mala_fwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int B, int total_q, int total_k, int max_seqlen_q,
+                            int max_seqlen_k, int Hq, int Hkv, int d, float tau, int Bq, int Bk, mala_t3 o,
+                            float* lse, const mala_tile_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+    if (B <= 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return MALA_ERR_INVALID_ARG;
+    if (Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
+    if (max_seqlen_q > max_seqlen_k || max_seqlen_q > total_q || max_seqlen_k > total_k) return MALA_ERR_INVALID_ARG;
+    if (!cu_seqlens_q || !cu_seqlens_k || !lse) return MALA_ERR_INVALID_ARG;
+    if (!t4_ok({q.ptr, 0, q.sl, q.sh}, true) || !t4_ok({k.ptr, 0, k.sl, k.sh}, true) ||
+        !t4_ok({v.ptr, 0, v.sl, v.sh}, true) || !t4_ok({o.ptr, 0, o.sl, o.sh}, true))
+        return MALA_ERR_INVALID_ARG;
+    if ((int64_t)total_q * Hq > INT32_MAX / 2 || (int64_t)total_k + (int64_t)B * Bk > INT32_MAX / 2)
+        return MALA_ERR_INVALID_ARG;
+    if (!fwd_shape_supported(d, Bq, Bk) || B > 65535) return MALA_ERR_UNSUPPORTED;
+    // one sequence's keys of a KV head and its fp16 V copy are addressed through 32-bit buffer ranges
+    const int64_t mk = max_seqlen_k > 0 ? max_seqlen_k : 1;
+    if (((mk - 1) * k.sl + d) * 2 > INT32_MAX || (mk + Bk) * d * 2 > INT32_MAX) return MALA_ERR_UNSUPPORTED;
+    const size_t need = mala_fwd_varlen_workspace_size(B, total_k, Hkv, d, Bq, Bk);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
+    if (total_q == 0) return MALA_OK;      // no query rows: nothing to compute or write
+    FwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = (const uint16_t*)q.ptr; p.k = (const uint16_t*)k.ptr; p.v = (const uint16_t*)v.ptr;
+    p.o = (uint16_t*)o.ptr; p.lse = lse;
+    p.q_sl = q.sl; p.q_sh = q.sh; p.k_sl = k.sl; p.k_sh = k.sh;
+    p.v_sl = v.sl; p.v_sh = v.sh; p.o_sl = o.sl; p.o_sh = o.sh;
+    p.B = B; p.L = 0; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+    p.total_q = total_q; p.total_k = total_k; p.max_q = max_seqlen_q; p.max_k = max_seqlen_k;
+    p.nQB = max_seqlen_q > 0 ? (max_seqlen_q + Bq - 1) / Bq : 1;
+    p.nKT = max_seqlen_k > 0 ? (max_seqlen_k + Bk - 1) / Bk : 1;
+    p.nunits = B * Hq * p.nQB;
+    p.chunk = pick_chunk(Hq, Hkv);
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    p.log2_tau = log2_tau(tau);
+    p.nwords = (p.nKT + 31) / 32;
+    p.vh = (uint16_t*)ws;
+    p.Rk = total_k + B * Bk;
+    bool st = false;
+    if (stats) {
+        p.kept_tiles = stats->kept_tiles;
+        p.kept_slots = stats->kept_slots;
+        p.omitted = stats->omitted_mass;
+        p.bits = stats->decision_bits;
+        st = stats->omitted_mass != nullptr;
+    }
+    hipError_t e = launch_fwd(p, d, Bq, Bk, st, (hipStream_t)stream);
+    return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
+}
+
 size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk) {
     if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
     const size_t Lpad = (size_t)((L + Bq - 1) / Bq) * Bq;

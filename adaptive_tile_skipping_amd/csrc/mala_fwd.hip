@@ -61,6 +61,48 @@ __global__ __launch_bounds__(256) void mala_v_to_f16(const FwdParams p) {
         *(u32x4*)(p.vh + row * D + 8 * c) = o;
     }
 }
+
+// Sequence b of a packed batch: row offsets and counts, or false when its
+// cumulative lengths are inconsistent with the call's totals and maxima
+// (such a sequence is left untouched).
+struct SeqSpan {
+    int q0, k0, Lq, Lk;
+};
+__device__ __forceinline__ bool seq_span(const FwdParams& p, int b, SeqSpan& s) {
+    s.q0 = p.cu_q[b];
+    s.k0 = p.cu_k[b];
+    const int q1 = p.cu_q[b + 1], k1 = p.cu_k[b + 1];
+    s.Lq = q1 - s.q0;
+    s.Lk = k1 - s.k0;
+    return s.q0 >= 0 && s.k0 >= 0 && q1 <= p.total_q && k1 <= p.total_k && s.Lq >= 0 && s.Lk >= s.Lq &&
+           s.Lq <= p.max_q && s.Lk <= p.max_k;
+}
+
+// V copy of a packed batch: bf16 [total_k, Hkv, D] -> fp16 [Hkv, Rk, D]; the
+// keys of sequence b start at row cu_k[b] + b * BK and are followed by zero
+// rows up to the next sequence (at least BK of them).  grid.y = sequence.
+template <int D, int BK>
+__global__ __launch_bounds__(256) void mala_v_to_f16_varlen(const FwdParams p) {
+    constexpr int CH = D / 8;
+    const int b = blockIdx.y;
+    SeqSpan sp;
+    if (!seq_span(p, b, sp)) return;
+    const int rows = sp.Lk + BK;
+    const int64_t n = (int64_t)p.Hkv * rows * CH;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
+        const int c = (int)(idx % CH);
+        const int64_t rr = idx / CH;
+        const int j = (int)(rr % rows);
+        const int kh = (int)(rr / rows);
+        u32x4 o = {0, 0, 0, 0};
+        if (j < sp.Lk) {
+            const u32x4 x = *(const u32x4*)(p.v + (int64_t)(sp.k0 + j) * p.v_sl + kh * p.v_sh + 8 * c);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) o[m] = pack2_f16_from_f32bits(x[m] << 16, x[m] & 0xFFFF0000u);
+        }
+        *(u32x4*)(p.vh + ((int64_t)kh * p.Rk + sp.k0 + (int64_t)b * BK + j) * D + 8 * c) = o;
+    }
+}
 }  // namespace
 
 template <int D, int BQ, int BK, bool STATS>
@@ -95,22 +137,55 @@ void mala_fwd_kernel(const FwdParams p) {
     const int b = bh / p.Hq;
     const int h = bh % p.Hq;
     const int kh = h / p.G;
-    const int L = p.L;
 
+    // The block's sequence: Lq queries that are the last Lq of its Lk keys
+    // (Lq = Lk = L for the fixed-length layout), so query row i sees keys
+    // j <= off + i and has L_i = off + i + 1 visible keys.
+    int Lq, Lk;
+    const uint16_t *qbase, *kbase, *vhbase;
+    uint16_t* obase;
+    int64_t rowbase;                             // lse / kept_slots / omitted index of row 0
+    int64_t vh_rows;                             // rows of this KV head's fp16 V range
+    if (p.cu_q) {
+        SeqSpan sp;
+        const bool ok = seq_span(p, b, sp);
+        Lq = ok ? sp.Lq : 0;
+        Lk = sp.Lk;
+        qbase = p.q + (int64_t)sp.q0 * p.q_sl + h * p.q_sh;
+        obase = p.o + (int64_t)sp.q0 * p.o_sl + h * p.o_sh;
+        kbase = p.k + (int64_t)sp.k0 * p.k_sl + kh * p.k_sh;
+        vhbase = p.vh + ((int64_t)kh * p.Rk + sp.k0 + (int64_t)b * BK) * D;
+        vh_rows = (int64_t)Lk + BK;
+        rowbase = (int64_t)h * p.total_q + sp.q0;
+    } else {
+        Lq = Lk = p.L;
+        qbase = p.q + b * p.q_sb + h * p.q_sh;
+        obase = p.o + b * p.o_sb + h * p.o_sh;
+        kbase = p.k + b * p.k_sb + kh * p.k_sh;
+        vhbase = p.vh + ((int64_t)b * p.Hkv + kh) * p.Lpad * D;
+        vh_rows = p.Lpad;
+        rowbase = (int64_t)bh * p.L;
+    }
+    const int off = Lk - Lq;
     const int i0 = qb * BQ;
+    if (i0 >= Lq) {
+        // past the sequence's queries: nothing to visit (statistics read as such)
+        if (tid == 0 && p.kept_tiles) p.kept_tiles[(int64_t)bh * p.nQB + qb] = 0;
+        if (tid == 0 && p.bits)
+            for (int wd = 0; wd < p.nwords; ++wd) p.bits[((int64_t)bh * p.nQB + qb) * p.nwords + wd] = 0u;
+        return;
+    }
     const int i = i0 + 32 * w + l32;             // this lane's query row
-    const bool valid = i < L;
-    const int rend = (i0 + BQ < L) ? i0 + BQ : L;
-    const int kt_first = (rend - 1) / BK;
-    const bool ragged = (i0 + BQ > L);
-
-    const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh;
-    const uint16_t* vhbase = p.vh + ((int64_t)b * p.Hkv + kh) * p.Lpad * D;
+    const bool valid = i < Lq;
+    const int ik = off + i;                      // its last visible key
+    const int rend = (i0 + BQ < Lq) ? i0 + BQ : Lq;
+    const int kt_first = (off + rend - 1) / BK;
+    const bool ragged = (i0 + BQ > Lq);
 
     // ---- Q fragments (B operand: column = query, 8 consecutive d per lane)
     bf16x8 qf[KSTEPS];
     {
-        const uint16_t* qrow = p.q + b * p.q_sb + (int64_t)(valid ? i : 0) * p.q_sl + h * p.q_sh;
+        const uint16_t* qrow = qbase + (int64_t)(valid ? i : 0) * p.q_sl;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
             u32x4 x = valid ? *(const u32x4*)(qrow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
@@ -131,11 +206,11 @@ void mala_fwd_kernel(const FwdParams p) {
         koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
         voff[n] = (uint32_t)((r * D + 8 * (pc ^ ((4 * (r & 3)) % QCH))) * 2);
     }
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhbase, (uint32_t)((int64_t)p.Lpad * D * 2));
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhbase, (uint32_t)(vh_rows * D * 2));
     auto copy_k = [&](int kt, int buf) {
         const int j0 = kt * BK;
         const __amdgpu_buffer_rsrc_t krs =
-            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(L - 1 - j0) * p.k_sl + D) * 2));
+            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(Lk - 1 - j0) * p.k_sl + D) * 2));
 #pragma unroll
         for (int n = 0; n < INST; ++n)
             buffer16_to_lds(krs, koff[n], reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
@@ -163,9 +238,9 @@ void mala_fwd_kernel(const FwdParams p) {
     // causal mask (diagonal / ragged tiles) and raw row max
     auto mask_max = [&](int kt, f32x16* s) -> float {
         float M = kNegInf;
-        const bool need = ragged || (kt * BK + BK - 1 > i0);
+        const bool need = ragged || (kt * BK + BK - 1 > off + i0);
         if (need) {
-            const int lim = valid ? (i - kt * BK) : -1;
+            const int lim = valid ? (ik - kt * BK) : -1;
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -209,7 +284,7 @@ void mala_fwd_kernel(const FwdParams p) {
     float m2 = kNegInf;          // running max of retained base-2 scores
     float lsum = 0.f;            // retained sum, shifted by m2
     float thr = kNegInf;         // cached keep threshold m2 + log2(lsum) + theta
-    const float theta = p.log2_tau - fast_log2((float)(i + 1));
+    const float theta = p.log2_tau - fast_log2((float)(ik + 1));
     float om = kNegInf, ol = 0.f;            // omitted mass (statistics mode)
     int slots = 0;
     f32x16 acc[DT];
@@ -350,7 +425,7 @@ void mala_fwd_kernel(const FwdParams p) {
             pend_buf = buf;
             pending = true;
             if (valid) {
-                const int lim = i - kt * BK;
+                const int lim = ik - kt * BK;
                 if (lim >= 0) slots += (lim < BK - 1 ? lim : BK - 1) + 1;
             }
             ++kept_count;
@@ -392,7 +467,7 @@ void mala_fwd_kernel(const FwdParams p) {
     // ---- epilogue: O = acc / l, LSE = (m2 + log2 l) ln 2
     if (valid) {
         const float inv = 1.f / lsum;
-        uint16_t* orow = p.o + b * p.o_sb + (int64_t)i * p.o_sl + h * p.o_sh;
+        uint16_t* orow = obase + (int64_t)i * p.o_sl;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -405,7 +480,7 @@ void mala_fwd_kernel(const FwdParams p) {
             }
         }
         if (hi == 0) {
-            const int64_t ri = (int64_t)bh * L + i;
+            const int64_t ri = rowbase + i;
             const float lz2 = m2 + fast_log2(lsum);
             p.lse[ri] = lz2 * kLn2;
             if (p.kept_slots) p.kept_slots[ri] = slots;
@@ -422,7 +497,12 @@ void mala_fwd_kernel(const FwdParams p) {
 template <int D, int BQ, int BK>
 static hipError_t launch_fwd_t(const FwdParams& p, bool stats, hipStream_t s) {
     constexpr int NT = BQ / 32 * 64;
-    {
+    if (p.cu_q) {
+        const int64_t n = (int64_t)p.Hkv * (p.max_k + BK) * (D / 8);
+        int g = (int)((n + 255) / 256);
+        if (g > 4096) g = 4096;
+        hipLaunchKernelGGL((mala_v_to_f16_varlen<D, BK>), dim3(g, p.B), dim3(256), 0, s, p);
+    } else {
         const int64_t n = (int64_t)p.B * p.Hkv * p.Lpad * (D / 8);
         int g = (int)((n + 255) / 256);
         if (g > 16384) g = 16384;

@@ -20,8 +20,15 @@ struct FwdParams {
     float* omitted;
     uint32_t* bits;
     int nwords;
-    uint16_t* vh;       // [B, Hkv, Lpad, d] fp16 copy of V (workspace)
+    uint16_t* vh;       // fp16 copy of V (workspace): [B, Hkv, Lpad, d], or [Hkv, Rk, d] packed
     int Lpad;           // nKT * Bk
+    // packed variable-length batches (cu_q == nullptr: the fixed-length layout
+    // above, with q/k/v/o strides sb, sl, sh and lse [B, Hq, L])
+    const int32_t* cu_q;   // [B + 1] device: first query row of each sequence
+    const int32_t* cu_k;   // [B + 1] device: first key row of each sequence
+    int total_q, total_k;  // packed rows; lse / kept_slots / omitted are [Hq, total_q]
+    int max_q, max_k;      // longest query and key counts (nQB, nKT derive from them)
+    int Rk;                // total_k + B * Bk: V copy rows per KV head (sequence b at cu_k[b] + b Bk)
 };
 
 struct BwdParams {

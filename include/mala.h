@@ -69,6 +69,13 @@ typedef struct {
     int64_t sb, sl, sh;
 } mala_t4;
 
+/* A packed bf16 tensor [total, H, d] of variable-length sequences (rows of
+ * all sequences back to back); element strides; d stride is 1. */
+typedef struct {
+    void* ptr;
+    int64_t sl, sh;
+} mala_t3;
+
 /* Optional per-call tile statistics (every pointer may be NULL).
  *   kept_tiles    [B, Hq, nQB] int32: retained key tiles per query block.
  *   kept_slots    [B, Hq, L]   int32: legal (causal) keys inside retained
@@ -102,6 +109,44 @@ size_t mala_fwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int
 mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int Hkv, int d,
                      float tau, int Bq, int Bk, mala_t4 o, float* lse,
                      const mala_tile_stats* stats, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace mala_fwd_varlen needs (an fp16 copy of V with
+ * Bk zero rows after each sequence). */
+size_t mala_fwd_varlen_workspace_size(int B, int total_k, int Hkv, int d, int Bq, int Bk);
+
+/* Forward over a packed batch of B variable-length sequences, each a chunk of
+ * Lq queries over Lk >= Lq keys: prompt prefill (Lq = Lk), chunked prefill
+ * onto an existing cache (Lq < Lk) and mixed batches of both.  The queries
+ * are the last Lq positions of the sequence (bottom-right causal alignment):
+ * query row i of the chunk sees keys j <= Lk - Lq + i, so L_i = Lk - Lq + i + 1
+ * in the decision rule.  Key tiles are aligned to key 0 and query blocks to
+ * the chunk's first row, so a chunk that starts at a multiple of Bq gives the
+ * rows mala_fwd gives for the whole sequence.  (Summary page: prefill is a
+ * mode under the same tau; review page "One tolerance governs everything":
+ * the threshold tau / L_i uses the row's visible-key count.)
+ *   q [total_q, Hq, d], k, v [total_k, Hkv, d] bf16 (mala_t3), in device memory.
+ *   cu_seqlens_q, cu_seqlens_k: int32 [B + 1] in DEVICE memory, cumulative
+ *   lengths (cu[0] = 0, cu[B] = total): sequence b owns query rows
+ *   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ *   cu_seqlens_k[b+1]-1.  They are read by the kernels, not on the host: a
+ *   sequence whose lengths break 0 <= Lq <= Lk, Lq <= max_seqlen_q,
+ *   Lk <= max_seqlen_k, or whose rows leave [0, total) is skipped and its
+ *   outputs are left unwritten (no out-of-range access is made).
+ *   o [total_q, Hq, d] bf16 output; lse [Hq, total_q] fp32 output (contiguous).
+ *   stats: NULL or statistics as for mala_fwd, with nQB = ceil(max_seqlen_q /
+ *   Bq) and nKT = ceil(max_seqlen_k / Bk) (kept_tiles and decision_bits indexed
+ *   [B, Hq, nQB, ...], 0 for blocks past a sequence's queries; kept_slots and
+ *   omitted_mass [Hq, total_q]).
+ *   ws: device workspace of at least mala_fwd_varlen_workspace_size(...)
+ *   bytes, 256-byte aligned; overwritten by the call.
+ * INVALID_ARG for bad sizes (max_seqlen_q > max_seqlen_k, a maximum above its
+ * total, negative counts) besides the shared conditions; UNSUPPORTED when
+ * B > 65535 or when ((max_seqlen_k - 1) * k's L stride + d) * 2 or
+ * (max_seqlen_k + Bk) * d * 2 exceeds INT32_MAX.  total_q = 0 returns MALA_OK and enqueues nothing. */
+mala_status mala_fwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int B, int total_q, int total_k, int max_seqlen_q,
+                            int max_seqlen_k, int Hq, int Hkv, int d, float tau, int Bq, int Bk, mala_t3 o,
+                            float* lse, const mala_tile_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of device workspace mala_bwd needs (row terms and kept-tile bits). */
 size_t mala_bwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk);

@@ -211,7 +211,7 @@ WORKLOADS = {
     "prefill_128k": dict(tag=3, lens_q=(16384,), lens_k=(131072,), Hq=5, Hkv=1, d=128, p=0.02, diffuse=(),
                          Bq=128, Bk=64, taus=(1.0, 0.0)),
     # a ragged batch: fresh prompts (Lq = Lk), chunks onto caches, single tokens
-    "varlen_mix": dict(tag=5, lens_q=(1000, 333, 1, 4096, 0, 700), lens_k=(1000, 2900, 5000, 6000, 77, 700),
+    "varlen_mix": dict(tag=5, lens_q=(1000, 333, 1, 2048, 0, 700), lens_k=(1000, 2900, 5000, 5000, 77, 700),
                        Hq=8, Hkv=2, d=128, p=0.1, diffuse=(1,), Bq=128, Bk=64, taus=(0.0, 0.25, 1.0, 4.0)),
 }
 

@@ -19,8 +19,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("mala_fwd", "mala_fwd_workspace_size", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
-              "mala_decode_workspace_size", "mala_status_string", "mala_version"):
+    for n in ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
+              "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
+              "mala_status_string", "mala_version"):
         assert n in names
 
 
@@ -118,3 +119,52 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 128, 1, 128, dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="GPU only"):
         mala.mala_fwd(x, x, x, 1.0)
+
+
+def _t3(ptr=16 * 1024, sl=8 * 16, sh=128):
+    return mala.MalaT3(ptr, sl, sh)
+
+
+def _fwd_varlen(**kw):
+    a = dict(q=_t3(), k=_t3(), v=_t3(), cu_q=ctypes.c_void_p(4096), cu_k=ctypes.c_void_p(8192), B=2,
+             total_q=300, total_k=900, max_q=200, max_k=600, Hq=2, Hkv=1, d=128, tau=1.0, Bq=128, Bk=64,
+             o=_t3(), lse=ctypes.c_void_p(12288), stats=None)
+    a.update(kw)
+    lib = mala.load_library()
+    return lib.mala_fwd_varlen(a["q"], a["k"], a["v"], a["cu_q"], a["cu_k"], a["B"], a["total_q"], a["total_k"],
+                               a["max_q"], a["max_k"], a["Hq"], a["Hkv"], a["d"], a["tau"], a["Bq"], a["Bk"],
+                               a["o"], a["lse"], a["stats"], a.get("ws", ctypes.c_void_p(1 << 20)),
+                               a.get("ws_bytes", 1 << 30), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu_q=None), mala.MALA_ERR_INVALID_ARG),
+    (dict(cu_k=None), mala.MALA_ERR_INVALID_ARG),
+    (dict(lse=None), mala.MALA_ERR_INVALID_ARG),
+    (dict(q=mala.MalaT3(None, 0, 0)), mala.MALA_ERR_INVALID_ARG),
+    (dict(o=_t3(ptr=16 * 1024 + 4)), mala.MALA_ERR_INVALID_ARG),
+    (dict(k=_t3(sh=100)), mala.MALA_ERR_INVALID_ARG),
+    (dict(B=0), mala.MALA_ERR_INVALID_ARG),
+    (dict(max_q=700), mala.MALA_ERR_INVALID_ARG),          # longer than max_k
+    (dict(max_q=400, max_k=950), mala.MALA_ERR_INVALID_ARG),  # beyond the totals
+    (dict(total_q=-1), mala.MALA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), mala.MALA_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), mala.MALA_ERR_INVALID_ARG),
+    (dict(d=96), mala.MALA_ERR_UNSUPPORTED),
+    (dict(Bq=64), mala.MALA_ERR_UNSUPPORTED),
+    (dict(B=70000, total_q=70000, total_k=90000, max_q=100, max_k=600), mala.MALA_ERR_UNSUPPORTED),
+    (dict(ws=None), mala.MALA_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), mala.MALA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 16)), mala.MALA_ERR_WORKSPACE),
+    # no query rows: nothing to do, nothing enqueued
+    (dict(total_q=0, max_q=0), mala.MALA_OK),
+])
+def test_fwd_varlen_rejects_bad_arguments(kw, code):
+    assert _fwd_varlen(**kw) == code
+
+
+def test_fwd_varlen_workspace_size():
+    lib = mala.load_library()
+    # fp16 V copy with one tile of zero rows after each sequence
+    assert lib.mala_fwd_varlen_workspace_size(3, 1000, 2, 128, 128, 64) >= (1000 + 3 * 64) * 2 * 128 * 2
+    assert lib.mala_fwd_varlen_workspace_size(3, 1000, 2, 96, 128, 64) == 0
