@@ -13,7 +13,13 @@ the same run for the speedups, the dominant kernel's roofline is measured live
 with HIP events on the launch stream, and the fp64 oracle is timed on a
 bounded sample of the same workload on the host cores.
 
+`--workload prefill_128k` instead times the variable-length forward on a
+chunked prefill: the last 16384 queries of the 128K sequence against all of its
+131072 keys (the cache of the 114688 keys before them plus the chunk itself),
+and prints that measurement's own JSON line.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tau0]
+                       [--workload step|prefill_128k]
 """
 from __future__ import annotations
 
@@ -41,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison")
     ap.add_argument("--cpu-blocks", type=int, default=48, help="query blocks per head in the CPU sample")
+    ap.add_argument("--workload", choices=("step", "prefill_128k"), default="step",
+                    help="step: training forward+backward and decode (default); prefill_128k: chunked prefill")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run two forward launches and a plain 1 GiB device copy, then exit (for PMC passes)")
     return ap.parse_args()
@@ -91,6 +99,107 @@ def legal_pairs_block(L, Bq, qb):
     return sum(i + 1 for i in range(r0, r1))
 
 
+def main_prefill(args):
+    """Chunked prefill through mala_fwd_varlen (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import adaptive_tile_skipping_amd as mala
+    import mala_gen as G
+
+    dev = torch.device("cuda:0")
+    torch.cuda.init()
+    tau = args.tau
+    W = G.WORKLOADS["prefill_128k"]
+    Hq, Hkv, d, Bq, Bk = W["Hq"], W["Hkv"], W["d"], W["Bq"], W["Bk"]
+    t_gen = time.time()
+    inp = G.workload_inputs("prefill_128k")
+    cu_q, cu_k = inp["cu_q"], inp["cu_k"]
+    Lq, Lk = int(cu_q[-1]), int(cu_k[-1])
+    off = Lk - Lq
+
+    def tens(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = (tens(inp[x]) for x in ("q", "k", "v"))
+    cq, ck = torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev)
+    t_gen = time.time() - t_gen
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, Lq), dtype=torch.float32, device=dev)
+    ws = mala.fwd_varlen_workspace(1, Lk, Hkv, d, Bq, Bk, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(t):
+        mala.mala_fwd_varlen(q, k, v, cq, ck, Lq, Lk, t, Bq, Bk, o=o, lse=lse, ws=ws)
+
+    def timed(t, steps, warmup):
+        for _ in range(warmup):
+            run(t)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in ev:
+            e0.record(stream); run(t); e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        return wall, float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    wall, ms = timed(tau, max(args.steps, 5), args.warmup)
+    print(f"# prefill tau={tau}: {ms:.3f} ms per call (wall {wall:.3f})", file=sys.stderr, flush=True)
+    ms0 = None
+    if not args.no_tau0:
+        _, ms0 = timed(0.0, max(3, min(args.steps, 5)), 1)
+        print(f"# prefill tau=0: {ms0:.3f} ms", file=sys.stderr, flush=True)
+
+    st = mala.make_varlen_stats(1, Hq, Lq, Lq, Lk, Bq, Bk, dev)
+    mala.mala_fwd_varlen(q, k, v, cq, ck, Lq, Lk, tau, Bq, Bk, o=o, lse=lse, stats=st, ws=ws)
+    torch.cuda.synchronize()
+    nQB = -(-Lq // Bq)
+    n_visit = Hq * sum((off + min(Lq, qb * Bq + Bq) - 1) // Bk + 1 for qb in range(nQB))
+    kf = int(st["kept_tiles"].sum().item())
+    slots = float(st["kept_slots"].double().sum().item())
+    pairs = Hq * (Lq * off + Lq * (Lq + 1) // 2)
+    alg = 2.0 * d * pairs + 2.0 * d * slots
+    achieved = alg / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "MALA chunked prefill (16K queries onto a 128K-key sequence, 1 GPU share): effective TFLOP/s",
+        "value": round(4.0 * d * pairs / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": max(args.steps, 5), "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"prefill_128k (B=1 Lq={Lq} Lk={Lk} Hq={Hq} Hkv={Hkv} d={d} Bq={Bq} Bk={Bk})",
+                   "tau": tau},
+        "wall_ms_per_call": round(wall, 4),
+        "kept_tile_frac": round(kf / n_visit, 4),
+        "slots_per_query": round(slots / (Hq * Lq), 1),
+        "roofline": {"kernel": "mala_fwd_kernel (varlen launch, with its V copy)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_tflop_per_launch": round(alg / 1e12, 3), "launch_ms": round(ms, 4)},
+        "gen_s": round(t_gen, 1),
+    }
+    if ms0 is not None:
+        out["tau0_ms"] = round(ms0, 4)
+        out["speedup_vs_tau0"] = round(ms0 / ms, 3)
+    if not args.no_cpu:
+        from oracle import oracle_fwd_varlen, oracle_threads
+        f64 = {x: G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v")}
+        nb = max(1, args.cpu_blocks // 2)
+        qbs = [int((j + 0.5) * nQB / nb) for j in range(nb)]
+        blocks = [h * nQB + qb for h in range(Hq) for qb in qbs]
+        pairs_s = Hq * sum(sum(off + i + 1 for i in range(qb * Bq, min(Lq, qb * Bq + Bq))) for qb in qbs)
+        t0 = time.perf_counter()
+        oracle_fwd_varlen(f64["q"], f64["k"], f64["v"], cu_q, cu_k, tau, Bq, Bk, blocks=blocks)
+        tcpu = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(4.0 * d * pairs_s / tcpu / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle varlen forward on {len(blocks)} query blocks of prefill_128k ({nb} evenly "
+                      f"spaced blocks x {Hq} heads, tau={tau}); credited 4d FLOPs per legal pair; {tcpu:.1f} s",
+            "seconds": round(tcpu, 2)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -98,6 +207,9 @@ def main():
               "(the attention operator shards by heads with no communication; run one process per GPU).",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "prefill_128k":
+        main_prefill(args)
+        return
 
     import numpy as np
     import torch
