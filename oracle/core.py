@@ -48,7 +48,7 @@ def _load():
                                     P, i32, P, i32, P, P, P, P, P, i32]
     lib.mala_oracle_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, i32,
                                            P, P, P, P, P, P, i32]
-    lib.mala_oracle_decode.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32,
+    lib.mala_oracle_decode.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, P,
                                        P, P, P, P, P, P, i32]
     for f in (lib.mala_oracle_fwd, lib.mala_oracle_fwd_varlen, lib.mala_oracle_bwd, lib.mala_oracle_decode):
         f.restype = ctypes.c_int
@@ -161,9 +161,13 @@ def oracle_bwd(q, k, v, o, dout, lse, tau: float, Bq: int, Bk: int,
     return {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
 
 
-def oracle_decode(q, kc, vc, tau: float, Bkd: int, nthreads: int = 0):
-    """Decode rule.  Returns dict(o, lse, keep, margin, kept_tiles, omitted)."""
+def oracle_decode(q, kc, vc, tau: float, Bkd: int, seqlens=None, nthreads: int = 0):
+    """Decode rule.  Returns dict(o, lse, keep, margin, kept_tiles, omitted).
+
+    `seqlens`: optional [B] cache lengths (1 <= N_b <= N); sequence b then
+    sees only its first N_b cache rows (tiles past them stay 255 / NaN)."""
     q, kc, vc = _f64(q), _f64(kc), _f64(vc)
+    sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
     B, Hq, d = q.shape
     N, Hkv = kc.shape[1], kc.shape[2]
     nT = -(-N // Bkd)
@@ -173,7 +177,7 @@ def oracle_decode(q, kc, vc, tau: float, Bkd: int, nthreads: int = 0):
     margin = np.full((B, Hkv, nT), np.nan)
     kept = np.full((B, Hkv), -1, np.int32)
     omitted = np.full((B, Hq), np.nan)
-    rc = _load().mala_oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), B, N, Hq, Hkv, d, float(tau), Bkd,
+    rc = _load().mala_oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), B, N, Hq, Hkv, d, float(tau), Bkd, _ptr(sl),
                                     _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(kept), _ptr(omitted),
                                     int(nthreads))
     if rc:

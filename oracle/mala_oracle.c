@@ -522,23 +522,32 @@ int mala_oracle_bwd(const double* q, const double* k, const double* v, const dou
 /* Rows of a decision are the G q heads sharing a KV head; L_i = N.          */
 /* q, o: [B][Hq][d]; kc, vc: [B][N][Hkv][d]; lse, omitted: [B][Hq];          */
 /* keep, margin: [B][Hkv][nT] with nT = ceil(N/Bkd); kept_tiles: [B][Hkv].   */
+/* seqlens: NULL, or [B] cache lengths 1 <= N_b <= N: sequence b then uses   */
+/* its first N_b cache rows, with L_i = N_b and tiles 0 .. ceil(N_b/Bkd)-1   */
+/* (entries of later tiles are not written).                                 */
 /* ------------------------------------------------------------------------ */
 int mala_oracle_decode(const double* q, const double* kc, const double* vc,
                        int B, int N, int Hq, int Hkv, int d, double tau, int Bkd,
+                       const int32_t* seqlens,
                        double* o, double* lse, uint8_t* keep, double* margin,
                        int32_t* kept_tiles, double* omitted, int nthreads) {
     if (!q || !kc || !vc || !o || !lse) return OR_EINVAL;
     if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bkd <= 0) return OR_EINVAL;
     if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
+    if (seqlens)
+        for (int b = 0; b < B; ++b)
+            if (seqlens[b] < 1 || seqlens[b] > N) return OR_EINVAL;
     const int G = Hq / Hkv;
-    const int nT = (N + Bkd - 1) / Bkd;
+    const int nTmax = (N + Bkd - 1) / Bkd;     /* stride of keep / margin */
     const double scale = 1.0 / sqrt((double)d);
-    const double th = log_threshold(tau, (double)N);
     int err = OR_OK;
     set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
     for (long u = 0; u < (long)B * Hkv; ++u) {
         const int b = (int)(u / Hkv), kh = (int)(u % Hkv);
+        const int Nb = seqlens ? seqlens[b] : N;          /* this sequence's keys */
+        const int nT = (Nb + Bkd - 1) / Bkd;
+        const double th = log_threshold(tau, (double)Nb);
         double* buf = (double*)malloc(sizeof(double) * ((size_t)G * (5 + d) + (size_t)G * Bkd));
         if (!buf) { err = OR_ENOMEM; continue; }
         double *m = buf, *l = m + G, *om = l + G, *ol = om + G, *M = ol + G;
@@ -549,7 +558,7 @@ int mala_oracle_decode(const double* q, const double* kc, const double* vc,
         int nkept = 0;
         for (int t = nT - 1; t >= 0; --t) {            /* newest tile first */
             const int j0 = t * Bkd;
-            const int j1 = (j0 + Bkd < N) ? j0 + Bkd : N;
+            const int j1 = (j0 + Bkd < Nb) ? j0 + Bkd : Nb;
             double lam = -INFINITY;
             for (int g = 0; g < G; ++g) {
                 const double* qg = q + ((size_t)b * Hq + kh * G + g) * d;
@@ -564,8 +573,8 @@ int mala_oracle_decode(const double* q, const double* kc, const double* vc,
                 if (x > lam) lam = x;
             }
             const int kp = (lam >= 0.0);
-            if (keep) keep[((size_t)b * Hkv + kh) * nT + t] = (uint8_t)kp;
-            if (margin) margin[((size_t)b * Hkv + kh) * nT + t] = lam;
+            if (keep) keep[((size_t)b * Hkv + kh) * nTmax + t] = (uint8_t)kp;
+            if (margin) margin[((size_t)b * Hkv + kh) * nTmax + t] = lam;
             nkept += kp;
             for (int g = 0; g < G; ++g) {
                 if (kp) {

@@ -159,3 +159,54 @@ def test_varlen_prop1_bound_and_first_tile(tau):
             assert (f["keep"][b, :, i // Bq, (lk[b] - lq[b] + i) // Bk] == 1).all()
     # unvisited blocks of short sequences stay unvisited
     assert (f["keep"][2, :, 1:] == 255).all()
+
+
+# ------------------------------------------------- decode with per-sequence cache lengths
+@pytest.mark.parametrize("tau", [0.0, 0.25, 1.0, 4.0])
+def test_decode_seqlens_match_one_row_varlen_forward(tau):
+    """Decode with cache lengths N_b equals, for G = 1, the variable-length
+    forward of one query over N_b keys (a separate code path): same tiles
+    newest first, L_i = N_b, same retained set."""
+    N, B, H, d = 500, 4, 3, 32
+    lens = np.array([500, 1, 64, 333], np.int32)
+    di = G.decode_inputs(360, B, N, H, H, d)
+    q, kc, vc = [G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")]
+    r = oracle_decode(q, kc, vc, tau, 64, seqlens=lens)
+    cu_q = np.arange(B + 1, dtype=np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kp = np.concatenate([kc[b, :lens[b]] for b in range(B)])
+    vp = np.concatenate([vc[b, :lens[b]] for b in range(B)])
+    f = oracle_fwd_varlen(q, kp, vp, cu_q, cu_k, tau, 16, 64)
+    nT = r["keep"].shape[-1]
+    assert np.array_equal(f["keep"][:, :, 0, :], r["keep"][..., :f["keep"].shape[-1]])
+    for b in range(B):
+        assert (r["keep"][b, :, -(-lens[b] // 64):nT] == 255).all()
+    assert np.abs(f["o"] - r["o"]).max() <= 1e-13 * np.abs(r["o"]).max()
+    assert np.abs(f["lse"].T - r["lse"]).max() <= 1e-13 * np.abs(r["lse"]).max()
+    assert (r["kept_tiles"] == (r["keep"] == 1).sum(-1)).all()
+
+
+def test_decode_seqlens_tau0_is_softmax_over_the_prefix():
+    N, B, Hq, Hkv, d = 300, 3, 4, 2, 16
+    lens = np.array([300, 17, 129], np.int32)
+    di = G.decode_inputs(370, B, N, Hq, Hkv, d)
+    q, kc, vc = [G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")]
+    r = oracle_decode(q, kc, vc, 0.0, 64, seqlens=lens)
+    for b in range(B):
+        for h in range(Hq):
+            s = kc[b, :lens[b], h // 2] @ q[b, h] / np.sqrt(d)
+            w = np.exp(s - s.max())
+            o = w @ vc[b, :lens[b], h // 2] / w.sum()
+            assert np.abs(r["o"][b, h] - o).max() <= 1e-12 * np.abs(o).max()
+            assert abs(r["lse"][b, h] - (s.max() + np.log(w.sum()))) <= 1e-12 * max(1.0, abs(s.max()))
+
+
+def test_decode_seqlens_full_length_is_plain_decode():
+    di = G.decode_inputs(380, 2, 200, 4, 2, 16)
+    q, kc, vc = [G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")]
+    a = oracle_decode(q, kc, vc, 1.0, 64)
+    b = oracle_decode(q, kc, vc, 1.0, 64, seqlens=np.array([200, 200], np.int32))
+    for key in ("o", "lse", "keep", "kept_tiles"):
+        assert np.array_equal(a[key], b[key])
+    with pytest.raises(ValueError):
+        oracle_decode(q, kc, vc, 1.0, 64, seqlens=np.array([0, 200], np.int32))
