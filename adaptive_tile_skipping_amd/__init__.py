@@ -43,7 +43,7 @@ class MalaTileStats(ctypes.Structure):
 
 EXPORTS = ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
            "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
-           "mala_status_string", "mala_version")
+           "mala_decode_varlen", "mala_status_string", "mala_version")
 
 _lib = None
 
@@ -78,6 +78,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mala_decode_workspace_size.restype = S
     lib.mala_decode.argtypes = [P, MalaT4, MalaT4, I, I, I, I, I, F, I, P, P, P, P, P, S, P]
     lib.mala_decode.restype = I
+    lib.mala_decode_varlen.argtypes = [P, MalaT4, MalaT4, P, I, I, I, I, I, F, I, P, P, P, P, P, S, P]
+    lib.mala_decode_varlen.restype = I
     lib.mala_status_string.argtypes = [I]
     lib.mala_status_string.restype = ctypes.c_char_p
     lib.mala_version.restype = ctypes.c_char_p
@@ -261,12 +263,14 @@ def decode_workspace(B, N, Hq, Hkv, d, Bk_dec=64, device="cuda"):
 
 
 def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, lse=None, kept_tiles=None, ws=None,
-                decision_bits=None):
+                decision_bits=None, cache_seqlens=None):
     """Decode one token.  q [B,Hq,d] bf16 contiguous; caches [B,N,Hkv,d] bf16.
     Returns (o [B,Hq,d] bf16, lse [B,Hq] fp32, kept_tiles [B,Hkv] int32).
     decision_bits: optional int32 tensor [B, Hkv, ceil(nT/32)] filled with the
-    per-tile keep bits."""
-    _dev_check(q, kcache, vcache)
+    per-tile keep bits.  cache_seqlens: optional int32 [B] tensor on the same
+    device; sequence b then uses only its first cache_seqlens[b] cache rows
+    (mala_decode_varlen)."""
+    _dev_check(q, kcache, vcache, cache_seqlens)
     B, Hq, d = q.shape
     N, Hkv = kcache.shape[1], kcache.shape[2]
     if not q.is_contiguous() or q.dtype != torch.bfloat16:
@@ -277,9 +281,18 @@ def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, l
     if ws is None:
         ws = decode_workspace(B, N, Hq, Hkv, d, Bk_dec, q.device)
     lib = load_library()
-    rc = lib.mala_decode(_ptr(q), _t4(kcache), _t4(vcache), B, N, Hq, Hkv, d, float(tau), Bk_dec,
-                         _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits), _ptr(ws), ws.numel(), _stream(q))
-    _check("mala_decode", rc)
+    if cache_seqlens is None:
+        rc = lib.mala_decode(_ptr(q), _t4(kcache), _t4(vcache), B, N, Hq, Hkv, d, float(tau), Bk_dec,
+                             _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits), _ptr(ws), ws.numel(),
+                             _stream(q))
+        _check("mala_decode", rc)
+    else:
+        if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != B or not cache_seqlens.is_contiguous():
+            raise ValueError("cache_seqlens must be a contiguous int32 [B] tensor")
+        rc = lib.mala_decode_varlen(_ptr(q), _t4(kcache), _t4(vcache), _ptr(cache_seqlens), B, N, Hq, Hkv, d,
+                                    float(tau), Bk_dec, _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits),
+                                    _ptr(ws), ws.numel(), _stream(q))
+        _check("mala_decode_varlen", rc)
     return o, lse, kept_tiles
 
 

@@ -277,8 +277,11 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
     return s;
 }
 
-mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
-                        int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
+}  // extern "C"
+
+namespace {
+mala_status decode_impl(const void* q, mala_t4 kcache, mala_t4 vcache, const int32_t* seqlens, int B, int N,
+                        int Hq, int Hkv, int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
                         uint32_t* decision_bits, void* ws, size_t ws_bytes, void* stream) {
     if (!dims_ok(B, N, Hq, Hkv, d) || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
     if (!q || !aligned16(q) || !o || !aligned16(o) || !lse) return MALA_ERR_INVALID_ARG;
@@ -292,6 +295,7 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
     memset(&p, 0, sizeof(p));
     p.q = (const uint16_t*)q; p.k = (const uint16_t*)kcache.ptr; p.v = (const uint16_t*)vcache.ptr;
     p.o = (uint16_t*)o; p.lse = lse; p.kept_tiles = kept_tiles; p.bits = decision_bits;
+    p.seqlens = seqlens;
     p.k_sb = kcache.sb; p.k_sl = kcache.sl; p.k_sh = kcache.sh;
     p.v_sb = vcache.sb; p.v_sl = vcache.sl; p.v_sh = vcache.sh;
     p.B = B; p.N = N; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
@@ -314,6 +318,25 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
     p.part_ml = (float*)w;
     hipError_t e = launch_decode(p, d, Bk_dec, tau == 0.f, (hipStream_t)stream);
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
+                        int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
+                        uint32_t* decision_bits, void* ws, size_t ws_bytes, void* stream) {
+    return decode_impl(q, kcache, vcache, nullptr, B, N, Hq, Hkv, d, tau, Bk_dec, o, lse, kept_tiles, decision_bits,
+                       ws, ws_bytes, stream);
+}
+
+mala_status mala_decode_varlen(const void* q, mala_t4 kcache, mala_t4 vcache, const int32_t* cache_seqlens, int B,
+                               int N, int Hq, int Hkv, int d, float tau, int Bk_dec, void* o, float* lse,
+                               int32_t* kept_tiles, uint32_t* decision_bits, void* ws, size_t ws_bytes,
+                               void* stream) {
+    if (!cache_seqlens) return MALA_ERR_INVALID_ARG;
+    return decode_impl(q, kcache, vcache, cache_seqlens, B, N, Hq, Hkv, d, tau, Bk_dec, o, lse, kept_tiles,
+                       decision_bits, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

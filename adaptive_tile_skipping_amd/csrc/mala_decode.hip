@@ -51,10 +51,18 @@ __device__ __forceinline__ void lse_combine(float& m, float& l, float m2, float 
 }
 }  // namespace
 
+// Keys of sequence b: its cache length, or N without per-sequence lengths; 0
+// when the given length lies outside [1, N] (the sequence is then skipped).
+__device__ __forceinline__ int dec_len(const DecParams& p, int b) {
+    if (!p.seqlens) return p.N;
+    const int n = p.seqlens[b];
+    return (n >= 1 && n <= p.N) ? n : 0;
+}
+
 // Stages one 64-key tile into this wave's LDS slice [64][D] with 16-byte chunk
-// c of row r stored at chunk c ^ (r % (D/8)).  Rows past N repeat row N-1.
+// c of row r stored at chunk c ^ (r % (D/8)).  Rows past Nb repeat row Nb-1.
 template <int D>
-__device__ __forceinline__ void stage_k_tile(const DecParams& p, int b, int kh, int t, uint16_t* slice) {
+__device__ __forceinline__ void stage_k_tile(const DecParams& p, int b, int kh, int t, int Nb, uint16_t* slice) {
     constexpr int QCH = D / 8;
     const int lane = threadIdx.x & 63;
     const uint16_t* kb = p.k + b * p.k_sb + kh * p.k_sh;
@@ -64,7 +72,7 @@ __device__ __forceinline__ void stage_k_tile(const DecParams& p, int b, int kh, 
         const int r = slot / QCH, pc = slot % QCH;
         const int c = pc ^ (r % QCH);
         int j = t * BKD + r;
-        j = j < p.N ? j : p.N - 1;
+        j = j < Nb ? j : Nb - 1;
         load16_to_lds(kb + (int64_t)j * p.k_sl + 8 * c, reinterpret_cast<unsigned char*>(slice) + 1024 * n);
     }
 }
@@ -84,10 +92,10 @@ __device__ __forceinline__ void load_q_frags(const DecParams& p, int b, int kh, 
 }
 
 // Scores of the staged tile: s[sub][r] is row g = lane%32, key
-// 32 sub + 8(r/4) + 4 hi + r%4, base 2, -inf past N.
+// 32 sub + 8(r/4) + 4 hi + r%4, base 2, -inf past Nb.
 template <int D>
-__device__ __forceinline__ void tile_scores(const DecParams& p, int t, const uint16_t* slice, const bf16x8* qf,
-                                            f32x16* s) {
+__device__ __forceinline__ void tile_scores(const DecParams& p, int t, int Nb, const uint16_t* slice,
+                                            const bf16x8* qf, f32x16* s) {
     constexpr int QCH = D / 8;
     const int lane = threadIdx.x & 63;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -107,7 +115,7 @@ __device__ __forceinline__ void tile_scores(const DecParams& p, int t, const uin
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int j = t * BKD + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
-            s[sub][r] = (j < p.N) ? s[sub][r] * p.scale_log2 : kNegInf;
+            s[sub][r] = (j < Nb) ? s[sub][r] * p.scale_log2 : kNegInf;
         }
 }
 
@@ -131,11 +139,13 @@ void mala_dec_score(const DecParams p) {
     auto load_tile = [&](int tk, bf16x8 (&kf)[2][KSTEPS]) {
         const int grp = tk / p.nT, t = tk % p.nT;
         const int b = grp / p.Hkv, kh = grp % p.Hkv;
+        const int Nb = dec_len(p, b);
+        if (t * BKD >= Nb) return;                     // past this sequence's cache
         const uint16_t* kb = p.k + b * p.k_sb + kh * p.k_sh;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             int j = t * BKD + 32 * sub + l32;
-            j = j < p.N ? j : p.N - 1;                 // rows past N are masked below
+            j = j < Nb ? j : Nb - 1;                   // rows past Nb are masked below
             const uint16_t* row = kb + (int64_t)j * p.k_sl + 8 * hi;
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) kf[sub][st] = *(const bf16x8*)(row + 16 * st);
@@ -152,6 +162,8 @@ void mala_dec_score(const DecParams p) {
         }
         // per-call reset owned by this tile
         if (p.bits && lane == 0 && (t % 32) == 0) p.bits[(int64_t)grp * p.nwords + t / 32] = 0u;
+        const int Nb = dec_len(p, grp / p.Hkv);
+        if (t * BKD >= Nb) return;
         f32x16 sv[2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
@@ -164,7 +176,7 @@ void mala_dec_score(const DecParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = t * BKD + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                sv[sub][r] = (j < p.N) ? sv[sub][r] * p.scale_log2 : kNegInf;
+                sv[sub][r] = (j < Nb) ? sv[sub][r] * p.scale_log2 : kNegInf;
             }
         float M = kNegInf;
 #pragma unroll
@@ -181,7 +193,7 @@ void mala_dec_score(const DecParams p) {
         const int g = l32;
         if (g < p.G) {
             float* sp = p.spill + ((int64_t)grp * p.G + g) * p.N + (int64_t)t * BKD;
-            const bool full = (t + 1) * BKD <= p.N;
+            const bool full = (t + 1) * BKD <= Nb;
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -193,7 +205,7 @@ void mala_dec_score(const DecParams p) {
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            if (t * BKD + j0 + e < p.N) sp[j0 + e] = sv[sub][4 * q4 + e];
+                            if (t * BKD + j0 + e < Nb) sp[j0 + e] = sv[sub][4 * q4 + e];
                     }
                 }
             if (hi == 0) {
@@ -276,7 +288,16 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     const int grp = blockIdx.x;
     const int lane = threadIdx.x;
     const int G = p.G;
-    const float theta = p.log2_tau - p.log2_N;
+    const int Nb = dec_len(p, grp / p.Hkv);
+    if (Nb == 0) {                              // skipped sequence: nothing retained
+        if (lane == 0) {
+            p.kcount[grp] = 0;
+            if (p.kept_tiles) p.kept_tiles[grp] = 0;
+        }
+        return;
+    }
+    const int nTb = (Nb + BKD - 1) / BKD;      // this sequence's tiles (p.nT is the stride)
+    const float theta = p.log2_tau - (p.seqlens ? (float)log2((double)Nb) : p.log2_N);
     const bool lin_ok = theta >= -120.f && theta <= 120.f;
     const float cthr = fast_exp2(theta);
     float m[GP], l[GP];                   // retained state (identical in all lanes)
@@ -285,7 +306,7 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     int kept = 0;
     int32_t* klist = p.klist + (int64_t)grp * p.nT;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int nchunk = (p.nT + 63) / 64;
+    const int nchunk = (nTb + 63) / 64;
     const float* tmax = p.tmax + (int64_t)grp * p.nT * G;
     const float* tsum = p.tsum + (int64_t)grp * p.nT * G;
 
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
 #pragma unroll
         for (int g = 0; g < GP; ++g) { mx[g] = kNegInf; mn[g] = __builtin_inff(); }
         // the flat [tile][row] array in 64-lane strides, eight loads in flight per lane
-        const int ntot = p.nT * G;
+        const int ntot = nTb * G;
 #pragma unroll 8
         for (int e = lane; e < ntot; e += 64) {
             const float v = tmax[e];
@@ -335,10 +356,10 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     constexpr int DEPTH = (63 / (2 * GP)) < 7 ? ((63 / (2 * GP)) < 1 ? 1 : 63 / (2 * GP)) : 7;
     constexpr int RING = DEPTH + 1;
     __shared__ float sStat[RING][2][64 * GP];
-    const __amdgpu_buffer_rsrc_t rmax = make_rsrc(tmax, (uint32_t)(p.nT * G * 4));
-    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(tsum, (uint32_t)(p.nT * G * 4));
+    const __amdgpu_buffer_rsrc_t rmax = make_rsrc(tmax, (uint32_t)(nTb * G * 4));
+    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(tsum, (uint32_t)(nTb * G * 4));
     auto issue_chunk = [&](int c) {
-        const int t_lo = p.nT - 64 * (c + 1);          // may be negative
+        const int t_lo = nTb - 64 * (c + 1);           // may be negative
         const uint32_t base = (uint32_t)(t_lo * G * 4);
         float* dm = sStat[c % RING][0];
         float* ds = sStat[c % RING][1];
@@ -354,7 +375,7 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     for (int c = 0; c < DEPTH; ++c)
         if (c < nchunk) issue_chunk(c);
     for (int c = 0; c < nchunk; ++c) {
-        const int t = p.nT - 1 - (c * 64 + lane);
+        const int t = nTb - 1 - (c * 64 + lane);
         const bool valid = t >= 0;
         if (c + DEPTH < nchunk) {
             issue_chunk(c + DEPTH);
@@ -564,6 +585,7 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
     const int G = p.G;
     const int cnt = p.kcount[grp];
     if (blockIdx.x * 4 >= cnt) return;          // the whole workgroup: no partial is read
+    const int Nb = dec_len(p, b);
     const int idx = blockIdx.x * 4 + w;
     const bool has = idx < cnt;
     const int t = has ? p.klist[(int64_t)grp * p.nT + idx] : 0;
@@ -574,7 +596,7 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
 #pragma unroll
     for (int r = 0; r < KPL; ++r) {
         int key = t * BKD + kg * KPL + r;
-        key = key < p.N ? key : p.N - 1;
+        key = key < Nb ? key : Nb - 1;
         vx[r] = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
     }
     // P of the tile: lane = key, one value per row
@@ -583,7 +605,7 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
             float pr = 0.f;
-            if (has && g < G && key < p.N)
+            if (has && g < G && key < Nb)
                 pr = fast_exp2(p.spill[((int64_t)grp * G + g) * p.N + key] - p.lse2[(int64_t)grp * G + g]);
             sP[w][g][lane] = pr;
         }
@@ -639,6 +661,7 @@ __global__ __launch_bounds__(256) void mala_dec_sum_combine(const DecParams p) {
     const int grp = blockIdx.x, g = blockIdx.y, dq = blockIdx.z;
     const int G = p.G;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
+    if (dec_len(p, b) == 0) return;              // skipped sequence: o is left as it was
     const int64_t base = (int64_t)grp * p.npart;
     const int d = 32 * dq + (tid & 31), cls = tid >> 5;
     const int nused = (p.kcount[grp] + 3) / 4;   // P.V workgroups that wrote a partial
@@ -675,8 +698,10 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
     const int s = blockIdx.x, grp = blockIdx.y;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
     const int G = p.G;
+    const int Nb = dec_len(p, b);
+    const int nTb = (Nb + BKD - 1) / BKD;
     const int t0 = s * p.tiles_per_split;
-    const int t1 = (t0 + p.tiles_per_split < p.nT) ? t0 + p.tiles_per_split : p.nT;
+    const int t1 = (t0 + p.tiles_per_split < nTb) ? t0 + p.tiles_per_split : nTb;   // may be empty
     bf16x8 qf[D / 16];
     load_q_frags<D>(p, b, kh, qf);
     if (tid < GP) { sState[tid][0] = kNegInf; sState[tid][1] = 0.f; }
@@ -690,19 +715,19 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
     __syncthreads();
     for (int tb = t0; tb < t1; tb += 4) {
         const int t = tb + w;
-        if (t < t1) stage_k_tile<D>(p, b, kh, t, sK[w]);
+        if (t < t1) stage_k_tile<D>(p, b, kh, t, Nb, sK[w]);
         u32x4 vx[KPT];
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
             int key = tb * BKD + kg * KPT + r;
-            key = (key < t1 * BKD && key < p.N) ? key : 0;
+            key = (key < t1 * BKD && key < Nb) ? key : 0;
             vx[r] = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
         }
         {
             f32x16 sc[2];
             if (t < t1) {
                 __builtin_amdgcn_s_waitcnt(0);
-                tile_scores<D>(p, t, sK[w], qf, sc);
+                tile_scores<D>(p, t, Nb, sK[w], qf, sc);
             } else {
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
@@ -760,7 +785,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
         for (int r = 0; r < KPT; ++r) {
             const int jj = kg * KPT + r;
             const int key = tb * BKD + jj;
-            if (key >= t1 * BKD || key >= p.N) continue;
+            if (key >= t1 * BKD || key >= Nb) continue;
             float vv[8];
 #pragma unroll
             for (int m2 = 0; m2 < 4; ++m2) {
@@ -810,7 +835,18 @@ __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p)
     const int grp = blockIdx.x, g = blockIdx.y, dq = blockIdx.z;
     const int G = p.G;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
+    const int nTb = (dec_len(p, b) + BKD - 1) / BKD;     // 0: skipped sequence
     const int64_t base = (int64_t)grp * p.nsplit;
+    if (dq == 0 && g == 0) {
+        if (tid == 0 && p.kept_tiles) p.kept_tiles[grp] = nTb;
+        if (p.bits)
+            for (int wd = tid; wd < p.nwords; wd += 256) {
+                const int rem = nTb - 32 * wd;
+                p.bits[(int64_t)grp * p.nwords + wd] =
+                    rem >= 32 ? 0xFFFFFFFFu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
+            }
+    }
+    if (nTb == 0) return;                         // o and lse are left as they were
     // global max over splits
     float mx = kNegInf;
     for (int s = tid; s < p.nsplit; s += 256) mx = fmaxf(mx, p.part_ml[((base + s) * G + g) * 2]);
@@ -840,14 +876,6 @@ __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p)
         for (int c = 0; c < 8; ++c) { o += sO[c][tid]; l += sL[c]; }
         p.o[((int64_t)b * p.Hq + kh * G + g) * D + 32 * dq + tid] = (uint16_t)float_to_bf16_bits(o / l);
         if (dq == 0 && tid == 0) p.lse[(int64_t)b * p.Hq + kh * G + g] = (M + fast_log2(l)) * kLn2;
-    }
-    if (dq == 0 && g == 0) {
-        if (tid == 0 && p.kept_tiles) p.kept_tiles[grp] = p.nT;
-        if (p.bits)
-            for (int wd = tid; wd < p.nwords; wd += 256) {
-                const int rem = p.nT - 32 * wd;
-                p.bits[(int64_t)grp * p.nwords + wd] = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
-            }
     }
 }
 

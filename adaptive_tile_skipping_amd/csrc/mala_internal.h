@@ -76,6 +76,7 @@ struct DecParams {
     float scale_log2;
     float log2_tau;
     float log2_N;
+    const int32_t* seqlens; // [B] device cache lengths (1 .. N), or null: every sequence has N keys
     // workspace
     float* tmax;            // [B, Hkv, G, nT]  tile row max (base 2)
     float* tsum;            // [B, Hkv, G, nT]  sum 2^(s - tile max)

@@ -188,6 +188,22 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
                         int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
                         uint32_t* decision_bits, void* ws, size_t ws_bytes, void* stream);
 
+/* Decode against caches of different lengths per sequence (the cache tensor
+ * padded to N rows): sequence b uses its first cache_seqlens[b] rows, which
+ * include the new token's key and value, and its decision uses
+ * L_i = cache_seqlens[b] (same rule and summary/review passages as
+ * mala_decode).  Arguments as for mala_decode, plus:
+ *   cache_seqlens: int32 [B] in DEVICE memory, read by the kernels.  A
+ *   sequence whose length lies outside [1, N] is skipped: its o and lse are
+ *   left unwritten, its kept_tiles entry and decision bits are 0.
+ * Cache tiles past a sequence's length are not read; decision_bits of those
+ * tiles are 0.  The workspace is mala_decode_workspace_size(B, N, ...).
+ * cache_seqlens = NULL returns MALA_ERR_INVALID_ARG. */
+mala_status mala_decode_varlen(const void* q, mala_t4 kcache, mala_t4 vcache, const int32_t* cache_seqlens, int B,
+                               int N, int Hq, int Hkv, int d, float tau, int Bk_dec, void* o, float* lse,
+                               int32_t* kept_tiles, uint32_t* decision_bits, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Static string naming a status code. */
 const char* mala_status_string(mala_status s);
 

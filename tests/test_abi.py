@@ -21,7 +21,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
               "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
-              "mala_status_string", "mala_version"):
+              "mala_decode_varlen", "mala_status_string", "mala_version"):
         assert n in names
 
 
@@ -168,3 +168,19 @@ def test_fwd_varlen_workspace_size():
     # fp16 V copy with one tile of zero rows after each sequence
     assert lib.mala_fwd_varlen_workspace_size(3, 1000, 2, 128, 128, 64) >= (1000 + 3 * 64) * 2 * 128 * 2
     assert lib.mala_fwd_varlen_workspace_size(3, 1000, 2, 96, 128, 64) == 0
+
+
+def test_decode_varlen_errors():
+    lib = mala.load_library()
+    t = _t4()
+    q = ctypes.c_void_p(4096)
+    tail = [2, 1000, 4, 2, 128, 1.0, 64, ctypes.c_void_p(8192), ctypes.c_void_p(12288), None, None]
+    # the lengths array is required
+    assert lib.mala_decode_varlen(q, t, t, None, *tail, ctypes.c_void_p(1 << 20), 1 << 30, None) == \
+        mala.MALA_ERR_INVALID_ARG
+    sl = ctypes.c_void_p(16384)
+    assert lib.mala_decode_varlen(q, t, t, sl, *tail, None, 0, None) == mala.MALA_ERR_WORKSPACE
+    bad = list(tail)
+    bad[6] = 32
+    assert lib.mala_decode_varlen(q, t, t, sl, *bad, ctypes.c_void_p(1 << 20), 1 << 30, None) == \
+        mala.MALA_ERR_UNSUPPORTED

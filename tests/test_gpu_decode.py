@@ -19,18 +19,24 @@ def _dev():
     return torch.device("cuda:0")
 
 
-def run_decode_case(di, tau, label=""):
+def run_decode_case(di, tau, label="", seqlens=None):
     dev = _dev()
     B, Hq, d = di["q"].shape
     N, Hkv = di["k"].shape[1], di["k"].shape[2]
     nT = -(-N // 64)
     q, kc, vc = (bf16_tensor(di[x], dev) for x in ("q", "k", "v"))
     bits = torch.empty((B, Hkv, -(-nT // 32)), dtype=torch.int32, device=dev)
-    print(f"[decode] {label} B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} tau={tau}", flush=True)
-    o, lse, kept = mala.mala_decode(q, kc, vc, tau, decision_bits=bits)
+    sl = None if seqlens is None else torch.from_numpy(np.asarray(seqlens, np.int32)).to(dev)
+    print(f"[decode] {label} B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} tau={tau} seqlens={seqlens}", flush=True)
+    o, lse, kept = mala.mala_decode(q, kc, vc, tau, decision_bits=bits, cache_seqlens=sl)
     torch.cuda.synchronize()
-    ref = oracle_decode(*(G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")), tau, 64)
+    ref = oracle_decode(*(G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")), tau, 64, seqlens=seqlens)
     gk = unpack_bits(bits.cpu().numpy(), nT)
+    if seqlens is not None:
+        # tiles past a sequence's cache are not visited: their bits read 0
+        unv = ref["keep"] == 255
+        assert (gk[unv] == 0).all()
+        gk = np.where(unv, 255, gk)
     dec = compare_decisions(gk, ref["keep"], ref["margin"], descending=True)
     assert dec["nonexempt"] == 0, dec
     bad = (gk != ref["keep"]).any(-1)                     # [B, Hkv]
@@ -48,7 +54,7 @@ def run_decode_case(di, tau, label=""):
         assert lerr.max() <= LSE_TOL + 1e-5 * np.abs(ref["lse"]).max(), lerr.max()
     kt = kept.cpu().numpy()
     assert np.array_equal(kt[~bad], ref["kept_tiles"][~bad])
-    assert np.array_equal(kt, gk.sum(-1))
+    assert np.array_equal(kt, (gk == 1).sum(-1))
     return dict(dec=dec, o_worst=worst, keep_frac=float(ref["keep"].mean()))
 
 
@@ -87,3 +93,48 @@ def test_decode_strided_cache():
     o2, l2, _ = mala.mala_decode(q, kc, vc, 1.0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.25, 1.0, 4.0])
+def test_decode_cache_seqlens(tau):
+    """Caches of different lengths in one call (padded to N = 5000): full,
+    one key, tile-aligned, ragged, and a long one with a short neighbour."""
+    di = G.decode_inputs(1300, 6, 5000, 10, 2, 128)
+    run_decode_case(di, tau, "cache_seqlens", seqlens=[5000, 1, 64, 65, 4097, 130])
+
+
+def test_decode_cache_seqlens_d64_groups():
+    di = G.decode_inputs(1310, 3, 3000, 8, 1, 64)
+    for tau in (0.0, 1.0):
+        run_decode_case(di, tau, "cache_seqlens d64 G=8", seqlens=[2999, 200, 1000])
+
+
+def test_decode_cache_seqlens_full_equals_plain():
+    """Every length equal to N gives the plain call's bits exactly."""
+    dev = _dev()
+    di = G.decode_inputs(1320, 4, 3000, 5, 1, 128)
+    q, kc, vc = (bf16_tensor(di[x], dev) for x in ("q", "k", "v"))
+    sl = torch.full((4,), 3000, dtype=torch.int32, device=dev)
+    for tau in (0.0, 1.0):
+        o1, l1, k1 = mala.mala_decode(q, kc, vc, tau)
+        o2, l2, k2 = mala.mala_decode(q, kc, vc, tau, cache_seqlens=sl)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(k1, k2)
+
+
+def test_decode_cache_seqlens_invalid_sequence_skipped():
+    """A length outside [1, N] skips that sequence (o and lse untouched, no
+    tile kept); the others are unaffected."""
+    dev = _dev()
+    di = G.decode_inputs(1330, 3, 1000, 4, 2, 128)
+    q, kc, vc = (bf16_tensor(di[x], dev) for x in ("q", "k", "v"))
+    good = torch.tensor([700, 1000, 300], dtype=torch.int32, device=dev)
+    for tau in (0.0, 1.0):
+        o1, l1, k1 = mala.mala_decode(q, kc, vc, tau, cache_seqlens=good)
+        bad = torch.tensor([700, 1001, 0], dtype=torch.int32, device=dev)
+        o2 = torch.full_like(q, 5.0)
+        l2 = torch.full((3, 4), -1.0, device=dev)
+        _, _, k2 = mala.mala_decode(q, kc, vc, tau, o=o2, lse=l2, cache_seqlens=bad)
+        torch.cuda.synchronize()
+        assert torch.equal(o2[0], o1[0]) and torch.equal(l2[0], l1[0]) and torch.equal(k2[0], k1[0])
+        assert (o2[1:] == 5.0).all() and (l2[1:] == -1.0).all() and (k2[1:] == 0).all()
