@@ -18,8 +18,14 @@ chunked prefill: the last 16384 queries of the 128K sequence against all of its
 131072 keys (the cache of the 114688 keys before them plus the chunk itself),
 and prints that measurement's own JSON line.
 
+`--workload tau_sweep` measures fidelity against cost over the sweep workload
+(Hq=16, Hkv=4, half the heads diffuse; L = 1K .. 32K): per (L, tau) the forward
+time, kept tiles, retained key slots per query, the omitted probability mass
+(kernel statistics mode) and the relative L2 distance of O from the tau = 0
+output of the same kernel, per head.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tau0]
-                       [--workload step|prefill_128k]
+                       [--workload step|prefill_128k|tau_sweep]
 """
 from __future__ import annotations
 
@@ -47,8 +53,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison")
     ap.add_argument("--cpu-blocks", type=int, default=48, help="query blocks per head in the CPU sample")
-    ap.add_argument("--workload", choices=("step", "prefill_128k"), default="step",
-                    help="step: training forward+backward and decode (default); prefill_128k: chunked prefill")
+    ap.add_argument("--workload", choices=("step", "prefill_128k", "tau_sweep"), default="step",
+                    help="step: training forward+backward and decode (default); prefill_128k: chunked prefill; "
+                         "tau_sweep: fidelity and cost against tau")
+    ap.add_argument("--taus", type=str, default="0.01,0.05,0.25,1,4,16",
+                    help="tau values of the tau_sweep workload (tau = 0 is always run as the reference)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run two forward launches and a plain 1 GiB device copy, then exit (for PMC passes)")
     return ap.parse_args()
@@ -200,6 +209,79 @@ def main_prefill(args):
     print(json.dumps(out), flush=True)
 
 
+def main_tau_sweep(args):
+    """Fidelity and cost against tau over the sweep workload (module docstring)."""
+    import numpy as np
+    import torch
+
+    import adaptive_tile_skipping_amd as mala
+    import mala_gen as G
+
+    dev = torch.device("cuda:0")
+    torch.cuda.init()
+    W = G.WORKLOADS["sweep"]
+    Hq, Hkv, d, Bq, Bk = W["Hq"], W["Hkv"], W["d"], W["Bq"], W["Bk"]
+    taus = [float(x) for x in args.taus.split(",") if float(x) > 0]
+    rows = []
+    for L in W["Ls"]:
+        inp = G.workload_inputs("sweep", L=L, with_dout=False)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(inp[x]).view(np.int16)).view(torch.bfloat16).to(dev)
+                   for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((1, Hq, L), dtype=torch.float32, device=dev)
+        ws = mala.fwd_workspace(1, L, Hq, Hkv, d, Bq, Bk, dev)
+        stream = torch.cuda.current_stream(dev)
+        nQB = -(-L // Bq)
+        n_visit = Hq * sum((min(L, qb * Bq + Bq) - 1) // Bk + 1 for qb in range(nQB))
+
+        def timed(t, n=max(5, args.steps)):
+            for _ in range(args.warmup):
+                mala.mala_fwd(q, k, v, t, Bq, Bk, o=o, lse=lse, ws=ws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for e0, e1 in ev:
+                e0.record(stream); mala.mala_fwd(q, k, v, t, Bq, Bk, o=o, lse=lse, ws=ws); e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+        ms0 = timed(0.0)
+        o_ref, _ = mala.mala_fwd(q, k, v, 0.0, Bq, Bk, ws=ws)
+        ref = o_ref.float()
+        for t in taus:
+            ms = timed(t)
+            st = mala.make_stats(1, Hq, L, Bq, Bk, dev, omitted=True)
+            ot, _ = mala.mala_fwd(q, k, v, t, Bq, Bk, stats=st, ws=ws)
+            torch.cuda.synchronize()
+            om = st["omitted_mass"][0].double()                      # [Hq, L]
+            err = (ot.float() - ref).double().pow(2).sum(dim=(0, 1, 3)).sqrt()
+            nrm = ref.double().pow(2).sum(dim=(0, 1, 3)).sqrt()
+            rel = (err / nrm).cpu().numpy()
+            rows.append({
+                "L": L, "tau": t, "fwd_ms": round(ms, 4), "tau0_fwd_ms": round(ms0, 4),
+                "speedup_vs_tau0": round(ms0 / ms, 3),
+                "kept_tile_frac": round(int(st["kept_tiles"].sum().item()) / n_visit, 4),
+                "slots_per_query": round(float(st["kept_slots"].double().mean().item()), 1),
+                "omitted_mean": float(om.mean().item()), "omitted_max": float(om.max().item()),
+                "omitted_bound": t / (1 + t),
+                "o_rel_l2_per_head": [float(f"{x:.3e}") for x in rel],
+            })
+            print(f"# L={L} tau={t}: {ms:.3f} ms (tau=0 {ms0:.3f}), kept {rows[-1]['kept_tile_frac']}, "
+                  f"omitted mean {rows[-1]['omitted_mean']:.2e} max {rows[-1]['omitted_max']:.2e}, "
+                  f"O rel-L2 max {rel.max():.2e}", file=sys.stderr, flush=True)
+        del q, k, v, o, ws
+    last = [r for r in rows if r["L"] == W["Ls"][-1] and r["tau"] == 1.0]
+    out = {
+        "metric": "MALA fidelity vs cost against tau (sweep workload: forward ms, kept tiles, slots/query, "
+                  "omitted mass, O rel-L2 vs tau=0)",
+        "value": last[0]["speedup_vs_tau0"] if last else None,
+        "unit": "forward speedup vs tau=0 at the longest L, tau=1",
+        "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"sweep (B=1 Hq={Hq} Hkv={Hkv} d={d} Bq={Bq} Bk={Bk}, KV heads 2-3 diffuse)",
+                   "Ls": list(W["Ls"]), "taus": taus},
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -209,6 +291,9 @@ def main():
         sys.exit(2)
     if args.workload == "prefill_128k":
         main_prefill(args)
+        return
+    if args.workload == "tau_sweep":
+        main_tau_sweep(args)
         return
 
     import numpy as np
