@@ -149,6 +149,7 @@ def varlen_inputs(tag: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, p: float,
     q = np.zeros((int(cu_q[-1]), Hq, d), np.uint16)
     k = np.zeros((int(cu_k[-1]), Hkv, d), np.uint16)
     v = np.zeros((int(cu_k[-1]), Hkv, d), np.uint16)
+    do = np.zeros((int(cu_q[-1]), Hq, d), np.uint16)
     diffuse = set(diffuse_kv_heads)
     for s, (lq, lk) in enumerate(zip(lens_q, lens_k)):
         if lk == 0:
@@ -156,13 +157,14 @@ def varlen_inputs(tag: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, p: float,
         for kh in range(Hkv):
             rng = _rng(tag, s, kh)
             if kh in diffuse:
-                Q, K, V, _ = _diffuse_head(rng, lk, G, d)
+                Q, K, V, dO = _diffuse_head(rng, lk, G, d)
             else:
-                Q, K, V, _ = _local_retrieval_head(rng, lk, G, d, p)
+                Q, K, V, dO = _local_retrieval_head(rng, lk, G, d, p)
             q[cu_q[s]:cu_q[s + 1], kh * G:(kh + 1) * G, :] = round_to_bf16_bits(Q[lk - lq:])
             k[cu_k[s]:cu_k[s + 1], kh, :] = round_to_bf16_bits(K)
             v[cu_k[s]:cu_k[s + 1], kh, :] = round_to_bf16_bits(V)
-    return {"q": q, "k": k, "v": v, "cu_q": cu_q, "cu_k": cu_k, "Hq": Hq, "Hkv": Hkv, "d": d}
+            do[cu_q[s]:cu_q[s + 1], kh * G:(kh + 1) * G, :] = round_to_bf16_bits(dO[lk - lq:])
+    return {"q": q, "k": k, "v": v, "dout": do, "cu_q": cu_q, "cu_k": cu_k, "Hq": Hq, "Hkv": Hkv, "d": d}
 
 
 def decode_inputs(tag: int, B: int, N: int, Hq: int, Hkv: int, d: int) -> dict:

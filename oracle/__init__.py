@@ -12,5 +12,5 @@ Two independent implementations live here:
   * `oracle.ref_numpy`: a small numpy statement of the same rule, written
     separately, used only to cross-check the C oracle on tiny inputs.
 """
-from .core import (build_oracle, oracle_fwd, oracle_fwd_varlen, oracle_bwd,  # noqa: F401
+from .core import (build_oracle, oracle_fwd, oracle_fwd_varlen, oracle_bwd, oracle_bwd_varlen,  # noqa: F401
                    oracle_decode, oracle_threads, KEEP_UNVISITED)

@@ -48,9 +48,12 @@ def _load():
                                     P, i32, P, i32, P, P, P, P, P, i32]
     lib.mala_oracle_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, i32,
                                            P, P, P, P, P, P, i32]
+    lib.mala_oracle_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32,
+                                           P, i32, P, i32, P, P, P, P, P, i32]
     lib.mala_oracle_decode.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, P,
                                        P, P, P, P, P, P, i32]
-    for f in (lib.mala_oracle_fwd, lib.mala_oracle_fwd_varlen, lib.mala_oracle_bwd, lib.mala_oracle_decode):
+    for f in (lib.mala_oracle_fwd, lib.mala_oracle_fwd_varlen, lib.mala_oracle_bwd, lib.mala_oracle_bwd_varlen,
+              lib.mala_oracle_decode):
         f.restype = ctypes.c_int
     lib.mala_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -158,6 +161,42 @@ def oracle_bwd(q, k, v, o, dout, lse, tau: float, Bq: int, Bk: int,
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(keep), _ptr(margin), int(nthreads))
     if rc:
         raise ValueError(f"oracle_bwd failed with code {rc}")
+    return {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
+
+
+def oracle_bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, tau: float, Bq: int, Bk: int,
+                      qunits=None, kunits=None, do_dq=True, do_dkdv=True, nthreads: int = 0):
+    """Variable-length backward over the packed layout of oracle_fwd_varlen
+    (lse [Hq, total_q]).  Returns dict(dq, dk, dv, keep, margin); unit ids as
+    in oracle_bwd with nQB, nKT from the longest sequence."""
+    q, k, v, o, dout, lse = map(_f64, (q, k, v, o, dout, lse))
+    cq = np.ascontiguousarray(cu_q, dtype=np.int32)
+    ck = np.ascontiguousarray(cu_k, dtype=np.int32)
+    B = len(cq) - 1
+    Hq, d = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    maxq = int(np.max(np.diff(cq))) if B > 0 else 0
+    maxk = int(np.max(np.diff(ck))) if B > 0 else 0
+    nQB, nKT = max(1, -(-maxq // Bq)), max(1, -(-maxk // Bk))
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(k.shape, np.nan)
+    keep = np.full((B, Hq, nQB, nKT), KEEP_UNVISITED, np.uint8)
+    margin = np.full((B, Hq, nQB, nKT), np.nan)
+    qa = None if qunits is None else np.ascontiguousarray(qunits, dtype=np.int32)
+    ka = None if kunits is None else np.ascontiguousarray(kunits, dtype=np.int32)
+    nq = (len(qa) if qa is not None else 0) if do_dq else -1
+    nk = (len(ka) if ka is not None else 0) if do_dkdv else -1
+    if not do_dq:
+        qa = None
+    if not do_dkdv:
+        ka = None
+    rc = _load().mala_oracle_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                        _ptr(cq), _ptr(ck), B, Hq, Hkv, d, float(tau), Bq, Bk,
+                                        _ptr(qa), nq, _ptr(ka), nk,
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(keep), _ptr(margin), int(nthreads))
+    if rc:
+        raise ValueError(f"oracle_bwd_varlen failed with code {rc}")
     return {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
 
 

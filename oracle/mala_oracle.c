@@ -340,32 +340,47 @@ int mala_oracle_fwd_varlen(const double* q, const double* k, const double* v,
 /* ------------------------------------------------------------------------ */
 typedef struct {
     const double *q, *k, *v, *o, *dout, *lse;
-    int B, L, Hq, Hkv, d, Bq, Bk, nQB, nKT;
+    int B, Hq, Hkv, d, Bq, Bk, nQB, nKT;
+    /* per sequence, as in fwd_ctx */
+    const long *qoff, *koff, *lseoff;
+    const int *lq, *lk;
+    long lse_hstride;
     double tau, scale;
     double *dq, *dk, *dv, *margin;
     uint8_t* keep;
 } bwd_ctx;
 
+/* Row i of sequence b in a [rows][H][d] array, and its lse entry for head h. */
+static size_t qrow(const bwd_ctx* c, int b, int i, int h) {
+    return (((size_t)c->qoff[b] + i) * c->Hq + h) * c->d;
+}
+static size_t krow(const bwd_ctx* c, int b, int j, int kh) {
+    return (((size_t)c->koff[b] + j) * c->Hkv + kh) * c->d;
+}
+static double lse_at(const bwd_ctx* c, int b, int h, int i) {
+    return c->lse[(size_t)c->lseoff[b] + (size_t)h * c->lse_hstride + i];
+}
+
 /* Scores of tile (qb, kt) for q head h and the offline decision.  S is
  * [nr][Bk] with -inf on illegal entries.  Returns keep (0/1). */
 static int bwd_tile(const bwd_ctx* c, int b, int h, int qb, int kt, double* S, double* lam_out) {
-    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, L = c->L, Bk = c->Bk;
+    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, Bk = c->Bk;
+    const int Lq = c->lq[b], Lk = c->lk[b], off = Lk - Lq;
     const int kh = h / (Hq / Hkv);
     const int r0 = qb * c->Bq;
-    const int r1 = (r0 + c->Bq < L) ? r0 + c->Bq : L;
+    const int r1 = (r0 + c->Bq < Lq) ? r0 + c->Bq : Lq;
     const int j0 = kt * Bk;
-    const int j1 = (j0 + Bk < L) ? j0 + Bk : L;
+    const int j1 = (j0 + Bk < Lk) ? j0 + Bk : Lk;
     double lam = -INFINITY;
     for (int i = r0; i < r1; ++i) {
-        const double* qi = c->q + (((size_t)b * L + i) * Hq + h) * d;
-        const double lz = c->lse[((size_t)b * Hq + h) * L + i];
-        const double th = log_threshold(c->tau, (double)(i + 1));
+        const double* qi = c->q + qrow(c, b, i, h);
+        const double lz = lse_at(c, b, h, i);
+        const double th = log_threshold(c->tau, (double)(off + i + 1));
         double mx = -INFINITY;
         for (int j = j0; j < j1; ++j) {
             double s = -INFINITY;
-            if (j <= i) {
-                const double* kj = c->k + (((size_t)b * L + j) * Hkv + kh) * d;
-                s = dot(qi, kj, d) * c->scale;
+            if (j <= off + i) {
+                s = dot(qi, c->k + krow(c, b, j, kh), d) * c->scale;
                 if (s > mx) mx = s;
             }
             S[(size_t)(i - r0) * Bk + (j - j0)] = s;
@@ -386,33 +401,35 @@ static void record_bwd(const bwd_ctx* c, int b, int h, int qb, int kt, int keep,
 
 /* dq for one query block: sum over its kept tiles. */
 static int bwd_dq_block(const bwd_ctx* c, int b, int h, int qb) {
-    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, L = c->L, Bk = c->Bk;
+    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, Bk = c->Bk;
+    const int Lq = c->lq[b], Lk = c->lk[b], off = Lk - Lq;
     const int kh = h / (Hq / Hkv);
     const int r0 = qb * c->Bq;
-    const int r1 = (r0 + c->Bq < L) ? r0 + c->Bq : L;
+    if (r0 >= Lq) return OR_OK;                /* past the sequence's queries */
+    const int r1 = (r0 + c->Bq < Lq) ? r0 + c->Bq : Lq;
     const int nr = r1 - r0;
     double* S = (double*)malloc(sizeof(double) * ((size_t)nr * Bk + nr));
     if (!S) return OR_ENOMEM;
     double* D = S + (size_t)nr * Bk;
     for (int i = r0; i < r1; ++i) {
-        const size_t row = (((size_t)b * L + i) * Hq + h) * d;
+        const size_t row = qrow(c, b, i, h);
         D[i - r0] = dot(c->dout + row, c->o + row, d);
         for (int cc = 0; cc < d; ++cc) c->dq[row + cc] = 0.0;
     }
-    const int kt_last = (r1 - 1) / Bk;
+    const int kt_last = (off + r1 - 1) / Bk;
     for (int kt = 0; kt <= kt_last; ++kt) {
         double lam;
         const int keep = bwd_tile(c, b, h, qb, kt, S, &lam);
         record_bwd(c, b, h, qb, kt, keep, lam);
         if (!keep) continue;
         const int j0 = kt * Bk;
-        const int j1 = (j0 + Bk < L) ? j0 + Bk : L;
+        const int j1 = (j0 + Bk < Lk) ? j0 + Bk : Lk;
         for (int i = r0; i < r1; ++i) {
-            const size_t row = (((size_t)b * L + i) * Hq + h) * d;
-            const double lz = c->lse[((size_t)b * Hq + h) * L + i];
-            for (int j = j0; j < j1 && j <= i; ++j) {
-                const double* vj = c->v + (((size_t)b * L + j) * Hkv + kh) * d;
-                const double* kj = c->k + (((size_t)b * L + j) * Hkv + kh) * d;
+            const size_t row = qrow(c, b, i, h);
+            const double lz = lse_at(c, b, h, i);
+            for (int j = j0; j < j1 && j <= off + i; ++j) {
+                const double* vj = c->v + krow(c, b, j, kh);
+                const double* kj = c->k + krow(c, b, j, kh);
                 const double p = exp(S[(size_t)(i - r0) * Bk + (j - j0)] - lz);
                 const double dp = dot(c->dout + row, vj, d);
                 const double ds = p * (dp - D[i - r0]);
@@ -427,35 +444,39 @@ static int bwd_dq_block(const bwd_ctx* c, int b, int h, int qb) {
 /* dk, dv for one key tile of one KV head: sum over the q heads of the group
  * and over every query block that can see the tile. */
 static int bwd_dkdv_tile(const bwd_ctx* c, int b, int kh, int kt) {
-    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, L = c->L, Bk = c->Bk, Bq = c->Bq;
+    const int d = c->d, Hq = c->Hq, Hkv = c->Hkv, Bk = c->Bk, Bq = c->Bq;
+    const int Lq = c->lq[b], Lk = c->lk[b], off = Lk - Lq;
     const int G = Hq / Hkv;
     const int j0 = kt * Bk;
-    const int j1 = (j0 + Bk < L) ? j0 + Bk : L;
+    if (j0 >= Lk) return OR_OK;                /* past the sequence's keys */
+    const int j1 = (j0 + Bk < Lk) ? j0 + Bk : Lk;
+    const int nQBb = (Lq + Bq - 1) / Bq;
+    const int qb_lo = (j0 - off > 0 ? j0 - off : 0) / Bq;   /* first block with a row seeing key j0 */
     double* S = (double*)malloc(sizeof(double) * ((size_t)Bq * Bk + Bq));
     if (!S) return OR_ENOMEM;
     double* D = S + (size_t)Bq * Bk;
     for (int j = j0; j < j1; ++j) {
-        const size_t kr = (((size_t)b * L + j) * Hkv + kh) * d;
+        const size_t kr = krow(c, b, j, kh);
         for (int cc = 0; cc < d; ++cc) { c->dk[kr + cc] = 0.0; c->dv[kr + cc] = 0.0; }
     }
     for (int g = 0; g < G; ++g) {
         const int h = kh * G + g;
-        for (int qb = j0 / Bq; qb < c->nQB; ++qb) {
+        for (int qb = qb_lo; qb < nQBb; ++qb) {
             const int r0 = qb * Bq;
-            const int r1 = (r0 + Bq < L) ? r0 + Bq : L;
+            const int r1 = (r0 + Bq < Lq) ? r0 + Bq : Lq;
             double lam;
             const int keep = bwd_tile(c, b, h, qb, kt, S, &lam);
             record_bwd(c, b, h, qb, kt, keep, lam);
             if (!keep) continue;
             for (int i = r0; i < r1; ++i) {
-                const size_t row = (((size_t)b * L + i) * Hq + h) * d;
+                const size_t row = qrow(c, b, i, h);
                 D[i - r0] = dot(c->dout + row, c->o + row, d);
             }
             for (int i = r0; i < r1; ++i) {
-                const size_t row = (((size_t)b * L + i) * Hq + h) * d;
-                const double lz = c->lse[((size_t)b * Hq + h) * L + i];
-                for (int j = j0; j < j1 && j <= i; ++j) {
-                    const size_t kr = (((size_t)b * L + j) * Hkv + kh) * d;
+                const size_t row = qrow(c, b, i, h);
+                const double lz = lse_at(c, b, h, i);
+                for (int j = j0; j < j1 && j <= off + i; ++j) {
+                    const size_t kr = krow(c, b, j, kh);
                     const double p = exp(S[(size_t)(i - r0) * Bk + (j - j0)] - lz);
                     const double dp = dot(c->dout + row, c->v + kr, d);
                     const double ds = p * (dp - D[i - r0]);
@@ -474,6 +495,37 @@ static int bwd_dkdv_tile(const bwd_ctx* c, int b, int kh, int kt) {
 /* qunits: ids (b*Hq + h)*nQB + qb whose dq rows are computed (NULL: all).
  * kunits: ids (b*Hkv + kh)*nKT + kt whose dk/dv rows are computed (NULL: all).
  * nq / nk < 0 with a NULL list skips that pass entirely. */
+static int bwd_run(const bwd_ctx* c, const int32_t* qunits, int nq, const int32_t* kunits, int nk, int nthreads) {
+    const int B = c->B, Hq = c->Hq, Hkv = c->Hkv;
+    int err = OR_OK;
+    set_threads(nthreads);
+    const long totq = (long)B * Hq * c->nQB;
+    const long nqq = qunits ? nq : (nq < 0 ? 0 : totq);
+    if (nqq > 0 && !c->dq) return OR_EINVAL;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < nqq; ++u) {
+        long id = qunits ? (long)qunits[u] : u;
+        if (id < 0 || id >= totq) { err = OR_EINVAL; continue; }
+        const int qb = (int)(id % c->nQB);
+        const int bh = (int)(id / c->nQB);
+        int e = bwd_dq_block(c, bh / Hq, bh % Hq, qb);
+        if (e) err = e;
+    }
+    const long totk = (long)B * Hkv * c->nKT;
+    const long nkk = kunits ? nk : (nk < 0 ? 0 : totk);
+    if (nkk > 0 && (!c->dk || !c->dv)) return OR_EINVAL;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < nkk; ++u) {
+        long id = kunits ? (long)kunits[u] : u;
+        if (id < 0 || id >= totk) { err = OR_EINVAL; continue; }
+        const int kt = (int)(id % c->nKT);
+        const int bk = (int)(id / c->nKT);
+        int e = bwd_dkdv_tile(c, bk / Hkv, bk % Hkv, kt);
+        if (e) err = e;
+    }
+    return err;
+}
+
 int mala_oracle_bwd(const double* q, const double* k, const double* v, const double* o,
                     const double* dout, const double* lse,
                     int B, int L, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
@@ -482,38 +534,69 @@ int mala_oracle_bwd(const double* q, const double* k, const double* v, const dou
     if (!q || !k || !v || !o || !dout || !lse) return OR_EINVAL;
     if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return OR_EINVAL;
     if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
+    long* offs = (long*)malloc(sizeof(long) * 2 * (size_t)B);
+    int* lens = (int*)malloc(sizeof(int) * (size_t)B);
+    if (!offs || !lens) { free(offs); free(lens); return OR_ENOMEM; }
+    for (int b = 0; b < B; ++b) {
+        offs[b] = (long)b * L;
+        offs[B + b] = (long)b * Hq * L;
+        lens[b] = L;
+    }
     bwd_ctx c;
     c.q = q; c.k = k; c.v = v; c.o = o; c.dout = dout; c.lse = lse;
-    c.B = B; c.L = L; c.Hq = Hq; c.Hkv = Hkv; c.d = d; c.Bq = Bq; c.Bk = Bk;
+    c.B = B; c.Hq = Hq; c.Hkv = Hkv; c.d = d; c.Bq = Bq; c.Bk = Bk;
     c.nQB = (L + Bq - 1) / Bq; c.nKT = (L + Bk - 1) / Bk;
+    c.qoff = offs; c.koff = offs; c.lseoff = offs + B; c.lq = lens; c.lk = lens; c.lse_hstride = L;
     c.tau = tau; c.scale = 1.0 / sqrt((double)d);
     c.dq = dq; c.dk = dk; c.dv = dv; c.keep = keep; c.margin = margin;
-    int err = OR_OK;
-    set_threads(nthreads);
-    const long totq = (long)B * Hq * c.nQB;
-    const long nqq = qunits ? nq : (nq < 0 ? 0 : totq);
-    if (nqq > 0 && !dq) return OR_EINVAL;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (long u = 0; u < nqq; ++u) {
-        long id = qunits ? (long)qunits[u] : u;
-        if (id < 0 || id >= totq) { err = OR_EINVAL; continue; }
-        const int qb = (int)(id % c.nQB);
-        const int bh = (int)(id / c.nQB);
-        int e = bwd_dq_block(&c, bh / Hq, bh % Hq, qb);
-        if (e) err = e;
+    const int err = bwd_run(&c, qunits, nq, kunits, nk, nthreads);
+    free(offs);
+    free(lens);
+    return err;
+}
+
+/* Variable-length backward over the packed layout of mala_oracle_fwd_varlen:
+ * q, o, dout, dq [total_q][Hq][d]; k, v, dk, dv [total_k][Hkv][d]; lse
+ * [Hq][total_q]; keep/margin [B][Hq][nQB][nKT] with nQB, nKT from the longest
+ * query and key lengths.  Keys of a sequence without queries get dk = dv = 0. */
+int mala_oracle_bwd_varlen(const double* q, const double* k, const double* v, const double* o,
+                           const double* dout, const double* lse, const int32_t* cu_q, const int32_t* cu_k,
+                           int B, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
+                           const int32_t* qunits, int nq, const int32_t* kunits, int nk,
+                           double* dq, double* dk, double* dv, uint8_t* keep, double* margin, int nthreads) {
+    if (!q || !k || !v || !o || !dout || !lse || !cu_q || !cu_k) return OR_EINVAL;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return OR_EINVAL;
+    if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
+    if (cu_q[0] != 0 || cu_k[0] != 0) return OR_EINVAL;
+    int maxq = 0, maxk = 0;
+    for (int b = 0; b < B; ++b) {
+        const int lq = cu_q[b + 1] - cu_q[b], lk = cu_k[b + 1] - cu_k[b];
+        if (lq < 0 || lk < lq) return OR_EINVAL;
+        if (lq > maxq) maxq = lq;
+        if (lk > maxk) maxk = lk;
     }
-    const long totk = (long)B * Hkv * c.nKT;
-    const long nkk = kunits ? nk : (nk < 0 ? 0 : totk);
-    if (nkk > 0 && (!dk || !dv)) return OR_EINVAL;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (long u = 0; u < nkk; ++u) {
-        long id = kunits ? (long)kunits[u] : u;
-        if (id < 0 || id >= totk) { err = OR_EINVAL; continue; }
-        const int kt = (int)(id % c.nKT);
-        const int bk = (int)(id / c.nKT);
-        int e = bwd_dkdv_tile(&c, bk / Hkv, bk % Hkv, kt);
-        if (e) err = e;
+    long* offs = (long*)malloc(sizeof(long) * 3 * (size_t)B);
+    int* lens = (int*)malloc(sizeof(int) * 2 * (size_t)B);
+    if (!offs || !lens) { free(offs); free(lens); return OR_ENOMEM; }
+    for (int b = 0; b < B; ++b) {
+        offs[b] = cu_q[b];
+        offs[B + b] = cu_k[b];
+        offs[2 * B + b] = cu_q[b];
+        lens[b] = cu_q[b + 1] - cu_q[b];
+        lens[B + b] = cu_k[b + 1] - cu_k[b];
     }
+    bwd_ctx c;
+    c.q = q; c.k = k; c.v = v; c.o = o; c.dout = dout; c.lse = lse;
+    c.B = B; c.Hq = Hq; c.Hkv = Hkv; c.d = d; c.Bq = Bq; c.Bk = Bk;
+    c.nQB = maxq > 0 ? (maxq + Bq - 1) / Bq : 1;
+    c.nKT = maxk > 0 ? (maxk + Bk - 1) / Bk : 1;
+    c.qoff = offs; c.koff = offs + B; c.lseoff = offs + 2 * B; c.lq = lens; c.lk = lens + B;
+    c.lse_hstride = cu_q[B];
+    c.tau = tau; c.scale = 1.0 / sqrt((double)d);
+    c.dq = dq; c.dk = dk; c.dv = dv; c.keep = keep; c.margin = margin;
+    const int err = bwd_run(&c, qunits, nq, kunits, nk, nthreads);
+    free(offs);
+    free(lens);
     return err;
 }
 

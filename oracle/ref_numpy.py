@@ -168,6 +168,51 @@ def bwd(q, k, v, o, dout, lse, tau, Bq, Bk):
     return {"dq": dq, "dk": dk, "dv": dv, "keep": keep}
 
 
+def bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, tau, Bq, Bk):
+    """Offline backward rule over packed sequences (queries at the end of
+    their keys; lse [Hq, Tq]).  Returns dq, dk, dv, keep [B,Hq,nQB,nKT]."""
+    Tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    B = len(cu_q) - 1
+    lqs = [cu_q[b + 1] - cu_q[b] for b in range(B)]
+    lks = [cu_k[b + 1] - cu_k[b] for b in range(B)]
+    nQB, nKT = max(1, -(-max(lqs) // Bq)), max(1, -(-max(lks) // Bk))
+    sc = 1.0 / np.sqrt(d)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    keep = np.full((B, Hq, nQB, nKT), 255, np.uint8)
+    for b in range(B):
+        Lq, Lk = lqs[b], lks[b]
+        off = Lk - Lq
+        qs, ks = cu_q[b], cu_k[b]
+        vis = np.arange(Lk)[None, :] <= (off + np.arange(Lq))[:, None]
+        th = _log_thr(tau, off + np.arange(Lq) + 1)
+        for h in range(Hq):
+            kh = h // G
+            Q, K, V = q[qs:qs + Lq, h], k[ks:ks + Lk, kh], v[ks:ks + Lk, kh]
+            S = (Q @ K.T) * sc
+            lz = lse[h, qs:qs + Lq]
+            P = np.where(vis, np.exp(S - lz[:, None]), 0.0)
+            mask = np.zeros((Lq, Lk), bool)
+            for qb in range(-(-Lq // Bq)):
+                r0, r1 = qb * Bq, min(Lq, (qb + 1) * Bq)
+                for kt in range(0, (off + r1 - 1) // Bk + 1):
+                    j0, j1 = kt * Bk, min(Lk, (kt + 1) * Bk)
+                    leg = vis[r0:r1, j0:j1]
+                    x = np.where(leg, S[r0:r1, j0:j1] - lz[r0:r1, None] - th[r0:r1, None], -np.inf)
+                    kp = bool(x.max() >= 0)
+                    keep[b, h, qb, kt] = kp
+                    if kp:
+                        mask[r0:r1, j0:j1] = leg
+            Pm = np.where(mask, P, 0.0)
+            Dr = (dout[qs:qs + Lq, h] * o[qs:qs + Lq, h]).sum(axis=1)
+            dS = Pm * (dout[qs:qs + Lq, h] @ V.T - Dr[:, None])
+            dq[qs:qs + Lq, h] = sc * dS @ K
+            dk[ks:ks + Lk, kh] += sc * dS.T @ Q
+            dv[ks:ks + Lk, kh] += Pm.T @ dout[qs:qs + Lq, h]
+    return {"dq": dq, "dk": dk, "dv": dv, "keep": keep}
+
+
 def decode(q, kc, vc, tau, Bkd):
     """q [B,Hq,d], caches [B,N,Hkv,d].  Returns o, lse, keep [B,Hkv,nT]."""
     B, Hq, d = q.shape

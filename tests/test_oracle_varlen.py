@@ -210,3 +210,103 @@ def test_decode_seqlens_full_length_is_plain_decode():
         assert np.array_equal(a[key], b[key])
     with pytest.raises(ValueError):
         oracle_decode(q, kc, vc, 1.0, 64, seqlens=np.array([0, 200], np.int32))
+
+
+# ------------------------------------------------- backward over packed sequences
+from oracle import oracle_bwd, oracle_bwd_varlen  # noqa: E402
+
+
+def _f64b(inp):
+    return [G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")]
+
+
+@settings(max_examples=40, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(lens, st.sampled_from([1, 8, 32, 64]), st.sampled_from([1, 16, 64]),
+       st.sampled_from([0.0, 0.25, 1.0, 4.0]), st.integers(1, 2), st.integers(0, 10_000))
+def test_varlen_backward_matches_numpy(pairs, Bq, Bk, tau, Gq, seed):
+    lq = [min(a, b) for a, b in pairs]
+    lk = [max(a, b) for a, b in pairs]
+    inp = G.varlen_inputs(400 + seed, lq, lk, 2 * Gq, 2, 8, 0.3, diffuse_kv_heads=(1,))
+    q, k, v, do = _f64b(inp)
+    f = oracle_fwd_varlen(q, k, v, inp["cu_q"], inp["cu_k"], tau, Bq, Bk)
+    a = oracle_bwd_varlen(q, k, v, f["o"], do, f["lse"], inp["cu_q"], inp["cu_k"], tau, Bq, Bk)
+    b = R.bwd_varlen(q, k, v, f["o"], do, f["lse"], inp["cu_q"], inp["cu_k"], tau, Bq, Bk)
+    assert (a["keep"] == b["keep"]).all()
+    for n in ("dq", "dk", "dv"):
+        if a[n].size:
+            assert np.abs(a[n] - b[n]).max() <= 1e-10 * max(1.0, np.abs(b[n]).max()), n
+    # nested support: the backward keeps no tile the forward skipped
+    vis = b["keep"] != 255
+    assert not ((b["keep"] == 1) & (f["keep"] == 0) & vis).any()
+
+
+def test_varlen_backward_tau0_is_autograd():
+    """tau = 0: the gradient of softmax attention with the queries at the end
+    of their keys (torch autograd in fp64 on the CPU, per sequence)."""
+    import torch
+    lq, lk = [70, 1, 0, 33], [70, 90, 20, 100]
+    inp = G.varlen_inputs(410, lq, lk, 4, 2, 16, 0.2)
+    q, k, v, do = _f64b(inp)
+    cu_q, cu_k = inp["cu_q"], inp["cu_k"]
+    f = oracle_fwd_varlen(q, k, v, cu_q, cu_k, 0.0, 32, 16)
+    r = oracle_bwd_varlen(q, k, v, f["o"], do, f["lse"], cu_q, cu_k, 0.0, 32, 16)
+    for b in range(4):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        tq = torch.tensor(q[qs:qe], requires_grad=True)
+        tk = torch.tensor(k[ks:ke], requires_grad=True)
+        tv = torch.tensor(v[ks:ke], requires_grad=True)
+        if qe > qs:
+            S = torch.einsum("ihc,jhc->hij", tq, tk.repeat_interleave(2, dim=1)) / np.sqrt(16)
+            vis = torch.arange(ke - ks)[None, :] <= (ke - ks - (qe - qs) + torch.arange(qe - qs))[:, None]
+            P = torch.softmax(S.masked_fill(~vis, float("-inf")), dim=-1)
+            o = torch.einsum("hij,jhc->ihc", P, tv.repeat_interleave(2, dim=1))
+            (o * torch.tensor(do[qs:qe])).sum().backward()
+            gq, gk, gv = tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+        else:
+            gq = np.zeros_like(q[qs:qe])
+            gk, gv = np.zeros_like(k[ks:ke]), np.zeros_like(v[ks:ke])
+        for name, got, ref in (("dq", r["dq"][qs:qe], gq), ("dk", r["dk"][ks:ke], gk), ("dv", r["dv"][ks:ke], gv)):
+            if ref.size:
+                assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max()), (b, name)
+
+
+@pytest.mark.parametrize("tau", [0.25, 1.0, 4.0])
+def test_varlen_backward_chunk_reproduces_full_dq(tau):
+    """A chunk starting at a multiple of Bq: its dq rows and kept tiles equal the
+    full backward's rows (its dk/dv hold only the chunk's queries' share)."""
+    L, start, Bq, Bk = 300, 128, 64, 32
+    full = G.attn_inputs(420, 1, L, 4, 2, 16, 0.2, diffuse_kv_heads=(1,))
+    fq, fk, fv, fdo = [G.bf16_bits_to_f64(full[x]) for x in ("q", "k", "v", "dout")]
+    ff = oracle_fwd(fq, fk, fv, tau, Bq, Bk)
+    fb = oracle_bwd(fq, fk, fv, ff["o"], fdo, ff["lse"], tau, Bq, Bk)
+    cu_q = np.array([0, L - start], np.int32)
+    cu_k = np.array([0, L], np.int32)
+    cb = oracle_bwd_varlen(fq[0, start:], fk[0], fv[0], ff["o"][0, start:], fdo[0, start:], ff["lse"][0][:, start:],
+                           cu_q, cu_k, tau, Bq, Bk)
+    assert np.array_equal(cb["dq"], fb["dq"][0, start:])
+    nqb = cb["keep"].shape[2]
+    assert np.array_equal(cb["keep"][0], fb["keep"][0][:, start // Bq:start // Bq + nqb])
+
+
+def test_varlen_backward_equal_lengths_match_fixed_layout():
+    B, L, Hq, Hkv, d = 3, 150, 4, 2, 16
+    inp = G.attn_inputs(430, B, L, Hq, Hkv, d, 0.2)
+    q, k, v, do = [G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")]
+    f = oracle_fwd(q, k, v, 1.0, 64, 32)
+    a = oracle_bwd(q, k, v, f["o"], do, f["lse"], 1.0, 64, 32)
+    cu = np.arange(0, (B + 1) * L, L, dtype=np.int32)
+    pk = lambda x: x.reshape(B * L, x.shape[2], d)  # noqa: E731
+    r = oracle_bwd_varlen(pk(q), pk(k), pk(v), pk(f["o"]), pk(do), f["lse"].transpose(1, 0, 2).reshape(Hq, B * L),
+                          cu, cu, 1.0, 64, 32)
+    for n in ("dq", "dk", "dv"):
+        assert np.array_equal(r[n], pk(a[n]))
+    assert np.array_equal(r["keep"], a["keep"])
+
+
+def test_varlen_backward_keys_without_queries_get_zero():
+    inp = G.varlen_inputs(440, [0, 50], [40, 60], 2, 1, 16, 0.2)
+    q, k, v, do = _f64b(inp)
+    f = oracle_fwd_varlen(q, k, v, inp["cu_q"], inp["cu_k"], 1.0, 32, 16)
+    r = oracle_bwd_varlen(q, k, v, f["o"], do, f["lse"], inp["cu_q"], inp["cu_k"], 1.0, 32, 16)
+    assert (r["dk"][:40] == 0).all() and (r["dv"][:40] == 0).all()
+    assert np.isfinite(r["dk"]).all() and np.isfinite(r["dq"]).all()
