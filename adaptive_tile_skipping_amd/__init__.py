@@ -6,7 +6,8 @@ PyTorch supplies device memory and the current HIP stream.  There is no CPU
 fallback: if the library is missing or the tensors are not on a HIP device,
 the calls raise.
 
-Names follow the C ABI: mala_fwd, mala_fwd_varlen, mala_bwd, mala_decode, plus the autograd
+Names follow the C ABI: mala_fwd, mala_fwd_varlen, mala_bwd, mala_bwd_varlen, mala_decode (with optional
+per-sequence cache lengths: mala_decode_varlen), plus the autograd
 wrapper `mala_attention` (saves only q, k, v, o and lse for the backward).
 """
 from __future__ import annotations
@@ -42,8 +43,8 @@ class MalaTileStats(ctypes.Structure):
 
 
 EXPORTS = ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
-           "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
-           "mala_decode_varlen", "mala_status_string", "mala_version")
+           "mala_bwd", "mala_bwd_workspace_size", "mala_bwd_varlen", "mala_bwd_varlen_workspace_size",
+           "mala_decode", "mala_decode_workspace_size", "mala_decode_varlen", "mala_status_string", "mala_version")
 
 _lib = None
 
@@ -74,6 +75,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mala_bwd.argtypes = [MalaT4, MalaT4, MalaT4, MalaT4, MalaT4, P, I, I, I, I, I, F, I, I,
                              MalaT4, MalaT4, MalaT4, P, S, ctypes.POINTER(MalaTileStats), P]
     lib.mala_bwd.restype = I
+    lib.mala_bwd_varlen_workspace_size.argtypes = [I, I, I, I, I, I, I, I, I]
+    lib.mala_bwd_varlen_workspace_size.restype = S
+    lib.mala_bwd_varlen.argtypes = [MalaT3, MalaT3, MalaT3, MalaT3, MalaT3, P, P, P, I, I, I, I, I, I, I, I, F, I, I,
+                                    MalaT3, MalaT3, MalaT3, P, S, ctypes.POINTER(MalaTileStats), P]
+    lib.mala_bwd_varlen.restype = I
     lib.mala_decode_workspace_size.argtypes = [I, I, I, I, I, I]
     lib.mala_decode_workspace_size.restype = S
     lib.mala_decode.argtypes = [P, MalaT4, MalaT4, I, I, I, I, I, F, I, P, P, P, P, P, S, P]
@@ -252,6 +258,43 @@ def mala_bwd(q, k, v, o, dout, lse, tau: float = 1.0, Bq: int = 128, Bk: int = 6
     rc = lib.mala_bwd(_t4(q), _t4(k), _t4(v), _t4(o), _t4(dout), _ptr(lse), B, L, Hq, Hkv, d, float(tau), Bq, Bk,
                       _t4(dq), _t4(dk), _t4(dv), _ptr(ws), ws.numel(), _stats_struct(stats), _stream(q))
     _check("mala_bwd", rc)
+    return dq, dk, dv
+
+
+def bwd_varlen_workspace(B, total_q, max_q, max_k, Hq, Hkv, d, Bq=128, Bk=64, device="cuda"):
+    n = load_library().mala_bwd_varlen_workspace_size(B, total_q, max_q, max_k, Hq, Hkv, d, Bq, Bk)
+    if n == 0:
+        raise MalaError("mala_bwd_varlen_workspace_size", MALA_ERR_UNSUPPORTED, "unsupported shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def mala_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    tau: float = 1.0, Bq: int = 128, Bk: int = 64, dq=None, dk=None, dv=None, ws=None,
+                    stats: dict | None = None):
+    """Backward of mala_fwd_varlen.  Packed q/o/dout [total_q,Hq,d], k/v
+    [total_k,Hkv,d] bf16, lse [Hq,total_q] fp32.  Returns (dq, dk, dv) bf16."""
+    _dev_check(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k)
+    Tq, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or not c.is_contiguous() or c.dim() != 1:
+            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] tensors")
+    B = cu_seqlens_q.numel() - 1
+    if B < 1 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 entries")
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, Tq):
+        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if ws is None:
+        ws = bwd_varlen_workspace(B, Tq, max_seqlen_q, max_seqlen_k, Hq, Hkv, d, Bq, Bk, q.device)
+    lib = load_library()
+    rc = lib.mala_bwd_varlen(_t3(q), _t3(k), _t3(v), _t3(o), _t3(dout), _ptr(lse), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), B, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, d,
+                             float(tau), Bq, Bk, _t3(dq), _t3(dk), _t3(dv), _ptr(ws), ws.numel(),
+                             _stats_struct(stats), _stream(q))
+    _check("mala_bwd_varlen", rc)
     return dq, dk, dv
 
 

@@ -257,6 +257,87 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
 }
 
+size_t mala_bwd_varlen_workspace_size(int B, int total_q, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv,
+                                      int d, int Bq, int Bk) {
+    if (B <= 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
+        !fwd_shape_supported(d, Bq, Bk))
+        return 0;
+    const size_t prow = (size_t)Hq * ((size_t)total_q + (size_t)B * Bq);
+    const size_t nQB = max_seqlen_q > 0 ? (size_t)(max_seqlen_q + Bq - 1) / Bq : 1;
+    const size_t nKT = max_seqlen_k > 0 ? (size_t)(max_seqlen_k + Bk - 1) / Bk : 1;
+    const size_t nwT = ((size_t)(Hq / Hkv) * nQB + 31) / 32;
+    const size_t tb = (size_t)B * Hkv * nKT * nwT * sizeof(uint32_t);
+    const size_t qbb = (size_t)B * Hq * nQB * ((nKT + 31) / 32) * sizeof(uint32_t);
+    return 2 * align256(prow * sizeof(float)) + align256(tb) + align256(qbb);
+}
+
+mala_status mala_bwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, mala_t3 o, mala_t3 dout, const float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int total_q,
+                            int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d, float tau,
+                            int Bq, int Bk, mala_t3 dq, mala_t3 dk, mala_t3 dv, void* ws, size_t ws_bytes,
+                            const mala_tile_stats* bwd_stats, void* stream) {
+    if (B <= 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return MALA_ERR_INVALID_ARG;
+    if (Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv || !tau_ok(tau)) return MALA_ERR_INVALID_ARG;
+    if (max_seqlen_q > max_seqlen_k || max_seqlen_q > total_q || max_seqlen_k > total_k) return MALA_ERR_INVALID_ARG;
+    if (!cu_seqlens_q || !cu_seqlens_k || !lse) return MALA_ERR_INVALID_ARG;
+    const mala_t3 ts[8] = {q, k, v, o, dout, dq, dk, dv};
+    for (const mala_t3& t : ts)
+        if (!t4_ok({t.ptr, 0, t.sl, t.sh}, true)) return MALA_ERR_INVALID_ARG;
+    if (bwd_stats && bwd_stats->omitted_mass) return MALA_ERR_INVALID_ARG;
+    if ((int64_t)total_q * Hq > INT32_MAX / 2 || (int64_t)total_k * Hkv > INT32_MAX / 2 ||
+        (int64_t)total_q + (int64_t)B * Bq > INT32_MAX / 2)
+        return MALA_ERR_INVALID_ARG;
+    if (!fwd_shape_supported(d, Bq, Bk) || B > 65535) return MALA_ERR_UNSUPPORTED;
+    // a query block and one sequence's keys are read through 32-bit buffer ranges
+    const int64_t mk = max_seqlen_k > 0 ? max_seqlen_k : 1;
+    if (((int64_t)Bq * q.sl + d) * 2 > INT32_MAX || ((int64_t)Bq * dout.sl + d) * 2 > INT32_MAX ||
+        ((mk - 1) * k.sl + d) * 2 > INT32_MAX || ((mk - 1) * v.sl + d) * 2 > INT32_MAX)
+        return MALA_ERR_UNSUPPORTED;
+    const size_t need = mala_bwd_varlen_workspace_size(B, total_q, max_seqlen_q, max_seqlen_k, Hq, Hkv, d, Bq, Bk);
+    if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MALA_ERR_WORKSPACE;
+    if (total_k == 0) return MALA_OK;      // no keys, so no queries either: nothing to write
+    BwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = (const uint16_t*)q.ptr; p.k = (const uint16_t*)k.ptr; p.v = (const uint16_t*)v.ptr;
+    p.o = (const uint16_t*)o.ptr; p.dout = (const uint16_t*)dout.ptr; p.lse = lse;
+    p.dq = (uint16_t*)dq.ptr; p.dk = (uint16_t*)dk.ptr; p.dv = (uint16_t*)dv.ptr;
+    p.q_sl = q.sl; p.q_sh = q.sh; p.k_sl = k.sl; p.k_sh = k.sh; p.v_sl = v.sl; p.v_sh = v.sh;
+    p.o_sl = o.sl; p.o_sh = o.sh; p.do_sl = dout.sl; p.do_sh = dout.sh;
+    p.dq_sl = dq.sl; p.dq_sh = dq.sh; p.dk_sl = dk.sl; p.dk_sh = dk.sh; p.dv_sl = dv.sl; p.dv_sh = dv.sh;
+    p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+    p.total_q = total_q; p.total_k = total_k; p.max_q = max_seqlen_q; p.max_k = max_seqlen_k;
+    p.Rq = total_q + B * Bq;
+    p.B = B; p.L = 0; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.nQB = max_seqlen_q > 0 ? (max_seqlen_q + Bq - 1) / Bq : 1;
+    p.nKT = max_seqlen_k > 0 ? (max_seqlen_k + Bk - 1) / Bk : 1;
+    p.Lpad = p.nQB * Bq;
+    char* w = (char*)ws;
+    const size_t prow = (size_t)Hq * p.Rq;
+    p.rowd = (float*)w; w += align256(prow * sizeof(float));
+    p.rowc = (float*)w; w += align256(prow * sizeof(float));
+    p.nwT = (p.G * p.nQB + 31) / 32;
+    p.tbits = (uint32_t*)w; w += align256((size_t)B * Hkv * p.nKT * p.nwT * sizeof(uint32_t));
+    p.qbits = (uint32_t*)w;
+    p.nunits = B * Hkv * p.nKT;
+    p.chunk = 4;
+    p.nslab = (p.nQB * Bq + 255) / 256;
+    p.nunits_scan = p.nslab * B * Hq;
+    p.chunk_scan = pick_chunk(Hq, Hkv);
+    p.nunits_dq = B * Hq * p.nQB;
+    p.chunk_dq = pick_chunk(Hq, Hkv);
+    p.scale = (float)(1.0 / sqrt((double)d));
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+    p.log2_tau = log2_tau(tau);
+    p.nwords = (p.nKT + 31) / 32;
+    if (bwd_stats) {
+        p.kept_tiles = bwd_stats->kept_tiles;
+        p.kept_slots = bwd_stats->kept_slots;
+        p.bits = bwd_stats->decision_bits;
+    }
+    hipError_t e = launch_bwd(p, d, Bq, Bk, (hipStream_t)stream);
+    return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;
+}
+
 size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_dec) {
     if (!dims_ok(B, N, Hq, Hkv, d) || (d != 128 && d != 64) || Bk_dec != 64) return 0;
     const int G = Hq / Hkv;

@@ -54,12 +54,67 @@ constexpr int PRE_ROWS = 64;
 
 }  // namespace
 
+// One sequence as the kernels see it: Lq queries that are the last Lq of its
+// Lk keys (Lq = Lk = L for the fixed-length layout), so query row i sees keys
+// j <= off + i and has L_i = off + i + 1.  Pointers address row 0 of the
+// sequence (head 0); lse / kept_slots entries of (h, i) sit at
+// lse0 + h lse_hs + i, the row terms at row0 + h row_hs + i.  A packed
+// sequence whose lengths are inconsistent with the call's totals and maxima
+// reads as empty (Lq = Lk = 0) and is skipped.
+struct SeqView {
+    int Lq, Lk, off;
+    const uint16_t *q, *k, *v, *o, *dout;
+    uint16_t *dq, *dk, *dv;
+    int64_t lse0, lse_hs, row0, row_hs;
+};
+template <int BQ>
+__device__ __forceinline__ SeqView seq_view(const BwdParams& p, int b) {
+    SeqView s;
+    if (p.cu_q) {
+        const int q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
+        const bool ok = q0 >= 0 && k0 >= 0 && q1 <= p.total_q && k1 <= p.total_k && q1 - q0 >= 0 &&
+                        k1 - k0 >= q1 - q0 && q1 - q0 <= p.max_q && k1 - k0 <= p.max_k;
+        s.Lq = ok ? q1 - q0 : 0;
+        s.Lk = ok ? k1 - k0 : 0;
+        s.q = p.q + (int64_t)q0 * p.q_sl;
+        s.o = p.o + (int64_t)q0 * p.o_sl;
+        s.dout = p.dout + (int64_t)q0 * p.do_sl;
+        s.dq = p.dq + (int64_t)q0 * p.dq_sl;
+        s.k = p.k + (int64_t)k0 * p.k_sl;
+        s.v = p.v + (int64_t)k0 * p.v_sl;
+        s.dk = p.dk + (int64_t)k0 * p.dk_sl;
+        s.dv = p.dv + (int64_t)k0 * p.dv_sl;
+        s.lse0 = q0;
+        s.lse_hs = p.total_q;
+        s.row0 = (int64_t)q0 + (int64_t)b * BQ;
+        s.row_hs = p.Rq;
+    } else {
+        s.Lq = s.Lk = p.L;
+        s.q = p.q + b * p.q_sb;
+        s.o = p.o + b * p.o_sb;
+        s.dout = p.dout + b * p.do_sb;
+        s.dq = p.dq + b * p.dq_sb;
+        s.k = p.k + b * p.k_sb;
+        s.v = p.v + b * p.v_sb;
+        s.dk = p.dk + b * p.dk_sb;
+        s.dv = p.dv + b * p.dv_sb;
+        s.lse0 = (int64_t)b * p.Hq * p.L;
+        s.lse_hs = p.L;
+        s.row0 = (int64_t)b * p.Hq * p.Lpad;
+        s.row_hs = p.Lpad;
+    }
+    s.off = s.Lk - s.Lq;
+    return s;
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
     const int tid = threadIdx.x;
     const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int r0 = rb * PRE_ROWS;
-    const int L = p.L;
+    const SeqView sv = seq_view<BQ>(p, b);
+    const int L = sv.Lq;
+    const int Lrows = (L + BQ - 1) / BQ * BQ;     // the sequence's padded row-term rows
     const int64_t bh = (int64_t)b * p.Hq + h;
     // D_i = dO_i . O_i and LSE in base 2 (4 threads per row; 0 past L)
     {
@@ -67,8 +122,8 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
         const int i = r0 + r;
         float acc = 0.f;
         if (i < L) {
-            const uint16_t* orow = p.o + b * p.o_sb + (int64_t)i * p.o_sl + h * p.o_sh;
-            const uint16_t* grow = p.dout + b * p.do_sb + (int64_t)i * p.do_sl + h * p.do_sh;
+            const uint16_t* orow = sv.o + (int64_t)i * p.o_sl + h * p.o_sh;
+            const uint16_t* grow = sv.dout + (int64_t)i * p.do_sl + h * p.do_sh;
             for (int c = part * 8; c < D; c += 32) {
                 const u32x4 a = *(const u32x4*)(orow + c);
                 const u32x4 g = *(const u32x4*)(grow + c);
@@ -81,11 +136,12 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
-        if (part == 0) {
-            const int64_t ri = bh * p.Lpad + i;
+        if (part == 0 && i < Lrows) {
+            const int64_t ri = sv.row0 + h * sv.row_hs + i;
+            const int64_t li = sv.lse0 + h * sv.lse_hs + i;
             p.rowd[ri] = (i < L) ? acc : 0.f;
-            p.rowc[ri] = (i < L) ? p.lse[bh * L + i] * kLog2e : 0.f;
-            if (p.kept_slots && i < L) p.kept_slots[bh * L + i] = 0;
+            p.rowc[ri] = (i < L) ? p.lse[li] * kLog2e : 0.f;
+            if (p.kept_slots && i < L) p.kept_slots[li] = 0;
         }
     }
     // zero the kept-tile bits (the scan only sets bits)
@@ -133,13 +189,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int b = (u % BH) / p.Hq;
     const int h = (u % BH) % p.Hq;
     const int kh = h / p.G;
-    const int L = p.L;
+    const SeqView sv = seq_view<BQ>(p, b);
+    const int L = sv.Lq, Lk = sv.Lk, off = sv.off;
     const int R0 = slab * 256;
+    if (R0 >= L) return;                     // past the sequence's queries
     const int rw0 = R0 + 64 * w;             // the wave's 64 queries
     const int last = (R0 + 255 < L - 1) ? R0 + 255 : L - 1;
-    const int kt_hi = last / BK;
-    const int kt_w = rw0 / BK;               // the wave's diagonal key tile
+    const int kt_hi = (off + last) / BK;
     const bool live = rw0 < L;
+    // the wave's last key tile with a legal entry, and the key offset of its
+    // first row's last legal key: tiles ending past it need the causal mask
+    const int kt_w = live ? (off + ((rw0 + 63 < L - 1) ? rw0 + 63 : L - 1)) / BK : -1;
+    const int jdiag = off + rw0;
     const float c2 = p.scale_log2;
     const int64_t bh = (int64_t)b * p.Hq + h;
 
@@ -151,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < 2; ++t) {
         const int i = rw0 + 32 * t + l32;
         const bool ok = i < L;
-        const uint16_t* qr = p.q + b * p.q_sb + (int64_t)(ok ? i : 0) * p.q_sl + h * p.q_sh;
+        const uint16_t* qr = sv.q + (int64_t)(ok ? i : 0) * p.q_sl + h * p.q_sh;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
             const u32x4 x = ok ? *(const u32x4*)(qr + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
@@ -160,7 +221,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int ir = rw0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-            seed[t][r] = (ir < L) ? -(p.lse[bh * L + ir] * kLog2e + (p.log2_tau - fast_log2((float)(ir + 1)))) / c2
+            seed[t][r] = (ir < L) ? -(p.lse[sv.lse0 + h * sv.lse_hs + ir] * kLog2e +
+                                      (p.log2_tau - fast_log2((float)(off + ir + 1)))) / c2
                                   : kNegInf;
         }
     }
@@ -173,10 +235,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int r = sl / QCH, pc = sl % QCH;
         koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
     }
-    const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh;
+    const uint16_t* kbase = sv.k + kh * p.k_sh;
     auto copy_tile = [&](int kt, int buf) {
         const int j0 = kt * BK;
-        const int nrow = (L - j0 < BK) ? L - j0 : BK;
+        const int nrow = (Lk - j0 < BK) ? Lk - j0 : BK;
         const __amdgpu_buffer_rsrc_t rk =
             make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((nrow - 1) * p.k_sl + D) * 2));
         unsigned char* dst = reinterpret_cast<unsigned char*>(sK[buf]);
@@ -236,16 +298,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // C[i = query][j = key]: lane = key 32uu + l32, register r = query
             // 32t + 8(r/4) + 4hi + r%4.  Keep iff a legal entry is >= 0.
             float mx = kNegInf;
-            if (kt == kt_w) {
+            if (kt * BK + BK - 1 > jdiag) {
+                // key kt BK + 32uu + l32 is legal for query rw0 + iq iff it is <= off + rw0 + iq
+                const int kk = kt * BK + l32 - jdiag;
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int uu = 0; uu <= t; ++uu)
+                    for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int iq = 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-                            const bool legal = (uu < t) || (l32 <= iq);
-                            mx = fmaxf(mx, legal ? acc[t][uu][r] : kNegInf);
+                            mx = fmaxf(mx, (kk + 32 * uu <= iq) ? acc[t][uu][r] : kNegInf);
                         }
             } else {
                 // four independent chains, then combined
@@ -278,18 +341,20 @@ struct StepCursor {
     uint32_t my, cur;
     uint64_t mask;
     bool dense;
-    int hl, qb, qb_lo, nQB, G;
+    int hl, qb, qb_lo, qb_hi, nQB, G;
 
-    __device__ void init(bool dense_, const uint32_t* words_, int nw_, int qb_lo_, int nQB_, int G_) {
+    // dense: blocks qb_hi down to qb_lo of every q head (none if qb_hi < qb_lo);
+    // nQB is the stride of the step index
+    __device__ void init(bool dense_, const uint32_t* words_, int nw_, int qb_lo_, int qb_hi_, int nQB_, int G_) {
         dense = dense_; words = words_; nw = nw_;
         wb = -64; wi = -65; my = 0u; cur = 0u; mask = 0ull;
-        hl = 0; qb = nQB_ - 1; qb_lo = qb_lo_; nQB = nQB_; G = G_;
+        hl = 0; qb = qb_hi_; qb_lo = qb_lo_; qb_hi = qb_hi_; nQB = nQB_; G = G_;
     }
     __device__ int next(int lane) {
         if (dense) {
-            if (hl >= G) return -1;
+            if (hl >= G || qb_hi < qb_lo) return -1;
             const int idx = hl * nQB + qb;
-            if (--qb < qb_lo) { qb = nQB - 1; ++hl; }
+            if (--qb < qb_lo) { qb = qb_hi; ++hl; }
             return idx;
         }
         for (;;) {
@@ -361,8 +426,10 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int bk = u / p.nKT;
     const int b = bk / p.Hkv;
     const int kh = bk % p.Hkv;
-    const int L = p.L;
+    const SeqView sv = seq_view<BQ>(p, b);
+    const int L = sv.Lq, Lk = sv.Lk, off = sv.off;
     const int j0 = kt * BK;
+    if (j0 >= Lk) return;                   // past the sequence's keys
     const int G = p.G;
     const float c2 = p.scale_log2;
 
@@ -370,9 +437,9 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int jme = j0 + 32 * kw + l32;
     bf16x8 kf[KSTEPS], vf[KSTEPS];
     {
-        const bool ok = jme < L;
-        const uint16_t* kr = p.k + b * p.k_sb + (int64_t)(ok ? jme : 0) * p.k_sl + kh * p.k_sh;
-        const uint16_t* vr = p.v + b * p.v_sb + (int64_t)(ok ? jme : 0) * p.v_sl + kh * p.v_sh;
+        const bool ok = jme < Lk;
+        const uint16_t* kr = sv.k + (int64_t)(ok ? jme : 0) * p.k_sl + kh * p.k_sh;
+        const uint16_t* vr = sv.v + (int64_t)(ok ? jme : 0) * p.v_sl + kh * p.v_sh;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
             const u32x4 a = ok ? *(const u32x4*)(kr + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
@@ -385,7 +452,9 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) { dv[dt] = f32x16{}; dk[dt] = f32x16{}; }
 
-    const int qb_lo = j0 / BQ;
+    // query blocks that can see the tile: from the one holding row j0 - off
+    const int qb_lo = (j0 - off > 0 ? j0 - off : 0) / BQ;
+    const int qb_hi = (L + BQ - 1) / BQ - 1;
     const bool dense = p.log2_tau == kNegInf;   // tau = 0: every legal step is kept
     const uint32_t* trow = p.tbits + ((int64_t)(b * p.Hkv + kh) * p.nKT + kt) * p.nwT;
 
@@ -403,18 +472,17 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     // idx % nQB): its row terms, Q block and dO block, into buffer `buf`
     auto fetch = [&](int idx, int buf) {
         const int f_h = kh * G + idx / p.nQB, f_qb = idx % p.nQB;
-        const int64_t fbh = (int64_t)b * p.Hq + f_h;
         const int row0 = f_qb * BQ;
         // row terms: waves 0..1 copy lse2 / D (BQ floats each)
         if (w < 2 && lane * 4 < BQ) {
-            const float* src = (w == 0 ? p.rowc : p.rowd) + fbh * p.Lpad + row0;
+            const float* src = (w == 0 ? p.rowc : p.rowd) + sv.row0 + f_h * sv.row_hs + row0;
             load16_to_lds(src + 4 * lane, &sRow[buf][w][0]);
         }
         // the blocks' rows through buffer resources ending at row L-1, so the
         // rows past L read as zero without per-lane clamps
         const int nrow = (L - row0 < BQ) ? L - row0 : BQ;
-        const uint16_t* qblk = p.q + b * p.q_sb + (int64_t)row0 * p.q_sl + f_h * p.q_sh;
-        const uint16_t* gblk = p.dout + b * p.do_sb + (int64_t)row0 * p.do_sl + f_h * p.do_sh;
+        const uint16_t* qblk = sv.q + (int64_t)row0 * p.q_sl + f_h * p.q_sh;
+        const uint16_t* gblk = sv.dout + (int64_t)row0 * p.do_sl + f_h * p.do_sh;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qblk, (uint32_t)(((nrow - 1) * p.q_sl + D) * 2));
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(gblk, (uint32_t)(((nrow - 1) * p.do_sl + D) * 2));
         unsigned char* dq_ = sU + buf * (2 * BLK * 2);
@@ -450,7 +518,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     };
 
     StepCursor cc;
-    cc.init(dense, trow, p.nwT, qb_lo, p.nQB, G);
+    cc.init(dense, trow, p.nwT, qb_lo, qb_hi, p.nQB, G);
     int cur = cc.next(lane), nxt = -1;
     if (cur >= 0) {
         fetch(cur, 0);
@@ -498,7 +566,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * g4 + e;
                     const int ig = qb * BQ + ql + e;
-                    const bool legal = (jme <= ig) && (ig < L);
+                    const bool legal = (jme <= off + ig) && (ig < L);
                     const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e])) : 0.f;
                     const float ds = pr * (dp[t][r] - dd[e]);
                     pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
@@ -524,8 +592,9 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         }
         if (p.kept_slots && tid < BQ) {
             const int i = qb * BQ + tid;
-            const int last = i - j0;
-            if (i < L && last >= 0) atomicAdd(p.kept_slots + bh * L + i, (last < BK - 1 ? last : BK - 1) + 1);
+            const int last = off + i - j0;
+            if (i < L && last >= 0)
+                atomicAdd(p.kept_slots + sv.lse0 + h * sv.lse_hs + i, (last < BK - 1 ? last : BK - 1) + 1);
         }
         __syncthreads();                         // every wave is done with buffer `buf`
         const int n2 = (nxt >= 0) ? cc.next(lane) : -1;
@@ -563,11 +632,10 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = j0 + 32 * kw + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (j < L) {
+                if (j < Lk) {
                     const int d = 32 * dt + l32;
-                    p.dv[b * p.dv_sb + (int64_t)j * p.dv_sl + kh * p.dv_sh + d] =
-                        (uint16_t)float_to_bf16_bits(dv[dt][r]);
-                    p.dk[b * p.dk_sb + (int64_t)j * p.dk_sl + kh * p.dk_sh + d] =
+                    sv.dv[(int64_t)j * p.dv_sl + kh * p.dv_sh + d] = (uint16_t)float_to_bf16_bits(dv[dt][r]);
+                    sv.dk[(int64_t)j * p.dk_sl + kh * p.dk_sh + d] =
                         (uint16_t)float_to_bf16_bits(dk[dt][r] * p.scale);
                 }
             }
@@ -602,18 +670,20 @@ void mala_bwd_dq(const BwdParams p) {
     const int b = (int)(bh / p.Hq);
     const int h = (int)(bh % p.Hq);
     const int kh = h / p.G;
-    const int L = p.L;
+    const SeqView sv = seq_view<BQ>(p, b);
+    const int L = sv.Lq, Lk = sv.Lk, off = sv.off;
+    if (qb * BQ >= L) return;                     // past the sequence's queries
     const int i = qb * BQ + 32 * w + l32;         // this lane's query row
     const bool valid = i < L;
     const int rend = (qb * BQ + BQ < L) ? qb * BQ + BQ : L;
-    const int kt_first = (rend - 1) / BK;
+    const int kt_first = (off + rend - 1) / BK;
     const float c2 = p.scale_log2;
 
     // ---- Q and dO fragments (B operands: column = query, 8 consecutive d)
     bf16x8 qf[KSTEPS], gf[KSTEPS];
     {
-        const uint16_t* qr = p.q + b * p.q_sb + (int64_t)(valid ? i : 0) * p.q_sl + h * p.q_sh;
-        const uint16_t* gr = p.dout + b * p.do_sb + (int64_t)(valid ? i : 0) * p.do_sl + h * p.do_sh;
+        const uint16_t* qr = sv.q + (int64_t)(valid ? i : 0) * p.q_sl + h * p.q_sh;
+        const uint16_t* gr = sv.dout + (int64_t)(valid ? i : 0) * p.do_sl + h * p.do_sh;
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
             const u32x4 x = valid ? *(const u32x4*)(qr + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
@@ -622,8 +692,8 @@ void mala_bwd_dq(const BwdParams p) {
             gf[st] = __builtin_bit_cast(bf16x8, y);
         }
     }
-    const float lse2 = valid ? p.rowc[bh * p.Lpad + i] : 0.f;
-    const float dval = valid ? p.rowd[bh * p.Lpad + i] : 0.f;
+    const float lse2 = valid ? p.rowc[sv.row0 + h * sv.row_hs + i] : 0.f;
+    const float dval = valid ? p.rowd[sv.row0 + h * sv.row_hs + i] : 0.f;
 
     // ---- tile copies: buffer resources from the tile to key L-1 (rows past L read zero)
     uint32_t koff[INST], voff[INST];
@@ -634,14 +704,14 @@ void mala_bwd_dq(const BwdParams p) {
         koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ kswz<QCH>(r))) * 2);
         voff[n] = (uint32_t)((r * p.v_sl + 8 * (pc ^ (r % QCH))) * 2);
     }
-    const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh;
-    const uint16_t* vbase = p.v + b * p.v_sb + kh * p.v_sh;
+    const uint16_t* kbase = sv.k + kh * p.k_sh;
+    const uint16_t* vbase = sv.v + kh * p.v_sh;
     auto fetch = [&](int kt, int buf) {
         const int j0 = kt * BK;
         const __amdgpu_buffer_rsrc_t kr =
-            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(L - 1 - j0) * p.k_sl + D) * 2));
+            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(Lk - 1 - j0) * p.k_sl + D) * 2));
         const __amdgpu_buffer_rsrc_t vr =
-            make_rsrc(vbase + (int64_t)j0 * p.v_sl, (uint32_t)(((int64_t)(L - 1 - j0) * p.v_sl + D) * 2));
+            make_rsrc(vbase + (int64_t)j0 * p.v_sl, (uint32_t)(((int64_t)(Lk - 1 - j0) * p.v_sl + D) * 2));
 #pragma unroll
         for (int n = 0; n < INST; ++n) {
             buffer16_to_lds(kr, koff[n], reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
@@ -703,12 +773,12 @@ void mala_bwd_dq(const BwdParams p) {
         }
         // P and dS on legal (causal) entries; dS^T as the B operand of dQ^T
         bf16x8 dsf[4];
-        const int j0 = tcur * BK;
+        const int jo = tcur * BK - off;          // key j0 relative to the row offset: j <= off + i
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = j0 + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const int j = jo + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
                 const bool legal = valid && j <= i;
                 const float pr = legal ? fast_exp2(__builtin_fmaf(sc[sub][r], c2, -lse2)) : 0.f;
                 dsf[2 * sub + (r >> 3)][r & 7] = to_bf16(pr * (dp[sub][r] - dval));
@@ -742,7 +812,7 @@ void mala_bwd_dq(const BwdParams p) {
 
     // ---- dQ = scale * acc, C[i = d][j = query]: registers = 4 consecutive d
     if (valid) {
-        uint16_t* orow = p.dq + b * p.dq_sb + (int64_t)i * p.dq_sl + h * p.dq_sh;
+        uint16_t* orow = sv.dq + (int64_t)i * p.dq_sl + h * p.dq_sh;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll

@@ -59,6 +59,13 @@ struct BwdParams {
     int32_t* kept_slots;
     uint32_t* bits;
     int nwords;
+    // packed variable-length batches (cu_q == nullptr: the fixed-length layout
+    // with strides sb, sl, sh, lse [B, Hq, L] and row terms [B, Hq, Lpad])
+    const int32_t* cu_q;   // [B + 1] device: first query row of each sequence
+    const int32_t* cu_k;   // [B + 1] device: first key row of each sequence
+    int total_q, total_k;  // packed rows; lse / kept_slots are [Hq, total_q]
+    int max_q, max_k;      // longest query and key counts (nQB, nKT derive from them)
+    int Rq;                // total_q + B * Bq: row-term rows per q head (sequence b at cu_q[b] + b Bq)
 };
 
 struct DecParams {

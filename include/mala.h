@@ -167,6 +167,35 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
                      mala_t4 dq, mala_t4 dk, mala_t4 dv, void* ws, size_t ws_bytes,
                      const mala_tile_stats* bwd_stats, void* stream);
 
+/* Bytes of device workspace mala_bwd_varlen needs (row terms with Bq rows of
+ * padding per sequence, and kept-tile bits). */
+size_t mala_bwd_varlen_workspace_size(int B, int total_q, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv,
+                                      int d, int Bq, int Bk);
+
+/* Backward of mala_fwd_varlen over the same packed batch: training on packed
+ * sequences (Lq = Lk per sequence) and on chunks whose queries sit at the end
+ * of their keys.  Same rule as mala_bwd with L_i = Lk - Lq + i + 1 (review
+ * page "Backward: offline sparse probabilities"; summary page, backward
+ * paragraph).
+ *   q, o, dout [total_q, Hq, d]; k, v [total_k, Hkv, d] bf16 (mala_t3); lse
+ *   [Hq, total_q] fp32 as written by mala_fwd_varlen; cu_seqlens_q/_k int32
+ *   [B + 1] in device memory, read by the kernels (a sequence whose lengths
+ *   break the conditions of mala_fwd_varlen is skipped and its gradients are
+ *   left unwritten).
+ *   dq [total_q, Hq, d], dk, dv [total_k, Hkv, d] bf16 outputs; keys of a
+ *   sequence without queries get dk = dv = 0.
+ *   ws: at least mala_bwd_varlen_workspace_size(...) bytes, 256-byte aligned,
+ *   cleared by the call itself.  bwd_stats: as for mala_bwd, with nQB, nKT from
+ *   max_seqlen_q / max_seqlen_k and kept_slots [Hq, total_q].
+ * Errors as for mala_fwd_varlen; UNSUPPORTED also when (Bq * q's (or dout's)
+ * row stride + d) * 2 or ((max_seqlen_k - 1) * k's (or v's) row stride + d) * 2
+ * exceeds INT32_MAX.  total_k = 0 returns MALA_OK and enqueues nothing. */
+mala_status mala_bwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, mala_t3 o, mala_t3 dout, const float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int total_q,
+                            int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d, float tau,
+                            int Bq, int Bk, mala_t3 dq, mala_t3 dk, mala_t3 dv, void* ws, size_t ws_bytes,
+                            const mala_tile_stats* bwd_stats, void* stream);
+
 /* Bytes of device workspace mala_decode needs (tile statistics, score spill,
  * retained-tile lists, partial outputs). */
 size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_dec);

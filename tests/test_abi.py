@@ -20,8 +20,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
-              "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
-              "mala_decode_varlen", "mala_status_string", "mala_version"):
+              "mala_bwd", "mala_bwd_workspace_size", "mala_bwd_varlen", "mala_bwd_varlen_workspace_size",
+              "mala_decode", "mala_decode_workspace_size", "mala_decode_varlen", "mala_status_string",
+              "mala_version"):
         assert n in names
 
 
@@ -184,3 +185,27 @@ def test_decode_varlen_errors():
     bad[6] = 32
     assert lib.mala_decode_varlen(q, t, t, sl, *bad, ctypes.c_void_p(1 << 20), 1 << 30, None) == \
         mala.MALA_ERR_UNSUPPORTED
+
+
+def test_bwd_varlen_workspace_and_errors():
+    lib = mala.load_library()
+    n = lib.mala_bwd_varlen_workspace_size(2, 300, 200, 600, 4, 2, 128, 128, 64)
+    assert n >= 2 * 4 * (300 + 2 * 128) * 4       # D_i and LSE rows with Bq rows of padding per sequence
+    assert lib.mala_bwd_varlen_workspace_size(2, 300, 200, 600, 4, 2, 96, 128, 64) == 0
+    t = _t3()
+    cq, ck, lse = ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288)
+    head = [t, t, t, t, t, lse, cq, ck]
+    mid = [2, 300, 900, 200, 600, 4, 2, 128, 1.0, 128, 64, t, t, t]
+    ok_ws = [ctypes.c_void_p(1 << 20), 1 << 30]
+    assert lib.mala_bwd_varlen(*head, *mid, None, 0, None, None) == mala.MALA_ERR_WORKSPACE
+    bad = list(head)
+    bad[6] = None
+    assert lib.mala_bwd_varlen(*bad, *mid, *ok_ws, None, None) == mala.MALA_ERR_INVALID_ARG
+    bad = list(mid)
+    bad[3] = 700                                      # max_q > max_k
+    assert lib.mala_bwd_varlen(*head, *bad, *ok_ws, None, None) == mala.MALA_ERR_INVALID_ARG
+    bad = list(mid)
+    bad[7] = 96
+    assert lib.mala_bwd_varlen(*head, *bad, *ok_ws, None, None) == mala.MALA_ERR_UNSUPPORTED
+    st = mala.MalaTileStats(None, None, 4096, None)    # omitted mass is forward-only
+    assert lib.mala_bwd_varlen(*head, *mid, *ok_ws, ctypes.pointer(st), None) == mala.MALA_ERR_INVALID_ARG

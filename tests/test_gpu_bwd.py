@@ -202,3 +202,28 @@ def test_bwd_workspace_reuse_and_determinism_of_decisions():
     assert torch.equal(s1["decision_bits"], s2["decision_bits"])
     assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])   # dk, dv: no atomics
     assert (g1[0].float() - g2[0].float()).abs().max().item() <= 1e-2  # dq: atomic order
+
+
+def test_bwd_scan_masks_future_keys_of_the_second_query_half():
+    """Regression: on a diagonal key tile the decision must ignore every future
+    key, including those pairing a wave's second 32 queries with the tile's
+    second 32 keys.  Every query attends almost only to key 0; query 170 is
+    also aligned with key 180, which it may not see.  No legal entry of key
+    tile 2 reaches tau / L_i for query block 1, so the tile is skipped."""
+    L, d = 256, 128
+    rng = np.random.default_rng(7)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    wv = rng.standard_normal(d)
+    wv -= (wv @ u) * u
+    wv /= np.linalg.norm(wv)
+    K = 0.1 * rng.standard_normal((L, d))
+    K[0] = 16 * u
+    K[180] = 16 * wv
+    Q = np.tile(16 * u, (L, 1))
+    Q[170] += 16 * wv
+    V = rng.standard_normal((L, d))
+    dO = rng.standard_normal((L, d))
+    inp = {x: G.round_to_bf16_bits(a)[None, :, None, :] for x, a in (("q", Q), ("k", K), ("v", V), ("dout", dO))}
+    r = run_bwd_case(inp, 1.0, 128, 64, label="masked future key")
+    assert r["dec"]["mismatch"] == 0

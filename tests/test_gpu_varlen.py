@@ -191,3 +191,133 @@ def test_prefill_128k_sampled():
     nQB = 16384 // 128
     blocks = [h * nQB + qb for h, qb in ((0, 0), (1, 37), (2, 64), (3, nQB - 2), (4, nQB - 1))]
     print(run_varlen_case(inp, 1.0, w["Bq"], w["Bk"], blocks=blocks, stats_mode=False, label="prefill_128k"))
+
+
+# ------------------------------------------------------------------ backward
+from oracle import oracle_bwd_varlen  # noqa: E402
+from parity import grad_floors, rel_l2_floored  # noqa: E402
+
+GRAD_TOL = 1e-2
+
+
+def run_bwd_varlen_case(inp, tau, Bq, Bk, label=""):
+    """mala_bwd_varlen as a function of its inputs: both sides get the same
+    (q, k, v, o, dout, lse), with o and lse from the oracle's varlen forward
+    rounded to the stored types (bf16 O, fp32 LSE)."""
+    dev = _dev()
+    cu_q, cu_k = inp["cu_q"], inp["cu_k"]
+    B = len(cu_q) - 1
+    lq, lk = np.diff(cu_q), np.diff(cu_k)
+    max_q, max_k = int(lq.max()), int(lk.max())
+    Tq, Hq, d = inp["q"].shape
+    Hkv = inp["k"].shape[1]
+    Gq = Hq // Hkv
+    print(f"[bwd_varlen] {label} lens_q={lq.tolist()[:8]} lens_k={lk.tolist()[:8]} Hq={Hq} Hkv={Hkv} d={d} "
+          f"tau={tau}", flush=True)
+    f64 = {x: G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")}
+    rf = oracle_fwd_varlen(f64["q"], f64["k"], f64["v"], cu_q, cu_k, tau, Bq, Bk)
+    o_bits = G.round_to_bf16_bits(np.nan_to_num(rf["o"]))
+    lse32 = np.nan_to_num(rf["lse"]).astype(np.float32)
+    q, k, v, do = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v", "dout"))
+    o_in = bf16_tensor(o_bits, dev)
+    lse_in = torch.from_numpy(lse32).to(dev)
+    cq, ck = torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev)
+    bst = mala.make_varlen_stats(B, Hq, Tq, max_q, max_k, Bq, Bk, dev)
+    dq, dk, dv = mala.mala_bwd_varlen(q, k, v, o_in, do, lse_in, cq, ck, max_q, max_k, tau, Bq, Bk, stats=bst)
+    torch.cuda.synchronize()
+    rb = oracle_bwd_varlen(f64["q"], f64["k"], f64["v"], G.bf16_bits_to_f64(o_bits), f64["dout"],
+                           lse32.astype(np.float64), cu_q, cu_k, tau, Bq, Bk)
+    nKT = rb["keep"].shape[3]
+    bkeep = unpack_bits(bst["decision_bits"].cpu().numpy(), nKT)
+    vis = rb["keep"] != 255
+    assert (bkeep[~vis] == 0).all()
+    dec = compare_decisions(np.where(vis, bkeep, 255), rb["keep"], rb["margin"], descending=False)
+    assert dec["nonexempt"] == 0, dec
+    mism = vis & (np.where(vis, bkeep, 0) != np.where(vis, rb["keep"], 0))
+    qbad = np.zeros((Tq, Hq), bool)
+    kbad = np.zeros((inp["k"].shape[0], Hkv), bool)
+    for b_, h_, qb_, kt_ in zip(*np.nonzero(mism)):
+        qbad[cu_q[b_] + qb_ * Bq:min(cu_q[b_ + 1], cu_q[b_] + (qb_ + 1) * Bq), h_] = True
+        kbad[cu_k[b_] + kt_ * Bk:min(cu_k[b_ + 1], cu_k[b_] + (kt_ + 1) * Bk), h_ // Gq] = True
+    got = {n: to_f64(t) for n, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+    scale = 1.0 / np.sqrt(d)
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in range(B):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if ke == ks:
+            continue
+        sq = {x: f64[x][qs:qe][None] for x in ("q", "dout")}
+        sk = {x: f64[x][ks:ke][None] for x in ("k", "v")}
+        rowm = ~qbad[qs:qe][None]
+        for name in ("dq", "dk", "dv"):
+            sl = slice(qs, qe) if name == "dq" else slice(ks, ke)
+            bad = (qbad if name == "dq" else kbad)[sl][None, ..., None]
+            if qe == qs:
+                # no query rows; the keys of such a sequence get exactly zero
+                if name != "dq":
+                    assert (got[name][sl] == 0).all(), name
+                continue
+            fl = grad_floors(name, sq["q"], sk["k"], sk["v"], sq["dout"], rowm, scale)
+            e, _ = rel_l2_floored(np.where(bad, 0.0, got[name][sl][None]), np.where(bad, 0.0, rb[name][sl][None]), fl)
+            worst[name] = max(worst[name], e)
+    print("grad errors", worst, flush=True)
+    for name, e in worst.items():
+        assert e <= GRAD_TOL, (name, e)
+    clean = ~mism.any(-1)
+    kt_g = bst["kept_tiles"].cpu().numpy()
+    assert np.array_equal(kt_g[clean], (rb["keep"] == 1).sum(-1)[clean])
+    return dict(dec=dec, worst=worst)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.25, 1.0, 4.0])
+def test_bwd_varlen_mix(tau):
+    w = G.WORKLOADS["varlen_mix"]
+    inp = G.workload_inputs("varlen_mix")
+    print(run_bwd_varlen_case(inp, tau, w["Bq"], w["Bk"], label="varlen_mix"))
+
+
+@pytest.mark.parametrize("off", [1, 63, 100, 129])
+def test_bwd_varlen_offsets(off):
+    inp = G.varlen_inputs(560 + off, [200, 129, 0], [200 + off, 129 + off, 50], 6, 2, 128, 0.1,
+                          diffuse_kv_heads=(1,))
+    run_bwd_varlen_case(inp, 1.0, 128, 64, label=f"off={off}")
+
+
+def test_bwd_varlen_d64():
+    inp = G.varlen_inputs(570, [64, 1, 65, 130], [64, 200, 65, 777], 4, 1, 64, 0.2)
+    for tau in (0.0, 1.0):
+        run_bwd_varlen_case(inp, tau, 64, 64, label="d64")
+
+
+def test_bwd_chunk_matches_full_backward_bitwise():
+    """With the full backward's own O / LSE rows, a chunk starting at a
+    multiple of Bq gives the full backward's dq rows bit for bit."""
+    dev = _dev()
+    L, start = 3000, 1280
+    full = G.attn_inputs(580, 1, L, 6, 2, 128, 0.1, diffuse_kv_heads=(1,))
+    q, k, v, do = (bf16_tensor(full[x], dev) for x in ("q", "k", "v", "dout"))
+    o, lse = mala.mala_fwd(q, k, v, 1.0, 128, 64)
+    dq_f, _, _ = mala.mala_bwd(q, k, v, o, do, lse, 1.0, 128, 64)
+    cq = torch.tensor([0, L - start], dtype=torch.int32, device=dev)
+    ck = torch.tensor([0, L], dtype=torch.int32, device=dev)
+    dq_c, _, _ = mala.mala_bwd_varlen(q[0, start:].contiguous(), k[0], v[0], o[0, start:].contiguous(),
+                                      do[0, start:].contiguous(), lse[0][:, start:].contiguous(), cq, ck,
+                                      L - start, L, 1.0, 128, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(dq_c, dq_f[0, start:])
+
+
+def test_bwd_varlen_equal_lengths_match_fixed_layout():
+    dev = _dev()
+    inp = G.attn_inputs(590, 3, 700, 4, 2, 128, 0.1)
+    q, k, v, do = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v", "dout"))
+    for tau in (0.0, 1.0):
+        o, lse = mala.mala_fwd(q, k, v, tau, 128, 64)
+        g1 = mala.mala_bwd(q, k, v, o, do, lse, tau, 128, 64)
+        cu = torch.arange(0, 4 * 700, 700, dtype=torch.int32, device=dev)
+        pk = lambda x: x.reshape(2100, x.shape[2], 128)  # noqa: E731
+        g2 = mala.mala_bwd_varlen(pk(q), pk(k), pk(v), pk(o), pk(do), lse.permute(1, 0, 2).reshape(4, 2100).contiguous(),
+                                  cu, cu, 700, 700, tau, 128, 64)
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(pk(a), b)
