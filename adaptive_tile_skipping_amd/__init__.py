@@ -359,3 +359,27 @@ class MalaAttention(torch.autograd.Function):
 
 def mala_attention(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64):
     return MalaAttention.apply(q, k, v, tau, Bq, Bk)
+
+
+class MalaAttentionVarlen(torch.autograd.Function):
+    """Autograd wrapper of the packed variable-length path: forward saves
+    (q, k, v, o, lse) only -- no mask."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, tau, Bq, Bk):
+        o, lse = mala_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, tau, Bq, Bk)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k)
+        ctx.cfg = (max_seqlen_q, max_seqlen_k, tau, Bq, Bk)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, cq, ck = ctx.saved_tensors
+        max_q, max_k, tau, Bq, Bk = ctx.cfg
+        dq, dk, dv = mala_bwd_varlen(q, k, v, o, do.contiguous(), lse, cq, ck, max_q, max_k, tau, Bq, Bk)
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
+def mala_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                          tau: float = 1.0, Bq: int = 128, Bk: int = 64):
+    return MalaAttentionVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, tau, Bq, Bk)

@@ -67,10 +67,10 @@ struct SeqView {
     uint16_t *dq, *dk, *dv;
     int64_t lse0, lse_hs, row0, row_hs;
 };
-template <int BQ>
+template <int BQ, bool VARLEN>
 __device__ __forceinline__ SeqView seq_view(const BwdParams& p, int b) {
     SeqView s;
-    if (p.cu_q) {
+    if constexpr (VARLEN) {
         const int q0 = p.cu_q[b], q1 = p.cu_q[b + 1], k0 = p.cu_k[b], k1 = p.cu_k[b + 1];
         const bool ok = q0 >= 0 && k0 >= 0 && q1 <= p.total_q && k1 <= p.total_k && q1 - q0 >= 0 &&
                         k1 - k0 >= q1 - q0 && q1 - q0 <= p.max_q && k1 - k0 <= p.max_k;
@@ -107,12 +107,12 @@ __device__ __forceinline__ SeqView seq_view(const BwdParams& p, int b) {
     return s;
 }
 
-template <int D, int BQ>
+template <int D, int BQ, bool VARLEN>
 __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
     const int tid = threadIdx.x;
     const int rb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int r0 = rb * PRE_ROWS;
-    const SeqView sv = seq_view<BQ>(p, b);
+    const SeqView sv = seq_view<BQ, VARLEN>(p, b);
     const int L = sv.Lq;
     const int Lrows = (L + BQ - 1) / BQ * BQ;     // the sequence's padded row-term rows
     const int64_t bh = (int64_t)b * p.Hq + h;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void mala_bwd_pre(const BwdParams p) {
 }
 
 // Decision pass of the backward (tau > 0).  See the file comment.
-template <int D, int BQ>
+template <int D, int BQ, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mala_bwd_scan(
     const BwdParams p) {
     constexpr int KSTEPS = D / 16;
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int b = (u % BH) / p.Hq;
     const int h = (u % BH) % p.Hq;
     const int kh = h / p.G;
-    const SeqView sv = seq_view<BQ>(p, b);
+    const SeqView sv = seq_view<BQ, VARLEN>(p, b);
     const int L = sv.Lq, Lk = sv.Lk, off = sv.off;
     const int R0 = slab * 256;
     if (R0 >= L) return;                     // past the sequence's queries
@@ -391,7 +391,7 @@ __device__ __forceinline__ int kswz(int r) {
     return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) % QCH;
 }
 
-template <int D, int BQ>
+template <int D, int BQ, bool VARLEN>
 __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int bk = u / p.nKT;
     const int b = bk / p.Hkv;
     const int kh = bk % p.Hkv;
-    const SeqView sv = seq_view<BQ>(p, b);
+    const SeqView sv = seq_view<BQ, VARLEN>(p, b);
     const int L = sv.Lq, Lk = sv.Lk, off = sv.off;
     const int j0 = kt * BK;
     if (j0 >= Lk) return;                   // past the sequence's keys
@@ -644,7 +644,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
 
 // dQ pass: see the file comment.  dQ_i = scale * sum over kept tiles of
 // dS_ij k_j, with dS = P (dP - D), P = exp(S - LSE).
-template <int D, int BQ>
+template <int D, int BQ, bool VARLEN>
 __global__ __launch_bounds__(BQ / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mala_bwd_dq(const BwdParams p) {
     constexpr int NW = BQ / 32;
@@ -670,7 +670,7 @@ void mala_bwd_dq(const BwdParams p) {
     const int b = (int)(bh / p.Hq);
     const int h = (int)(bh % p.Hq);
     const int kh = h / p.G;
-    const SeqView sv = seq_view<BQ>(p, b);
+    const SeqView sv = seq_view<BQ, VARLEN>(p, b);
     const int L = sv.Lq, Lk = sv.Lk, off = sv.off;
     if (qb * BQ >= L) return;                     // past the sequence's queries
     const int i = qb * BQ + 32 * w + l32;         // this lane's query row
@@ -829,26 +829,31 @@ void mala_bwd_dq(const BwdParams p) {
     }
 }
 
-template <int D, int BQ>
+// The packed variable-length layout is a template parameter, so the kernels of
+// the fixed-length layout see a zero row offset at compile time.
+template <int D, int BQ, bool VARLEN>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((mala_bwd_pre<D, BQ>), dim3(p.Lpad / PRE_ROWS, p.Hq, p.B), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((mala_bwd_pre<D, BQ, VARLEN>), dim3(p.Lpad / PRE_ROWS, p.Hq, p.B), dim3(256), 0, s, p);
     if (p.log2_tau != -INFINITY) {
         const int per_s = 8 * p.chunk_scan;
         const int grid_s = (p.nunits_scan + per_s - 1) / per_s * per_s;
-        hipLaunchKernelGGL((mala_bwd_scan<D, BQ>), dim3(grid_s), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_bwd_scan<D, BQ, VARLEN>), dim3(grid_s), dim3(256), 0, s, p);
     }
     const int per = 8 * p.chunk;
     const int grid = (p.nunits + per - 1) / per * per;
-    hipLaunchKernelGGL((mala_bwd_kernel<D, BQ>), dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((mala_bwd_kernel<D, BQ, VARLEN>), dim3(grid), dim3(256), 0, s, p);
     const int per_q = 8 * p.chunk_dq;
     const int grid_q = (p.nunits_dq + per_q - 1) / per_q * per_q;
-    hipLaunchKernelGGL((mala_bwd_dq<D, BQ>), dim3(grid_q), dim3(BQ / 32 * 64), 0, s, p);
+    hipLaunchKernelGGL((mala_bwd_dq<D, BQ, VARLEN>), dim3(grid_q), dim3(BQ / 32 * 64), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, int d, int Bq, int Bk, hipStream_t s) {
-    if (d == 128 && Bq == 128 && Bk == 64) return launch_bwd_t<128, 128>(p, s);
-    if (d == 64 && Bq == 64 && Bk == 64) return launch_bwd_t<64, 64>(p, s);
+    const bool vl = p.cu_q != nullptr;
+    if (d == 128 && Bq == 128 && Bk == 64)
+        return vl ? launch_bwd_t<128, 128, true>(p, s) : launch_bwd_t<128, 128, false>(p, s);
+    if (d == 64 && Bq == 64 && Bk == 64)
+        return vl ? launch_bwd_t<64, 64, true>(p, s) : launch_bwd_t<64, 64, false>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void mala_v_to_f16_varlen(const FwdParams p) {
 }
 }  // namespace
 
-template <int D, int BQ, int BK, bool STATS>
+template <int D, int BQ, int BK, bool STATS, bool VARLEN>
 __global__ __launch_bounds__(BQ / 32 * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mala_fwd_kernel(const FwdParams p) {
     constexpr int NW = BQ / 32;
@@ -146,7 +146,7 @@ void mala_fwd_kernel(const FwdParams p) {
     uint16_t* obase;
     int64_t rowbase;                             // lse / kept_slots / omitted index of row 0
     int64_t vh_rows;                             // rows of this KV head's fp16 V range
-    if (p.cu_q) {
+    if constexpr (VARLEN) {
         SeqSpan sp;
         const bool ok = seq_span(p, b, sp);
         Lq = ok ? sp.Lq : 0;
@@ -508,12 +508,19 @@ static hipError_t launch_fwd_t(const FwdParams& p, bool stats, hipStream_t s) {
         if (g > 16384) g = 16384;
         hipLaunchKernelGGL((mala_v_to_f16<D>), dim3(g), dim3(256), 0, s, p);
     }
+    // the packed layout is a template parameter: the fixed-length kernels see a
+    // zero row offset at compile time
     const int per = 8 * p.chunk;
     const int grid = (p.nunits + per - 1) / per * per;
-    if (stats)
-        hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, true>), dim3(grid), dim3(NT), 0, s, p);
+    const bool vl = p.cu_q != nullptr;
+    if (stats && vl)
+        hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, true, true>), dim3(grid), dim3(NT), 0, s, p);
+    else if (stats)
+        hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, true, false>), dim3(grid), dim3(NT), 0, s, p);
+    else if (vl)
+        hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, false, true>), dim3(grid), dim3(NT), 0, s, p);
     else
-        hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, false>), dim3(grid), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, false, false>), dim3(grid), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
