@@ -24,8 +24,18 @@ time, kept tiles, retained key slots per query, the omitted probability mass
 (kernel statistics mode) and the relative L2 distance of O from the tau = 0
 output of the same kernel, per head.
 
+`--workload matched_work` compares allocation policies at matched post-score
+work (8K context, 16 q heads over 4 KV heads): MALA's own online decisions at
+tau = 1 set the budget (its retained key slots), and three policies that pick
+key tiles by their finalized reference mass (the exact softmax mass of the
+tile) spend exactly that budget: the same slots per query everywhere
+(static), a per-(head, query block) profile measured on separate calibration
+inputs (head-position), and one ranking over the whole instance (per-instance
+oracle).  Every policy keeps each block's newest (diagonal) tile.  Reported:
+omitted probability mass and relative L2 error of O against dense attention.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tau0]
-                       [--workload step|prefill_128k|tau_sweep]
+                       [--workload step|prefill_128k|tau_sweep|matched_work]
 """
 from __future__ import annotations
 
@@ -53,7 +63,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison")
     ap.add_argument("--cpu-blocks", type=int, default=48, help="query blocks per head in the CPU sample")
-    ap.add_argument("--workload", choices=("step", "prefill_128k", "tau_sweep"), default="step",
+    ap.add_argument("--workload", choices=("step", "prefill_128k", "tau_sweep", "matched_work"), default="step",
                     help="step: training forward+backward and decode (default); prefill_128k: chunked prefill; "
                          "tau_sweep: fidelity and cost against tau")
     ap.add_argument("--taus", type=str, default="0.01,0.05,0.25,1,4,16",
@@ -209,6 +219,219 @@ def main_prefill(args):
     print(json.dumps(out), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Matched-work allocation (summary/review: the matched-work control of the
+# paper's Table 1 -- equal total post-score work, only its distribution over
+# decisions differs).  Everything here is plain torch on per-tile arrays
+# [H, nQB, nKT]; `legal` tiles are those a block visits.
+# ---------------------------------------------------------------------------
+def dense_tile_stats(q, k, v, Bq, Bk):
+    """Exact softmax attention of one sequence, reduced to tiles.
+
+    q [L, Hq, d], k/v [L, Hkv, d] (float tensors, any device).  Returns
+    P-mass per tile mass[H, nQB, nKT], legal key slots per tile cost[H, nQB,
+    nKT] (int64), the dense output o [L, Hq, d] and a function giving, for a
+    tile keep mask, (omitted mass per row [Hq, L], renormalised output)."""
+    import torch
+    L, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    nQB, nKT = -(-L // Bq), -(-L // Bk)
+    dev = q.device
+    i = torch.arange(L, device=dev)
+    causal = i[None, :] <= i[:, None]
+    rows_pad, keys_pad = nQB * Bq, nKT * Bk
+    cost1 = torch.zeros(rows_pad, keys_pad, dtype=torch.int64, device=dev)
+    cost1[:L, :L] = causal.long()
+    cost = cost1.view(nQB, Bq, nKT, Bk).sum(dim=(1, 3))
+    probs = []
+    mass = torch.zeros(Hq, nQB, nKT, dtype=torch.float64, device=dev)
+    o = torch.empty(L, Hq, d, dtype=torch.float64, device=dev)
+    for h in range(Hq):
+        s = (q[:, h].double() @ k[:, h // G].double().T) / d ** 0.5
+        s = s.masked_fill(~causal, float("-inf"))
+        pr = torch.softmax(s, dim=-1)
+        probs.append(pr)
+        pp = torch.zeros(rows_pad, keys_pad, dtype=torch.float64, device=dev)
+        pp[:L, :L] = pr
+        mass[h] = pp.view(nQB, Bq, nKT, Bk).sum(dim=(1, 3))
+        o[:, h] = pr @ v[:, h // G].double()
+
+    def evaluate(keep):
+        om = torch.empty(Hq, L, dtype=torch.float64, device=dev)
+        out = torch.empty_like(o)
+        for h in range(Hq):
+            m = keep[h].repeat_interleave(Bq, 0).repeat_interleave(Bk, 1)[:L, :L]
+            pk = torch.where(m, probs[h], torch.zeros((), dtype=torch.float64, device=dev))
+            om[h] = torch.where(m, torch.zeros((), dtype=torch.float64, device=dev), probs[h]).sum(-1)
+            out[:, h] = (pk @ v[:, h // G].double()) / pk.sum(-1, keepdim=True)
+        return om, out
+
+    return mass, cost.expand(Hq, nQB, nKT).contiguous(), o, evaluate
+
+
+def diagonal_tiles(cost, Bq, Bk, L):
+    """Tiles holding some row's own key, i.e. each row's first legal tile in
+    visit order -- the tiles MALA always keeps and every policy keeps."""
+    import torch
+    H, nQB, nKT = cost.shape
+    qb = torch.arange(nQB, device=cost.device)[:, None]
+    kt = torch.arange(nKT, device=cost.device)[None, :]
+    r0, r1 = qb * Bq, torch.clamp((qb + 1) * Bq, max=L)
+    diag = (kt * Bk <= r1 - 1) & ((kt + 1) * Bk - 1 >= r0)
+    return diag.expand(H, nQB, nKT) & (cost > 0)
+
+
+def alloc_within_blocks(mass, cost, budget, forced):
+    """Per block, the forced tiles plus the tiles of largest mass while the
+    block's slots stay within budget[H, nQB]."""
+    import torch
+    rest = budget - (cost * forced).sum(-1)
+    m = torch.where((cost > 0) & ~forced, mass, torch.full_like(mass, -1.0))
+    order = torch.argsort(m, dim=-1, descending=True)
+    c = torch.gather(torch.where((cost > 0) & ~forced, cost, torch.zeros_like(cost)), -1, order)
+    take = (torch.cumsum(c, -1) <= rest[..., None]) & (torch.gather(m, -1, order) >= 0)
+    keep = torch.zeros_like(forced)
+    keep.scatter_(-1, order, take)
+    return keep | forced
+
+
+def alloc_global(mass, cost, total, forced):
+    """Per-instance oracle: the forced tiles, then one ranking of every other
+    legal tile by mass while the instance's slots stay within total."""
+    import torch
+    rest = total - int((cost * forced).sum())
+    cand = (cost > 0) & ~forced
+    m = torch.where(cand, mass, torch.full_like(mass, -1.0)).flatten()
+    order = torch.argsort(m, descending=True)
+    c = torch.where(cand, cost, torch.zeros_like(cost)).flatten()[order]
+    take = (torch.cumsum(c, 0) <= rest) & (m[order] >= 0)
+    keep = torch.zeros_like(m, dtype=torch.bool)
+    keep[order] = take
+    return keep.view(mass.shape) | forced
+
+
+def static_budget(cost, total, Bq, L):
+    """The same slots per query for every block (water-filled: blocks that
+    cannot use their share give it to the others), summing to total."""
+    import torch
+    nQB = cost.shape[1]
+    rows = torch.tensor([min(Bq, L - qb * Bq) for qb in range(nQB)], dtype=torch.float64, device=cost.device)
+    cap = cost.sum(-1).double()                               # [H, nQB] legal slots
+    lo, hi = 0.0, float(L)
+    for _ in range(60):
+        mid = 0.5 * (lo + hi)
+        if float(torch.minimum(mid * rows, cap).sum()) < total:
+            lo = mid
+        else:
+            hi = mid
+    return torch.minimum(hi * rows, cap).floor().long()
+
+
+def profile_budget(profile, cost, total):
+    """A [H, nQB] slot profile scaled to the instance's total, capped at each
+    block's legal slots."""
+    import torch
+    cap = cost.sum(-1)
+    prof = profile / profile.sum()
+    lo, hi = 0.0, 4.0 * total
+    for _ in range(60):
+        mid = 0.5 * (lo + hi)
+        if float(torch.minimum(prof * mid, cap.double()).sum()) < total:
+            lo = mid
+        else:
+            hi = mid
+    return torch.minimum(prof * hi, cap.double()).floor().long()
+
+
+def main_matched_work(args):
+    """Matched-work allocation study (module docstring)."""
+    import numpy as np
+    import torch
+
+    import adaptive_tile_skipping_amd as mala
+    import mala_gen as G
+
+    dev = torch.device("cuda:0")
+    torch.cuda.init()
+    L, Hq, Hkv, d, Bq, Bk, p = 8192, 16, 4, 128, 128, 64, 0.02
+    tau = args.tau
+    calib, evals = [700, 701, 702, 703], [710, 711, 712, 713]
+
+    def instance(tag):
+        inp = G.attn_inputs(tag, 1, L, Hq, Hkv, d, p, with_dout=False)
+        t = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa
+        q, k, v = (t(inp[x]) for x in ("q", "k", "v"))
+        st = mala.make_stats(1, Hq, L, Bq, Bk, dev)
+        mala.mala_fwd(q, k, v, tau, Bq, Bk, stats=st)
+        torch.cuda.synchronize()
+        nKT = -(-L // Bk)
+        bits = st["decision_bits"][0].long() & 0xFFFFFFFF                     # [Hq, nQB, words]
+        kt = torch.arange(nKT, device=dev)
+        mala_keep = ((bits[..., kt // 32] >> (kt % 32)) & 1).bool()
+        mass, cost, o, evaluate = dense_tile_stats(q[0].float(), k[0].float(), v[0].float(), Bq, Bk)
+        return mala_keep & (cost > 0), mass, cost, o, evaluate
+
+    # two work budgets: MALA's own retained slots at tau, and a fixed 1024
+    # slots per query (the reference policies only)
+    FIXED = 1024 * Hq * L
+    insts = {}
+
+    def budgets(mk, cost):
+        return {"mala": int((cost * mk).sum()), "fixed_1024": FIXED}
+
+    # calibration: the per-instance oracle's mean allocation per (head, block), per budget
+    prof = {}
+    for tag in calib:
+        mk, mass, cost, _, _ = instance(tag)
+        fz = diagonal_tiles(cost, Bq, Bk, L)
+        for bname, total in budgets(mk, cost).items():
+            a = (cost * alloc_global(mass, cost, total, fz)).sum(-1).double()
+            prof[bname] = a if bname not in prof else prof[bname] + a
+        print(f"# calibration input {tag}: MALA {int((cost * mk).sum()) / (Hq * L):.1f} slots/query",
+              file=sys.stderr, flush=True)
+
+    acc = {}
+    for tag in evals:
+        mk, mass, cost, o, evaluate = instance(tag)
+        fz = diagonal_tiles(cost, Bq, Bk, L)
+        for bname, total in budgets(mk, cost).items():
+            keeps = {
+                "static": alloc_within_blocks(mass, cost, static_budget(cost, total, Bq, L), fz),
+                "head_position": alloc_within_blocks(mass, cost, profile_budget(prof[bname], cost, total), fz),
+                "per_instance_oracle": alloc_global(mass, cost, total, fz),
+            }
+            if bname == "mala":
+                keeps["mala"] = mk
+            for name, kp in keeps.items():
+                om, out = evaluate(kp)
+                a = acc.setdefault(bname, {}).setdefault(name, {"omitted": [], "o_num": 0.0, "o_den": 0.0,
+                                                                 "slots": 0})
+                a["omitted"].append(om.flatten())
+                a["o_num"] += float(((out - o) ** 2).sum())
+                a["o_den"] += float((o ** 2).sum())
+                a["slots"] += int((cost * kp).sum())
+        print(f"# input {tag}: MALA budget {int((cost * mk).sum()) / (Hq * L):.1f} slots/query",
+              file=sys.stderr, flush=True)
+    rows = {}
+    for bname, pols in acc.items():
+        rows[bname] = {}
+        for name, a in pols.items():
+            om = torch.cat(a["omitted"])
+            rows[bname][name] = {"omitted_mass_pct": float(om.mean()) * 100,
+                                 "omitted_mass_max_pct": float(om.max()) * 100,
+                                 "o_rel_l2_pct": (a["o_num"] / a["o_den"]) ** 0.5 * 100,
+                                 "slots_per_query": a["slots"] / (len(evals) * Hq * L)}
+    out = {
+        "metric": "matched-work allocation: omitted mass and O rel-L2 (%) at equal post-score work",
+        "value": rows["mala"]["mala"]["omitted_mass_pct"], "unit": "% omitted mass (MALA, at its own work)",
+        "higher_is_better": False, "n_gpus": 1, "dtype": "bf16 inputs, fp64 reference", "data": "synthetic",
+        "config": {"workload": f"B=1 L={L} Hq={Hq} Hkv={Hkv} d={d} Bq={Bq} Bk={Bk} p={p}, tau={tau}; "
+                               f"calibration inputs {calib}, evaluated inputs {evals}"},
+        "budgets": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main_tau_sweep(args):
     """Fidelity and cost against tau over the sweep workload (module docstring)."""
     import numpy as np
@@ -294,6 +517,9 @@ def main():
         return
     if args.workload == "tau_sweep":
         main_tau_sweep(args)
+        return
+    if args.workload == "matched_work":
+        main_matched_work(args)
         return
 
     import numpy as np
