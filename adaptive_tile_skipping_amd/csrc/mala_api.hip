@@ -348,7 +348,7 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
     const size_t nsplit = (size_t)ns;
     const size_t npart = nsplit > (nT + 3) / 4 ? nsplit : (nT + 3) / 4;
     size_t s = 0;
-    s += 2 * align256(grp * G * nT * sizeof(float));          // tmax, tsum
+    s += 2 * align256(grp * G * ((nT + 3) / 4 * 4) * sizeof(float));   // tmax, tsum
     s += align256(grp * G * (size_t)N * sizeof(float));       // spill
     s += align256(grp * nT * sizeof(int32_t));                // klist
     s += align256(grp * sizeof(int32_t));                     // kcount
@@ -388,8 +388,9 @@ mala_status decode_impl(const void* q, mala_t4 kcache, mala_t4 vcache, const int
     p.log2_N = (float)log2((double)N);
     const size_t nT = (size_t)p.nT, grp = (size_t)B * Hkv;
     char* w = (char*)ws;
-    p.tmax = (float*)w; w += align256(grp * G * nT * sizeof(float));
-    p.tsum = (float*)w; w += align256(grp * G * nT * sizeof(float));
+    p.nTp = (p.nT + 3) / 4 * 4;
+    p.tmax = (float*)w; w += align256(grp * G * (size_t)p.nTp * sizeof(float));
+    p.tsum = (float*)w; w += align256(grp * G * (size_t)p.nTp * sizeof(float));
     p.spill = (float*)w; w += align256(grp * G * (size_t)N * sizeof(float));
     p.klist = (int32_t*)w; w += align256(grp * nT * sizeof(int32_t));
     p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));

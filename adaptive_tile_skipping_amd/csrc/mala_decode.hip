@@ -209,8 +209,8 @@ void mala_dec_score(const DecParams p) {
                     }
                 }
             if (hi == 0) {
-                p.tmax[((int64_t)grp * p.nT + t) * p.G + g] = M;
-                p.tsum[((int64_t)grp * p.nT + t) * p.G + g] = sum;
+                p.tmax[((int64_t)grp * p.G + g) * p.nTp + t] = M;
+                p.tsum[((int64_t)grp * p.G + g) * p.nTp + t] = sum;
             }
         }
     };
@@ -307,8 +307,8 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     int32_t* klist = p.klist + (int64_t)grp * p.nT;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int nchunk = (nTb + 63) / 64;
-    const float* tmax = p.tmax + (int64_t)grp * p.nT * G;
-    const float* tsum = p.tsum + (int64_t)grp * p.nT * G;
+    const float* tmax = p.tmax + (int64_t)grp * G * p.nTp;   // row g at g * nTp
+    const float* tsum = p.tsum + (int64_t)grp * G * p.nTp;
 
     // Group reference: the largest tile max of each row.  When every tile max
     // lies within 96 of it and tau/N within 2^+-120, linear masses relative to
@@ -320,18 +320,46 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
         float mx[GP], mn[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) { mx[g] = kNegInf; mn[g] = __builtin_inff(); }
-        // the flat [tile][row] array in 64-lane strides, eight loads in flight per lane
-        const int ntot = nTb * G;
-#pragma unroll 8
-        for (int e = lane; e < ntot; e += 64) {
-            const float v = tmax[e];
-            const int g = e % G;
+        // each row is contiguous: 16-byte loads, U of them per row and lane
+        // issued together before any is used (the score pass wrote these from
+        // other XCDs, so each batch is one far round trip).  The loads are
+        // branch-free -- rows past G and indexes past the row re-read valid
+        // memory and are discarded -- so none waits for another.
+        constexpr int U = GP <= 5 ? 4 : (GP <= 8 ? 2 : 1);
+        const int nq = nTb >> 2;
+        for (int j0 = 0; j0 < nq; j0 += 64 * U) {
+            f32x4 v[U][GP];
 #pragma unroll
-            for (int gg = 0; gg < GP; ++gg)
-                if (gg == g) {
-                    mx[gg] = fmaxf(mx[gg], v);
-                    mn[gg] = fminf(mn[gg], v);
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + 64 * u + lane;
+                const int jc = j < nq ? j : 0;
+#pragma unroll
+                for (int g = 0; g < GP; ++g)
+                    v[u][g] = *(const f32x4*)(tmax + (int64_t)(g < G ? g : 0) * p.nTp + 4 * jc);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = j0 + 64 * u + lane < nq;
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    const float a = fmaxf(fmaxf(v[u][g][0], v[u][g][1]), fmaxf(v[u][g][2], v[u][g][3]));
+                    const float b = fminf(fminf(v[u][g][0], v[u][g][1]), fminf(v[u][g][2], v[u][g][3]));
+                    mx[g] = ok ? fmaxf(mx[g], a) : mx[g];
+                    mn[g] = ok ? fminf(mn[g], b) : mn[g];
                 }
+            }
+        }
+        {
+            const bool ok = lane < nTb - 4 * nq;
+            const int t = ok ? 4 * nq + lane : 0;
+            float v[GP];
+#pragma unroll
+            for (int g = 0; g < GP; ++g) v[g] = tmax[(int64_t)(g < G ? g : 0) * p.nTp + t];
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                mx[g] = ok ? fmaxf(mx[g], v[g]) : mx[g];
+                mn[g] = ok ? fminf(mn[g], v[g]) : mn[g];
+            }
         }
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
@@ -351,21 +379,24 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
     };
 
     // Tile statistics stream through an LDS ring of RING chunk slots, DEPTH
-    // chunks ahead, with buffer-resource copies (reads before tile 0 return 0).
-    // Slot layout: [max | sum][64 * GP] floats, tile t_lo + i at entry i * G + g.
+    // chunks ahead, with buffer-resource copies (reads before tile 0 return 0;
+    // such lanes are invalid anyway).  Slot layout: [max | sum][GP][64]
+    // floats, tile t_lo + i of row g at entry 64 g + i.  Every chunk issues GP
+    // copies per array (rows past G repeat row 0), which the vmcnt waits count.
     constexpr int DEPTH = (63 / (2 * GP)) < 7 ? ((63 / (2 * GP)) < 1 ? 1 : 63 / (2 * GP)) : 7;
     constexpr int RING = DEPTH + 1;
     __shared__ float sStat[RING][2][64 * GP];
-    const __amdgpu_buffer_rsrc_t rmax = make_rsrc(tmax, (uint32_t)(nTb * G * 4));
-    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(tsum, (uint32_t)(nTb * G * 4));
+    const __amdgpu_buffer_rsrc_t rmax = make_rsrc(tmax, (uint32_t)(G * p.nTp * 4));
+    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(tsum, (uint32_t)(G * p.nTp * 4));
     auto issue_chunk = [&](int c) {
         const int t_lo = nTb - 64 * (c + 1);           // may be negative
-        const uint32_t base = (uint32_t)(t_lo * G * 4);
         float* dm = sStat[c % RING][0];
         float* ds = sStat[c % RING][1];
 #pragma unroll
         for (int i = 0; i < GP; ++i) {
-            const uint32_t off = base + (uint32_t)((64 * i + lane) * 4);
+            const int gr = i < G ? i : 0;
+            const int t = t_lo + lane;                  // lanes with t < 0 are never used
+            const uint32_t off = (t >= 0) ? (uint32_t)((gr * p.nTp + t) * 4) : 0xFFFFFFF0u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rmax, (__attribute__((address_space(3))) void*)(dm + 64 * i), 4,
                                                     (int)off, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsum, (__attribute__((address_space(3))) void*)(ds + 64 * i), 4,
@@ -390,8 +421,8 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
             const int i = 63 - lane;                   // t - t_lo
 #pragma unroll
             for (int g = 0; g < GP; ++g) {
-                Mg[g] = (g < G && valid) ? sm[i * G + g] : kNegInf;
-                Sg[g] = (g < G && valid) ? ss[i * G + g] : 0.f;
+                Mg[g] = (g < G && valid) ? sm[64 * g + i] : kNegInf;
+                Sg[g] = (g < G && valid) ? ss[64 * g + i] : 0.f;
             }
         }
         const bool empty0 = l[0] == 0.f;

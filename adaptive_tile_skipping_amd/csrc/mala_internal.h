@@ -85,8 +85,9 @@ struct DecParams {
     float log2_N;
     const int32_t* seqlens; // [B] device cache lengths (1 .. N), or null: every sequence has N keys
     // workspace
-    float* tmax;            // [B, Hkv, G, nT]  tile row max (base 2)
-    float* tsum;            // [B, Hkv, G, nT]  sum 2^(s - tile max)
+    float* tmax;            // [B, Hkv, G, nTp] tile row max (base 2); nTp = nT rounded up to 4
+    float* tsum;            // [B, Hkv, G, nTp] sum 2^(s - tile max)
+    int nTp;
     float* spill;           // [B, Hkv, G, N]   base-2 scores
     int32_t* klist;         // [B, Hkv, nT]     retained tiles, newest first
     int32_t* kcount;        // [B, Hkv]

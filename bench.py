@@ -602,13 +602,16 @@ def main():
     print(f"# tau={tau}: step {ms_step:.3f} ms (fwd {fwd_ms:.3f}, bwd {bwd_ms:.3f}, decode {dec_ms * 1e3:.1f} us)",
           file=sys.stderr, flush=True)
 
-    # decode alone with the caches flushed from the 256 MB Infinity Cache
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    # decode alone with the caches flushed from the 256 MB Infinity Cache: a
+    # 512 MB read before each call (a write would leave dirty lines whose
+    # write-back to HBM lands inside the timed decode)
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def dec_flushed(t, n=10):
         times = []
         for _ in range(n + 2):
-            flush.fill_(1.0)
+            torch.sum(flush, dim=0, out=sink)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(); dec(t); e1.record()
             torch.cuda.synchronize()
