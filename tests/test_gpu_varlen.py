@@ -350,3 +350,32 @@ def test_autograd_wrappers_match_direct_calls():
     assert torch.equal(o.detach(), o2)
     for a, b in zip((qa.grad, ka.grad, va.grad), g2):
         assert torch.equal(a, b)
+
+
+def test_varlen_many_ragged_sequences_fwd_bwd():
+    """40 sequences of random lengths (empty chunks, single tokens, chunks onto
+    caches, fresh prompts) with 5 q heads per KV head."""
+    rng = np.random.default_rng(620)
+    lk = rng.integers(0, 400, size=40)
+    lq = np.array([rng.integers(0, k + 1) if rng.random() < 0.7 else k for k in lk])
+    lq[3], lk[3] = 1, 1
+    lq[5] = 0
+    inp = G.varlen_inputs(620, lq, lk, 10, 2, 128, 0.1, diffuse_kv_heads=(1,))
+    print(run_varlen_case(inp, 1.0, 128, 64, label="40 ragged"))
+    print(run_bwd_varlen_case(inp, 1.0, 128, 64, label="40 ragged"))
+
+
+def test_varlen_larger_max_seqlen_changes_nothing():
+    """max_seqlen_q / _k above the true maxima only add empty work units."""
+    dev = _dev()
+    inp = G.varlen_inputs(630, [200, 77], [300, 500], 4, 2, 128, 0.1)
+    q, k, v, do = (bf16_tensor(inp[x], dev) for x in ("q", "k", "v", "dout"))
+    cq, ck = (torch.from_numpy(inp[x]).to(dev) for x in ("cu_q", "cu_k"))
+    o1, l1 = mala.mala_fwd_varlen(q, k, v, cq, ck, 200, 500, 1.0)
+    o2, l2 = mala.mala_fwd_varlen(q, k, v, cq, ck, 277, 800, 1.0)
+    g1 = mala.mala_bwd_varlen(q, k, v, o1, do, l1, cq, ck, 200, 500, 1.0)
+    g2 = mala.mala_bwd_varlen(q, k, v, o1, do, l1, cq, ck, 277, 800, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
