@@ -619,6 +619,29 @@ def main():
         return float(np.median(times[2:]))
 
     dec_us = dec_flushed(tau) * 1e3
+
+    # the same decode captured once in a HIP graph and replayed (the library
+    # enqueues kernels only), flushed the same way before each replay
+    def dec_graph_us(t, n=10):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            dec(t)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            dec(t)
+        times = []
+        for _ in range(n + 2):
+            torch.sum(flush, dim=0, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(); gr.replay(); e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return float(np.median(times[2:])) * 1e3
+
+    dec_graph = dec_graph_us(tau)
     res0 = None
     if not args.no_tau0:
         ms0, f0, b0, _ = timed_steps(0.0, max(2, min(args.steps, 3)), 1)
@@ -688,6 +711,7 @@ def main():
         "bwd_ms": round(bwd_ms, 4),
         "decode_us_in_step": round(dec_ms * 1e3, 2),
         "decode_us": round(dec_us, 2),
+        "decode_us_graph": round(dec_graph, 2),
         "decode_tokens_per_s": round(DB / (dec_us * 1e-6), 1),
         "decode_hbm_gbs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
         "effective_tflops": {"fwd": round(dense_fwd / (fwd_ms * 1e-3) / 1e12, 2),
