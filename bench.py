@@ -68,8 +68,9 @@ def parse():
                          "tau_sweep: fidelity and cost against tau")
     ap.add_argument("--taus", type=str, default="0.01,0.05,0.25,1,4,16",
                     help="tau values of the tau_sweep workload (tau = 0 is always run as the reference)")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="run two forward launches and a plain 1 GiB device copy, then exit (for PMC passes)")
+    ap.add_argument("--traffic-probe", nargs="?", const="fwd", default=None, choices=("fwd", "decode"),
+                    help="run two forward (or two decode, each after a 512 MB read flush) launches and a plain "
+                         "1 GiB device copy, then exit (for PMC passes)")
     return ap.parse_args()
 
 
@@ -568,16 +569,25 @@ def main():
         mala.mala_decode(qd, kc, vc, t, 64, o=od, lse=lsed, kept_tiles=keptd, ws=dws)
 
     if args.traffic_probe:
-        fwd(tau)
-        torch.cuda.synchronize()
-        fwd(tau)
-        torch.cuda.synchronize()
+        if args.traffic_probe == "fwd":
+            what = "2 x mala_fwd (train_128k, tau=%g)" % tau
+            for _ in range(2):
+                fwd(tau)
+                torch.cuda.synchronize()
+        else:
+            what = "2 x mala_decode (decode_128k, tau=%g), each after a 512 MB read" % tau
+            flush = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+            for _ in range(2):
+                float(flush.sum())
+                dec(tau)
+                torch.cuda.synchronize()
+            del flush
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"traffic_probe": "2 x mala_fwd (train_128k, tau=%g) + 1 GiB device copy" % tau,
-                          "copy_bytes": src.numel() * 4}), flush=True)
+        print(json.dumps({"traffic_probe": what + " + 1 GiB device copy", "copy_bytes": src.numel() * 4}),
+              flush=True)
         return
 
     def timed_steps(t, steps, warmup):
