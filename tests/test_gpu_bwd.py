@@ -200,8 +200,8 @@ def test_bwd_workspace_reuse_and_determinism_of_decisions():
     g2 = mala.mala_bwd(q, k, v, o, do, lse, 1.0, ws=ws, stats=s2)
     torch.cuda.synchronize()
     assert torch.equal(s1["decision_bits"], s2["decision_bits"])
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])   # dk, dv: no atomics
-    assert (g1[0].float() - g2[0].float()).abs().max().item() <= 1e-2  # dq: atomic order
+    # no atomics on any gradient: each is accumulated in registers and written once
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
 
 
 def test_bwd_scan_masks_future_keys_of_the_second_query_half():
@@ -227,3 +227,24 @@ def test_bwd_scan_masks_future_keys_of_the_second_query_half():
     inp = {x: G.round_to_bf16_bits(a)[None, :, None, :] for x, a in (("q", Q), ("k", K), ("v", V), ("dout", dO))}
     r = run_bwd_case(inp, 1.0, 128, 64, label="masked future key")
     assert r["dec"]["mismatch"] == 0
+
+
+def test_bwd_strided_views():
+    """q/k/v as views into a packed [B, L, 3, H, d] buffer, o/dout into a
+    [B, L, 2, H, d] one, and dq/dk/dv written into views of a [B, L, 3, H, d]
+    output: the same gradients as contiguous tensors (B = 2, ragged L)."""
+    dev = _dev()
+    B, L, H, d = 2, 700, 4, 128
+    inp = G.attn_inputs(510, B, L, H, H, d, 0.1)
+    qkv = torch.stack([bf16_tensor(inp[x], dev) for x in ("q", "k", "v")], dim=2)
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    assert not q.is_contiguous()
+    o, lse = mala.mala_fwd(q.contiguous(), k.contiguous(), v.contiguous(), 1.0)
+    od = torch.stack([o, bf16_tensor(inp["dout"], dev)], dim=2)
+    o_v, do_v = od[:, :, 0], od[:, :, 1]
+    out = torch.full((B, L, 3, H, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    g1 = mala.mala_bwd(q, k, v, o_v, do_v, lse, 1.0, dq=out[:, :, 0], dk=out[:, :, 1], dv=out[:, :, 2])
+    g2 = mala.mala_bwd(q.contiguous(), k.contiguous(), v.contiguous(), o_v.contiguous(), do_v.contiguous(), lse, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    assert torch.isfinite(g1[0].float()).all()
