@@ -283,19 +283,14 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
 // no value can leave fp32's normal range (state and tile maxima within 96 of
 // the reference, tau/N within 2^+-120); otherwise the chunk runs the same
 // rounds with log-sum-exp pairs.
+//
+// This single-wave form is the general one; mala_dec_decide below runs it
+// (on its first wave) for groups outside the linear range.
 template <int GP>
-__global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
+__device__ __forceinline__ void decide_one_wave(const DecParams& p, const int Nb) {
     const int grp = blockIdx.x;
     const int lane = threadIdx.x;
     const int G = p.G;
-    const int Nb = dec_len(p, grp / p.Hkv);
-    if (Nb == 0) {                              // skipped sequence: nothing retained
-        if (lane == 0) {
-            p.kcount[grp] = 0;
-            if (p.kept_tiles) p.kept_tiles[grp] = 0;
-        }
-        return;
-    }
     const int nTb = (Nb + BKD - 1) / BKD;      // this sequence's tiles (p.nT is the stride)
     const float theta = p.log2_tau - (p.seqlens ? (float)log2((double)Nb) : p.log2_N);
     const bool lin_ok = theta >= -120.f && theta <= 120.f;
@@ -594,6 +589,190 @@ __global__ __launch_bounds__(64) void mala_dec_decide(const DecParams p) {
         p.lse2[(int64_t)grp * G + lane] = lz2;
         const int b = grp / p.Hkv, kh = grp % p.Hkv;
         p.lse[(int64_t)b * p.Hq + kh * G + lane] = lz2 * kLn2;
+    }
+}
+
+// The sequential decode rule with one wave per q head of the group (lane =
+// tile, 64 tiles per chunk, newest first).  Same rounds, votes and prefix
+// sums as the single-wave form, taken per row: each wave scans only its own
+// row's linear masses, and the rows meet through two 64-bit masks per round
+// in LDS (the candidates: some row votes keep; the survivors: some row still
+// votes keep after the earlier candidates' mass), so a round is a few dozen
+// instructions per wave instead of a loop over every row.  Runs when every
+// row's tile maxima lie within 96 of its largest and tau/N within 2^+-120
+// (the linear range); otherwise the first wave runs the single-wave form.
+// Groups of more than 8 rows run the single-wave form on one wave (16 waves
+// would leave the single-wave form too few registers).
+template <int GP>
+constexpr int decide_threads() { return GP <= 8 ? 64 * GP : 64; }
+
+template <int GP>
+__global__ __launch_bounds__(decide_threads<GP>()) void mala_dec_decide(const DecParams p) {
+    const int grp = blockIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int G = p.G;
+    const int Nb = dec_len(p, grp / p.Hkv);
+    if (Nb == 0) {                              // skipped sequence: nothing retained
+        if (threadIdx.x == 0) {
+            p.kcount[grp] = 0;
+            if (p.kept_tiles) p.kept_tiles[grp] = 0;
+        }
+        return;
+    }
+    if constexpr (GP > 8) {
+        decide_one_wave<GP>(p, Nb);
+        return;
+    }
+    const int nTb = (Nb + BKD - 1) / BKD;      // this sequence's tiles (p.nT is the stride)
+    const float theta = p.log2_tau - (p.seqlens ? (float)log2((double)Nb) : p.log2_N);
+    const bool lin_ok = theta >= -120.f && theta <= 120.f;
+    const float cthr = fast_exp2(theta);
+    const int nchunk = (nTb + 63) / 64;
+    const bool row = w < G;                     // waves past G hold no row (they only meet the barriers)
+    const float* tmax = p.tmax + ((int64_t)grp * G + (row ? w : 0)) * p.nTp;
+    const float* tsum = p.tsum + ((int64_t)grp * G + (row ? w : 0)) * p.nTp;
+
+    // This row's tile statistics stream through an LDS ring, DEPTH chunks
+    // ahead: two 4-byte copies per chunk (max, sum), tile t_lo + i at entry i
+    // (reads before tile 0 return 0; such lanes are invalid).
+    constexpr int DEPTH = 8, RING = DEPTH + 1;
+    __shared__ __attribute__((aligned(16))) float sRow[RING][2][GP][64];
+    __shared__ int sLin[GP];
+    __shared__ uint64_t sCand[2][GP], sKeep[2][GP];
+    const __amdgpu_buffer_rsrc_t rmax = make_rsrc(tmax, (uint32_t)(p.nTp * 4));
+    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(tsum, (uint32_t)(p.nTp * 4));
+    auto issue_row = [&](int c) {
+        const int t = nTb - 64 * (c + 1) + lane;
+        const uint32_t off = (t >= 0) ? (uint32_t)(t * 4) : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rmax, (__attribute__((address_space(3))) void*)(&sRow[c % RING][0][w][0]),
+                                                4, (int)off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsum, (__attribute__((address_space(3))) void*)(&sRow[c % RING][1][w][0]),
+                                                4, (int)off, 0, 0, 0);
+    };
+    if (row)
+        for (int c = 0; c < DEPTH && c < nchunk; ++c) issue_row(c);
+
+    // Row reference: the largest tile max; the row is in the linear range when
+    // its smallest tile max lies within 96 of it.  16-byte loads, 8 per lane
+    // issued together, branch-free (indexes past the row re-read entry 0).
+    float gref = 0.f;
+    {
+        bool lin = true;
+        if (row) {
+            float mx = kNegInf, mn = __builtin_inff();
+            const int nq = nTb >> 2;
+            for (int j0 = 0; j0 < nq; j0 += 64 * 8) {
+                f32x4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + 64 * u + lane;
+                    v[u] = *(const f32x4*)(tmax + 4 * (j < nq ? j : 0));
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const bool ok = j0 + 64 * u + lane < nq;
+                    const float a = fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3]));
+                    const float b = fminf(fminf(v[u][0], v[u][1]), fminf(v[u][2], v[u][3]));
+                    mx = ok ? fmaxf(mx, a) : mx;
+                    mn = ok ? fminf(mn, b) : mn;
+                }
+            }
+            const bool ok = lane < nTb - 4 * nq;
+            const float v = tmax[ok ? 4 * nq + lane : 0];
+            mx = ok ? fmaxf(mx, v) : mx;
+            mn = ok ? fminf(mn, v) : mn;
+            gref = wave_max_all(mx);
+            const float lo = -wave_max_all(-mn);
+            lin = lo >= gref - 96.f;
+        }
+        if (lane == 0) sLin[w] = lin ? 1 : 0;
+    }
+    __syncthreads();
+    bool linear = lin_ok;
+#pragma unroll
+    for (int g = 0; g < GP; ++g) linear = linear && (sLin[g] != 0);
+    if (!linear) {
+        if (w == 0) decide_one_wave<GP>(p, Nb);
+        return;
+    }
+
+    int32_t* klist = p.klist + (int64_t)grp * p.nT;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    float Z = row ? 0.f : 1.f;                  // retained mass of this row, relative to gref
+    bool empty = true;                          // nothing retained yet: the next candidate is kept
+    int kept = 0;
+    int par = 0;                                // mask slots alternate between rounds
+    for (int c = 0; c < nchunk; ++c) {
+        const int t = nTb - 1 - (c * 64 + lane);
+        const bool valid = t >= 0;
+        float a = 0.f, x = 0.f;
+        if (row) {
+            if (c + DEPTH < nchunk) {
+                issue_row(c + DEPTH);
+                wait_vmcnt<2 * DEPTH>();                  // chunk c has landed
+            } else {
+                wait_vmcnt<0>();
+            }
+            const float M = sRow[c % RING][0][w][63 - lane];
+            const float S = sRow[c % RING][1][w][63 - lane];
+            a = valid ? fast_exp2(M - gref) : 0.f;
+            x = valid ? S * a : 0.f;
+        }
+        int pos = 0;
+        while (true) {
+            const bool active = valid && lane >= pos;
+            const uint64_t mine = __ballot(active && (a >= cthr * Z));
+            if (lane == 0) sCand[par][w] = mine;
+            __syncthreads();
+            uint64_t K0 = 0ull;
+#pragma unroll
+            for (int g = 0; g < GP; ++g) K0 |= sCand[par][g];
+            if (empty) K0 = __ballot(active);
+            if (K0 == 0ull) {                             // the rest of the chunk is skipped
+                par ^= 1;
+                break;
+            }
+            const int first = __builtin_ctzll(K0);
+            const bool cand = (K0 >> lane) & 1ull;
+            const float inc = wave_incl_sum(cand ? x : 0.f);
+            // the previous lane's inclusive sum, never inc minus this tile's mass
+            const float exc = wave_shr1(inc);
+            const uint64_t still = __ballot(cand && (a >= cthr * (Z + exc)));
+            if (lane == 0) sKeep[par][w] = still;
+            __syncthreads();
+            uint64_t V1 = empty ? (1ull << first) : 0ull;
+#pragma unroll
+            for (int g = 0; g < GP; ++g) V1 |= sKeep[par][g];
+            par ^= 1;
+            const uint64_t flips = K0 & ~V1;
+            uint64_t acc;
+            if (flips == 0ull) {
+                acc = K0;
+                Z += readlane_f(inc, 63);
+            } else {
+                const int f = __builtin_ctzll(flips);
+                acc = K0 & ((f == 0) ? 0ull : (~0ull >> (64 - f)));
+                Z += readlane_f(exc, f);
+                pos = f + 1;
+            }
+            if (w == 0 && ((acc >> lane) & 1ull)) {
+                klist[kept + __builtin_popcountll(acc & lt_mask)] = t;
+                if (p.bits) atomicOr(p.bits + (int64_t)grp * p.nwords + t / 32, 1u << (t % 32));
+            }
+            kept += __builtin_popcountll(acc);
+            if (acc) empty = false;
+            if (flips == 0ull) break;
+        }
+    }
+    if (threadIdx.x == 0) {
+        p.kcount[grp] = kept;
+        if (p.kept_tiles) p.kept_tiles[grp] = kept;
+    }
+    if (row && lane == 0) {
+        const float lz2 = gref + fast_log2(Z);
+        p.lse2[(int64_t)grp * G + w] = lz2;
+        const int b = grp / p.Hkv, kh = grp % p.Hkv;
+        p.lse[(int64_t)b * p.Hq + kh * G + w] = lz2 * kLn2;
     }
 }
 
@@ -921,7 +1100,7 @@ static hipError_t launch_decode_t(const DecParams& p, bool dense, hipStream_t s)
         int nwg = (tasks + 3) / 4;
         if (nwg > 512) nwg = 512;        // two workgroups (8 waves) per CU
         hipLaunchKernelGGL((mala_dec_score<D>), dim3(nwg), dim3(256), 0, s, p);
-        hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(64), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(decide_threads<GP>()), 0, s, p);
         hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3((p.nT + 3) / 4, ngrp), dim3(256), 0, s, p);
         hipLaunchKernelGGL((mala_dec_sum_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     }

@@ -138,3 +138,24 @@ def test_decode_cache_seqlens_invalid_sequence_skipped():
         torch.cuda.synchronize()
         assert torch.equal(o2[0], o1[0]) and torch.equal(l2[0], l1[0]) and torch.equal(k2[0], k1[0])
         assert (o2[1:] == 5.0).all() and (l2[1:] == -1.0).all() and (k2[1:] == 0).all()
+
+
+def test_decode_wide_score_range():
+    """Tile maxima more than 2^96 apart within a group: the decision leaves the
+    linear-mass form (per-chunk references, then log-sum-exp rounds).  One
+    cache key is strongly aligned with its group's queries, old in sequence
+    0 and recent in sequence 1; tau covers both sides of the linear range."""
+    rng = np.random.default_rng(1500)
+    B, N, Hq, Hkv, d = 2, 3000, 4, 2, 128
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    k = rng.standard_normal((B, N, Hkv, d))
+    v = rng.standard_normal((B, N, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    q[:, :2] += 40.0 * u                       # KV group 0 (q heads 0, 1)
+    k[0, 100, 0] = 25.0 * u
+    k[1, 2900, 0] = 25.0 * u
+    di = {x: G.round_to_bf16_bits(a) for x, a in (("q", q), ("k", k), ("v", v))}
+    for tau in (1e-38, 1.0, 1e6):
+        r = run_decode_case(di, tau, f"wide range tau={tau}")
+        print(tau, r)
