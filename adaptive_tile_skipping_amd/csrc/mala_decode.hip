@@ -606,6 +606,19 @@ __device__ __forceinline__ void decide_one_wave(const DecParams& p, const int Nb
 template <int GP>
 constexpr int decide_threads() { return GP <= 8 ? 64 * GP : 64; }
 
+// Workgroup barrier after this wave's LDS writes have completed.  Unlike
+// __syncthreads() it does not wait for vector-memory operations, so the
+// statistics copies in flight (several chunks ahead) and the tile-list stores
+// stay in flight across the barrier.  The scheduling barriers keep every LDS
+// access on its side.
+__device__ __forceinline__ void lds_only_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    // gfx9 s_waitcnt: lgkmcnt(0), vmcnt and expcnt at their maxima (no wait)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int GP>
 __global__ __launch_bounds__(decide_threads<GP>()) void mala_dec_decide(const DecParams p) {
     const int grp = blockIdx.x;
@@ -723,7 +736,7 @@ __global__ __launch_bounds__(decide_threads<GP>()) void mala_dec_decide(const De
             const bool active = valid && lane >= pos;
             const uint64_t mine = __ballot(active && (a >= cthr * Z));
             if (lane == 0) sCand[par][w] = mine;
-            __syncthreads();
+            lds_only_barrier();
             uint64_t K0 = 0ull;
 #pragma unroll
             for (int g = 0; g < GP; ++g) K0 |= sCand[par][g];
@@ -739,7 +752,7 @@ __global__ __launch_bounds__(decide_threads<GP>()) void mala_dec_decide(const De
             const float exc = wave_shr1(inc);
             const uint64_t still = __ballot(cand && (a >= cthr * (Z + exc)));
             if (lane == 0) sKeep[par][w] = still;
-            __syncthreads();
+            lds_only_barrier();
             uint64_t V1 = empty ? (1ull << first) : 0ull;
 #pragma unroll
             for (int g = 0; g < GP; ++g) V1 |= sKeep[par][g];
