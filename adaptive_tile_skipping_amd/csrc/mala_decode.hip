@@ -806,12 +806,16 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
     const int grp = blockIdx.y;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
     const int G = p.G;
+    const int idx = blockIdx.x * 4 + w;
+    // the list entry is read together with the count (one round trip instead
+    // of two); entries past the count are stale and not used
+    const int tl = p.klist[(int64_t)grp * p.nT + (idx < p.nT ? idx : p.nT - 1)];
     const int cnt = p.kcount[grp];
+    asm volatile("" ::"v"(tl));                 // keep the list load ahead of the count test
     if (blockIdx.x * 4 >= cnt) return;          // the whole workgroup: no partial is read
     const int Nb = dec_len(p, b);
-    const int idx = blockIdx.x * 4 + w;
     const bool has = idx < cnt;
-    const int t = has ? p.klist[(int64_t)grp * p.nT + idx] : 0;
+    const int t = has ? tl : 0;
     const int dc = lane % DC, kg = lane / DC;
     // V rows of this lane's keys (16-byte chunk dc)
     u32x4 vx[KPL];
