@@ -49,6 +49,19 @@ int pick_chunk(int Hq, int Hkv) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Persistent forward workgroups: two per CU of the current device (the CU
+// count is cached per device; concurrent first calls store the same value).
+int forward_slots() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 512;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cached[dev] = 2 * n;
+    return 2 * n;
+}
+
 // Decode splits per (sequence, KV head): enough workgroups (~2048) to keep
 // many cache loads in flight, never more than the cache has tiles.
 void decode_split(int B, int Hkv, int nT, int* nsplit, int* tps) {
@@ -83,7 +96,7 @@ const char* mala_version(void) { return "0.1.0 gfx950"; }
 size_t mala_fwd_workspace_size(int B, int L, int Hq, int Hkv, int d, int Bq, int Bk) {
     if (!dims_ok(B, L, Hq, Hkv, d) || !fwd_shape_supported(d, Bq, Bk)) return 0;
     const size_t Lpad = (size_t)((L + Bk - 1) / Bk) * Bk;
-    return align256((size_t)B * Hkv * Lpad * d * 2);
+    return align256((size_t)B * Hkv * Lpad * d * 2) + 256;      // fp16 V copy, work queues
 }
 
 mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int Hkv, int d,
@@ -115,6 +128,8 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
     p.nwords = (p.nKT + 31) / 32;
     p.vh = (uint16_t*)ws;
     p.Lpad = p.nKT * Bk;
+    p.queue = (int*)((char*)ws + need - 256);
+    p.nslot = forward_slots();
     bool st = false;
     if (stats) {
         p.kept_tiles = stats->kept_tiles;
@@ -129,7 +144,7 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
 
 size_t mala_fwd_varlen_workspace_size(int B, int total_k, int Hkv, int d, int Bq, int Bk) {
     if (B <= 0 || total_k < 0 || Hkv <= 0 || !fwd_shape_supported(d, Bq, Bk)) return 0;
-    return align256(((size_t)total_k + (size_t)B * Bk) * Hkv * d * 2);
+    return align256(((size_t)total_k + (size_t)B * Bk) * Hkv * d * 2) + 256;   // fp16 V copy, work queues
 }
 
 mala_status mala_fwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, const int32_t* cu_seqlens_q,
@@ -170,6 +185,8 @@ mala_status mala_fwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, const int32_t* cu_s
     p.nwords = (p.nKT + 31) / 32;
     p.vh = (uint16_t*)ws;
     p.Rk = total_k + B * Bk;
+    p.queue = (int*)((char*)ws + need - 256);
+    p.nslot = forward_slots();
     bool st = false;
     if (stats) {
         p.kept_tiles = stats->kept_tiles;

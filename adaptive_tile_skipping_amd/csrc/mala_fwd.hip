@@ -44,6 +44,7 @@ namespace {
 // V copy: bf16 [B, L, Hkv, D] -> fp16 [B, Hkv, Lpad, D], zero rows past L.
 template <int D>
 __global__ __launch_bounds__(256) void mala_v_to_f16(const FwdParams p) {
+    if (blockIdx.x == 0 && threadIdx.x < 8) p.queue[threadIdx.x] = 0;   // the forward's work queues
     constexpr int CH = D / 8;
     const int64_t n = (int64_t)p.B * p.Hkv * p.Lpad * CH;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
@@ -83,6 +84,7 @@ __device__ __forceinline__ bool seq_span(const FwdParams& p, int b, SeqSpan& s) 
 // rows up to the next sequence (at least BK of them).  grid.y = sequence.
 template <int D, int BK>
 __global__ __launch_bounds__(256) void mala_v_to_f16_varlen(const FwdParams p) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 8) p.queue[threadIdx.x] = 0;   // the forward's work queues
     constexpr int CH = D / 8;
     const int b = blockIdx.y;
     SeqSpan sp;
@@ -129,8 +131,17 @@ void mala_fwd_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const int u = xcd_unit(blockIdx.x, p.chunk);
-    if (u >= p.nunits) return;
+    // Persistent workgroups (two per CU) take query blocks from eight queues,
+    // one per XCD, each holding that XCD's share of the blocks in the launch
+    // order below (longest first, chunks of blocks sharing K/V tiles together).
+    // A workgroup drains its own XCD's queue, then the others'.  Blocks differ
+    // in cost (kept tiles), and taking work from queues keeps every CU busy
+    // where a launch of one workgroup per block would stall the in-order
+    // dispatch behind the busiest XCD.
+    __shared__ int sUnit;
+    const int xcd = blockIdx.x & 7;
+    int qsel = xcd;                              // next queue to draw from (thread 0)
+    auto run_unit = [&](const int u) {
     const int nbh = p.B * p.Hq;
     const int qb = p.nQB - 1 - u / nbh;          // longest blocks first
     const int bh = u % nbh;
@@ -492,6 +503,29 @@ void mala_fwd_kernel(const FwdParams p) {
         }
     }
     if (tid == 0 && p.kept_tiles) p.kept_tiles[(int64_t)bh * p.nQB + qb] = kept_count;
+    };
+
+    while (true) {
+        if (tid == 0) {
+            int u = -1;
+            while (qsel < xcd + 8) {
+                const int x = qsel & 7;
+                const int sl = atomicAdd(p.queue + x, 1);       // slot sl of XCD x's blocks
+                const int uu = ((sl / p.chunk) * 8 + x) * p.chunk + sl % p.chunk;
+                if (uu < p.nunits) {
+                    u = uu;
+                    break;
+                }
+                ++qsel;                                         // queue x is drained
+            }
+            sUnit = u;
+        }
+        __syncthreads();
+        const int u = sUnit;
+        __syncthreads();                         // every wave has read it before the next write
+        if (u < 0) break;
+        run_unit(u);
+    }
 }
 
 template <int D, int BQ, int BK>
@@ -510,8 +544,8 @@ static hipError_t launch_fwd_t(const FwdParams& p, bool stats, hipStream_t s) {
     }
     // the packed layout is a template parameter: the fixed-length kernels see a
     // zero row offset at compile time
-    const int per = 8 * p.chunk;
-    const int grid = (p.nunits + per - 1) / per * per;
+    // two workgroups per CU, persistent (fewer when there are fewer blocks)
+    const int grid = (p.nunits < p.nslot ? (p.nunits + 7) / 8 * 8 : p.nslot);
     const bool vl = p.cu_q != nullptr;
     if (stats && vl)
         hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, true, true>), dim3(grid), dim3(NT), 0, s, p);

@@ -29,6 +29,8 @@ struct FwdParams {
     int total_q, total_k;  // packed rows; lse / kept_slots / omitted are [Hq, total_q]
     int max_q, max_k;      // longest query and key counts (nQB, nKT derive from them)
     int Rk;                // total_k + B * Bk: V copy rows per KV head (sequence b at cu_k[b] + b Bk)
+    int* queue;            // [8] work queues of the forward kernel (workspace; zeroed by the V copy)
+    int nslot;             // persistent forward workgroups: two per CU
 };
 
 struct BwdParams {
