@@ -142,367 +142,369 @@ void mala_fwd_kernel(const FwdParams p) {
     const int xcd = blockIdx.x & 7;
     int qsel = xcd;                              // next queue to draw from (thread 0)
     auto run_unit = [&](const int u) {
-    const int nbh = p.B * p.Hq;
-    const int qb = p.nQB - 1 - u / nbh;          // longest blocks first
-    const int bh = u % nbh;
-    const int b = bh / p.Hq;
-    const int h = bh % p.Hq;
-    const int kh = h / p.G;
+        const int nbh = p.B * p.Hq;
+        const int qb = p.nQB - 1 - u / nbh;          // longest blocks first
+        const int bh = u % nbh;
+        const int b = bh / p.Hq;
+        const int h = bh % p.Hq;
+        const int kh = h / p.G;
 
-    // The block's sequence: Lq queries that are the last Lq of its Lk keys
-    // (Lq = Lk = L for the fixed-length layout), so query row i sees keys
-    // j <= off + i and has L_i = off + i + 1 visible keys.
-    int Lq, Lk;
-    const uint16_t *qbase, *kbase, *vhbase;
-    uint16_t* obase;
-    int64_t rowbase;                             // lse / kept_slots / omitted index of row 0
-    int64_t vh_rows;                             // rows of this KV head's fp16 V range
-    if constexpr (VARLEN) {
-        SeqSpan sp;
-        const bool ok = seq_span(p, b, sp);
-        Lq = ok ? sp.Lq : 0;
-        Lk = sp.Lk;
-        qbase = p.q + (int64_t)sp.q0 * p.q_sl + h * p.q_sh;
-        obase = p.o + (int64_t)sp.q0 * p.o_sl + h * p.o_sh;
-        kbase = p.k + (int64_t)sp.k0 * p.k_sl + kh * p.k_sh;
-        vhbase = p.vh + ((int64_t)kh * p.Rk + sp.k0 + (int64_t)b * BK) * D;
-        vh_rows = (int64_t)Lk + BK;
-        rowbase = (int64_t)h * p.total_q + sp.q0;
-    } else {
-        Lq = Lk = p.L;
-        qbase = p.q + b * p.q_sb + h * p.q_sh;
-        obase = p.o + b * p.o_sb + h * p.o_sh;
-        kbase = p.k + b * p.k_sb + kh * p.k_sh;
-        vhbase = p.vh + ((int64_t)b * p.Hkv + kh) * p.Lpad * D;
-        vh_rows = p.Lpad;
-        rowbase = (int64_t)bh * p.L;
-    }
-    const int off = Lk - Lq;
-    const int i0 = qb * BQ;
-    if (i0 >= Lq) {
-        // past the sequence's queries: nothing to visit (statistics read as such)
-        if (tid == 0 && p.kept_tiles) p.kept_tiles[(int64_t)bh * p.nQB + qb] = 0;
-        if (tid == 0 && p.bits)
-            for (int wd = 0; wd < p.nwords; ++wd) p.bits[((int64_t)bh * p.nQB + qb) * p.nwords + wd] = 0u;
-        return;
-    }
-    const int i = i0 + 32 * w + l32;             // this lane's query row
-    const bool valid = i < Lq;
-    const int ik = off + i;                      // its last visible key
-    const int rend = (i0 + BQ < Lq) ? i0 + BQ : Lq;
-    const int kt_first = (off + rend - 1) / BK;
-    const bool ragged = (i0 + BQ > Lq);
-
-    // ---- Q fragments (B operand: column = query, 8 consecutive d per lane)
-    bf16x8 qf[KSTEPS];
-    {
-        const uint16_t* qrow = qbase + (int64_t)(valid ? i : 0) * p.q_sl;
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-            u32x4 x = valid ? *(const u32x4*)(qrow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
-            qf[st] = __builtin_bit_cast(bf16x8, x);
+        // The block's sequence: Lq queries that are the last Lq of its Lk keys
+        // (Lq = Lk = L for the fixed-length layout), so query row i sees keys
+        // j <= off + i and has L_i = off + i + 1 visible keys.
+        int Lq, Lk;
+        const uint16_t *qbase, *kbase, *vhbase;
+        uint16_t* obase;
+        int64_t rowbase;                             // lse / kept_slots / omitted index of row 0
+        int64_t vh_rows;                             // rows of this KV head's fp16 V range
+        if constexpr (VARLEN) {
+            SeqSpan sp;
+            const bool ok = seq_span(p, b, sp);
+            Lq = ok ? sp.Lq : 0;
+            Lk = sp.Lk;
+            qbase = p.q + (int64_t)sp.q0 * p.q_sl + h * p.q_sh;
+            obase = p.o + (int64_t)sp.q0 * p.o_sl + h * p.o_sh;
+            kbase = p.k + (int64_t)sp.k0 * p.k_sl + kh * p.k_sh;
+            vhbase = p.vh + ((int64_t)kh * p.Rk + sp.k0 + (int64_t)b * BK) * D;
+            vh_rows = (int64_t)Lk + BK;
+            rowbase = (int64_t)h * p.total_q + sp.q0;
+        } else {
+            Lq = Lk = p.L;
+            qbase = p.q + b * p.q_sb + h * p.q_sh;
+            obase = p.o + b * p.o_sb + h * p.o_sh;
+            kbase = p.k + b * p.k_sb + kh * p.k_sh;
+            vhbase = p.vh + ((int64_t)b * p.Hkv + kh) * p.Lpad * D;
+            vh_rows = p.Lpad;
+            rowbase = (int64_t)bh * p.L;
         }
-    }
+        const int off = Lk - Lq;
+        const int i0 = qb * BQ;
+        if (i0 >= Lq) {
+            // past the sequence's queries: nothing to visit (statistics read as such)
+            if (tid == 0 && p.kept_tiles) p.kept_tiles[(int64_t)bh * p.nQB + qb] = 0;
+            if (tid == 0 && p.bits)
+                for (int wd = 0; wd < p.nwords; ++wd) p.bits[((int64_t)bh * p.nQB + qb) * p.nwords + wd] = 0u;
+            return;
+        }
+        const int i = i0 + 32 * w + l32;             // this lane's query row
+        const bool valid = i < Lq;
+        const int ik = off + i;                      // its last visible key
+        const int rend = (i0 + BQ < Lq) ? i0 + BQ : Lq;
+        const int kt_first = (off + rend - 1) / BK;
+        const bool ragged = (i0 + BQ > Lq);
 
-    // K and V tiles move global -> LDS through buffer resources with fixed
-    // per-lane byte offsets.  K: one resource per tile, starting at the tile and
-    // ending at key L-1, so rows past L read as zero (they are masked by
-    // causality).  V: one resource over the padded fp16 copy, the tile offset
-    // in a scalar (every access stays inside the copy).
-    uint32_t koff[INST], voff[INST];
-#pragma unroll
-    for (int n = 0; n < INST; ++n) {
-        const int sl = (n * NW + w) * 64 + lane;
-        const int r = sl / QCH, pc = sl % QCH;
-        koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
-        voff[n] = (uint32_t)((r * D + 8 * (pc ^ ((4 * (r & 3)) % QCH))) * 2);
-    }
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhbase, (uint32_t)(vh_rows * D * 2));
-    auto copy_k = [&](int kt, int buf) {
-        const int j0 = kt * BK;
-        const __amdgpu_buffer_rsrc_t krs =
-            make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(Lk - 1 - j0) * p.k_sl + D) * 2));
-#pragma unroll
-        for (int n = 0; n < INST; ++n)
-            buffer16_to_lds(krs, koff[n], reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
-    };
-    auto copy_v = [&](int kt, int buf) {
-        const uint32_t so = (uint32_t)(kt * BK * D * 2);
-#pragma unroll
-        for (int n = 0; n < INST; ++n)
-            buffer16_to_lds_s(vrs, voff[n], so, reinterpret_cast<unsigned char*>(sV[buf]) + (n * NW + w) * 64 * 16);
-    };
-    // S^T = K Q^T for the tile in sK[buf]; raw (unscaled) scores
-    auto scores = [&](int buf, f32x16* s) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int row = 32 * sub + l32;
-            s[sub] = f32x16{};
-#pragma unroll
+        // ---- Q fragments (B operand: column = query, 8 consecutive d per lane)
+        bf16x8 qf[KSTEPS];
+        {
+            const uint16_t* qrow = qbase + (int64_t)(valid ? i : 0) * p.q_sl;
+    #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) {
-                const int pc = (2 * st + hi) ^ (row % QCH);
-                const bf16x8 a = *(const bf16x8*)(&sK[buf][row * D + 8 * pc]);
-                s[sub] = mfma32x32x16(a, qf[st], s[sub]);
+                u32x4 x = valid ? *(const u32x4*)(qrow + 16 * st + 8 * hi) : u32x4{0, 0, 0, 0};
+                qf[st] = __builtin_bit_cast(bf16x8, x);
             }
         }
-    };
-    // causal mask (diagonal / ragged tiles) and raw row max
-    auto mask_max = [&](int kt, f32x16* s) -> float {
-        float M = kNegInf;
-        const bool need = ragged || (kt * BK + BK - 1 > off + i0);
-        if (need) {
-            const int lim = valid ? (ik - kt * BK) : -1;
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int jj = 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    s[sub][r] = (jj <= lim) ? s[sub][r] : kNegInf;
-                }
+
+        // K and V tiles move global -> LDS through buffer resources with fixed
+        // per-lane byte offsets.  K: one resource per tile, starting at the tile and
+        // ending at key L-1, so rows past L read as zero (they are masked by
+        // causality).  V: one resource over the padded fp16 copy, the tile offset
+        // in a scalar (every access stays inside the copy).
+        uint32_t koff[INST], voff[INST];
+    #pragma unroll
+        for (int n = 0; n < INST; ++n) {
+            const int sl = (n * NW + w) * 64 + lane;
+            const int r = sl / QCH, pc = sl % QCH;
+            koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
+            voff[n] = (uint32_t)((r * D + 8 * (pc ^ ((4 * (r & 3)) % QCH))) * 2);
         }
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) M = fmaxf(M, s[sub][r]);
-        return wave_max_pair(M);
-    };
-    // O^T += V^T P^T with V^T fragments from the transposing LDS read
-    auto pv = [&](int buf, const f16x8* pb, f32x16* acc) {
-        const int j16 = lane & 15;
-        const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                u32x2 half2x[2];
-#pragma unroll
-                for (int rd = 0; rd < 2; ++rd) {
-                    const int row = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
-                    const int col = 32 * dt + dsel;
-                    const int phys = ((col >> 3) ^ ((4 * (row & 3)) % QCH)) * 8 + (col & 7);
-                    half2x[rd] = lds_read_tr16(&sV[buf][0] + row * D + phys);
-                }
-                // whole-dword assembly of the operand (element-wise 16-bit inserts
-                // of the transposed results are not reliable with this compiler)
-                const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
-                acc[dt] = mfma32x32x16_f16(__builtin_bit_cast(f16x8, w4), pb[ks], acc[dt]);
-            }
-        }
-    };
-
-    // ---- per-row state (this lane's query; lanes l and l^32 hold identical copies)
-    const float c2 = p.scale_log2;
-    float m2 = kNegInf;          // running max of retained base-2 scores
-    float lsum = 0.f;            // retained sum, shifted by m2
-    float thr = kNegInf;         // cached keep threshold m2 + log2(lsum) + theta
-    const float theta = p.log2_tau - fast_log2((float)(ik + 1));
-    float om = kNegInf, ol = 0.f;            // omitted mass (statistics mode)
-    int slots = 0;
-    f32x16 acc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-
-    int kept_count = 0;
-    uint32_t bitword = 0;
-    const bool want_bits = p.bits != nullptr;
-    uint32_t* bitrow = want_bits ? p.bits + ((int64_t)bh * p.nQB + qb) * p.nwords : nullptr;
-    if (want_bits && tid == 0) {
-        for (int wd = kt_first / 32 + 1; wd < p.nwords; ++wd) bitrow[wd] = 0u;
-    }
-
-    // ---- prologue
-    copy_k(kt_first, kt_first & 1);
-    if (kt_first >= 1) copy_k(kt_first - 1, (kt_first - 1) & 1);
-    wait_all_then_barrier();
-    f32x16 sA[2], sB[2];         // scores: of the tile being decided / of the next tile
-    f16x8 pp[4];                 // P of the pending tile, then of the tile being kept
-    scores(kt_first & 1, sA);
-    float Mraw = mask_max(kt_first, sA);
-
-    bool pending = false;        // P.V of the last kept tile not yet accumulated
-    int pend_buf = 0;
-    float pend_alpha = 1.f;
-
-    // One tile: decide tile kt from (m, l); then, in one straight-line block per
-    // (keep, pending) case, issue the P.V MFMAs of the pending tile, then the
-    // score MFMAs of tile kt-1 interleaved with the softmax of tile kt (whose P
-    // reuses the registers the P.V just consumed).  scur/snext swap roles from
-    // one tile to the next (the loop is unrolled by two), so no copies.
-    auto tile = [&](int kt, f32x16* scur, f32x16* snext) {
-        const int buf = kt & 1;
-        const float M = Mraw * c2;
-        const bool has = Mraw > kNegInf;
-        const bool vote = has && (lsum == 0.f || M >= thr);
-        const bool wave_any = __ballot(vote) != 0ull;
-        if (lane == 0) sFlag[buf][w] = wave_any ? 1 : 0;
-        wait_all_then_barrier();                 // K(kt-1) and V of the pending tile have landed
-        int kflag = 0;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) kflag |= sFlag[buf][ww];
-        // identical in every lane: make the branches below scalar
-        const bool keep = __builtin_amdgcn_readfirstlane(kflag) != 0;
-
-        if (keep) copy_v(kt, buf);
-        if (kt >= 2) copy_k(kt - 2, buf);
-        if (pending && __ballot(pend_alpha != 1.f) != 0ull) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
-        }
-        float mn = m2, muse = 0.f, alpha = 1.f;
-        if (keep) {
-            mn = fmaxf(m2, M);
-            muse = (mn == kNegInf) ? 0.f : mn;
-            alpha = fast_exp2(m2 - muse);
-        }
-        float ps0 = 0.f, ps1 = 0.f;
-        const uint16_t* kb = sK[buf ^ 1];        // K(kt-1); stale but harmless when kt == 0
-        const uint16_t* vb = sV[pend_buf];
-        // P.V of the pending tile (MFMA and LDS only).  Operand reads run two
-        // MFMAs ahead through small register rings, and a scheduling barrier
-        // closes every step, so the compiler keeps this order instead of
-        // hoisting every LDS read.
-        if (pending) {
-            constexpr int NPV = 4 * DT;
-            const int j16 = lane & 15;
-            const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
-            auto vread = [&](int s2) -> f16x8 {
-                const int dt = s2 % DT, ks = s2 / DT;
-                u32x2 half2x[2];
-#pragma unroll
-                for (int rd = 0; rd < 2; ++rd) {
-                    const int vrow = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
-                    const int col = 32 * dt + dsel;
-                    const int phys = ((col >> 3) ^ ((4 * (vrow & 3)) % QCH)) * 8 + (col & 7);
-                    half2x[rd] = lds_read_tr16(vb + vrow * D + phys);
-                }
-                // whole-dword assembly of the operand (element-wise 16-bit inserts
-                // of the transposed results are not reliable with this compiler)
-                const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
-                return __builtin_bit_cast(f16x8, w4);
-            };
-            f16x8 vq[3];
-            vq[0] = vread(0);
-            vq[1] = vread(1);
-#pragma unroll
-            for (int s2 = 0; s2 < NPV; ++s2) {
-                if (s2 + 2 < NPV) vq[(s2 + 2) % 3] = vread(s2 + 2);
-                const int dt = s2 % DT, ks = s2 / DT;
-                acc[dt] = mfma32x32x16_f16(vq[s2 % 3], pp[ks], acc[dt]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // Scores of tile kt-1, with the softmax of tile kt (when kept) spread
-        // over the MFMA steps; its P reuses the registers the P.V consumed.
-        auto body = [&](auto keep_c) {
-            constexpr bool KEEP = decltype(keep_c)::value;
-            constexpr int NS = 2 * KSTEPS;       // score MFMAs of one tile
-            constexpr int EPS = 32 / NS;         // softmax elements per score MFMA
-            auto kread = [&](int s2) -> bf16x8 {
-                const int sub = s2 & 1, st = s2 >> 1;
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhbase, (uint32_t)(vh_rows * D * 2));
+        auto copy_k = [&](int kt, int buf) {
+            const int j0 = kt * BK;
+            const __amdgpu_buffer_rsrc_t krs =
+                make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(Lk - 1 - j0) * p.k_sl + D) * 2));
+    #pragma unroll
+            for (int n = 0; n < INST; ++n)
+                buffer16_to_lds(krs, koff[n], reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
+        };
+        auto copy_v = [&](int kt, int buf) {
+            const uint32_t so = (uint32_t)(kt * BK * D * 2);
+    #pragma unroll
+            for (int n = 0; n < INST; ++n)
+                buffer16_to_lds_s(vrs, voff[n], so, reinterpret_cast<unsigned char*>(sV[buf]) + (n * NW + w) * 64 * 16);
+        };
+        // S^T = K Q^T for the tile in sK[buf]; raw (unscaled) scores
+        auto scores = [&](int buf, f32x16* s) {
+    #pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
                 const int row = 32 * sub + l32;
-                return *(const bf16x8*)(&kb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
-            };
-            bf16x8 kq[3];
-            kq[0] = kread(0);
-            kq[1] = kread(1);
-#pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2) {
-                if (s2 + 2 < NS) kq[(s2 + 2) % 3] = kread(s2 + 2);
-                const int sub = s2 & 1, st = s2 >> 1;
-                snext[sub] = mfma32x32x16(kq[s2 % 3], qf[st], st == 0 ? f32x16{} : snext[sub]);
-                if (KEEP) {
-#pragma unroll
-                    for (int e2 = 0; e2 < EPS; ++e2) {
-                        const int e = s2 * EPS + e2;
-                        const int sx = e >> 4, r = e & 15;
-                        const float ex = fast_exp2(__builtin_fmaf(scur[sx][r], c2, -muse));
-                        if (e2 & 1) ps1 += ex; else ps0 += ex;
-                        pp[2 * sx + (r >> 3)][r & 7] = to_f16(ex);
-                    }
+                s[sub] = f32x16{};
+    #pragma unroll
+                for (int st = 0; st < KSTEPS; ++st) {
+                    const int pc = (2 * st + hi) ^ (row % QCH);
+                    const bf16x8 a = *(const bf16x8*)(&sK[buf][row * D + 8 * pc]);
+                    s[sub] = mfma32x32x16(a, qf[st], s[sub]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if (keep) body(std::true_type{});
-        else body(std::false_type{});
-
-        pending = false;
-        if (keep) {
-            const float psum = wave_sum_pair(ps0 + ps1);
-            lsum = lsum * alpha + psum;
-            m2 = mn;
-            thr = (lsum > 0.f) ? m2 + fast_log2(lsum) + theta : kNegInf;
-            pend_alpha = alpha;
-            pend_buf = buf;
-            pending = true;
-            if (valid) {
-                const int lim = ik - kt * BK;
-                if (lim >= 0) slots += (lim < BK - 1 ? lim : BK - 1) + 1;
-            }
-            ++kept_count;
-            bitword |= 1u << (kt & 31);
-        } else if (STATS) {
-            if (has) {
-                const float on = fmaxf(om, M);
-                float osum = 0.f;
-#pragma unroll
+        // causal mask (diagonal / ragged tiles) and raw row max
+        auto mask_max = [&](int kt, f32x16* s) -> float {
+            float M = kNegInf;
+            const bool need = ragged || (kt * BK + BK - 1 > off + i0);
+            if (need) {
+                const int lim = valid ? (ik - kt * BK) : -1;
+    #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) osum += fast_exp2(__builtin_fmaf(scur[sub][r], c2, -on));
-                osum = wave_sum_pair(osum);
-                ol = ol * fast_exp2(om - on) + osum;
-                om = on;
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int jj = 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        s[sub][r] = (jj <= lim) ? s[sub][r] : kNegInf;
+                    }
             }
-        }
-        if (want_bits && tid == 0 && ((kt & 31) == 0)) {
-            bitrow[kt >> 5] = bitword;
-            bitword = 0;
-        }
-        if (kt >= 1) Mraw = mask_max(kt - 1, snext);
-    };
+    #pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) M = fmaxf(M, s[sub][r]);
+            return wave_max_pair(M);
+        };
+        // O^T += V^T P^T with V^T fragments from the transposing LDS read
+        auto pv = [&](int buf, const f16x8* pb, f32x16* acc) {
+            const int j16 = lane & 15;
+            const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+    #pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    u32x2 half2x[2];
+    #pragma unroll
+                    for (int rd = 0; rd < 2; ++rd) {
+                        const int row = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
+                        const int col = 32 * dt + dsel;
+                        const int phys = ((col >> 3) ^ ((4 * (row & 3)) % QCH)) * 8 + (col & 7);
+                        half2x[rd] = lds_read_tr16(&sV[buf][0] + row * D + phys);
+                    }
+                    // whole-dword assembly of the operand (element-wise 16-bit inserts
+                    // of the transposed results are not reliable with this compiler)
+                    const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
+                    acc[dt] = mfma32x32x16_f16(__builtin_bit_cast(f16x8, w4), pb[ks], acc[dt]);
+                }
+            }
+        };
 
-    for (int kt = kt_first; kt >= 0; --kt) {
-        tile(kt, sA, sB);
-        sA[0] = sB[0];
-        sA[1] = sB[1];
-    }
-    if (pending) {
+        // ---- per-row state (this lane's query; lanes l and l^32 hold identical copies)
+        const float c2 = p.scale_log2;
+        float m2 = kNegInf;          // running max of retained base-2 scores
+        float lsum = 0.f;            // retained sum, shifted by m2
+        float thr = kNegInf;         // cached keep threshold m2 + log2(lsum) + theta
+        const float theta = p.log2_tau - fast_log2((float)(ik + 1));
+        float om = kNegInf, ol = 0.f;            // omitted mass (statistics mode)
+        int slots = 0;
+        f32x16 acc[DT];
+    #pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+        int kept_count = 0;
+        uint32_t bitword = 0;
+        const bool want_bits = p.bits != nullptr;
+        uint32_t* bitrow = want_bits ? p.bits + ((int64_t)bh * p.nQB + qb) * p.nwords : nullptr;
+        if (want_bits && tid == 0) {
+            for (int wd = kt_first / 32 + 1; wd < p.nwords; ++wd) bitrow[wd] = 0u;
+        }
+
+        // ---- prologue
+        copy_k(kt_first, kt_first & 1);
+        if (kt_first >= 1) copy_k(kt_first - 1, (kt_first - 1) & 1);
         wait_all_then_barrier();
-        if (__ballot(pend_alpha != 1.f) != 0ull) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
-        }
-        pv(pend_buf, pp, acc);
-    }
+        f32x16 sA[2], sB[2];         // scores: of the tile being decided / of the next tile
+        f16x8 pp[4];                 // P of the pending tile, then of the tile being kept
+        scores(kt_first & 1, sA);
+        float Mraw = mask_max(kt_first, sA);
 
-    // ---- epilogue: O = acc / l, LSE = (m2 + log2 l) ln 2
-    if (valid) {
-        const float inv = 1.f / lsum;
-        uint16_t* orow = obase + (int64_t)i * p.o_sl;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * dt + 8 * g + 4 * hi;
-                u32x2 pk;
-                pk[0] = float_to_bf16_bits(acc[dt][4 * g + 0] * inv) | (float_to_bf16_bits(acc[dt][4 * g + 1] * inv) << 16);
-                pk[1] = float_to_bf16_bits(acc[dt][4 * g + 2] * inv) | (float_to_bf16_bits(acc[dt][4 * g + 3] * inv) << 16);
-                *(u32x2*)(orow + d0) = pk;
+        bool pending = false;        // P.V of the last kept tile not yet accumulated
+        int pend_buf = 0;
+        float pend_alpha = 1.f;
+
+        // One tile: decide tile kt from (m, l); then, in one straight-line block per
+        // (keep, pending) case, issue the P.V MFMAs of the pending tile, then the
+        // score MFMAs of tile kt-1 interleaved with the softmax of tile kt (whose P
+        // reuses the registers the P.V just consumed).  scur/snext swap roles from
+        // one tile to the next (the loop is unrolled by two), so no copies.
+        auto tile = [&](int kt, f32x16* scur, f32x16* snext) {
+            const int buf = kt & 1;
+            const float M = Mraw * c2;
+            const bool has = Mraw > kNegInf;
+            const bool vote = has && (lsum == 0.f || M >= thr);
+            const bool wave_any = __ballot(vote) != 0ull;
+            if (lane == 0) sFlag[buf][w] = wave_any ? 1 : 0;
+            wait_all_then_barrier();                 // K(kt-1) and V of the pending tile have landed
+            int kflag = 0;
+    #pragma unroll
+            for (int ww = 0; ww < NW; ++ww) kflag |= sFlag[buf][ww];
+            // identical in every lane: make the branches below scalar
+            const bool keep = __builtin_amdgcn_readfirstlane(kflag) != 0;
+
+            if (keep) copy_v(kt, buf);
+            if (kt >= 2) copy_k(kt - 2, buf);
+            if (pending && __ballot(pend_alpha != 1.f) != 0ull) {
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
+            }
+            float mn = m2, muse = 0.f, alpha = 1.f;
+            if (keep) {
+                mn = fmaxf(m2, M);
+                muse = (mn == kNegInf) ? 0.f : mn;
+                alpha = fast_exp2(m2 - muse);
+            }
+            float ps0 = 0.f, ps1 = 0.f;
+            const uint16_t* kb = sK[buf ^ 1];        // K(kt-1); stale but harmless when kt == 0
+            const uint16_t* vb = sV[pend_buf];
+            // P.V of the pending tile (MFMA and LDS only).  Operand reads run two
+            // MFMAs ahead through small register rings, and a scheduling barrier
+            // closes every step, so the compiler keeps this order instead of
+            // hoisting every LDS read.
+            if (pending) {
+                constexpr int NPV = 4 * DT;
+                const int j16 = lane & 15;
+                const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+                auto vread = [&](int s2) -> f16x8 {
+                    const int dt = s2 % DT, ks = s2 / DT;
+                    u32x2 half2x[2];
+    #pragma unroll
+                    for (int rd = 0; rd < 2; ++rd) {
+                        const int vrow = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
+                        const int col = 32 * dt + dsel;
+                        const int phys = ((col >> 3) ^ ((4 * (vrow & 3)) % QCH)) * 8 + (col & 7);
+                        half2x[rd] = lds_read_tr16(vb + vrow * D + phys);
+                    }
+                    // whole-dword assembly of the operand (element-wise 16-bit inserts
+                    // of the transposed results are not reliable with this compiler)
+                    const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
+                    return __builtin_bit_cast(f16x8, w4);
+                };
+                f16x8 vq[3];
+                vq[0] = vread(0);
+                vq[1] = vread(1);
+    #pragma unroll
+                for (int s2 = 0; s2 < NPV; ++s2) {
+                    if (s2 + 2 < NPV) vq[(s2 + 2) % 3] = vread(s2 + 2);
+                    const int dt = s2 % DT, ks = s2 / DT;
+                    acc[dt] = mfma32x32x16_f16(vq[s2 % 3], pp[ks], acc[dt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // Scores of tile kt-1, with the softmax of tile kt (when kept) spread
+            // over the MFMA steps; its P reuses the registers the P.V consumed.
+            auto body = [&](auto keep_c) {
+                constexpr bool KEEP = decltype(keep_c)::value;
+                constexpr int NS = 2 * KSTEPS;       // score MFMAs of one tile
+                constexpr int EPS = 32 / NS;         // softmax elements per score MFMA
+                auto kread = [&](int s2) -> bf16x8 {
+                    const int sub = s2 & 1, st = s2 >> 1;
+                    const int row = 32 * sub + l32;
+                    return *(const bf16x8*)(&kb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
+                };
+                bf16x8 kq[3];
+                kq[0] = kread(0);
+                kq[1] = kread(1);
+    #pragma unroll
+                for (int s2 = 0; s2 < NS; ++s2) {
+                    if (s2 + 2 < NS) kq[(s2 + 2) % 3] = kread(s2 + 2);
+                    const int sub = s2 & 1, st = s2 >> 1;
+                    snext[sub] = mfma32x32x16(kq[s2 % 3], qf[st], st == 0 ? f32x16{} : snext[sub]);
+                    if (KEEP) {
+    #pragma unroll
+                        for (int e2 = 0; e2 < EPS; ++e2) {
+                            const int e = s2 * EPS + e2;
+                            const int sx = e >> 4, r = e & 15;
+                            const float ex = fast_exp2(__builtin_fmaf(scur[sx][r], c2, -muse));
+                            if (e2 & 1) ps1 += ex; else ps0 += ex;
+                            pp[2 * sx + (r >> 3)][r & 7] = to_f16(ex);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (keep) body(std::true_type{});
+            else body(std::false_type{});
+
+            pending = false;
+            if (keep) {
+                const float psum = wave_sum_pair(ps0 + ps1);
+                lsum = lsum * alpha + psum;
+                m2 = mn;
+                thr = (lsum > 0.f) ? m2 + fast_log2(lsum) + theta : kNegInf;
+                pend_alpha = alpha;
+                pend_buf = buf;
+                pending = true;
+                if (valid) {
+                    const int lim = ik - kt * BK;
+                    if (lim >= 0) slots += (lim < BK - 1 ? lim : BK - 1) + 1;
+                }
+                ++kept_count;
+                bitword |= 1u << (kt & 31);
+            } else if (STATS) {
+                if (has) {
+                    const float on = fmaxf(om, M);
+                    float osum = 0.f;
+    #pragma unroll
+                    for (int sub = 0; sub < 2; ++sub)
+    #pragma unroll
+                        for (int r = 0; r < 16; ++r) osum += fast_exp2(__builtin_fmaf(scur[sub][r], c2, -on));
+                    osum = wave_sum_pair(osum);
+                    ol = ol * fast_exp2(om - on) + osum;
+                    om = on;
+                }
+            }
+            if (want_bits && tid == 0 && ((kt & 31) == 0)) {
+                bitrow[kt >> 5] = bitword;
+                bitword = 0;
+            }
+            if (kt >= 1) Mraw = mask_max(kt - 1, snext);
+        };
+
+        for (int kt = kt_first; kt >= 0; --kt) {
+            tile(kt, sA, sB);
+            sA[0] = sB[0];
+            sA[1] = sB[1];
+        }
+        if (pending) {
+            wait_all_then_barrier();
+            if (__ballot(pend_alpha != 1.f) != 0ull) {
+    #pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
+            }
+            pv(pend_buf, pp, acc);
+        }
+
+        // ---- epilogue: O = acc / l, LSE = (m2 + log2 l) ln 2
+        if (valid) {
+            const float inv = 1.f / lsum;
+            uint16_t* orow = obase + (int64_t)i * p.o_sl;
+    #pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+    #pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = 32 * dt + 8 * g + 4 * hi;
+                    u32x2 pk;
+                    pk[0] = float_to_bf16_bits(acc[dt][4 * g + 0] * inv) |
+                            (float_to_bf16_bits(acc[dt][4 * g + 1] * inv) << 16);
+                    pk[1] = float_to_bf16_bits(acc[dt][4 * g + 2] * inv) |
+                            (float_to_bf16_bits(acc[dt][4 * g + 3] * inv) << 16);
+                    *(u32x2*)(orow + d0) = pk;
+                }
+            }
+            if (hi == 0) {
+                const int64_t ri = rowbase + i;
+                const float lz2 = m2 + fast_log2(lsum);
+                p.lse[ri] = lz2 * kLn2;
+                if (p.kept_slots) p.kept_slots[ri] = slots;
+                if (STATS) {
+                    float wgt = 0.f;
+                    if (ol > 0.f) wgt = 1.f / (1.f + fast_exp2(lz2 - (om + fast_log2(ol))));
+                    p.omitted[ri] = wgt;
+                }
             }
         }
-        if (hi == 0) {
-            const int64_t ri = rowbase + i;
-            const float lz2 = m2 + fast_log2(lsum);
-            p.lse[ri] = lz2 * kLn2;
-            if (p.kept_slots) p.kept_slots[ri] = slots;
-            if (STATS) {
-                float wgt = 0.f;
-                if (ol > 0.f) wgt = 1.f / (1.f + fast_exp2(lz2 - (om + fast_log2(ol))));
-                p.omitted[ri] = wgt;
-            }
-        }
-    }
-    if (tid == 0 && p.kept_tiles) p.kept_tiles[(int64_t)bh * p.nQB + qb] = kept_count;
+        if (tid == 0 && p.kept_tiles) p.kept_tiles[(int64_t)bh * p.nQB + qb] = kept_count;
     };
 
     while (true) {
