@@ -448,12 +448,14 @@ def main_tau_sweep(args):
     taus = [float(x) for x in args.taus.split(",") if float(x) > 0]
     rows = []
     for L in W["Ls"]:
-        inp = G.workload_inputs("sweep", L=L, with_dout=False)
-        q, k, v = (torch.from_numpy(np.ascontiguousarray(inp[x]).view(np.int16)).view(torch.bfloat16).to(dev)
-                   for x in ("q", "k", "v"))
+        inp = G.workload_inputs("sweep", L=L, with_dout=True)
+        q, k, v, do = (torch.from_numpy(np.ascontiguousarray(inp[x]).view(np.int16)).view(torch.bfloat16).to(dev)
+                       for x in ("q", "k", "v", "dout"))
         o = torch.empty_like(q)
         lse = torch.empty((1, Hq, L), dtype=torch.float32, device=dev)
         ws = mala.fwd_workspace(1, L, Hq, Hkv, d, Bq, Bk, dev)
+        bws = mala.bwd_workspace(1, L, Hq, Hkv, d, Bq, Bk, dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         stream = torch.cuda.current_stream(dev)
         nQB = -(-L // Bq)
         n_visit = Hq * sum((min(L, qb * Bq + Bq) - 1) // Bk + 1 for qb in range(nQB))
@@ -467,13 +469,29 @@ def main_tau_sweep(args):
             torch.cuda.synchronize()
             return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
 
+        def timed_bwd(t, o_t, lse_t, n=max(5, args.steps)):
+            for _ in range(args.warmup):
+                mala.mala_bwd(q, k, v, o_t, do, lse_t, t, Bq, Bk, dq=dq, dk=dk, dv=dv, ws=bws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                mala.mala_bwd(q, k, v, o_t, do, lse_t, t, Bq, Bk, dq=dq, dk=dk, dv=dv, ws=bws)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
         ms0 = timed(0.0)
-        o_ref, _ = mala.mala_fwd(q, k, v, 0.0, Bq, Bk, ws=ws)
+        o_ref, lse_ref = mala.mala_fwd(q, k, v, 0.0, Bq, Bk, ws=ws)
+        bms0 = timed_bwd(0.0, o_ref, lse_ref)
         ref = o_ref.float()
         for t in taus:
             ms = timed(t)
             st = mala.make_stats(1, Hq, L, Bq, Bk, dev, omitted=True)
-            ot, _ = mala.mala_fwd(q, k, v, t, Bq, Bk, stats=st, ws=ws)
+            ot, lt = mala.mala_fwd(q, k, v, t, Bq, Bk, stats=st, ws=ws)
+            torch.cuda.synchronize()
+            bms = timed_bwd(t, ot, lt)
+            bst = mala.make_stats(1, Hq, L, Bq, Bk, dev)
+            mala.mala_bwd(q, k, v, ot, do, lt, t, Bq, Bk, dq=dq, dk=dk, dv=dv, ws=bws, stats=bst)
             torch.cuda.synchronize()
             om = st["omitted_mass"][0].double()                      # [Hq, L]
             err = (ot.float() - ref).double().pow(2).sum(dim=(0, 1, 3)).sqrt()
@@ -487,15 +505,20 @@ def main_tau_sweep(args):
                 "omitted_mean": float(om.mean().item()), "omitted_max": float(om.max().item()),
                 "omitted_bound": t / (1 + t),
                 "o_rel_l2_per_head": [float(f"{x:.3e}") for x in rel],
+                "bwd_ms": round(bms, 4), "tau0_bwd_ms": round(bms0, 4),
+                "bwd_kept_tile_frac": round(int(bst["kept_tiles"].sum().item()) / n_visit, 4),
+                "bwd_slots_per_query": round(float(bst["kept_slots"].double().mean().item()), 1),
             })
+            print(f"# L={L} tau={t}: bwd {bms:.3f} ms (tau=0 {bms0:.3f}), bwd kept {rows[-1]['bwd_kept_tile_frac']}",
+                  file=sys.stderr, flush=True)
             print(f"# L={L} tau={t}: {ms:.3f} ms (tau=0 {ms0:.3f}), kept {rows[-1]['kept_tile_frac']}, "
                   f"omitted mean {rows[-1]['omitted_mean']:.2e} max {rows[-1]['omitted_max']:.2e}, "
                   f"O rel-L2 max {rel.max():.2e}", file=sys.stderr, flush=True)
-        del q, k, v, o, ws
+        del q, k, v, do, o, ws, bws, dq, dk, dv
     last = [r for r in rows if r["L"] == W["Ls"][-1] and r["tau"] == 1.0]
     out = {
-        "metric": "MALA fidelity vs cost against tau (sweep workload: forward ms, kept tiles, slots/query, "
-                  "omitted mass, O rel-L2 vs tau=0)",
+        "metric": "MALA fidelity vs cost against tau (sweep workload: forward and backward ms, kept tiles, "
+                  "slots/query, omitted mass, O rel-L2 vs tau=0)",
         "value": last[0]["speedup_vs_tau0"] if last else None,
         "unit": "forward speedup vs tau=0 at the longest L, tau=1",
         "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
