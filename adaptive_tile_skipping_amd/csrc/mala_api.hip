@@ -49,17 +49,17 @@ int pick_chunk(int Hq, int Hkv) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Persistent forward workgroups: two per CU of the current device (the CU
-// count is cached per device; concurrent first calls store the same value).
-int forward_slots() {
+// Compute units of the current device, for the persistent forward launch
+// (cached per device; concurrent first calls store the same value).
+int device_cus() {
     static int cached[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 512;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
     if (dev < 64 && cached[dev] > 0) return cached[dev];
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    if (dev < 64) cached[dev] = 2 * n;
-    return 2 * n;
+    if (dev < 64) cached[dev] = n;
+    return n;
 }
 
 // Decode splits per (sequence, KV head): enough workgroups (~2048) to keep
@@ -129,7 +129,7 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
     p.vh = (uint16_t*)ws;
     p.Lpad = p.nKT * Bk;
     p.queue = (int*)((char*)ws + need - 256);
-    p.nslot = forward_slots();
+    p.ncu = device_cus();
     bool st = false;
     if (stats) {
         p.kept_tiles = stats->kept_tiles;
@@ -186,7 +186,7 @@ mala_status mala_fwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, const int32_t* cu_s
     p.vh = (uint16_t*)ws;
     p.Rk = total_k + B * Bk;
     p.queue = (int*)((char*)ws + need - 256);
-    p.nslot = forward_slots();
+    p.ncu = device_cus();
     bool st = false;
     if (stats) {
         p.kept_tiles = stats->kept_tiles;

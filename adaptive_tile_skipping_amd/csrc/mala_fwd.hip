@@ -131,7 +131,7 @@ void mala_fwd_kernel(const FwdParams p) {
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    // Persistent workgroups (two per CU) take query blocks from eight queues,
+    // Persistent workgroups (eight waves per CU) take query blocks from eight queues,
     // one per XCD, each holding that XCD's share of the blocks in the launch
     // order below (longest first, chunks of blocks sharing K/V tiles together).
     // A workgroup drains its own XCD's queue, then the others'.  Blocks differ
@@ -544,10 +544,12 @@ static hipError_t launch_fwd_t(const FwdParams& p, bool stats, hipStream_t s) {
         if (g > 16384) g = 16384;
         hipLaunchKernelGGL((mala_v_to_f16<D>), dim3(g), dim3(256), 0, s, p);
     }
-    // the packed layout is a template parameter: the fixed-length kernels see a
-    // zero row offset at compile time
-    // two workgroups per CU, persistent (fewer when there are fewer blocks)
-    const int grid = (p.nunits < p.nslot ? (p.nunits + 7) / 8 * 8 : p.nslot);
+    // persistent workgroups: eight waves per CU (two per SIMD, what 256 VGPRs
+    // allow), fewer when there are fewer blocks.  The packed layout is a
+    // template parameter: the fixed-length kernels see a zero row offset at
+    // compile time.
+    const int slots = p.ncu * (8 / (NT / 64));
+    const int grid = (p.nunits < slots ? (p.nunits + 7) / 8 * 8 : slots);
     const bool vl = p.cu_q != nullptr;
     if (stats && vl)
         hipLaunchKernelGGL((mala_fwd_kernel<D, BQ, BK, true, true>), dim3(grid), dim3(NT), 0, s, p);

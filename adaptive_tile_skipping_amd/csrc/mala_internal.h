@@ -30,7 +30,7 @@ struct FwdParams {
     int max_q, max_k;      // longest query and key counts (nQB, nKT derive from them)
     int Rk;                // total_k + B * Bk: V copy rows per KV head (sequence b at cu_k[b] + b Bk)
     int* queue;            // [8] work queues of the forward kernel (workspace; zeroed by the V copy)
-    int nslot;             // persistent forward workgroups: two per CU
+    int ncu;               // compute units of the device (persistent forward workgroups per CU follow)
 };
 
 struct BwdParams {
