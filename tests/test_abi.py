@@ -77,6 +77,18 @@ def test_fwd_rejects_bad_arguments(kw, code):
     assert _fwd(**kw) == code
 
 
+def test_fwd_workspace_holds_v_copy_and_work_queues():
+    """The forward workspace is the fp16 V copy [B, Hkv, L rounded up to Bk, d]
+    followed by 256 bytes of work queues; one byte less is refused before any
+    launch."""
+    lib = mala.load_library()
+    n = lib.mala_fwd_workspace_size(1, 1000, 4, 2, 128, 128, 64)
+    assert n == 1 * 2 * 1024 * 128 * 2 + 256
+    assert _fwd(L=1000, Hq=4, Hkv=2, ws_bytes=n - 1) == mala.MALA_ERR_WORKSPACE
+    nv = lib.mala_fwd_varlen_workspace_size(3, 5000, 2, 128, 128, 64)
+    assert nv == (5000 + 3 * 64) * 2 * 128 * 2 + 256
+
+
 def test_bwd_workspace_and_errors():
     lib = mala.load_library()
     n = lib.mala_bwd_workspace_size(1, 1000, 4, 2, 128, 128, 64)
