@@ -114,6 +114,27 @@ __device__ __forceinline__ void buffer16_to_lds_s(__amdgpu_buffer_rsrc_t r, uint
                                             (int)voffset, (int)soffset, 0, 0);
 }
 
+// The same 16-byte copy issued from inline assembly, with the resource as four
+// dwords (base, 48-bit; no stride; `nbytes` records; the flags above).  The
+// compiler cannot see these as writes to LDS, so it adds none of its own waits
+// for them before later LDS reads, which it otherwise does for any read it
+// cannot prove disjoint from a copy in flight.  Every read of the destination
+// must therefore follow an explicit s_waitcnt that covers the copy
+// (wait_all_then_barrier).  The copy has no destination register, and the
+// compiler's own partial vmcnt waits stay correct: operations it does not
+// count only make an in-order counter wait longer.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, uint32_t nbytes) {
+    const uint64_t b = (uint64_t)base;
+    return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, nbytes, 0x00020000u};
+}
+__device__ __forceinline__ void buffer16_to_lds_asm(const u32x4& r, uint32_t voffset, uint32_t soffset,
+                                                    void* lds_wave_base) {
+    // the low 32 bits of a generic address into the LDS aperture are the LDS offset
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voffset), "s"(r), "s"(soffset), "{m0}"(m0)
+                 : "memory");
+}
+
 // Wait for every outstanding memory operation of this wave (including the
 // global -> LDS copies above), then a workgroup barrier.
 __device__ __forceinline__ void wait_all_then_barrier() {

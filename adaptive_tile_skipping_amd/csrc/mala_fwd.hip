@@ -41,25 +41,57 @@
 namespace mala {
 
 namespace {
-// V copy: bf16 [B, L, Hkv, D] -> fp16 [B, Hkv, Lpad, D], zero rows past L.
-template <int D>
-__global__ __launch_bounds__(256) void mala_v_to_f16(const FwdParams p) {
-    if (blockIdx.x == 0 && threadIdx.x < 8) p.queue[threadIdx.x] = 0;   // the forward's work queues
+// One 64-key tile of V, bf16 rows (key j at src + j * src_stride, j < nvalid)
+// -> fp16, transposed: dst[d * BK + pos] holds key (pos & ~15) | vt_pos16(pos & 15)
+// of column d, zero for keys past nvalid.  Within each group of 16 keys the
+// order is the one the P.V contraction consumes, so that one 16-byte read
+// (8 positions) gives a lane exactly the 8 keys its P fragment holds.  The
+// tile passes through LDS: coalesced 16-byte reads of whole rows, and
+// coalesced 16-byte writes of whole transposed rows.
+template <int D, int BK>
+__device__ __forceinline__ void v_tile_to_f16t(const uint16_t* src, int64_t src_stride, int nvalid,
+                                               uint16_t* dst, uint16_t (*sT)[D + 8]) {
     constexpr int CH = D / 8;
-    const int64_t n = (int64_t)p.B * p.Hkv * p.Lpad * CH;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
-        const int c = (int)(idx % CH);
-        const int64_t row = idx / CH;
-        const int j = (int)(row % p.Lpad);
-        const int64_t bk = row / p.Lpad;
-        const int kh = (int)(bk % p.Hkv), b = (int)(bk / p.Hkv);
+    for (int q = threadIdx.x; q < BK * CH; q += 256) {
+        const int j = q / CH, c = q % CH;
         u32x4 o = {0, 0, 0, 0};
-        if (j < p.L) {
-            const u32x4 x = *(const u32x4*)(p.v + b * p.v_sb + (int64_t)j * p.v_sl + kh * p.v_sh + 8 * c);
+        if (j < nvalid) {
+            const u32x4 x = *(const u32x4*)(src + (int64_t)j * src_stride + 8 * c);
 #pragma unroll
             for (int m = 0; m < 4; ++m) o[m] = pack2_f16_from_f32bits(x[m] << 16, x[m] & 0xFFFF0000u);
         }
-        *(u32x4*)(p.vh + row * D + 8 * c) = o;
+        *(u32x4*)(&sT[j][8 * c]) = o;
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < D * (BK / 8); q += 256) {
+        const int d = q / (BK / 8), c = q % (BK / 8);
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int pos = 8 * c + e;
+            h[e] = sT[(pos & ~15) | vt_pos16(pos & 15)][d];
+        }
+        const u32x4 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        *(u32x4*)(dst + d * BK + 8 * c) = o;
+    }
+    __syncthreads();                             // sT is reused by the next tile
+}
+
+// V copy: bf16 [B, L, Hkv, D] -> fp16 [B, Hkv, Lpad / BK tiles, D, BK], each
+// tile transposed as above; keys past L are zero.  One workgroup per tile.
+template <int D, int BK>
+__global__ __launch_bounds__(256) void mala_v_to_f16(const FwdParams p) {
+    if (blockIdx.x == 0 && threadIdx.x < 8) p.queue[threadIdx.x] = 0;   // the forward's work queues
+    __shared__ __attribute__((aligned(16))) uint16_t sT[BK][D + 8];
+    const int ntile = p.Lpad / BK;
+    const int64_t n = (int64_t)p.B * p.Hkv * ntile;
+    for (int64_t u = blockIdx.x; u < n; u += gridDim.x) {
+        const int t = (int)(u % ntile);
+        const int64_t bk = u / ntile;
+        const int kh = (int)(bk % p.Hkv), b = (int)(bk / p.Hkv);
+        const int j0 = t * BK;
+        v_tile_to_f16t<D, BK>(p.v + b * p.v_sb + (int64_t)j0 * p.v_sl + kh * p.v_sh, p.v_sl, p.L - j0,
+                              p.vh + (bk * p.Lpad + j0) * D, sT);
     }
 }
 
@@ -79,30 +111,25 @@ __device__ __forceinline__ bool seq_span(const FwdParams& p, int b, SeqSpan& s) 
            s.Lq <= p.max_q && s.Lk <= p.max_k;
 }
 
-// V copy of a packed batch: bf16 [total_k, Hkv, D] -> fp16 [Hkv, Rk, D]; the
-// keys of sequence b start at row cu_k[b] + b * BK and are followed by zero
-// rows up to the next sequence (at least BK of them).  grid.y = sequence.
+// V copy of a packed batch: bf16 [total_k, Hkv, D] -> fp16 [Hkv, Rk, D] rows,
+// sequence b's keys starting at row cu_k[b] + b * BK (at least BK spare rows
+// follow each sequence).  From there its keys form transposed tiles as above;
+// the last tile is zero past the sequence's keys.  grid.y = sequence.
 template <int D, int BK>
 __global__ __launch_bounds__(256) void mala_v_to_f16_varlen(const FwdParams p) {
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 8) p.queue[threadIdx.x] = 0;   // the forward's work queues
-    constexpr int CH = D / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sT[BK][D + 8];
     const int b = blockIdx.y;
     SeqSpan sp;
     if (!seq_span(p, b, sp)) return;
-    const int rows = sp.Lk + BK;
-    const int64_t n = (int64_t)p.Hkv * rows * CH;
-    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * 256) {
-        const int c = (int)(idx % CH);
-        const int64_t rr = idx / CH;
-        const int j = (int)(rr % rows);
-        const int kh = (int)(rr / rows);
-        u32x4 o = {0, 0, 0, 0};
-        if (j < sp.Lk) {
-            const u32x4 x = *(const u32x4*)(p.v + (int64_t)(sp.k0 + j) * p.v_sl + kh * p.v_sh + 8 * c);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) o[m] = pack2_f16_from_f32bits(x[m] << 16, x[m] & 0xFFFF0000u);
-        }
-        *(u32x4*)(p.vh + ((int64_t)kh * p.Rk + sp.k0 + (int64_t)b * BK + j) * D + 8 * c) = o;
+    const int ntile = (sp.Lk + BK - 1) / BK;
+    const int64_t n = (int64_t)p.Hkv * ntile;
+    for (int64_t u = blockIdx.x; u < n; u += gridDim.x) {
+        const int t = (int)(u % ntile);
+        const int kh = (int)(u / ntile);
+        const int j0 = t * BK;
+        v_tile_to_f16t<D, BK>(p.v + (int64_t)(sp.k0 + j0) * p.v_sl + kh * p.v_sh, p.v_sl, sp.Lk - j0,
+                              p.vh + ((int64_t)kh * p.Rk + sp.k0 + (int64_t)b * BK + j0) * D, sT);
     }
 }
 }  // namespace
@@ -120,7 +147,8 @@ void mala_fwd_kernel(const FwdParams p) {
     static_assert(INST * NW * 64 == TILE_SLOTS, "copy split");
 
     // K: [2][BK][D] bf16, chunk c of row r at c ^ (r % QCH)
-    // V: [2][BK][D] fp16, chunk c of row r at c ^ (4 (r % 4)) % QCH
+    // V: [2][D][BK] fp16, a transposed tile of the V copy (row d, 8 key
+    //    positions per 16-byte chunk), chunk c of row d at c ^ (d % 8)
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * D];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][BK * D];
     __shared__ int sFlag[2][NW];
@@ -215,22 +243,28 @@ void mala_fwd_kernel(const FwdParams p) {
             const int sl = (n * NW + w) * 64 + lane;
             const int r = sl / QCH, pc = sl % QCH;
             koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
-            voff[n] = (uint32_t)((r * D + 8 * (pc ^ ((4 * (r & 3)) % QCH))) * 2);
+            const int dr = sl / (BK / 8), vc = sl % (BK / 8);
+            voff[n] = (uint32_t)((dr * BK + 8 * (vc ^ (dr & 7))) * 2);
         }
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhbase, (uint32_t)(vh_rows * D * 2));
+        // The copies are issued from inline assembly (no compiler-inserted waits
+        // before the reads of the other buffers); the wait before each barrier
+        // covers them.
+        const u32x4 vrs = raw_rsrc(vhbase, (uint32_t)(vh_rows * D * 2));
         auto copy_k = [&](int kt, int buf) {
             const int j0 = kt * BK;
-            const __amdgpu_buffer_rsrc_t krs =
-                make_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(Lk - 1 - j0) * p.k_sl + D) * 2));
+            const u32x4 krs =
+                raw_rsrc(kbase + (int64_t)j0 * p.k_sl, (uint32_t)(((int64_t)(Lk - 1 - j0) * p.k_sl + D) * 2));
     #pragma unroll
             for (int n = 0; n < INST; ++n)
-                buffer16_to_lds(krs, koff[n], reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
+                buffer16_to_lds_asm(krs, koff[n], 0u,
+                                    reinterpret_cast<unsigned char*>(sK[buf]) + (n * NW + w) * 64 * 16);
         };
         auto copy_v = [&](int kt, int buf) {
             const uint32_t so = (uint32_t)(kt * BK * D * 2);
     #pragma unroll
             for (int n = 0; n < INST; ++n)
-                buffer16_to_lds_s(vrs, voff[n], so, reinterpret_cast<unsigned char*>(sV[buf]) + (n * NW + w) * 64 * 16);
+                buffer16_to_lds_asm(vrs, voff[n], so,
+                                    reinterpret_cast<unsigned char*>(sV[buf]) + (n * NW + w) * 64 * 16);
         };
         // S^T = K Q^T for the tile in sK[buf]; raw (unscaled) scores
         auto scores = [&](int buf, f32x16* s) {
@@ -266,27 +300,18 @@ void mala_fwd_kernel(const FwdParams p) {
                 for (int r = 0; r < 16; ++r) M = fmaxf(M, s[sub][r]);
             return wave_max_pair(M);
         };
-        // O^T += V^T P^T with V^T fragments from the transposing LDS read
+        // V^T fragment of P.V step (dt, ks): row d = 32 dt + l32 of the
+        // transposed tile, key positions 16 ks + 8 hi .. +7 (one 16-byte read)
+        auto vt_frag = [&](const uint16_t* vbuf, int dt, int ks) -> f16x8 {
+            const int dr = 32 * dt + l32;
+            return *(const f16x8*)(vbuf + dr * BK + 8 * ((2 * ks + hi) ^ (dr & 7)));
+        };
+        // O^T += V^T P^T
         auto pv = [&](int buf, const f16x8* pb, f32x16* acc) {
-            const int j16 = lane & 15;
-            const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
     #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
     #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    u32x2 half2x[2];
-    #pragma unroll
-                    for (int rd = 0; rd < 2; ++rd) {
-                        const int row = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
-                        const int col = 32 * dt + dsel;
-                        const int phys = ((col >> 3) ^ ((4 * (row & 3)) % QCH)) * 8 + (col & 7);
-                        half2x[rd] = lds_read_tr16(&sV[buf][0] + row * D + phys);
-                    }
-                    // whole-dword assembly of the operand (element-wise 16-bit inserts
-                    // of the transposed results are not reliable with this compiler)
-                    const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
-                    acc[dt] = mfma32x32x16_f16(__builtin_bit_cast(f16x8, w4), pb[ks], acc[dt]);
-                }
+                for (int ks = 0; ks < 4; ++ks) acc[dt] = mfma32x32x16_f16(vt_frag(sV[buf], dt, ks), pb[ks], acc[dt]);
             }
         };
 
@@ -363,23 +388,7 @@ void mala_fwd_kernel(const FwdParams p) {
             // hoisting every LDS read.
             if (pending) {
                 constexpr int NPV = 4 * DT;
-                const int j16 = lane & 15;
-                const int dsel = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
-                auto vread = [&](int s2) -> f16x8 {
-                    const int dt = s2 % DT, ks = s2 / DT;
-                    u32x2 half2x[2];
-    #pragma unroll
-                    for (int rd = 0; rd < 2; ++rd) {
-                        const int vrow = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
-                        const int col = 32 * dt + dsel;
-                        const int phys = ((col >> 3) ^ ((4 * (vrow & 3)) % QCH)) * 8 + (col & 7);
-                        half2x[rd] = lds_read_tr16(vb + vrow * D + phys);
-                    }
-                    // whole-dword assembly of the operand (element-wise 16-bit inserts
-                    // of the transposed results are not reliable with this compiler)
-                    const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
-                    return __builtin_bit_cast(f16x8, w4);
-                };
+                auto vread = [&](int s2) -> f16x8 { return vt_frag(vb, s2 % DT, s2 / DT); };
                 f16x8 vq[3];
                 vq[0] = vread(0);
                 vq[1] = vread(1);
@@ -534,15 +543,15 @@ template <int D, int BQ, int BK>
 static hipError_t launch_fwd_t(const FwdParams& p, bool stats, hipStream_t s) {
     constexpr int NT = BQ / 32 * 64;
     if (p.cu_q) {
-        const int64_t n = (int64_t)p.Hkv * (p.max_k + BK) * (D / 8);
-        int g = (int)((n + 255) / 256);
+        const int64_t n = (int64_t)p.Hkv * ((p.max_k + BK - 1) / BK);   // tiles of the longest sequence
+        int g = (int)(n < 1 ? 1 : n);
         if (g > 4096) g = 4096;
         hipLaunchKernelGGL((mala_v_to_f16_varlen<D, BK>), dim3(g, p.B), dim3(256), 0, s, p);
     } else {
-        const int64_t n = (int64_t)p.B * p.Hkv * p.Lpad * (D / 8);
-        int g = (int)((n + 255) / 256);
+        const int64_t n = (int64_t)p.B * p.Hkv * (p.Lpad / BK);          // tiles
+        int g = (int)(n < 1 ? 1 : n);
         if (g > 16384) g = 16384;
-        hipLaunchKernelGGL((mala_v_to_f16<D>), dim3(g), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_v_to_f16<D, BK>), dim3(g), dim3(256), 0, s, p);
     }
     // persistent workgroups: eight waves per CU (two per SIMD, what 256 VGPRs
     // allow), fewer when there are fewer blocks.  The packed layout is a

@@ -20,7 +20,8 @@ struct FwdParams {
     float* omitted;
     uint32_t* bits;
     int nwords;
-    uint16_t* vh;       // fp16 copy of V (workspace): [B, Hkv, Lpad, d], or [Hkv, Rk, d] packed
+    uint16_t* vh;       // fp16 copy of V (workspace): B x Hkv x Lpad keys, or Hkv x Rk packed,
+                        // as transposed [d][Bk] tiles
     int Lpad;           // nKT * Bk
     // packed variable-length batches (cu_q == nullptr: the fixed-length layout
     // above, with q/k/v/o strides sb, sl, sh and lse [B, Hq, L])

@@ -112,7 +112,8 @@ mala_status mala_fwd(mala_t4 q, mala_t4 k, mala_t4 v, int B, int L, int Hq, int 
                      const mala_tile_stats* stats, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of device workspace mala_fwd_varlen needs (an fp16 copy of V with
- * Bk zero rows after each sequence, and the forward kernel's work queues). */
+ * room for Bk more keys after each sequence, and the forward kernel's work
+ * queues). */
 size_t mala_fwd_varlen_workspace_size(int B, int total_k, int Hkv, int d, int Bq, int Bk);
 
 /* Forward over a packed batch of B variable-length sequences, each a chunk of

@@ -78,9 +78,9 @@ def test_fwd_rejects_bad_arguments(kw, code):
 
 
 def test_fwd_workspace_holds_v_copy_and_work_queues():
-    """The forward workspace is the fp16 V copy [B, Hkv, L rounded up to Bk, d]
-    followed by 256 bytes of work queues; one byte less is refused before any
-    launch."""
+    """The forward workspace is the fp16 V copy (B x Hkv x L rounded up to Bk
+    keys of d values, as transposed tiles) followed by 256 bytes of work queues;
+    one byte less is refused before any launch."""
     lib = mala.load_library()
     n = lib.mala_fwd_workspace_size(1, 1000, 4, 2, 128, 128, 64)
     assert n == 1 * 2 * 1024 * 128 * 2 + 256
@@ -178,7 +178,7 @@ def test_fwd_varlen_rejects_bad_arguments(kw, code):
 
 def test_fwd_varlen_workspace_size():
     lib = mala.load_library()
-    # fp16 V copy with one tile of zero rows after each sequence
+    # fp16 V copy with room for one more tile after each sequence
     assert lib.mala_fwd_varlen_workspace_size(3, 1000, 2, 128, 128, 64) >= (1000 + 3 * 64) * 2 * 128 * 2
     assert lib.mala_fwd_varlen_workspace_size(3, 1000, 2, 96, 128, 64) == 0
 
