@@ -59,11 +59,18 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ float wave_max_pair(float x) {   // combine lane l with lane l^32
-    return fmaxf(x, __shfl_xor(x, 32));
+// Combine lane l with lane l^32.  v_permlane32_swap exchanges the upper half
+// of one register with the lower half of another; applied to two copies of x
+// it leaves {x[l % 32], x[l % 32 + 32]} in the two results of every lane, a
+// VALU operation instead of an LDS-routed shuffle.  max and + are commutative,
+// so the result is the same, bit for bit, as x op x[l ^ 32].
+__device__ __forceinline__ float wave_max_pair(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_sum_pair(float x) {
-    return x + __shfl_xor(x, 32);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Position of key kk (0..15 within a 16-key group) in the transposed-V LDS
