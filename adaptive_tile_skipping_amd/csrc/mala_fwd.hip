@@ -351,8 +351,9 @@ void mala_fwd_kernel(const FwdParams p) {
         // One tile: decide tile kt from (m, l); then, in one straight-line block per
         // (keep, pending) case, issue the P.V MFMAs of the pending tile, then the
         // score MFMAs of tile kt-1 interleaved with the softmax of tile kt (whose P
-        // reuses the registers the P.V just consumed).  scur/snext swap roles from
-        // one tile to the next (the loop is unrolled by two), so no copies.
+        // reuses the registers the P.V just consumed).  snext becomes the next
+        // tile's scur through a register copy at the end of the loop (a loop
+        // unrolled by two, with the roles swapped, does not fit in 256 VGPRs).
         auto tile = [&](int kt, f32x16* scur, f32x16* snext) {
             const int buf = kt & 1;
             const float M = Mraw * c2;
@@ -361,25 +362,18 @@ void mala_fwd_kernel(const FwdParams p) {
             const bool wave_any = __ballot(vote) != 0ull;
             if (lane == 0) sFlag[buf][w] = wave_any ? 1 : 0;
             wait_all_then_barrier();                 // K(kt-1) and V of the pending tile have landed
+            // The block's votes are read now but first used after the P.V of the
+            // pending tile, which does not depend on them: the LDS round trip of
+            // the read runs under that P.V.
             int kflag = 0;
     #pragma unroll
             for (int ww = 0; ww < NW; ++ww) kflag |= sFlag[buf][ww];
-            // identical in every lane: make the branches below scalar
-            const bool keep = __builtin_amdgcn_readfirstlane(kflag) != 0;
 
-            if (keep) copy_v(kt, buf);
             if (kt >= 2) copy_k(kt - 2, buf);
             if (pending && __ballot(pend_alpha != 1.f) != 0ull) {
     #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) acc[dt] *= pend_alpha;
             }
-            float mn = m2, muse = 0.f, alpha = 1.f;
-            if (keep) {
-                mn = fmaxf(m2, M);
-                muse = (mn == kNegInf) ? 0.f : mn;
-                alpha = fast_exp2(m2 - muse);
-            }
-            float ps0 = 0.f, ps1 = 0.f;
             const uint16_t* kb = sK[buf ^ 1];        // K(kt-1); stale but harmless when kt == 0
             const uint16_t* vb = sV[pend_buf];
             // P.V of the pending tile (MFMA and LDS only).  Operand reads run two
@@ -400,6 +394,16 @@ void mala_fwd_kernel(const FwdParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            // identical in every lane: make the branches below scalar
+            const bool keep = __builtin_amdgcn_readfirstlane(kflag) != 0;
+            if (keep) copy_v(kt, buf);
+            float mn = m2, muse = 0.f, alpha = 1.f;
+            if (keep) {
+                mn = fmaxf(m2, M);
+                muse = (mn == kNegInf) ? 0.f : mn;
+                alpha = fast_exp2(m2 - muse);
+            }
+            float ps0 = 0.f, ps1 = 0.f;
             // Scores of tile kt-1, with the softmax of tile kt (when kept) spread
             // over the MFMA steps; its P reuses the registers the P.V consumed.
             auto body = [&](auto keep_c) {
