@@ -148,7 +148,10 @@ void mala_fwd_kernel(const FwdParams p) {
 
     // K: [2][BK][D] bf16, chunk c of row r at c ^ (r % QCH)
     // V: [2][D][BK] fp16, a transposed tile of the V copy (row d, 8 key
-    //    positions per 16-byte chunk), chunk c of row d at c ^ (d % 8)
+    //    positions per 16-byte chunk), chunk c of row d at c ^ ((d / 2) % 8).
+    //    A 16-byte read serves 16 lanes at a time over 64 banks, i.e. 16 rows
+    //    d0..d0+15 of one chunk; rows of one parity share a 256-byte bank
+    //    cycle, and the swizzle gives those 8 rows 8 different chunks.
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * D];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][BK * D];
     __shared__ int sFlag[2][NW];
@@ -244,7 +247,7 @@ void mala_fwd_kernel(const FwdParams p) {
             const int r = sl / QCH, pc = sl % QCH;
             koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
             const int dr = sl / (BK / 8), vc = sl % (BK / 8);
-            voff[n] = (uint32_t)((dr * BK + 8 * (vc ^ (dr & 7))) * 2);
+            voff[n] = (uint32_t)((dr * BK + 8 * (vc ^ ((dr >> 1) & 7))) * 2);
         }
         // The copies are issued from inline assembly (no compiler-inserted waits
         // before the reads of the other buffers); the wait before each barrier
@@ -304,7 +307,7 @@ void mala_fwd_kernel(const FwdParams p) {
         // transposed tile, key positions 16 ks + 8 hi .. +7 (one 16-byte read)
         auto vt_frag = [&](const uint16_t* vbuf, int dt, int ks) -> f16x8 {
             const int dr = 32 * dt + l32;
-            return *(const f16x8*)(vbuf + dr * BK + 8 * ((2 * ks + hi) ^ (dr & 7)));
+            return *(const f16x8*)(vbuf + dr * BK + 8 * ((2 * ks + hi) ^ ((dr >> 1) & 7)));
         };
         // O^T += V^T P^T
         auto pv = [&](int buf, const f16x8* pb, f32x16* acc) {
