@@ -826,16 +826,23 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
         key = key < Nb ? key : Nb - 1;
         vx[r] = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
     }
-    // P of the tile: lane = key, one value per row
+    __builtin_amdgcn_sched_barrier(0);          // the V loads go out first, then the P loads
+    // P of the tile: lane = key, one value per row.  The loads take clamped
+    // (always valid) indices and are issued together; invalid entries are
+    // replaced by 0 afterwards.
     {
         const int key = t * BKD + lane;
+        const bool kok = has && key < Nb;
+        const int kk = kok ? key : 0;
+        float sv[GP], lv[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-            float pr = 0.f;
-            if (has && g < G && key < Nb)
-                pr = fast_exp2(p.spill[((int64_t)grp * G + g) * p.N + key] - p.lse2[(int64_t)grp * G + g]);
-            sP[w][g][lane] = pr;
+            const int gg = g < G ? g : G - 1;
+            sv[g] = p.spill[((int64_t)grp * G + gg) * p.N + kk];
+            lv[g] = p.lse2[(int64_t)grp * G + gg];
         }
+#pragma unroll
+        for (int g = 0; g < GP; ++g) sP[w][g][lane] = (kok && g < G) ? fast_exp2(sv[g] - lv[g]) : 0.f;
     }
     __syncthreads();
     float acc[GP][8];
