@@ -131,7 +131,8 @@ void mala_dec_score(const DecParams p) {
     const int ntask = p.B * p.Hkv * p.nT;
     const int nwave = gridDim.x * 4;
     const int per = (ntask + nwave - 1) / nwave;
-    const int gw = w * gridDim.x + blockIdx.x;     // neighbouring runs on different CUs
+    // wave-uniform, so the per-tile index arithmetic below runs on the scalar unit
+    const int gw = __builtin_amdgcn_readfirstlane(w * gridDim.x + blockIdx.x);   // neighbouring runs on different CUs
     int task = gw * per;
     const int tend = (task + per < ntask) ? task + per : ntask;
     if (task >= tend) return;
