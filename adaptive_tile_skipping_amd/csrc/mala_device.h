@@ -73,8 +73,8 @@ __device__ __forceinline__ float wave_sum_pair(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position of key kk (0..15 within a 16-key group) in the transposed-V LDS
-// rows: bits 2 and 3 swapped, so that the 8 consecutive positions a lane
+// Position of key kk (0..15 within a 16-key group) in a transposed V tile
+// (the forward's fp16 V copy): bits 2 and 3 swapped, so that the 8 consecutive positions a lane
 // feeds to the P.V contraction are exactly the 8 keys its score registers hold.
 __device__ __forceinline__ int vt_pos16(int kk) {
     return (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
@@ -112,17 +112,11 @@ __device__ __forceinline__ void buffer16_to_lds(__amdgpu_buffer_rsrc_t r, uint32
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
                                             (int)voffset, 0, 0, 0);
 }
-// Same with a wave-uniform byte offset added from a scalar register.  The
-// scalar offset is not part of the range check, so use this form only where
-// every access is known to stay inside the resource.
-__device__ __forceinline__ void buffer16_to_lds_s(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset,
-                                                  void* lds_wave_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
-                                            (int)voffset, (int)soffset, 0, 0);
-}
 
 // The same 16-byte copy issued from inline assembly, with the resource as four
 // dwords (base, 48-bit; no stride; `nbytes` records; the flags above).  The
+// range check covers voffset only: a nonzero wave-uniform soffset is added
+// outside it, so use one only where every access stays inside the resource.  The
 // compiler cannot see these as writes to LDS, so it adds none of its own waits
 // for them before later LDS reads, which it otherwise does for any read it
 // cannot prove disjoint from a copy in flight.  Every read of the destination
