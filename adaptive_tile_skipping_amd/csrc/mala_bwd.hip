@@ -723,14 +723,38 @@ void mala_bwd_dq(const BwdParams p) {
     // else the set bits of the block's word row
     const bool dense = p.log2_tau == kNegInf;
     const uint32_t* qrow = p.qbits + (bh * p.nQB + qb) * p.nwords;
-    int cwi = kt_first >> 5;                     // sparse cursor: word index and remaining bits
-    uint32_t cword = dense ? 0u : (qrow[cwi] & (kt_first % 32 == 31 ? ~0u : ((2u << (kt_first % 32)) - 1u)));
+    // Sparse cursor, newest tile first.  The row is read 64 words at a time:
+    // lane l holds word wtop - l of the current window, `nz` marks the window's
+    // non-zero words not yet taken, and cword holds the bits left of word cwi.
+    // A stretch of empty words costs one round trip per 64 words.
+    int wtop = kt_first >> 5;
+    int cwi = 0;
+    uint32_t wmy = 0u, cword = 0u;
+    uint64_t nz = 0ull;
+    if (!dense) {
+        const int wi = wtop - lane;
+        wmy = qrow[wi >= 0 ? wi : 0];
+        wmy = (wi >= 0) ? wmy : 0u;
+        if (lane == 0 && kt_first % 32 != 31) wmy &= (2u << (kt_first % 32)) - 1u;   // tiles past kt_first
+        nz = __ballot(wmy != 0u);
+    }
     int dnext = kt_first;
     auto next_tile = [&]() -> int {
         if (dense) return dnext >= 0 ? dnext-- : -1;
         while (cword == 0u) {
-            if (--cwi < 0) return -1;
-            cword = qrow[cwi];
+            if (nz == 0ull) {
+                wtop -= 64;
+                if (wtop < 0) return -1;
+                const int wi = wtop - lane;
+                wmy = qrow[wi >= 0 ? wi : 0];
+                wmy = (wi >= 0) ? wmy : 0u;
+                nz = __ballot(wmy != 0u);
+                continue;
+            }
+            const int l = __builtin_ctzll(nz);
+            nz &= nz - 1ull;
+            cwi = wtop - l;
+            cword = (uint32_t)__builtin_amdgcn_readlane((int)wmy, l);
         }
         const int bpos = 31 - __builtin_clz(cword);
         cword &= ~(1u << bpos);
