@@ -68,9 +68,9 @@ def parse():
                          "tau_sweep: fidelity and cost against tau")
     ap.add_argument("--taus", type=str, default="0.01,0.05,0.25,1,4,16",
                     help="tau values of the tau_sweep workload (tau = 0 is always run as the reference)")
-    ap.add_argument("--traffic-probe", nargs="?", const="fwd", default=None, choices=("fwd", "decode"),
-                    help="run two forward (or two decode, each after a 512 MB read flush) launches and a plain "
-                         "1 GiB device copy, then exit (for PMC passes)")
+    ap.add_argument("--traffic-probe", nargs="?", const="fwd", default=None, choices=("fwd", "decode", "bwd"),
+                    help="run two forward (or two decode, each after a 512 MB read flush; or one forward and "
+                         "two backward) launches and a plain 1 GiB device copy, then exit (for PMC passes)")
     return ap.parse_args()
 
 
@@ -596,6 +596,12 @@ def main():
             what = "2 x mala_fwd (train_128k, tau=%g)" % tau
             for _ in range(2):
                 fwd(tau)
+                torch.cuda.synchronize()
+        elif args.traffic_probe == "bwd":
+            what = "mala_fwd + 2 x mala_bwd (train_128k, tau=%g)" % tau
+            fwd(tau)
+            for _ in range(2):
+                bwd(tau)
                 torch.cuda.synchronize()
         else:
             what = "2 x mala_decode (decode_128k, tau=%g), each after a 512 MB read" % tau
