@@ -158,7 +158,7 @@ void mala_fwd_kernel(const FwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: w-derived addresses stay scalar
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
