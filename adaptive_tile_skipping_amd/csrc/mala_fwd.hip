@@ -384,6 +384,9 @@ void mala_fwd_kernel(const FwdParams p) {
             // closes every step, so the compiler keeps this order instead of
             // hoisting every LDS read.
             if (pending) {
+                // higher issue priority while this wave's MFMA-only phase runs, so
+                // the other wave on the SIMD fills the gaps with its VALU work
+                __builtin_amdgcn_s_setprio(1);
                 constexpr int NPV = 4 * DT;
                 auto vread = [&](int s2) -> f16x8 { return vt_frag(vb, s2 % DT, s2 / DT); };
                 f16x8 vq[3];
@@ -396,6 +399,7 @@ void mala_fwd_kernel(const FwdParams p) {
                     acc[dt] = mfma32x32x16_f16(vq[s2 % 3], pp[ks], acc[dt]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                __builtin_amdgcn_s_setprio(0);
             }
             // identical in every lane: make the branches below scalar
             const bool keep = __builtin_amdgcn_readfirstlane(kflag) != 0;
