@@ -384,9 +384,6 @@ void mala_fwd_kernel(const FwdParams p) {
             // closes every step, so the compiler keeps this order instead of
             // hoisting every LDS read.
             if (pending) {
-                // higher issue priority while this wave's MFMA-only phase runs, so
-                // the other wave on the SIMD fills the gaps with its VALU work
-                __builtin_amdgcn_s_setprio(1);
                 constexpr int NPV = 4 * DT;
                 auto vread = [&](int s2) -> f16x8 { return vt_frag(vb, s2 % DT, s2 / DT); };
                 f16x8 vq[3];
@@ -399,7 +396,6 @@ void mala_fwd_kernel(const FwdParams p) {
                     acc[dt] = mfma32x32x16_f16(vq[s2 % 3], pp[ks], acc[dt]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_s_setprio(0);
             }
             // identical in every lane: make the branches below scalar
             const bool keep = __builtin_amdgcn_readfirstlane(kflag) != 0;
@@ -443,8 +439,15 @@ void mala_fwd_kernel(const FwdParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
+            // Issue priority: normal for the score MFMAs and softmax, raised for the
+            // rest of the tile (row statistics, vote, barrier, and the next tile's
+            // MFMA-only P.V).  When both waves on a SIMD can issue, the one in its
+            // serial, latency-bound stretch goes first; the other wave's score
+            // MFMAs and softmax fill the gaps.
+            __builtin_amdgcn_s_setprio(0);
             if (keep) body(std::true_type{});
             else body(std::false_type{});
+            __builtin_amdgcn_s_setprio(1);
 
             pending = false;
             if (keep) {
