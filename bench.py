@@ -532,7 +532,7 @@ def main_tau_sweep(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
               "(the attention operator shards by heads with no communication; run one process per GPU).",
               file=sys.stderr)
         sys.exit(2)

@@ -221,3 +221,16 @@ def test_bwd_varlen_workspace_and_errors():
     assert lib.mala_bwd_varlen(*head, *bad, *ok_ws, None, None) == mala.MALA_ERR_UNSUPPORTED
     st = mala.MalaTileStats(None, None, 4096, None)    # omitted mass is forward-only
     assert lib.mala_bwd_varlen(*head, *mid, *ok_ws, ctypes.pointer(st), None) == mala.MALA_ERR_INVALID_ARG
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 exits with a message, before
+    touching any device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one MI355X" in (r.stdout + r.stderr)
