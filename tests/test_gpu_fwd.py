@@ -133,3 +133,25 @@ def test_fwd_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(s1["decision_bits"], s2["decision_bits"])
+
+
+def test_fwd_workspace_reused_across_shapes():
+    """One workspace serves calls of different shapes in a row.  Each call's V
+    copy re-zeroes the persistent kernel's work queues, so a smaller call after
+    a larger one (and the larger one again) matches the oracle and a call on a
+    fresh workspace bit for bit."""
+    dev = _dev()
+    big = G.attn_inputs(910, 2, 3000, 6, 2, 128, 0.1, diffuse_kv_heads=(1,))
+    small = G.attn_inputs(911, 1, 700, 4, 1, 128, 0.2)
+    ws = mala.fwd_workspace(2, 3000, 6, 2, 128, device=dev)
+    qb, kb, vb = (bf16_tensor(big[x], dev) for x in ("q", "k", "v"))
+    qs, ks, vs = (bf16_tensor(small[x], dev) for x in ("q", "k", "v"))
+    print("[fwd] workspace reuse: B=2 L=3000, then B=1 L=700, then B=2 L=3000", flush=True)
+    ob1, lb1 = mala.mala_fwd(qb, kb, vb, 1.0, ws=ws)
+    os_, ls_ = mala.mala_fwd(qs, ks, vs, 1.0, ws=ws)
+    ob2, lb2 = mala.mala_fwd(qb, kb, vb, 1.0, ws=ws)
+    os_f, ls_f = mala.mala_fwd(qs, ks, vs, 1.0)          # its own workspace
+    torch.cuda.synchronize()
+    assert torch.equal(ob1, ob2) and torch.equal(lb1, lb2)
+    assert torch.equal(os_, os_f) and torch.equal(ls_, ls_f)
+    run_fwd_case(small, 1.0, 128, 64, label="small after big, own workspace")
