@@ -37,19 +37,24 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build_oracle(force=True)
-    lib = ctypes.CDLL(_LIB)
+    # MALA_ORACLE_LIB names another build of mala_oracle.c to load instead
+    # (the mutation tests point it at deliberately broken copies)
+    path = os.environ.get("MALA_ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build_oracle(force=True)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, f64 = ctypes.c_int, ctypes.c_double
     lib.mala_oracle_fwd.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, i32, P, i32,
                                     P, P, P, P, P, P, i32]
     lib.mala_oracle_bwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, f64, i32, i32,
-                                    P, i32, P, i32, P, P, P, P, P, i32]
+                                    P, i32, P, i32, P, P, P, P, P, P, P, i32]
     lib.mala_oracle_fwd_varlen.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, i32,
                                            P, P, P, P, P, P, i32]
     lib.mala_oracle_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32,
-                                           P, i32, P, i32, P, P, P, P, P, i32]
+                                           P, i32, P, i32, P, P, P, P, P, P, P, i32]
     lib.mala_oracle_decode.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, P,
                                        P, P, P, P, P, P, i32]
     for f in (lib.mala_oracle_fwd, lib.mala_oracle_fwd_varlen, lib.mala_oracle_bwd, lib.mala_oracle_bwd_varlen,
@@ -132,8 +137,10 @@ def oracle_fwd_varlen(q, k, v, cu_q, cu_k, tau: float, Bq: int, Bk: int, blocks=
 
 
 def oracle_bwd(q, k, v, o, dout, lse, tau: float, Bq: int, Bk: int,
-               qunits=None, kunits=None, do_dq=True, do_dkdv=True, nthreads: int = 0):
-    """Backward rule.  Returns dict(dq, dk, dv, keep, margin).
+               qunits=None, kunits=None, do_dq=True, do_dkdv=True, cond: bool = False, nthreads: int = 0):
+    """Backward rule.  Returns dict(dq, dk, dv, keep, margin), plus dq_cond and
+    dk_cond (the first-order error scales of a binary32 evaluation of dP - D,
+    described in mala_oracle.c) when `cond` is set.
 
     `qunits` (flat (b*Hq + h)*nQB + qb) restricts the dq pass, `kunits`
     (flat (b*Hkv + kh)*nKT + kt) the dk/dv pass; rows outside stay NaN.
@@ -145,6 +152,8 @@ def oracle_bwd(q, k, v, o, dout, lse, tau: float, Bq: int, Bk: int,
     dq = np.full(q.shape, np.nan)
     dk = np.full(k.shape, np.nan)
     dv = np.full(k.shape, np.nan)
+    dqc = np.full(q.shape, np.nan) if cond else None
+    dkc = np.full(k.shape, np.nan) if cond else None
     keep = np.full((B, Hq, nQB, nKT), KEEP_UNVISITED, np.uint8)
     margin = np.full((B, Hq, nQB, nKT), np.nan)
     qa = None if qunits is None else np.ascontiguousarray(qunits, dtype=np.int32)
@@ -158,17 +167,22 @@ def oracle_bwd(q, k, v, o, dout, lse, tau: float, Bq: int, Bk: int,
     rc = _load().mala_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                  B, L, Hq, Hkv, d, float(tau), Bq, Bk,
                                  _ptr(qa), nq, _ptr(ka), nk,
-                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(keep), _ptr(margin), int(nthreads))
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(keep), _ptr(margin),
+                                 _ptr(dqc), _ptr(dkc), int(nthreads))
     if rc:
         raise ValueError(f"oracle_bwd failed with code {rc}")
-    return {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
+    out = {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
+    if cond:
+        out["dq_cond"], out["dk_cond"] = dqc, dkc
+    return out
 
 
 def oracle_bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, tau: float, Bq: int, Bk: int,
-                      qunits=None, kunits=None, do_dq=True, do_dkdv=True, nthreads: int = 0):
+                      qunits=None, kunits=None, do_dq=True, do_dkdv=True, cond: bool = False, nthreads: int = 0):
     """Variable-length backward over the packed layout of oracle_fwd_varlen
-    (lse [Hq, total_q]).  Returns dict(dq, dk, dv, keep, margin); unit ids as
-    in oracle_bwd with nQB, nKT from the longest sequence."""
+    (lse [Hq, total_q]).  Returns dict(dq, dk, dv, keep, margin), plus
+    dq_cond / dk_cond with `cond` as in oracle_bwd; unit ids as in oracle_bwd
+    with nQB, nKT from the longest sequence."""
     q, k, v, o, dout, lse = map(_f64, (q, k, v, o, dout, lse))
     cq = np.ascontiguousarray(cu_q, dtype=np.int32)
     ck = np.ascontiguousarray(cu_k, dtype=np.int32)
@@ -181,6 +195,8 @@ def oracle_bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, tau: float, Bq: int, Bk
     dq = np.full(q.shape, np.nan)
     dk = np.full(k.shape, np.nan)
     dv = np.full(k.shape, np.nan)
+    dqc = np.full(q.shape, np.nan) if cond else None
+    dkc = np.full(k.shape, np.nan) if cond else None
     keep = np.full((B, Hq, nQB, nKT), KEEP_UNVISITED, np.uint8)
     margin = np.full((B, Hq, nQB, nKT), np.nan)
     qa = None if qunits is None else np.ascontiguousarray(qunits, dtype=np.int32)
@@ -194,10 +210,14 @@ def oracle_bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, tau: float, Bq: int, Bk
     rc = _load().mala_oracle_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                         _ptr(cq), _ptr(ck), B, Hq, Hkv, d, float(tau), Bq, Bk,
                                         _ptr(qa), nq, _ptr(ka), nk,
-                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(keep), _ptr(margin), int(nthreads))
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(keep), _ptr(margin),
+                                        _ptr(dqc), _ptr(dkc), int(nthreads))
     if rc:
         raise ValueError(f"oracle_bwd_varlen failed with code {rc}")
-    return {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
+    out = {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
+    if cond:
+        out["dq_cond"], out["dk_cond"] = dqc, dkc
+    return out
 
 
 def oracle_decode(q, kc, vc, tau: float, Bkd: int, seqlens=None, nthreads: int = 0):

@@ -60,6 +60,23 @@
  *               (+inf if some row has l_i = 0),
  *     backward: max over rows with a legal key of (M_i - LSE_i - theta_i);
  * the tile is kept iff margin >= 0.
+ *
+ * Gradient error scales (optional backward outputs dq_cond, dk_cond, same
+ * layouts as dq, dk).  They are not part of the method: they size the error an
+ * evaluation of the gradient in binary32 arithmetic from bf16 inputs may
+ * make.  dS_ij = P_ij (dP_ij - D_i) subtracts two length-d
+ * dot products, dP_ij = dO_i . v_j and D_i = dO_i . o_i; summed in binary32
+ * from exact products, each errs by at most gamma_d times the same sum of
+ * absolute values, gamma_d = d u / (1 - d u), u = 2^-24 (Higham, "Accuracy and
+ * Stability of Numerical Algorithms", 2nd ed., section 3.1).  Carried through
+ * dq_i = scale sum_j dS_ij k_j and dk_j = scale sum_i dS_ij q_i, that moves
+ * the gradients by at most gamma_d times
+ *     dq_cond[i][c] = scale sum_j P_ij (|dO_i|.|v_j| + |dO_i|.|o_i|) |k_jc|
+ *     dk_cond[j][c] = scale sum_i P_ij (|dO_i|.|v_j| + |dO_i|.|o_i|) |q_ic|
+ * to first order (sums over the kept legal pairs; |x|.|y| = sum_c |x_c||y_c|;
+ * dk_cond summed over the q heads of the group).  Where dS cancels (a row
+ * whose attention sits on one key, so o_i is that key's value) this bound,
+ * not the gradient's own norm, is what such an evaluation can resolve.
  */
 #include <math.h>
 #include <stdint.h>
@@ -84,6 +101,12 @@ static double log_threshold(double tau, double L_vis) {
 static double dot(const double* a, const double* b, int d) {
     double s = 0.0;
     for (int c = 0; c < d; ++c) s += a[c] * b[c];
+    return s;
+}
+
+static double dot_abs(const double* a, const double* b, int d) {
+    double s = 0.0;
+    for (int c = 0; c < d; ++c) s += fabs(a[c]) * fabs(b[c]);
     return s;
 }
 
@@ -347,6 +370,7 @@ typedef struct {
     long lse_hstride;
     double tau, scale;
     double *dq, *dk, *dv, *margin;
+    double *dq_cond, *dk_cond;   /* NULL = not computed */
     uint8_t* keep;
 } bwd_ctx;
 
@@ -408,13 +432,17 @@ static int bwd_dq_block(const bwd_ctx* c, int b, int h, int qb) {
     if (r0 >= Lq) return OR_OK;                /* past the sequence's queries */
     const int r1 = (r0 + c->Bq < Lq) ? r0 + c->Bq : Lq;
     const int nr = r1 - r0;
-    double* S = (double*)malloc(sizeof(double) * ((size_t)nr * Bk + nr));
+    double* S = (double*)malloc(sizeof(double) * ((size_t)nr * Bk + 2 * (size_t)nr));
     if (!S) return OR_ENOMEM;
     double* D = S + (size_t)nr * Bk;
+    double* Da = D + nr;          /* |dO_i|.|o_i|, for dq_cond */
     for (int i = r0; i < r1; ++i) {
         const size_t row = qrow(c, b, i, h);
         D[i - r0] = dot(c->dout + row, c->o + row, d);
+        Da[i - r0] = dot_abs(c->dout + row, c->o + row, d);
         for (int cc = 0; cc < d; ++cc) c->dq[row + cc] = 0.0;
+        if (c->dq_cond)
+            for (int cc = 0; cc < d; ++cc) c->dq_cond[row + cc] = 0.0;
     }
     const int kt_last = (off + r1 - 1) / Bk;
     for (int kt = 0; kt <= kt_last; ++kt) {
@@ -434,6 +462,10 @@ static int bwd_dq_block(const bwd_ctx* c, int b, int h, int qb) {
                 const double dp = dot(c->dout + row, vj, d);
                 const double ds = p * (dp - D[i - r0]);
                 for (int cc = 0; cc < d; ++cc) c->dq[row + cc] += c->scale * ds * kj[cc];
+                if (c->dq_cond) {
+                    const double w = p * (dot_abs(c->dout + row, vj, d) + Da[i - r0]);
+                    for (int cc = 0; cc < d; ++cc) c->dq_cond[row + cc] += c->scale * w * fabs(kj[cc]);
+                }
             }
         }
     }
@@ -452,12 +484,15 @@ static int bwd_dkdv_tile(const bwd_ctx* c, int b, int kh, int kt) {
     const int j1 = (j0 + Bk < Lk) ? j0 + Bk : Lk;
     const int nQBb = (Lq + Bq - 1) / Bq;
     const int qb_lo = (j0 - off > 0 ? j0 - off : 0) / Bq;   /* first block with a row seeing key j0 */
-    double* S = (double*)malloc(sizeof(double) * ((size_t)Bq * Bk + Bq));
+    double* S = (double*)malloc(sizeof(double) * ((size_t)Bq * Bk + 2 * (size_t)Bq));
     if (!S) return OR_ENOMEM;
     double* D = S + (size_t)Bq * Bk;
+    double* Da = D + Bq;          /* |dO_i|.|o_i|, for dk_cond */
     for (int j = j0; j < j1; ++j) {
         const size_t kr = krow(c, b, j, kh);
         for (int cc = 0; cc < d; ++cc) { c->dk[kr + cc] = 0.0; c->dv[kr + cc] = 0.0; }
+        if (c->dk_cond)
+            for (int cc = 0; cc < d; ++cc) c->dk_cond[kr + cc] = 0.0;
     }
     for (int g = 0; g < G; ++g) {
         const int h = kh * G + g;
@@ -471,6 +506,7 @@ static int bwd_dkdv_tile(const bwd_ctx* c, int b, int kh, int kt) {
             for (int i = r0; i < r1; ++i) {
                 const size_t row = qrow(c, b, i, h);
                 D[i - r0] = dot(c->dout + row, c->o + row, d);
+                Da[i - r0] = dot_abs(c->dout + row, c->o + row, d);
             }
             for (int i = r0; i < r1; ++i) {
                 const size_t row = qrow(c, b, i, h);
@@ -483,6 +519,10 @@ static int bwd_dkdv_tile(const bwd_ctx* c, int b, int kh, int kt) {
                     for (int cc = 0; cc < d; ++cc) {
                         c->dv[kr + cc] += p * c->dout[row + cc];
                         c->dk[kr + cc] += c->scale * ds * c->q[row + cc];
+                    }
+                    if (c->dk_cond) {
+                        const double w = p * (dot_abs(c->dout + row, c->v + kr, d) + Da[i - r0]);
+                        for (int cc = 0; cc < d; ++cc) c->dk_cond[kr + cc] += c->scale * w * fabs(c->q[row + cc]);
                     }
                 }
             }
@@ -530,7 +570,8 @@ int mala_oracle_bwd(const double* q, const double* k, const double* v, const dou
                     const double* dout, const double* lse,
                     int B, int L, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
                     const int32_t* qunits, int nq, const int32_t* kunits, int nk,
-                    double* dq, double* dk, double* dv, uint8_t* keep, double* margin, int nthreads) {
+                    double* dq, double* dk, double* dv, uint8_t* keep, double* margin,
+                    double* dq_cond, double* dk_cond, int nthreads) {
     if (!q || !k || !v || !o || !dout || !lse) return OR_EINVAL;
     if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return OR_EINVAL;
     if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
@@ -549,6 +590,7 @@ int mala_oracle_bwd(const double* q, const double* k, const double* v, const dou
     c.qoff = offs; c.koff = offs; c.lseoff = offs + B; c.lq = lens; c.lk = lens; c.lse_hstride = L;
     c.tau = tau; c.scale = 1.0 / sqrt((double)d);
     c.dq = dq; c.dk = dk; c.dv = dv; c.keep = keep; c.margin = margin;
+    c.dq_cond = dq_cond; c.dk_cond = dk_cond;
     const int err = bwd_run(&c, qunits, nq, kunits, nk, nthreads);
     free(offs);
     free(lens);
@@ -563,7 +605,8 @@ int mala_oracle_bwd_varlen(const double* q, const double* k, const double* v, co
                            const double* dout, const double* lse, const int32_t* cu_q, const int32_t* cu_k,
                            int B, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
                            const int32_t* qunits, int nq, const int32_t* kunits, int nk,
-                           double* dq, double* dk, double* dv, uint8_t* keep, double* margin, int nthreads) {
+                           double* dq, double* dk, double* dv, uint8_t* keep, double* margin,
+                           double* dq_cond, double* dk_cond, int nthreads) {
     if (!q || !k || !v || !o || !dout || !lse || !cu_q || !cu_k) return OR_EINVAL;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return OR_EINVAL;
     if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
@@ -594,6 +637,7 @@ int mala_oracle_bwd_varlen(const double* q, const double* k, const double* v, co
     c.lse_hstride = cu_q[B];
     c.tau = tau; c.scale = 1.0 / sqrt((double)d);
     c.dq = dq; c.dk = dk; c.dv = dv; c.keep = keep; c.margin = margin;
+    c.dq_cond = dq_cond; c.dk_cond = dk_cond;
     const int err = bwd_run(&c, qunits, nq, kunits, nk, nthreads);
     free(offs);
     free(lens);

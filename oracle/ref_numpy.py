@@ -69,6 +69,7 @@ def fwd(q, k, v, tau, Bq, Bk):
     o = np.zeros_like(q)
     lse = np.zeros((B, Hq, L))
     keep = np.full((B, Hq, nQB, nKT), 255, np.uint8)
+    margin = np.full((B, Hq, nQB, nKT), np.nan)
     slots = np.zeros((B, Hq, L), np.int32)
     omitted = np.zeros((B, Hq, L))
     causal = np.tril(np.ones((L, L), bool))
@@ -82,9 +83,10 @@ def fwd(q, k, v, tau, Bq, Bk):
                 tiles = [(kt * Bk, min(L, (kt + 1) * Bk)) for kt in range(first, -1, -1)]
                 Sb = S[r0:r1]
                 leg = causal[r0:r1]
-                kept, m, l, dec, _ = rule_block(Sb, leg, np.arange(r0, r1) + 1, tau, tiles)
-                for t, kp in zip(range(first, -1, -1), dec):
+                kept, m, l, dec, mg = rule_block(Sb, leg, np.arange(r0, r1) + 1, tau, tiles)
+                for t, kp, x in zip(range(first, -1, -1), dec, mg):
                     keep[b, h, qb, t] = kp
+                    margin[b, h, qb, t] = x
                 w = np.where(kept, np.exp(Sb - m[:, None]), 0.0)
                 o[b, r0:r1, h, :] = (w @ v[b, :, kh, :]) / l[:, None]
                 lse[b, h, r0:r1] = m + np.log(l)
@@ -92,7 +94,7 @@ def fwd(q, k, v, tau, Bq, Bk):
                 # omitted probability mass among all legal keys
                 zall = np.where(leg, np.exp(Sb - m[:, None]), 0.0).sum(axis=1)
                 omitted[b, h, r0:r1] = 1.0 - l / zall
-    return {"o": o, "lse": lse, "keep": keep, "kept_slots": slots, "omitted": omitted}
+    return {"o": o, "lse": lse, "keep": keep, "margin": margin, "kept_slots": slots, "omitted": omitted}
 
 
 def fwd_varlen(q, k, v, cu_q, cu_k, tau, Bq, Bk):
@@ -140,6 +142,7 @@ def bwd(q, k, v, o, dout, lse, tau, Bq, Bk):
     sc = 1.0 / np.sqrt(d)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     keep = np.full((B, Hq, nQB, nKT), 255, np.uint8)
+    margin = np.full((B, Hq, nQB, nKT), np.nan)
     causal = np.tril(np.ones((L, L), bool))
     for b in range(B):
         for h in range(Hq):
@@ -156,6 +159,7 @@ def bwd(q, k, v, o, dout, lse, tau, Bq, Bk):
                     x = np.where(leg, S[r0:r1, j0:j1] - lse[b, h, r0:r1, None] - th[r0:r1, None], -np.inf)
                     kp = bool(x.max() >= 0)
                     keep[b, h, qb, kt] = kp
+                    margin[b, h, qb, kt] = x.max()
                     if kp:
                         mask[r0:r1, j0:j1] = leg
             Pm = np.where(mask, P, 0.0)
@@ -165,7 +169,7 @@ def bwd(q, k, v, o, dout, lse, tau, Bq, Bk):
             dq[b, :, h, :] = sc * dS @ k[b, :, kh, :]
             dk[b, :, kh, :] += sc * dS.T @ q[b, :, h, :]
             dv[b, :, kh, :] += Pm.T @ dout[b, :, h, :]
-    return {"dq": dq, "dk": dk, "dv": dv, "keep": keep}
+    return {"dq": dq, "dk": dk, "dv": dv, "keep": keep, "margin": margin}
 
 
 def bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, tau, Bq, Bk):
@@ -222,17 +226,19 @@ def decode(q, kc, vc, tau, Bkd):
     o = np.zeros_like(q)
     lse = np.zeros((B, Hq))
     keep = np.zeros((B, Hkv, nT), np.uint8)
+    margin = np.full((B, Hkv, nT), np.nan)
     for b in range(B):
         for kh in range(Hkv):
             S = (q[b, kh * G:(kh + 1) * G, :] @ kc[b, :, kh, :].T) / np.sqrt(d)
             tiles = [(t * Bkd, min(N, (t + 1) * Bkd)) for t in range(nT - 1, -1, -1)]
-            kept, m, l, dec, _ = rule_block(S, np.ones_like(S, bool), np.full(G, N), tau, tiles)
-            for t, kp in zip(range(nT - 1, -1, -1), dec):
+            kept, m, l, dec, mg = rule_block(S, np.ones_like(S, bool), np.full(G, N), tau, tiles)
+            for t, kp, x in zip(range(nT - 1, -1, -1), dec, mg):
                 keep[b, kh, t] = kp
+                margin[b, kh, t] = x
             w = np.where(kept, np.exp(S - m[:, None]), 0.0)
             o[b, kh * G:(kh + 1) * G, :] = (w @ vc[b, :, kh, :]) / l[:, None]
             lse[b, kh * G:(kh + 1) * G] = m + np.log(l)
-    return {"o": o, "lse": lse, "keep": keep}
+    return {"o": o, "lse": lse, "keep": keep, "margin": margin}
 
 
 def per_key_row(exp_scores, tau):

@@ -43,11 +43,20 @@ def run_decode_case(di, tau, label="", seqlens=None):
     Gq = Hq // Hkv
     badh = np.repeat(bad, Gq, axis=1)                      # [B, Hq]
     og = to_f64(o)
-    # one slice per sequence: its output [Hq, d] (a single head's d-vector is too
-    # few elements for a relative-L2 bound that includes the bf16 rounding of O)
+    # against the exact output, one slice per sequence ([Hq, d]): rounding a
+    # single head's 128 outputs to bf16 alone costs 1.7e-3 relative L2 on
+    # average and up to ~2.3e-3, too close to the 2e-3 bound to test per head
     worst, glob = rel_l2_per_head(np.where(badh[..., None], 0.0, og)[:, None],
                                   np.where(badh[..., None], 0.0, ref["o"])[:, None], head_axis=1)
     assert worst <= O_TOL, (worst, glob)
+    # per (sequence, head) against the exact output rounded to bf16 (the stored
+    # type): the rounding cancels, so what remains is the kernel's own error
+    # plus the rare element whose rounding the kernel's fp32 error flips
+    ob = G.bf16_bits_to_f64(G.round_to_bf16_bits(ref["o"]))
+    worst_bh = max((np.linalg.norm(og[b, h] - ob[b, h]) / np.linalg.norm(ob[b, h])
+                    for b in range(B) for h in range(Hq) if not badh[b, h] and np.isfinite(ob[b, h]).all()),
+                   default=0.0)
+    assert worst_bh <= O_TOL, worst_bh
     lg = lse.cpu().numpy().astype(np.float64)
     lerr = np.abs(lg - ref["lse"])[~badh]
     if lerr.size:
@@ -55,7 +64,7 @@ def run_decode_case(di, tau, label="", seqlens=None):
     kt = kept.cpu().numpy()
     assert np.array_equal(kt[~bad], ref["kept_tiles"][~bad])
     assert np.array_equal(kt, (gk == 1).sum(-1))
-    return dict(dec=dec, o_worst=worst, keep_frac=float(ref["keep"].mean()))
+    return dict(dec=dec, o_worst=worst, o_worst_per_head_vs_bf16=worst_bh, keep_frac=float(ref["keep"].mean()))
 
 
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 1000, 5000])

@@ -112,13 +112,17 @@ def test_fwd_gqa_8k():
     print(r)
 
 
-def test_fwd_train_128k_sampled():
-    """Full-size launch (L = 131072, Hq = 5, Hkv = 1); the oracle checks sampled blocks."""
+@pytest.mark.parametrize("stats_mode", [False, True])
+def test_fwd_train_128k_sampled(stats_mode):
+    """Full-size launch (L = 131072, Hq = 5, Hkv = 1); the oracle checks 8
+    query blocks of every head (40 of 5120).  Without statistics this is the
+    launch the benchmark times; with them it also checks omitted mass."""
     w = G.WORKLOADS["train_128k"]
     inp = G.workload_inputs("train_128k", with_dout=False)
     nQB = 131072 // 128
-    blocks = [h * nQB + qb for h, qb in ((0, 0), (1, 1), (2, 517), (3, nQB - 2), (4, nQB - 1), (0, nQB - 1))]
-    r = run_fwd_case(inp, 1.0, w["Bq"], w["Bk"], blocks=blocks, stats_mode=False, label="train_128k sampled")
+    blocks = [h * nQB + qb for h in range(5) for qb in (0, 1, 129 + h, 517, 700 + 3 * h, 900, nQB - 2, nQB - 1)]
+    r = run_fwd_case(inp, 1.0, w["Bq"], w["Bk"], blocks=blocks, stats_mode=stats_mode,
+                     label=f"train_128k sampled stats={stats_mode}")
     print(r)
 
 

@@ -29,7 +29,7 @@ def test_fwd_sweep(L, tau):
     inp = G.workload_inputs("sweep", L=L, with_dout=False)
     nQB = -(-L // w["Bq"])
     blocks = None if L <= 2048 else _sample_blocks(w["Hq"], nQB)
-    r = run_fwd_case(inp, tau, w["Bq"], w["Bk"], blocks=blocks, stats_mode=(L <= 2048), label=f"sweep L={L}")
+    r = run_fwd_case(inp, tau, w["Bq"], w["Bk"], blocks=blocks, stats_mode=True, label=f"sweep L={L}")
     print(L, tau, r)
 
 

@@ -8,6 +8,17 @@ import mala_gen as G
 from oracle import oracle_bwd, oracle_decode, oracle_fwd
 from oracle import ref_numpy as R
 
+def _same_margins(a, b, tol=1e-9):
+    """Decision log-margins agree: the same infinities and NaNs (unvisited
+    tiles), finite values within tol (relative above 1)."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(np.isposinf(a), np.isposinf(b))
+    assert np.array_equal(np.isneginf(a), np.isneginf(b))
+    f = np.isfinite(a)
+    assert np.all(np.abs(a[f] - b[f]) <= tol * np.maximum(1.0, np.abs(b[f])))
+
+
 shapes = st.fixed_dictionaries({
     "L": st.integers(1, 140),
     "Hkv": st.integers(1, 2),
@@ -32,6 +43,8 @@ def test_c_oracle_matches_numpy(s):
     a = oracle_fwd(q, k, v, s["tau"], s["Bq"], s["Bk"])
     b = R.fwd(q, k, v, s["tau"], s["Bq"], s["Bk"])
     assert (a["keep"] == b["keep"]).all()
+    _same_margins(a["margin"], b["margin"])
+    assert np.array_equal(a["margin"] >= 0, a["keep"] == 1)
     assert (a["kept_slots"] == b["kept_slots"]).all()
     assert np.abs(a["o"] - b["o"]).max() <= 1e-11
     assert np.abs(a["lse"] - b["lse"]).max() <= 1e-11
@@ -39,6 +52,7 @@ def test_c_oracle_matches_numpy(s):
     c = oracle_bwd(q, k, v, a["o"], do, a["lse"], s["tau"], s["Bq"], s["Bk"])
     e = R.bwd(q, k, v, a["o"], do, a["lse"], s["tau"], s["Bq"], s["Bk"])
     assert (c["keep"] == e["keep"]).all()
+    _same_margins(c["margin"], e["margin"])
     for n in ("dq", "dk", "dv"):
         assert np.abs(c[n] - e[n]).max() <= 1e-10 * max(1.0, np.abs(e[n]).max())
 
@@ -70,6 +84,7 @@ def test_c_decode_matches_numpy(N, Hkv, Gq, Bkd, tau, seed):
     a = oracle_decode(q, kc, vc, tau, Bkd)
     b = R.decode(q, kc, vc, tau, Bkd)
     assert (a["keep"] == b["keep"]).all()
+    _same_margins(a["margin"], b["margin"])
     assert np.abs(a["o"] - b["o"]).max() <= 1e-11
     assert np.abs(a["lse"] - b["lse"]).max() <= 1e-11
 

@@ -7,6 +7,7 @@ agihunt.info summary (rule, tau -> 0, bound) and the jaehun.me review
 bound on forward omitted mass", "How it works: a concrete example").
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -18,6 +19,23 @@ from oracle import oracle_bwd, oracle_decode, oracle_fwd
 from oracle import ref_numpy as R
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def hand_value(expr: str) -> float:
+    """Value of a fixture's hand-written expression: numbers, + - * / and
+    parentheses, ln(...) for the natural log, inf."""
+    import math
+    if not set(expr) <= set("0123456789.+-*/() lninf"):
+        raise ValueError(expr)
+    return float(eval(expr, {"__builtins__": {}}, {"ln": math.log, "inf": math.inf}))
+
+
+def assert_margin(got: float, expr: str):
+    want = hand_value(expr)
+    if math.isinf(want):
+        assert got == want, (got, expr)
+    else:
+        assert abs(got - want) <= 1e-12 * max(1.0, abs(want)), (got, want, expr)
 
 
 def _inputs(seed, B=1, L=300, Hq=4, Hkv=2, d=32, p=0.1, diffuse=()):
@@ -55,6 +73,11 @@ def test_worked_example_forward_and_backward():
     b = oracle_bwd(q, k, v, f["o"], dout, f["lse"], facts["tau"], 1, 1)
     bk = sorted(int(j) for j in range(4) if b["keep"][0, 0, 3, j] == 1)
     assert bk == sorted(facts["retained_keys"])
+    # decision log-margins of row 3, worked by hand from the exp-scores
+    for m in g["margins"]["fwd"]:
+        assert_margin(f["margin"][0, 0, 3, m["key"]], m["expr"])
+    for m in g["margins"]["bwd"]:
+        assert_margin(b["margin"][0, 0, 3, m["key"]], m["expr"])
 
 
 @pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "hand_rules.json")))["cases"],
@@ -80,6 +103,12 @@ def test_hand_derived_rules(case):
     for r in range(nr):
         i = r0 + r
         assert sorted(np.nonzero(kb[0, 0, i])[0].tolist()) == case["bwd_kept_keys"][r], (case["name"], i)
+    # decision log-margins of the case's block, worked by hand
+    qb = r0 // Bq
+    for m in case["fwd_margins"]:
+        assert_margin(f["margin"][0, 0, qb, m["key_tile"]], m["expr"])
+    for m in case["bwd_margins"]:
+        assert_margin(b["margin"][0, 0, qb, m["key_tile"]], m["expr"])
 
 
 # ---------------------------------------------------------------- tau -> 0 is full attention
