@@ -7,8 +7,10 @@ fallback: if the library is missing or the tensors are not on a HIP device,
 the calls raise.
 
 Names follow the C ABI: mala_fwd, mala_fwd_varlen, mala_bwd, mala_bwd_varlen, mala_decode (with optional
-per-sequence cache lengths: mala_decode_varlen), plus the autograd
-wrapper `mala_attention` (saves only q, k, v, o and lse for the backward).
+per-sequence cache lengths: mala_decode_varlen), mala_decode_noalloc (decode
+on the library's own fixed device scratch, for callers that cannot
+allocate), plus the autograd wrapper `mala_attention` (saves only q, k, v, o
+and lse for the backward).
 """
 from __future__ import annotations
 
@@ -44,7 +46,11 @@ class MalaTileStats(ctypes.Structure):
 
 EXPORTS = ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
            "mala_bwd", "mala_bwd_workspace_size", "mala_bwd_varlen", "mala_bwd_varlen_workspace_size",
-           "mala_decode", "mala_decode_workspace_size", "mala_decode_varlen", "mala_status_string", "mala_version")
+           "mala_decode", "mala_decode_workspace_size", "mala_decode_varlen", "mala_decode_noalloc",
+           "mala_status_string", "mala_version")
+
+# include/mala.h: MALA_DECODE_NOALLOC_MAX_BYTES
+DECODE_NOALLOC_MAX_BYTES = 64 << 20
 
 _lib = None
 
@@ -86,6 +92,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mala_decode.restype = I
     lib.mala_decode_varlen.argtypes = [P, MalaT4, MalaT4, P, I, I, I, I, I, F, I, P, P, P, P, P, S, P]
     lib.mala_decode_varlen.restype = I
+    lib.mala_decode_noalloc.argtypes = [P, MalaT4, MalaT4, I, I, I, I, I, F, I, P, P, P, P, P]
+    lib.mala_decode_noalloc.restype = I
     lib.mala_status_string.argtypes = [I]
     lib.mala_status_string.restype = ctypes.c_char_p
     lib.mala_version.restype = ctypes.c_char_p
@@ -336,6 +344,27 @@ def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, l
                                     float(tau), Bk_dec, _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits),
                                     _ptr(ws), ws.numel(), _stream(q))
         _check("mala_decode_varlen", rc)
+    return o, lse, kept_tiles
+
+
+def mala_decode_noalloc(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, lse=None, kept_tiles=None,
+                        decision_bits=None):
+    """mala_decode on the library's fixed per-GPU scratch (no workspace; the
+    C call allocates nothing).  Shapes as for mala_decode; the workspace the
+    shape needs (decode_workspace_size) must not exceed
+    DECODE_NOALLOC_MAX_BYTES.  Calls that overlap in time on one GPU share
+    the scratch and race: serialise them."""
+    _dev_check(q, kcache, vcache)
+    B, Hq, d = q.shape
+    N, Hkv = kcache.shape[1], kcache.shape[2]
+    if not q.is_contiguous() or q.dtype != torch.bfloat16:
+        raise ValueError("q must be a contiguous bf16 [B, Hq, d] tensor")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    kept_tiles = torch.empty((B, Hkv), dtype=torch.int32, device=q.device) if kept_tiles is None else kept_tiles
+    rc = load_library().mala_decode_noalloc(_ptr(q), _t4(kcache), _t4(vcache), B, N, Hq, Hkv, d, float(tau), Bk_dec,
+                                            _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits), _stream(q))
+    _check("mala_decode_noalloc", rc)
     return o, lse, kept_tiles
 
 

@@ -4,10 +4,19 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/mala.h"
 #include "mala_internal.h"
 
 using namespace mala;
+
+// Device scratch of mala_decode_noalloc, for callers that cannot allocate.
+// Each GPU holds its own copy for the life of the process.  Host code never
+// passes `scratch` itself (its host-side name is only a handle): the address
+// on each device comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and kept in scratch_addr[].
+static __device__ __align__(256) unsigned char scratch[MALA_DECODE_NOALLOC_MAX_BYTES];
 
 namespace {
 
@@ -74,6 +83,21 @@ void decode_split(int B, int Hkv, int nT, int* nsplit, int* tps) {
     ns = (nT + t - 1) / t;
     *nsplit = ns;
     *tps = t;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+
+// This device's address of `scratch` (nullptr on failure).  Concurrent first
+// calls on one device look it up twice and store the same value.
+void* device_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* ptr = scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_addr[dev].store(ptr, std::memory_order_release);
+    return ptr;
 }
 
 }  // namespace
@@ -427,6 +451,22 @@ mala_status mala_decode(const void* q, mala_t4 kcache, mala_t4 vcache, int B, in
                         uint32_t* decision_bits, void* ws, size_t ws_bytes, void* stream) {
     return decode_impl(q, kcache, vcache, nullptr, B, N, Hq, Hkv, d, tau, Bk_dec, o, lse, kept_tiles, decision_bits,
                        ws, ws_bytes, stream);
+}
+
+mala_status mala_decode_noalloc(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
+                                int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
+                                uint32_t* decision_bits, void* stream) {
+    const size_t need = mala_decode_workspace_size(B, N, Hq, Hkv, d, Bk_dec);
+    if (need == 0 || need > (size_t)MALA_DECODE_NOALLOC_MAX_BYTES) {
+        // reports the argument error if there is one, else MALA_ERR_WORKSPACE;
+        // with no workspace nothing is enqueued
+        return decode_impl(q, kcache, vcache, nullptr, B, N, Hq, Hkv, d, tau, Bk_dec, o, lse, kept_tiles,
+                           decision_bits, nullptr, 0, stream);
+    }
+    void* ws = device_scratch();
+    if (!ws) return MALA_ERR_HIP;
+    return decode_impl(q, kcache, vcache, nullptr, B, N, Hq, Hkv, d, tau, Bk_dec, o, lse, kept_tiles, decision_bits,
+                       ws, (size_t)MALA_DECODE_NOALLOC_MAX_BYTES, stream);
 }
 
 mala_status mala_decode_varlen(const void* q, mala_t4 kcache, mala_t4 vcache, const int32_t* cache_seqlens, int B,

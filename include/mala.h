@@ -27,7 +27,11 @@
  *     the scaled scores.
  *   - GQA: Hq must be a multiple of Hkv; q head h reads KV head h / (Hq/Hkv).
  *   - The caller owns every buffer, including workspaces; the library
- *     allocates no device memory and keeps no mutable global state.
+ *     allocates no device memory.  Its only global state is written once per
+ *     device and then only read: a cache of the device's compute-unit count,
+ *     and the device address of mala_decode_noalloc's fixed scratch array
+ *     (that array, one per GPU, is the one buffer the library owns).
+ *     Concurrent first calls store the same values.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting.  Arguments are validated on the host
  *     before anything is enqueued: an invalid call enqueues nothing.
@@ -234,6 +238,31 @@ mala_status mala_decode_varlen(const void* q, mala_t4 kcache, mala_t4 vcache, co
                                int N, int Hq, int Hkv, int d, float tau, int Bk_dec, void* o, float* lse,
                                int32_t* kept_tiles, uint32_t* decision_bits, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* Largest workspace mala_decode_noalloc can serve: 64 MiB, enough for
+ * mala_decode_workspace_size of 8 sequences x 131072 cached keys x 5 q heads
+ * per KV head (about 32 MiB) twice over. */
+#define MALA_DECODE_NOALLOC_MAX_BYTES (64u << 20)
+
+/* mala_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results as mala_decode, without ws / ws_bytes: the
+ * workspace is a fixed array of MALA_DECODE_NOALLOC_MAX_BYTES in the
+ * library's device code, one per GPU, held until the process ends.  Nothing
+ * is allocated, by the library or anything it calls.
+ *   Calls whose mala_decode_workspace_size(B, N, Hq, Hkv, d, Bk_dec) exceeds
+ *   MALA_DECODE_NOALLOC_MAX_BYTES return MALA_ERR_WORKSPACE and enqueue
+ *   nothing (after the argument checks of mala_decode, whose errors come
+ *   first).  MALA_ERR_HIP if the array's address cannot be found on the
+ *   current device (more than 64 devices, or a runtime failure).
+ *   Every call on one GPU shares that GPU's array, so calls that may overlap
+ *   in time on one GPU (other streams, other threads) race and give wrong
+ *   results: serialise them, or use mala_decode with separate workspaces.
+ *   Each call writes every part of the array it reads before reading it;
+ *   nothing from an earlier call carries over. */
+mala_status mala_decode_noalloc(const void* q, mala_t4 kcache, mala_t4 vcache, int B, int N, int Hq, int Hkv,
+                                int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
+                                uint32_t* decision_bits, void* stream);
 
 /* Static string naming a status code. */
 const char* mala_status_string(mala_status s);

@@ -127,6 +127,30 @@ def test_decode_workspace_and_errors():
     assert lib.mala_decode(*bad, ctypes.c_void_p(1 << 20), 1 << 30, None) == mala.MALA_ERR_INVALID_ARG
 
 
+def test_decode_noalloc_refuses_before_touching_the_gpu():
+    """The allocation-free decode: argument errors as mala_decode, then
+    MALA_ERR_WORKSPACE for shapes whose workspace exceeds the fixed scratch;
+    neither reaches HIP (this runs without a GPU)."""
+    lib = mala.load_library()
+    cap = mala.DECODE_NOALLOC_MAX_BYTES
+    hdr = open(os.path.join(ROOT, "include", "mala.h")).read()
+    assert f"#define MALA_DECODE_NOALLOC_MAX_BYTES ({cap >> 20}u << 20)" in hdr
+    # the benchmarked decode (8 sequences x 131072 keys, 5 q heads per KV head) fits; 32 sequences do not
+    assert 0 < lib.mala_decode_workspace_size(8, 131072, 5, 1, 128, 64) <= cap
+    assert lib.mala_decode_workspace_size(32, 131072, 5, 1, 128, 64) > cap
+    t = _t4()
+    q, o, lse = ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288)
+    big = [q, t, t, 32, 131072, 5, 1, 128, 1.0, 64, o, lse, None, None, None]
+    assert lib.mala_decode_noalloc(*big) == mala.MALA_ERR_WORKSPACE
+    bad = list(big)
+    bad[8] = float("nan")
+    assert lib.mala_decode_noalloc(*bad) == mala.MALA_ERR_INVALID_ARG
+    bad = [q, t, t, 2, 1000, 4, 2, 128, 1.0, 32, o, lse, None, None, None]
+    assert lib.mala_decode_noalloc(*bad) == mala.MALA_ERR_UNSUPPORTED
+    bad = [q, t, t, 2, 1000, 4, 3, 128, 1.0, 64, o, lse, None, None, None]     # Hq % Hkv != 0
+    assert lib.mala_decode_noalloc(*bad) == mala.MALA_ERR_INVALID_ARG
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 128, 1, 128, dtype=torch.bfloat16)

@@ -1,0 +1,67 @@
+"""mala_decode_noalloc (the allocation-free decode on the library's fixed
+per-GPU scratch) against mala_decode with its own workspace, through the C
+ABI, on two calls in a row -- the benchmarked decode (8 sequences x 131072
+cached keys, 5 q heads per KV head), then a smaller one that finds the first
+call's data still in the scratch -- and a dense (tau = 0) call.  Each result
+must equal mala_decode's bit for bit and match the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import adaptive_tile_skipping_amd as mala
+import mala_gen as G
+from oracle import oracle_decode
+from parity import bf16_tensor, compare_decisions, to_f64, unpack_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(di, tau, label):
+    dev = torch.device("cuda:0")
+    B, Hq, d = di["q"].shape
+    N, Hkv = di["k"].shape[1], di["k"].shape[2]
+    nT = -(-N // 64)
+    print(f"[noalloc] {label} B={B} N={N} Hq={Hq} Hkv={Hkv} d={d} tau={tau}", flush=True)
+    q, kc, vc = (bf16_tensor(di[x], dev) for x in ("q", "k", "v"))
+    bits_a = torch.empty((B, Hkv, -(-nT // 32)), dtype=torch.int32, device=dev)
+    bits_b = torch.empty_like(bits_a)
+    oa, la, ka = mala.mala_decode_noalloc(q, kc, vc, tau, decision_bits=bits_a)
+    ob, lb, kb = mala.mala_decode(q, kc, vc, tau, decision_bits=bits_b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(la, lb) and torch.equal(ka, kb) and torch.equal(bits_a, bits_b)
+    ref = oracle_decode(*(G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")), tau, 64)
+    gk = unpack_bits(bits_a.cpu().numpy(), nT)
+    dec = compare_decisions(gk, ref["keep"], ref["margin"], descending=True)
+    assert dec["nonexempt"] == 0, dec
+    og = to_f64(oa)
+    for b in range(B):
+        if (gk[b] != ref["keep"][b]).any():
+            continue      # a near-tie (exempt) decision flipped: outputs differ by design
+        err = np.linalg.norm(og[b] - ref["o"][b]) / np.linalg.norm(ref["o"][b])
+        assert err <= 2e-3, (b, err)
+    return oa
+
+
+def test_noalloc_decode_two_calls_then_dense():
+    big = G.workload_inputs("decode_128k")
+    assert mala.load_library().mala_decode_workspace_size(8, 131072, 5, 1, 128, 64) <= mala.DECODE_NOALLOC_MAX_BYTES
+    _case(big, 1.0, "decode_128k")
+    small = G.decode_inputs(1500, 3, 5000, 6, 2, 128)
+    _case(small, 1.0, "smaller, after decode_128k")
+    _case(small, 0.0, "smaller, dense")
+
+
+def test_noalloc_decode_refuses_oversized_shape_and_leaves_outputs():
+    dev = torch.device("cuda:0")
+    B, N, Hq, Hkv, d = 32, 131072, 5, 1, 128
+    assert mala.load_library().mala_decode_workspace_size(B, N, Hq, Hkv, d, 64) > mala.DECODE_NOALLOC_MAX_BYTES
+    q = torch.zeros((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((B, 64, Hkv, d), dtype=torch.bfloat16, device=dev).expand(B, 64, Hkv, d)
+    # a cache view claiming N rows is never read: the call is refused on the host
+    kc = torch.as_strided(kc, (B, N, Hkv, d), (0, 0, d, 1))
+    o = torch.full((B, Hq, d), 7.0, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(mala.MalaError) as e:
+        mala.mala_decode_noalloc(q, kc, kc, 1.0, o=o)
+    assert e.value.code == mala.MALA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert (o == 7.0).all()
