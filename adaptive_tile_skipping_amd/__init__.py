@@ -133,6 +133,40 @@ def _dev_check(*ts):
             raise RuntimeError("libmala runs on the GPU only: tensors must live on a HIP device")
 
 
+def _expect(t, shape, dtype, name: str, device, contiguous: bool = False):
+    """Raise ValueError unless t has exactly this shape and dtype, lives on
+    `device`, and (if asked) is contiguous.  Run before anything is enqueued:
+    a wrongly shaped buffer would be read or written out of its bounds."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_stats(stats, B, Hq, rows, nQB, nKT, device, varlen: bool = False):
+    """Shapes of the optional statistics outputs (make_stats /
+    make_varlen_stats)."""
+    if not stats:
+        return
+    row_shape = (Hq, rows) if varlen else (B, Hq, rows)
+    _expect(stats.get("kept_tiles"), (B, Hq, nQB), torch.int32, "stats['kept_tiles']", device, True)
+    _expect(stats.get("kept_slots"), row_shape, torch.int32, "stats['kept_slots']", device, True)
+    _expect(stats.get("omitted_mass"), row_shape, torch.float32, "stats['omitted_mass']", device, True)
+    _expect(stats.get("decision_bits"), (B, Hq, nQB, -(-nKT // 32)), torch.int32, "stats['decision_bits']", device,
+            True)
+
+
+def _check_ws(ws, device):
+    if ws is not None and (ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous uint8 tensor on the device of q")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -171,16 +205,21 @@ def mala_fwd(q, k, v, tau: float = 1.0, Bq: int = 128, Bk: int = 64, o=None, lse
     """Forward.  q [B,L,Hq,d], k/v [B,L,Hkv,d] bf16 on the GPU.
     Returns (o [B,L,Hq,d] bf16, lse [B,Hq,L] fp32)."""
     _dev_check(q, k, v)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, L, Hq, d] and k, v [B, L, Hkv, d]")
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
-    if k.shape != (B, L, Hkv, d) or v.shape != k.shape:
-        raise ValueError("q, k, v shapes disagree")
+    dev = q.device
+    _expect(k, (B, L, Hkv, d), torch.bfloat16, "k", dev)
+    _expect(v, (B, L, Hkv, d), torch.bfloat16, "v", dev)
+    _expect(o, (B, L, Hq, d), torch.bfloat16, "o", dev)
+    _expect(lse, (B, Hq, L), torch.float32, "lse", dev, True)
+    _check_stats(stats, B, Hq, L, -(-L // Bq), -(-L // Bk), dev)
+    _check_ws(ws, dev)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
-    if not lse.is_contiguous() or lse.dtype != torch.float32:
-        raise ValueError("lse must be a contiguous float32 [B, Hq, L] tensor")
     if ws is None:
         ws = fwd_workspace(B, L, Hq, Hkv, d, Bq, Bk, q.device)
     lib = load_library()
@@ -216,22 +255,28 @@ def mala_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     q [total_q,Hq,d], k/v [total_k,Hkv,d] bf16; cu_seqlens_* int32 [B+1] on the
     same device.  Returns (o [total_q,Hq,d] bf16, lse [Hq,total_q] fp32)."""
     _dev_check(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
     Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
-    if k.shape != (Tk, Hkv, d) or v.shape != k.shape:
-        raise ValueError("q, k, v shapes disagree")
+    dev = q.device
+    _expect(k, (Tk, Hkv, d), torch.bfloat16, "k", dev)
+    _expect(v, (Tk, Hkv, d), torch.bfloat16, "v", dev)
     for c in (cu_seqlens_q, cu_seqlens_k):
-        if c.dtype != torch.int32 or not c.is_contiguous() or c.dim() != 1:
-            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] tensors")
+        if c.dtype != torch.int32 or not c.is_contiguous() or c.dim() != 1 or c.device != dev:
+            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] tensors on the device of q")
     B = cu_seqlens_q.numel() - 1
     if B < 1 or cu_seqlens_k.numel() != B + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 entries")
+    _expect(o, (Tq, Hq, d), torch.bfloat16, "o", dev)
+    _expect(lse, (Hq, Tq), torch.float32, "lse", dev, True)
+    _check_stats(stats, B, Hq, Tq, max(1, -(-int(max_seqlen_q) // Bq)), max(1, -(-int(max_seqlen_k) // Bk)), dev,
+                 varlen=True)
+    _check_ws(ws, dev)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
-    if not lse.is_contiguous() or lse.dtype != torch.float32:
-        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
     if ws is None:
         ws = fwd_varlen_workspace(B, Tk, Hkv, d, Bq, Bk, q.device)
     lib = load_library()
@@ -253,15 +298,26 @@ def mala_bwd(q, k, v, o, dout, lse, tau: float = 1.0, Bq: int = 128, Bk: int = 6
              dq=None, dk=None, dv=None, ws=None, stats: dict | None = None):
     """Backward.  Returns (dq, dk, dv) bf16."""
     _dev_check(q, k, v, o, dout, lse)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, L, Hq, d] and k, v [B, L, Hkv, d]")
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
+    dev = q.device
+    _expect(k, (B, L, Hkv, d), torch.bfloat16, "k", dev)
+    _expect(v, (B, L, Hkv, d), torch.bfloat16, "v", dev)
+    _expect(o, (B, L, Hq, d), torch.bfloat16, "o", dev)
+    _expect(dout, (B, L, Hq, d), torch.bfloat16, "dout", dev)
+    _expect(lse, (B, Hq, L), torch.float32, "lse", dev, True)
+    _expect(dq, (B, L, Hq, d), torch.bfloat16, "dq", dev)
+    _expect(dk, (B, L, Hkv, d), torch.bfloat16, "dk", dev)
+    _expect(dv, (B, L, Hkv, d), torch.bfloat16, "dv", dev)
+    _check_stats(stats, B, Hq, L, -(-L // Bq), -(-L // Bk), dev)
+    _check_ws(ws, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if ws is None:
         ws = bwd_workspace(B, L, Hq, Hkv, d, Bq, Bk, q.device)
-    if not lse.is_contiguous() or lse.dtype != torch.float32:
-        raise ValueError("lse must be a contiguous float32 [B, Hq, L] tensor")
     lib = load_library()
     rc = lib.mala_bwd(_t4(q), _t4(k), _t4(v), _t4(o), _t4(dout), _ptr(lse), B, L, Hq, Hkv, d, float(tau), Bq, Bk,
                       _t4(dq), _t4(dk), _t4(dv), _ptr(ws), ws.numel(), _stats_struct(stats), _stream(q))
@@ -282,16 +338,28 @@ def mala_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
     """Backward of mala_fwd_varlen.  Packed q/o/dout [total_q,Hq,d], k/v
     [total_k,Hkv,d] bf16, lse [Hq,total_q] fp32.  Returns (dq, dk, dv) bf16."""
     _dev_check(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [total_q, Hq, d] and k, v [total_k, Hkv, d]")
     Tq, Hq, d = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
+    dev = q.device
     for c in (cu_seqlens_q, cu_seqlens_k):
-        if c.dtype != torch.int32 or not c.is_contiguous() or c.dim() != 1:
-            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] tensors")
+        if c.dtype != torch.int32 or not c.is_contiguous() or c.dim() != 1 or c.device != dev:
+            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] tensors on the device of q")
     B = cu_seqlens_q.numel() - 1
     if B < 1 or cu_seqlens_k.numel() != B + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 entries")
-    if not lse.is_contiguous() or lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, Tq):
-        raise ValueError("lse must be a contiguous float32 [Hq, total_q] tensor")
+    _expect(k, (Tk, Hkv, d), torch.bfloat16, "k", dev)
+    _expect(v, (Tk, Hkv, d), torch.bfloat16, "v", dev)
+    _expect(o, (Tq, Hq, d), torch.bfloat16, "o", dev)
+    _expect(dout, (Tq, Hq, d), torch.bfloat16, "dout", dev)
+    _expect(lse, (Hq, Tq), torch.float32, "lse", dev, True)
+    _expect(dq, (Tq, Hq, d), torch.bfloat16, "dq", dev)
+    _expect(dk, (Tk, Hkv, d), torch.bfloat16, "dk", dev)
+    _expect(dv, (Tk, Hkv, d), torch.bfloat16, "dv", dev)
+    _check_stats(stats, B, Hq, Tq, max(1, -(-int(max_seqlen_q) // Bq)), max(1, -(-int(max_seqlen_k) // Bk)), dev,
+                 varlen=True)
+    _check_ws(ws, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -304,6 +372,22 @@ def mala_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_k, max_seqle
                              _stats_struct(stats), _stream(q))
     _check("mala_bwd_varlen", rc)
     return dq, dk, dv
+
+
+def _check_decode(q, kcache, vcache, Bk_dec, o, lse, kept_tiles, decision_bits):
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and the caches [B, N, Hkv, d]")
+    B, Hq, d = q.shape
+    N, Hkv = kcache.shape[1], kcache.shape[2]
+    dev = q.device
+    _expect(q, (B, Hq, d), torch.bfloat16, "q", dev, True)
+    _expect(kcache, (B, N, Hkv, d), torch.bfloat16, "kcache", dev)
+    _expect(vcache, (B, N, Hkv, d), torch.bfloat16, "vcache", dev)
+    _expect(o, (B, Hq, d), torch.bfloat16, "o", dev, True)
+    _expect(lse, (B, Hq), torch.float32, "lse", dev, True)
+    _expect(kept_tiles, (B, Hkv), torch.int32, "kept_tiles", dev, True)
+    _expect(decision_bits, (B, Hkv, -(-(-(-N // Bk_dec)) // 32)), torch.int32, "decision_bits", dev, True)
+    return B, Hq, d, N, Hkv
 
 
 def decode_workspace(B, N, Hq, Hkv, d, Bk_dec=64, device="cuda"):
@@ -322,10 +406,7 @@ def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, l
     device; sequence b then uses only its first cache_seqlens[b] cache rows
     (mala_decode_varlen)."""
     _dev_check(q, kcache, vcache, cache_seqlens)
-    B, Hq, d = q.shape
-    N, Hkv = kcache.shape[1], kcache.shape[2]
-    if not q.is_contiguous() or q.dtype != torch.bfloat16:
-        raise ValueError("q must be a contiguous bf16 [B, Hq, d] tensor")
+    B, Hq, d, N, Hkv = _check_decode(q, kcache, vcache, Bk_dec, o, lse, kept_tiles, decision_bits)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
     kept_tiles = torch.empty((B, Hkv), dtype=torch.int32, device=q.device) if kept_tiles is None else kept_tiles
@@ -338,8 +419,7 @@ def mala_decode(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o=None, l
                              _stream(q))
         _check("mala_decode", rc)
     else:
-        if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != B or not cache_seqlens.is_contiguous():
-            raise ValueError("cache_seqlens must be a contiguous int32 [B] tensor")
+        _expect(cache_seqlens, (B,), torch.int32, "cache_seqlens", q.device, True)
         rc = lib.mala_decode_varlen(_ptr(q), _t4(kcache), _t4(vcache), _ptr(cache_seqlens), B, N, Hq, Hkv, d,
                                     float(tau), Bk_dec, _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits),
                                     _ptr(ws), ws.numel(), _stream(q))
@@ -355,10 +435,7 @@ def mala_decode_noalloc(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o
     DECODE_NOALLOC_MAX_BYTES.  Calls that overlap in time on one GPU share
     the scratch and race: serialise them."""
     _dev_check(q, kcache, vcache)
-    B, Hq, d = q.shape
-    N, Hkv = kcache.shape[1], kcache.shape[2]
-    if not q.is_contiguous() or q.dtype != torch.bfloat16:
-        raise ValueError("q must be a contiguous bf16 [B, Hq, d] tensor")
+    B, Hq, d, N, Hkv = _check_decode(q, kcache, vcache, Bk_dec, o, lse, kept_tiles, decision_bits)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
     kept_tiles = torch.empty((B, Hkv), dtype=torch.int32, device=q.device) if kept_tiles is None else kept_tiles

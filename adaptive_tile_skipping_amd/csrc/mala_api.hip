@@ -100,6 +100,13 @@ void* device_scratch() {
     return ptr;
 }
 
+// P.V workgroups of the tau > 0 decode: persistent, two per CU at most; the
+// kept tiles of all groups are split evenly over them on the device.
+int decode_pv_workgroups(int B, int Hkv, int nT) {
+    const int64_t tiles = (int64_t)B * Hkv * nT;
+    return (int)(tiles < 512 ? (tiles < 1 ? 1 : tiles) : 512);
+}
+
 }  // namespace
 
 extern "C" {
@@ -387,14 +394,16 @@ size_t mala_decode_workspace_size(int B, int N, int Hq, int Hkv, int d, int Bk_d
     int ns, tps;
     decode_split(B, Hkv, (int)nT, &ns, &tps);
     const size_t nsplit = (size_t)ns;
-    const size_t npart = nsplit > (nT + 3) / 4 ? nsplit : (nT + 3) / 4;
+    const size_t npv = decode_pv_workgroups(B, Hkv, (int)nT);
+    const size_t nslot = grp * nsplit > npv + grp ? grp * nsplit : npv + grp;
     size_t s = 0;
     s += 2 * align256(grp * G * ((nT + 3) / 4 * 4) * sizeof(float));   // tmax, tsum
-    s += align256(grp * G * (size_t)N * sizeof(float));       // spill
+    s += align256(grp * nT * G * Bk_dec * sizeof(uint16_t));   // spill
     s += align256(grp * nT * sizeof(int32_t));                // klist
     s += align256(grp * sizeof(int32_t));                     // kcount
     s += align256(grp * G * sizeof(float));                   // lse2
-    s += align256(grp * npart * G * d * sizeof(float));       // part_o
+    s += align256(grp * 2 * sizeof(int32_t));                 // pvinfo
+    s += align256(nslot * G * d * sizeof(float));             // part_o
     s += align256(grp * nsplit * G * 2 * sizeof(float));      // part_ml
     return s;
 }
@@ -432,12 +441,15 @@ mala_status decode_impl(const void* q, mala_t4 kcache, mala_t4 vcache, const int
     p.nTp = (p.nT + 3) / 4 * 4;
     p.tmax = (float*)w; w += align256(grp * G * (size_t)p.nTp * sizeof(float));
     p.tsum = (float*)w; w += align256(grp * G * (size_t)p.nTp * sizeof(float));
-    p.spill = (float*)w; w += align256(grp * G * (size_t)N * sizeof(float));
+    p.spill = (uint16_t*)w; w += align256(grp * nT * G * Bk_dec * sizeof(uint16_t));
     p.klist = (int32_t*)w; w += align256(grp * nT * sizeof(int32_t));
     p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));
     p.lse2 = (float*)w; w += align256(grp * G * sizeof(float));
-    p.npart = p.nsplit > (p.nT + 3) / 4 ? p.nsplit : (p.nT + 3) / 4;
-    p.part_o = (float*)w; w += align256(grp * (size_t)p.npart * G * d * sizeof(float));
+    p.pvinfo = (int32_t*)w; w += align256(grp * 2 * sizeof(int32_t));
+    p.npart = p.nsplit;
+    p.npv = decode_pv_workgroups(B, Hkv, p.nT);
+    const size_t nslot = grp * (size_t)p.nsplit > (size_t)p.npv + grp ? grp * (size_t)p.nsplit : (size_t)p.npv + grp;
+    p.part_o = (float*)w; w += align256(nslot * G * d * sizeof(float));
     p.part_ml = (float*)w;
     hipError_t e = launch_decode(p, d, Bk_dec, tau == 0.f, (hipStream_t)stream);
     return e == hipSuccess ? MALA_OK : MALA_ERR_HIP;

@@ -11,26 +11,20 @@
 //
 // Kernels (tau > 0):
 //   mala_dec_score   persistent waves, each streaming a contiguous run of
-//                    tiles with the next tile's K fragments loaded into
-//                    registers while the current tile is scored: S^T = K q^T
-//                    with 32x32x16 bf16 MFMAs (the G rows padded to 32
-//                    columns).  Writes per-row tile max and shifted sum and the
-//                    base-2 scores (spill).  Reads every K byte once: the
+//                    tiles: S^T = K q^T with 16x16x32 bf16 MFMAs (the G rows
+//                    as columns), per-row tile max and shifted sum, and the
+//                    shifted exponentials rounded to fp16 as the spill, staged
+//                    in LDS and written per run.  Reads every K byte once: the
 //                    HBM-bound score discovery.
-//   mala_dec_decide  one wave per (sequence, KV head): the sequential rule,
-//                    evaluated 64 tiles per round.  The candidate set is every
-//                    tile that votes keep under the state at the start of the
-//                    round; an exact log-sum-exp prefix scan gives each tile the
-//                    retained mass it would see if all earlier candidates are
-//                    kept.  Candidates that still vote keep up to the first one
-//                    that flips to skip are final (their prefixes were exact);
-//                    the flipped tile is skipped and the next round starts after
-//                    it.  A tile that votes skip under a smaller retained mass
-//                    can never turn to keep, so non-candidates are final too.
-//   mala_dec_pv      kept tiles only, one wave per tile: P = 2^(s - lse) from
-//                    the spill, V rows loaded at once, fp32 accumulation, one
-//                    partial output per workgroup of four tiles.
-//   mala_dec_sum_combine  sums the partials (already normalised) -> bf16 o.
+//   mala_dec_decide  one workgroup per (sequence, KV head): the sequential
+//                    rule decided in parallel from an upper and a lower bound
+//                    of each tile's retained mass (two workgroup prefix sums),
+//                    with an exact serial pass over the tiles the bounds leave
+//                    open.
+//   mala_dec_pv      persistent workgroups over the kept tiles of all groups:
+//                    P = spill x 2^(tile max - lse), V rows of kept tiles only,
+//                    fp32 accumulation, one partial per (workgroup, group).
+//   mala_dec_sum_combine  sums a group's partials (already normalised) -> bf16 o.
 // tau = 0 keeps every tile, so the scan is elided: mala_dec_dense is a fused
 // split-K decode (scores, online softmax and P.V per split) and
 // mala_dec_dense_combine merges the splits.
@@ -93,6 +87,8 @@ __device__ __forceinline__ void load_q_frags(const DecParams& p, int b, int kh, 
 
 // Scores of the staged tile: s[sub][r] is row g = lane%32, key
 // 32 sub + 8(r/4) + 4 hi + r%4, base 2, -inf past Nb.
+// Scores of the staged tile: s[sub][r] is row g = lane%32, key
+// 32 sub + 8(r/4) + 4 hi + r%4, base 2, -inf past Nb.
 template <int D>
 __device__ __forceinline__ void tile_scores(const DecParams& p, int t, int Nb, const uint16_t* slice,
                                             const bf16x8* qf, f32x16* s) {
@@ -119,15 +115,26 @@ __device__ __forceinline__ void tile_scores(const DecParams& p, int t, int Nb, c
         }
 }
 
-template <int D>
+// Score pass.  Persistent waves each stream a contiguous run of tiles, the
+// next tile's K fragments in flight while the current one is scored.  S^T =
+// K q^T with 16x16x32 bf16 MFMAs: the 16 rows of each of the tile's four key
+// blocks against the group's q heads as the 16 columns (G <= 16).  Per tile and
+// row it yields the base-2 max M and the sum of 2^(s - M); the values
+// 2^(s - M) themselves, rounded to fp16, are the spill that the P.V pass reads
+// back for kept tiles.  Spill and statistics of a wave's tiles are staged in
+// LDS and written when the run ends (or every RUN tiles): small stores
+// interleaved with the K stream slow the stream down; written in bursts they
+// cost little.
+template <int D, int GP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mala_dec_score(const DecParams p) {
-    constexpr int KSTEPS = D / 16;
+    constexpr int KS = D / 32;           // 16x16x32 steps over d
+    constexpr int RUN = 8;               // tiles staged per wave before a flush
+    __shared__ __attribute__((aligned(16))) uint16_t sSp[4][RUN * GP * BKD];   // [wave][tile][row][key]
+    __shared__ float sSt[4][2][GP][RUN];                                       // [wave][max|sum][row][tile]
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
-    // Each wave streams a contiguous run of tiles.  K fragments (A operands:
-    // row = key, 8 consecutive d) are loaded straight into registers, the next
-    // tile's loads in flight while the current tile is scored; no LDS.
+    const int i16 = lane & 15, q4 = lane >> 4;
+    const int G = p.G;
     const int ntask = p.B * p.Hkv * p.nT;
     const int nwave = gridDim.x * 4;
     const int per = (ntask + nwave - 1) / nwave;
@@ -136,87 +143,111 @@ void mala_dec_score(const DecParams p) {
     int task = gw * per;
     const int tend = (task + per < ntask) ? task + per : ntask;
     if (task >= tend) return;
+    uint16_t* sp = sSp[w];
 
-    auto load_tile = [&](int tk, bf16x8 (&kf)[2][KSTEPS]) {
+    // the staged run: group, first tile, tiles staged (consecutive tiles of one group)
+    int rgrp = -1, rt0 = 0, rn = 0;
+    auto flush = [&]() {
+        // this wave's LDS writes have landed before any lane reads them back
+        wave_lds_exchange();
+        const int nch = rn * G * (BKD / 8);            // 16-byte chunks, contiguous in the tile-major spill
+        u32x4* dst = (u32x4*)(p.spill + ((int64_t)rgrp * p.nT + rt0) * G * BKD);
+        for (int c = lane; c < nch; c += 64) {
+            const int tl = c / (G * 8), rem = c % (G * 8);
+            dst[c] = *(const u32x4*)(sp + tl * GP * BKD + rem * 8);
+        }
+        for (int c = lane; c < rn * G; c += 64) {
+            const int g = c / rn, tl = c % rn;
+            const int64_t at = ((int64_t)rgrp * G + g) * p.nTp + rt0 + tl;
+            p.tmax[at] = sSt[w][0][g][tl];
+            p.tsum[at] = sSt[w][1][g][tl];
+        }
+        wave_lds_exchange();                            // the next run's writes come after these reads
+        rn = 0;
+    };
+
+    auto load_tile = [&](int tk, bf16x8 (&kf)[4][KS]) {
         const int grp = tk / p.nT, t = tk % p.nT;
         const int b = grp / p.Hkv, kh = grp % p.Hkv;
         const int Nb = dec_len(p, b);
         if (t * BKD >= Nb) return;                     // past this sequence's cache
-        const uint16_t* kb = p.k + b * p.k_sb + kh * p.k_sh;
+        const uint16_t* kb = p.k + b * p.k_sb + kh * p.k_sh + 8 * q4;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            int j = t * BKD + 32 * sub + l32;
+        for (int blk = 0; blk < 4; ++blk) {
+            int j = t * BKD + 16 * blk + i16;
             j = j < Nb ? j : Nb - 1;                   // rows past Nb are masked below
-            const uint16_t* row = kb + (int64_t)j * p.k_sl + 8 * hi;
+            const uint16_t* row = kb + (int64_t)j * p.k_sl;
 #pragma unroll
-            for (int st = 0; st < KSTEPS; ++st) kf[sub][st] = *(const bf16x8*)(row + 16 * st);
+            for (int st = 0; st < KS; ++st) kf[blk][st] = *(const bf16x8*)(row + 32 * st);
         }
     };
     int qgrp = -1;
-    bf16x8 qf[D / 16];
-    auto score_tile = [&](int tk, const bf16x8 (&kf)[2][KSTEPS]) {
-        const int grp = tk / p.nT;
-        const int t = tk % p.nT;
+    bf16x8 qf[KS];
+    auto score_tile = [&](int tk, const bf16x8 (&kf)[4][KS]) {
+        const int grp = tk / p.nT, t = tk % p.nT;
         if (grp != qgrp) {
-            load_q_frags<D>(p, grp / p.Hkv, grp % p.Hkv, qf);
+            // B operand: column i16 = q head of the group, d = 32 st + 8 q4 ..
+            const bool ok = i16 < G;
+            const uint16_t* qrow = p.q + ((int64_t)(grp / p.Hkv) * p.Hq + (grp % p.Hkv) * G + (ok ? i16 : 0)) * D;
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                const u32x4 x = ok ? *(const u32x4*)(qrow + 32 * st + 8 * q4) : u32x4{0, 0, 0, 0};
+                qf[st] = __builtin_bit_cast(bf16x8, x);
+            }
             qgrp = grp;
         }
         // per-call reset owned by this tile
         if (p.bits && lane == 0 && (t % 32) == 0) p.bits[(int64_t)grp * p.nwords + t / 32] = 0u;
         const int Nb = dec_len(p, grp / p.Hkv);
         if (t * BKD >= Nb) return;
-        f32x16 sv[2];
+        if (rn > 0 && (grp != rgrp || t != rt0 + rn || rn == RUN)) flush();
+        if (rn == 0) { rgrp = grp; rt0 = t; }
+        const int slot = rn++;
+        // C[key][head]: lane i16 + 16 q4 holds head i16, keys 16 blk + 4 q4 + r
+        f32x4 c[4];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            sv[sub] = f32x16{};
+        for (int blk = 0; blk < 4; ++blk) {
+            c[blk] = f32x4{};
 #pragma unroll
-            for (int st = 0; st < KSTEPS; ++st) sv[sub] = mfma32x32x16(kf[sub][st], qf[st], sv[sub]);
+            for (int st = 0; st < KS; ++st) c[blk] = mfma16x16x32(kf[blk][st], qf[st], c[blk]);
         }
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = t * BKD + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                sv[sub][r] = (j < Nb) ? sv[sub][r] * p.scale_log2 : kNegInf;
-            }
         float M = kNegInf;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) M = fmaxf(M, sv[sub][r]);
+            for (int r = 0; r < 4; ++r) {
+                const int j = t * BKD + 16 * blk + 4 * q4 + r;
+                c[blk][r] = (j < Nb) ? c[blk][r] * p.scale_log2 : kNegInf;
+                M = fmaxf(M, c[blk][r]);
+            }
+        M = fmaxf(M, __shfl_xor(M, 16));
         M = wave_max_pair(M);
-        float sum = 0.f;
+        float sum = 0.f, e[4][4];
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+        for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sum += fast_exp2(sv[sub][r] - M);
+            for (int r = 0; r < 4; ++r) {
+                e[blk][r] = fast_exp2(c[blk][r] - M);
+                sum += e[blk][r];
+            }
+        sum += __shfl_xor(sum, 16);
         sum = wave_sum_pair(sum);
-        const int g = l32;
-        if (g < p.G) {
-            float* sp = p.spill + ((int64_t)grp * p.G + g) * p.N + (int64_t)t * BKD;
-            const bool full = (t + 1) * BKD <= Nb;
+        if (i16 < G) {
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int j0 = 32 * sub + 8 * q4 + 4 * hi;
-                    if (full) {
-                        *(f32x4*)(sp + j0) =
-                            f32x4{sv[sub][4 * q4], sv[sub][4 * q4 + 1], sv[sub][4 * q4 + 2], sv[sub][4 * q4 + 3]};
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (t * BKD + j0 + e < Nb) sp[j0 + e] = sv[sub][4 * q4 + e];
-                    }
-                }
-            if (hi == 0) {
-                p.tmax[((int64_t)grp * p.G + g) * p.nTp + t] = M;
-                p.tsum[((int64_t)grp * p.G + g) * p.nTp + t] = sum;
+            for (int blk = 0; blk < 4; ++blk) {
+                const f16x2v lo = {(_Float16)e[blk][0], (_Float16)e[blk][1]};
+                const f16x2v hi = {(_Float16)e[blk][2], (_Float16)e[blk][3]};
+                *(u32x2*)(sp + (slot * GP + i16) * BKD + 16 * blk + 4 * q4) =
+                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            }
+            if (q4 == 0) {
+                sSt[w][0][i16][slot] = M;
+                sSt[w][1][i16][slot] = sum;
             }
         }
     };
 
-    bf16x8 ka[2][KSTEPS], kb[2][KSTEPS];
+    bf16x8 ka[4][KS], kb[4][KS];
     load_tile(task, ka);
     for (; task < tend; task += 2) {
         if (task + 1 < tend) load_tile(task + 1, kb);
@@ -226,6 +257,7 @@ void mala_dec_score(const DecParams p) {
             score_tile(task + 1, kb);
         }
     }
+    if (rn > 0) flush();
 }
 
 // wave64 prefix sums and reductions built on DPP lane moves: row shifts inside
@@ -593,302 +625,537 @@ __device__ __forceinline__ void decide_one_wave(const DecParams& p, const int Nb
     }
 }
 
-// The sequential decode rule with one wave per q head of the group (lane =
-// tile, 64 tiles per chunk, newest first).  Same rounds, votes and prefix
-// sums as the single-wave form, taken per row: each wave scans only its own
-// row's linear masses, and the rows meet through two 64-bit masks per round
-// in LDS (the candidates: some row votes keep; the survivors: some row still
-// votes keep after the earlier candidates' mass), so a round is a few dozen
-// instructions per wave instead of a loop over every row.  Runs when every
-// row's tile maxima lie within 96 of its largest and tau/N within 2^+-120
-// (the linear range); otherwise the first wave runs the single-wave form.
-// Groups of more than 8 rows run the single-wave form on one wave (16 waves
-// would leave the single-wave form too few registers).
-template <int GP>
-constexpr int decide_threads() { return GP <= 8 ? 64 * GP : 64; }
-
-// Workgroup barrier after this wave's LDS writes have completed.  Unlike
-// __syncthreads() it does not wait for vector-memory operations, so the
-// statistics copies in flight (several chunks ahead) and the tile-list stores
-// stay in flight across the barrier.  The scheduling barriers keep every LDS
-// access on its side.
-__device__ __forceinline__ void lds_only_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    // gfx9 s_waitcnt: lgkmcnt(0), vmcnt and expcnt at their maxima (no wait)
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+// Exclusive prefix sums over the workgroup of N values per thread (thread
+// order is the order of the sums) and their totals.  sW holds one entry per
+// wave and value; the workgroup must not be using it.
+template <int N, int NW>
+__device__ __forceinline__ void block_excl_scan(float (&v)[N], float (&tot)[N], float (*sW)[N]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    float inc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) inc[i] = wave_incl_sum(v[i]);
+    if (lane == 63)
+#pragma unroll
+        for (int i = 0; i < N; ++i) sW[w][i] = inc[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        float off = 0.f, all = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const float s = sW[w2][i];
+            off += (w2 < w) ? s : 0.f;
+            all += s;
+        }
+        // the previous lane's inclusive sum, never inc minus this lane's value
+        v[i] = off + wave_shr1(inc[i]);
+        tot[i] = all;
+    }
+    __syncthreads();
 }
 
+// The sequential decode rule for one (sequence, KV head), decided in parallel
+// with bounds.  Visit position v = 0, 1, .. is tile nTb-1-v (newest first); Z
+// is each row's retained mass, a_v = 2^(M_v - ref) and x_v = tile sum * a_v
+// per row, linear masses against the row's largest tile max.  The rule keeps
+// tile v iff some row has Z(v) = 0 or a_v >= (tau/N) Z(v), Z(v) the mass of
+// the kept tiles before v.  Z(v) is at most the mass of ALL earlier tiles
+// (upper bound U) and at least the mass of the earlier tiles already known to
+// be kept (lower bound R).  So a tile that passes against U is surely kept,
+// one that fails against R is surely skipped, both from two prefix sums over
+// the workgroup, and only the rest -- ambiguous tiles, rare because skipped
+// tiles carry little mass -- need the sequential rule: a serial pass over
+// them in visit order with Z(v) = R(v) + the mass of the ambiguous tiles it
+// keeps before v.  The decisions are those of the sequential rule exactly.
+//
+// Tiles are taken in chunks of CH positions (the state carried across);
+// rows whose tile maxima span more than 2^96, or tau/N beyond 2^+-120, leave
+// fp32's range for linear masses: such groups run the round-based
+// log-sum-exp form decide_one_wave on the first wave.
 template <int GP>
-__global__ __launch_bounds__(decide_threads<GP>()) void mala_dec_decide(const DecParams p) {
+constexpr int decide_tpt() { return GP <= 5 ? 4 : (GP <= 8 ? 2 : 1); }
+
+template <int GP>
+__global__ __launch_bounds__(512) void mala_dec_decide(const DecParams p) {
+    constexpr int NTH = 512, NW = NTH / 64;
+    constexpr int TPT = decide_tpt<GP>();
+    constexpr int CH = NTH * TPT;
+    constexpr int AMBCAP = 256;            // ambiguous tiles resolved per serial pass
+    __shared__ float sW[NW][GP + 2];
+    __shared__ float sRef[NW][GP][2];
+    __shared__ float sAmb[AMBCAP][3][GP];   // a, x, R of each ambiguous tile of the pass
+    __shared__ int sAmbKeep[AMBCAP];
+    __shared__ float sE[GP];
     const int grp = blockIdx.x;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int G = p.G;
     const int Nb = dec_len(p, grp / p.Hkv);
     if (Nb == 0) {                              // skipped sequence: nothing retained
-        if (threadIdx.x == 0) {
+        if (tid == 0) {
             p.kcount[grp] = 0;
             if (p.kept_tiles) p.kept_tiles[grp] = 0;
         }
-        return;
-    }
-    if constexpr (GP > 8) {
-        decide_one_wave<GP>(p, Nb);
         return;
     }
     const int nTb = (Nb + BKD - 1) / BKD;      // this sequence's tiles (p.nT is the stride)
     const float theta = p.log2_tau - (p.seqlens ? (float)log2((double)Nb) : p.log2_N);
     const bool lin_ok = theta >= -120.f && theta <= 120.f;
     const float cthr = fast_exp2(theta);
-    const int nchunk = (nTb + 63) / 64;
-    const bool row = w < G;                     // waves past G hold no row (they only meet the barriers)
-    const float* tmax = p.tmax + ((int64_t)grp * G + (row ? w : 0)) * p.nTp;
-    const float* tsum = p.tsum + ((int64_t)grp * G + (row ? w : 0)) * p.nTp;
+    const float* tmax = p.tmax + (int64_t)grp * G * p.nTp;   // row g at g * nTp
+    const float* tsum = p.tsum + (int64_t)grp * G * p.nTp;
 
-    // This row's tile statistics stream through an LDS ring, DEPTH chunks
-    // ahead: two 4-byte copies per chunk (max, sum), tile t_lo + i at entry i
-    // (reads before tile 0 return 0; such lanes are invalid).
-    constexpr int DEPTH = 8, RING = DEPTH + 1;
-    __shared__ __attribute__((aligned(16))) float sRow[RING][2][GP][64];
-    __shared__ int sLin[GP];
-    __shared__ uint64_t sCand[2][GP], sKeep[2][GP];
-    const __amdgpu_buffer_rsrc_t rmax = make_rsrc(tmax, (uint32_t)(p.nTp * 4));
-    const __amdgpu_buffer_rsrc_t rsum = make_rsrc(tsum, (uint32_t)(p.nTp * 4));
-    auto issue_row = [&](int c) {
-        const int t = nTb - 64 * (c + 1) + lane;
-        const uint32_t off = (t >= 0) ? (uint32_t)(t * 4) : 0xFFFFFFF0u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rmax, (__attribute__((address_space(3))) void*)(&sRow[c % RING][0][w][0]),
-                                                4, (int)off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsum, (__attribute__((address_space(3))) void*)(&sRow[c % RING][1][w][0]),
-                                                4, (int)off, 0, 0, 0);
-    };
-    if (row)
-        for (int c = 0; c < DEPTH && c < nchunk; ++c) issue_row(c);
-
-    // Row reference: the largest tile max; the row is in the linear range when
-    // its smallest tile max lies within 96 of it.  16-byte loads, 8 per lane
-    // issued together, branch-free (indexes past the row re-read entry 0).
-    float gref = 0.f;
+    // Row references: the largest tile max, and whether the smallest lies within 96 of it.
+    float gref[GP];
+    bool linear = lin_ok;
     {
-        bool lin = true;
-        if (row) {
-            float mx = kNegInf, mn = __builtin_inff();
-            const int nq = nTb >> 2;
-            for (int j0 = 0; j0 < nq; j0 += 64 * 8) {
-                f32x4 v[8];
+        float mx[GP], mn[GP];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = j0 + 64 * u + lane;
-                    v[u] = *(const f32x4*)(tmax + 4 * (j < nq ? j : 0));
-                }
+        for (int g = 0; g < GP; ++g) { mx[g] = kNegInf; mn[g] = __builtin_inff(); }
+        for (int t0 = tid; t0 < nTb; t0 += TPT * NTH) {
+            float v[TPT][GP];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const bool ok = j0 + 64 * u + lane < nq;
-                    const float a = fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3]));
-                    const float b = fminf(fminf(v[u][0], v[u][1]), fminf(v[u][2], v[u][3]));
-                    mx = ok ? fmaxf(mx, a) : mx;
-                    mn = ok ? fminf(mn, b) : mn;
+            for (int j = 0; j < TPT; ++j) {
+                const int t = t0 + j * NTH;
+#pragma unroll
+                for (int g = 0; g < GP; ++g) v[j][g] = tmax[(int64_t)(g < G ? g : 0) * p.nTp + (t < nTb ? t : 0)];
+            }
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                const bool ok = t0 + j * NTH < nTb;
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    mx[g] = ok ? fmaxf(mx[g], v[j][g]) : mx[g];
+                    mn[g] = ok ? fminf(mn[g], v[j][g]) : mn[g];
                 }
             }
-            const bool ok = lane < nTb - 4 * nq;
-            const float v = tmax[ok ? 4 * nq + lane : 0];
-            mx = ok ? fmaxf(mx, v) : mx;
-            mn = ok ? fminf(mn, v) : mn;
-            gref = wave_max_all(mx);
-            const float lo = -wave_max_all(-mn);
-            lin = lo >= gref - 96.f;
         }
-        if (lane == 0) sLin[w] = lin ? 1 : 0;
-    }
-    __syncthreads();
-    bool linear = lin_ok;
 #pragma unroll
-    for (int g = 0; g < GP; ++g) linear = linear && (sLin[g] != 0);
+        for (int g = 0; g < GP; ++g) {
+            const float a = wave_max_all(mx[g]);
+            const float b = -wave_max_all(-mn[g]);
+            if (lane == 0) { sRef[w][g][0] = a; sRef[w][g][1] = b; }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            float a = kNegInf, b = __builtin_inff();
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) { a = fmaxf(a, sRef[w2][g][0]); b = fminf(b, sRef[w2][g][1]); }
+            gref[g] = (g < G) ? a : 0.f;
+            linear = linear && (g >= G || b >= a - 96.f);
+        }
+    }
     if (!linear) {
         if (w == 0) decide_one_wave<GP>(p, Nb);
         return;
     }
 
     int32_t* klist = p.klist + (int64_t)grp * p.nT;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    float Z = row ? 0.f : 1.f;                  // retained mass of this row, relative to gref
-    bool empty = true;                          // nothing retained yet: the next candidate is kept
-    int kept = 0;
-    int par = 0;                                // mask slots alternate between rounds
+    float Z[GP];                                // retained mass so far (identical in every thread)
+#pragma unroll
+    for (int g = 0; g < GP; ++g) Z[g] = 0.f;
+    int kbase = 0;
+    const int nchunk = (nTb + CH - 1) / CH;
     for (int c = 0; c < nchunk; ++c) {
-        const int t = nTb - 1 - (c * 64 + lane);
-        const bool valid = t >= 0;
-        float a = 0.f, x = 0.f;
-        if (row) {
-            if (c + DEPTH < nchunk) {
-                issue_row(c + DEPTH);
-                wait_vmcnt<2 * DEPTH>();                  // chunk c has landed
-            } else {
-                wait_vmcnt<0>();
-            }
-            const float M = sRow[c % RING][0][w][63 - lane];
-            const float S = sRow[c % RING][1][w][63 - lane];
-            a = valid ? fast_exp2(M - gref) : 0.f;
-            x = valid ? S * a : 0.f;
-        }
-        int pos = 0;
-        while (true) {
-            const bool active = valid && lane >= pos;
-            const uint64_t mine = __ballot(active && (a >= cthr * Z));
-            if (lane == 0) sCand[par][w] = mine;
-            lds_only_barrier();
-            uint64_t K0 = 0ull;
+        // this thread's positions: v = c CH + TPT tid + j, tile nTb - 1 - v
+        float a[TPT][GP], x[TPT][GP];
+        bool valid[TPT];
+        int tile[TPT];
+        {
+            float M[TPT][GP], S[TPT][GP];
 #pragma unroll
-            for (int g = 0; g < GP; ++g) K0 |= sCand[par][g];
-            if (empty) K0 = __ballot(active);
-            if (K0 == 0ull) {                             // the rest of the chunk is skipped
-                par ^= 1;
-                break;
-            }
-            const int first = __builtin_ctzll(K0);
-            const bool cand = (K0 >> lane) & 1ull;
-            const float inc = wave_incl_sum(cand ? x : 0.f);
-            // the previous lane's inclusive sum, never inc minus this tile's mass
-            const float exc = wave_shr1(inc);
-            const uint64_t still = __ballot(cand && (a >= cthr * (Z + exc)));
-            if (lane == 0) sKeep[par][w] = still;
-            lds_only_barrier();
-            uint64_t V1 = empty ? (1ull << first) : 0ull;
+            for (int j = 0; j < TPT; ++j) {
+                tile[j] = nTb - 1 - (c * CH + TPT * tid + j);
+                valid[j] = tile[j] >= 0;
+                const int t = valid[j] ? tile[j] : 0;
 #pragma unroll
-            for (int g = 0; g < GP; ++g) V1 |= sKeep[par][g];
-            par ^= 1;
-            const uint64_t flips = K0 & ~V1;
-            uint64_t acc;
-            if (flips == 0ull) {
-                acc = K0;
-                Z += readlane_f(inc, 63);
-            } else {
-                const int f = __builtin_ctzll(flips);
-                acc = K0 & ((f == 0) ? 0ull : (~0ull >> (64 - f)));
-                Z += readlane_f(exc, f);
-                pos = f + 1;
+                for (int g = 0; g < GP; ++g) {
+                    const int64_t at = (int64_t)(g < G ? g : 0) * p.nTp + t;
+                    M[j][g] = tmax[at];
+                    S[j][g] = tsum[at];
+                }
             }
-            if (w == 0 && ((acc >> lane) & 1ull)) {
-                klist[kept + __builtin_popcountll(acc & lt_mask)] = t;
-                if (p.bits) atomicOr(p.bits + (int64_t)grp * p.nwords + t / 32, 1u << (t % 32));
-            }
-            kept += __builtin_popcountll(acc);
-            if (acc) empty = false;
-            if (flips == 0ull) break;
+#pragma unroll
+            for (int j = 0; j < TPT; ++j)
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    const bool ok = valid[j] && g < G;
+                    a[j][g] = ok ? fast_exp2(M[j][g] - gref[g]) : 0.f;
+                    x[j][g] = ok ? S[j][g] * a[j][g] : 0.f;
+                }
         }
+        // upper bound: the mass of every earlier tile
+        bool sk[TPT];
+        {
+            float pre[GP], tot[GP];
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                pre[g] = 0.f;
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) pre[g] += x[j][g];
+            }
+            block_excl_scan<GP, NW>(pre, tot, (float(*)[GP])sW);
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                bool k = false;
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    k = k || (g < G && a[j][g] >= cthr * (Z[g] + pre[g]));
+                    pre[g] += x[j][g];
+                }
+                sk[j] = valid[j] && k;
+            }
+        }
+        // lower bound: the mass of the earlier surely-kept tiles (scanned with
+        // their count, which places the kept tiles when none is ambiguous)
+        bool amb[TPT];
+        float R[TPT][GP];
+        float sktot[GP];
+        int nk_before, nk_total, na = 0;
+        {
+            float pre[GP + 1], tot[GP + 1];
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                pre[g] = 0.f;
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) pre[g] += sk[j] ? x[j][g] : 0.f;
+            }
+            pre[GP] = 0.f;
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) pre[GP] += sk[j] ? 1.f : 0.f;
+            block_excl_scan<GP + 1, NW>(pre, tot, (float(*)[GP + 1])sW);
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                bool k = false;
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    R[j][g] = Z[g] + pre[g];
+                    k = k || (g < G && a[j][g] >= cthr * R[j][g]);
+                    pre[g] += sk[j] ? x[j][g] : 0.f;
+                }
+                amb[j] = valid[j] && !sk[j] && k;
+                na += amb[j] ? 1 : 0;
+            }
+#pragma unroll
+            for (int g = 0; g < GP; ++g) sktot[g] = tot[g];
+            nk_before = (int)pre[GP];
+            nk_total = (int)tot[GP];
+        }
+        bool keep[TPT];
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) keep[j] = sk[j];
+        float Etot[GP];
+#pragma unroll
+        for (int g = 0; g < GP; ++g) Etot[g] = 0.f;
+        if (__syncthreads_or(na)) {
+            // the sequential rule over the ambiguous tiles, in visit order,
+            // AMBCAP at a time; E = mass of the ambiguous tiles kept so far
+            float pa[1] = {(float)na}, ta[1];
+            block_excl_scan<1, NW>(pa, ta, (float(*)[1])sW);
+            const int namb_before = (int)pa[0], namb_total = (int)ta[0];
+            if (tid == 0)
+#pragma unroll
+                for (int g = 0; g < GP; ++g) sE[g] = 0.f;
+            for (int r0 = 0; r0 < namb_total; r0 += AMBCAP) {
+                int idx = namb_before;
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) {
+                    if (amb[j]) {
+                        if (idx >= r0 && idx < r0 + AMBCAP)
+#pragma unroll
+                            for (int g = 0; g < GP; ++g) {
+                                sAmb[idx - r0][0][g] = a[j][g];
+                                sAmb[idx - r0][1][g] = x[j][g];
+                                sAmb[idx - r0][2][g] = R[j][g];
+                            }
+                        ++idx;
+                    }
+                }
+                __syncthreads();
+                if (tid == 0) {
+                    float E[GP];
+#pragma unroll
+                    for (int g = 0; g < GP; ++g) E[g] = sE[g];
+                    const int n = (namb_total - r0 < AMBCAP) ? namb_total - r0 : AMBCAP;
+                    for (int i = 0; i < n; ++i) {
+                        bool k = false;
+#pragma unroll
+                        for (int g = 0; g < GP; ++g) k = k || (g < G && sAmb[i][0][g] >= cthr * (sAmb[i][2][g] + E[g]));
+                        if (k)
+#pragma unroll
+                            for (int g = 0; g < GP; ++g) E[g] += sAmb[i][1][g];
+                        sAmbKeep[i] = k ? 1 : 0;
+                    }
+#pragma unroll
+                    for (int g = 0; g < GP; ++g) sE[g] = E[g];
+                }
+                __syncthreads();
+                idx = namb_before;
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) {
+                    if (amb[j]) {
+                        if (idx >= r0 && idx < r0 + AMBCAP) keep[j] = sAmbKeep[idx - r0] != 0;
+                        ++idx;
+                    }
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int g = 0; g < GP; ++g) Etot[g] = sE[g];
+            // kept tiles before each position, ambiguous ones included
+            float pk[1] = {0.f}, tk[1];
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) pk[0] += keep[j] ? 1.f : 0.f;
+            block_excl_scan<1, NW>(pk, tk, (float(*)[1])sW);
+            nk_before = (int)pk[0];
+            nk_total = (int)tk[0];
+        }
+        // the kept tiles, newest first
+        {
+            int o = kbase + nk_before;
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                if (keep[j]) {
+                    klist[o++] = tile[j];
+                    if (p.bits) atomicOr(p.bits + (int64_t)grp * p.nwords + tile[j] / 32, 1u << (tile[j] % 32));
+                }
+            }
+        }
+        kbase += nk_total;
+#pragma unroll
+        for (int g = 0; g < GP; ++g) Z[g] += sktot[g] + Etot[g];
     }
-    if (threadIdx.x == 0) {
-        p.kcount[grp] = kept;
-        if (p.kept_tiles) p.kept_tiles[grp] = kept;
+    if (tid == 0) {
+        p.kcount[grp] = kbase;
+        if (p.kept_tiles) p.kept_tiles[grp] = kbase;
     }
-    if (row && lane == 0) {
-        const float lz2 = gref + fast_log2(Z);
-        p.lse2[(int64_t)grp * G + w] = lz2;
+    if (tid < G) {
+        float zz = 0.f, rr = 0.f;
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+            if (g == tid) { zz = Z[g]; rr = gref[g]; }
+        const float lz2 = rr + fast_log2(zz);
+        p.lse2[(int64_t)grp * G + tid] = lz2;
         const int b = grp / p.Hkv, kh = grp % p.Hkv;
-        p.lse[(int64_t)b * p.Hq + kh * G + w] = lz2 * kLn2;
+        p.lse[(int64_t)b * p.Hq + kh * G + tid] = lz2 * kLn2;
     }
 }
 
-// P.V over the kept tiles: one wave per kept tile, four per workgroup, every
-// load issued at once (the tile index, then its V rows and spilled scores).
-// Lane (dc, kg) owns d = 8 dc .. 8 dc + 7 of KPL consecutive keys; the wave's
-// partial output is reduced across kg with lane shuffles, the workgroup's
-// across its waves in LDS, and written as one partial per workgroup.
+// Integer wave prefix sums (DPP, as wave_incl_sum) and a workgroup scan of one
+// int per thread (thread order), with the total.
+template <int CTRL, int ROWMASK, bool BOUND0>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, BOUND0);
+}
+__device__ __forceinline__ int wave_incl_sum_i(int x) {
+    x += dpp_i<0x111, 0xF, true>(x);
+    x += dpp_i<0x112, 0xF, true>(x);
+    x += dpp_i<0x114, 0xF, true>(x);
+    x += dpp_i<0x118, 0xF, true>(x);
+    x += dpp_i<0x142, 0xA, false>(x);
+    x += dpp_i<0x143, 0xC, false>(x);
+    return x;
+}
+template <int NW>
+__device__ __forceinline__ int block_excl_scan_i(int v, int& tot, int* sWi) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int inc = wave_incl_sum_i(v);
+    if (lane == 63) sWi[w] = inc;
+    __syncthreads();
+    int off = 0, all = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+        const int s = sWi[w2];
+        off += (w2 < w) ? s : 0;
+        all += s;
+    }
+    __syncthreads();
+    tot = all;
+    return off + inc - v;
+}
+
+// P.V over the kept tiles of every group.  The kept lists of all groups,
+// concatenated in group order, are cut into equal ranges, one per workgroup,
+// so no workgroup waits on an empty list and none carries a group's whole
+// load; its four waves take every fourth tile of each group's part of the
+// range.  For a tile, O^T += V^T P^T runs on 16x16x32 bf16 MFMAs: d in 16-row
+// blocks, the group's q heads as the 16 columns, keys as the contraction.
+// P = (spilled fp16 2^(s - M)) x 2^(M - lse), M the row's tile max: the fp16
+// part is split exactly into two bf16 parts (high: the value rounded to bf16,
+// low: the rest, which fits bf16 exactly), each taken by its own MFMA, so the
+// product with bf16 V is that of fp16 P in fp32 arithmetic; the factor
+// 2^(M - lse) scales the tile's contribution per column afterwards.  V^T
+// operands come from the tile staged in LDS (global -> LDS copies, 16-byte
+// chunks XOR-swizzled by row) through transposing reads.  For each group its
+// range meets, a workgroup writes one partial output (already normalised) to
+// slot workgroup + group: a workgroup meets groups in increasing order, so no
+// two (workgroup, group) pairs share a slot.  The workgroup that holds a
+// group's first kept tile records the group's first slot and slot count
+// (pvinfo).
 template <int D, int GP>
 __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
-    constexpr int DC = D / 8;            // 16-byte chunks per V row
-    constexpr int KG = 64 / DC;          // key groups per wave
-    constexpr int KPL = BKD / KG;        // keys per lane
-    __shared__ float sP[4][GP][BKD];
-    __shared__ float sRed[4][GP][D];
+    constexpr int NB = D / 16;           // 16-row blocks of d
+    constexpr int CH = D / 8;            // 16-byte chunks per V row
+    constexpr int RPC = 64 / CH;         // V rows per 1 KB global -> LDS copy
+    constexpr int TLCAP = 1024;          // tile indices staged per pass
+    __shared__ __attribute__((aligned(16))) uint16_t sV[4][BKD * D];   // one V tile per wave
+    __shared__ int sTl[TLCAP];
+    __shared__ int sWi[4];
+    __shared__ int sFound[2];
+    float (*sRed)[16][D] = reinterpret_cast<float (*)[16][D]>(&sV[0][0]);   // [wave][head][d], after the tiles
+    static_assert(sizeof(sV) >= 4 * 16 * D * sizeof(float), "reduction buffer");
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const int grp = blockIdx.y;
-    const int b = grp / p.Hkv, kh = grp % p.Hkv;
+    const int j16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
-    const int idx = blockIdx.x * 4 + w;
-    // the list entry is read together with the count (one round trip instead
-    // of two); entries past the count are stale and not used
-    const int tl = p.klist[(int64_t)grp * p.nT + (idx < p.nT ? idx : p.nT - 1)];
-    const int cnt = p.kcount[grp];
-    asm volatile("" ::"v"(tl));                 // keep the list load ahead of the count test
-    if (blockIdx.x * 4 >= cnt) return;          // the whole workgroup: no partial is read
-    const int Nb = dec_len(p, b);
-    const bool has = idx < cnt;
-    const int t = has ? tl : 0;
-    const int dc = lane % DC, kg = lane / DC;
-    // V rows of this lane's keys (16-byte chunk dc)
-    u32x4 vx[KPL];
-    const uint16_t* vb = p.v + b * p.v_sb + kh * p.v_sh + 8 * dc;
-#pragma unroll
-    for (int r = 0; r < KPL; ++r) {
-        int key = t * BKD + kg * KPL + r;
-        key = key < Nb ? key : Nb - 1;
-        vx[r] = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
-    }
-    __builtin_amdgcn_sched_barrier(0);          // the V loads go out first, then the P loads
-    // P of the tile: lane = key, one value per row.  The loads take clamped
-    // (always valid) indices and are issued together; invalid entries are
-    // replaced by 0 afterwards.
+    const int ngrp = p.B * p.Hkv;
+    const int wg = blockIdx.x;
+
+    // total kept tiles, this workgroup's range [s, e)
+    int T = 0;
     {
-        const int key = t * BKD + lane;
-        const bool kok = has && key < Nb;
-        const int kk = kok ? key : 0;
-        float sv[GP], lv[GP];
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            const int gg = g < G ? g : G - 1;
-            sv[g] = p.spill[((int64_t)grp * G + gg) * p.N + kk];
-            lv[g] = p.lse2[(int64_t)grp * G + gg];
-        }
-#pragma unroll
-        for (int g = 0; g < GP; ++g) sP[w][g][lane] = (kok && g < G) ? fast_exp2(sv[g] - lv[g]) : 0.f;
+        int c = 0;
+        for (int g = tid; g < ngrp; g += 256) c += p.kcount[g];
+        int tot;
+        block_excl_scan_i<4>(c, tot, sWi);
+        T = tot;
     }
-    __syncthreads();
-    float acc[GP][8];
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-#pragma unroll
-    for (int r = 0; r < KPL; ++r) {
-        float vv[8];
-#pragma unroll
-        for (int m2 = 0; m2 < 4; ++m2) {
-            vv[2 * m2] = __uint_as_float(vx[r][m2] << 16);
-            vv[2 * m2 + 1] = __uint_as_float(vx[r][m2] & 0xFFFF0000u);
+    if (T == 0) return;
+    const int per = (T + gridDim.x - 1) / gridDim.x;
+    const int s = wg * per;
+    const int e = (s + per < T) ? s + per : T;
+    if (s >= e) return;
+    // the group holding item s, and its first item
+    {
+        int carry = 0;
+        for (int g0 = 0; g0 < ngrp; g0 += 256) {
+            const int g = g0 + tid;
+            const int kc = g < ngrp ? p.kcount[g] : 0;
+            int tot;
+            const int pre = carry + block_excl_scan_i<4>(kc, tot, sWi);
+            if (g < ngrp && pre <= s && s < pre + kc) { sFound[0] = g; sFound[1] = pre; }
+            carry += tot;
+            if (carry > s) break;                       // uniform: every thread holds the same carry
         }
+        __syncthreads();
+    }
+    int g = sFound[0];
+    int pre = sFound[1];
+    uint16_t* vt = sV[w];
+    int i = s;
+    while (i < e) {                                     // uniform over the workgroup
+        const int kc = p.kcount[g];
+        const int seg_end = (pre + kc < e) ? pre + kc : e;
+        if (seg_end > i) {
+            const int b = g / p.Hkv, kh = g % p.Hkv;
+            const int Nb = dec_len(p, b);
+            const int n = seg_end - i;
+            const int32_t* kl = p.klist + (int64_t)g * p.nT + (i - pre);
+            const uint16_t* vbase = p.v + b * p.v_sb + kh * p.v_sh;
+            // column (q head) of this lane in the B operand and the output
+            const bool hv = j16 < G;
+            const int hh = hv ? j16 : 0;
+            const float lse_h = p.lse2[(int64_t)g * G + hh];
+            f32x4 acc[NB];
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            const float pr = sP[w][g][kg * KPL + r];
+            for (int m = 0; m < NB; ++m) acc[m] = f32x4{};
+            for (int m0 = 0; m0 < n; m0 += TLCAP) {
+                const int nb = (n - m0 < TLCAP) ? n - m0 : TLCAP;
+                for (int m = tid; m < nb; m += 256) sTl[m] = kl[m0 + m];
+                __syncthreads();
+                for (int m = w; m < nb; m += 4) {
+                    const int t = sTl[m];
+                    // V tile -> this wave's LDS slice, 1 KB (RPC rows) per copy: lane l lands
+                    // at row RPC k + l / CH, position l % CH, and holds global chunk
+                    // (l % CH) ^ (row % 8)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] += pr * vv[e];
+                    for (int k = 0; k < BKD / RPC; ++k) {
+                        const int row = RPC * k + lane / CH;
+                        int key = t * BKD + row;
+                        key = key < Nb ? key : Nb - 1;
+                        const int ch = ((lane % CH) ^ (row & 7)) & (CH - 1);
+                        load16_to_lds(vbase + (int64_t)key * p.v_sl + 8 * ch, vt + k * RPC * D);
+                    }
+                    // P of the tile for head j16, keys 32 st + 8 q4 .. +7, and its factor
+                    const uint16_t* sp = p.spill + (((int64_t)g * p.nT + t) * G + hh) * BKD + 8 * q4;
+                    const u32x4 p0 = *(const u32x4*)(sp);
+                    const u32x4 p1 = *(const u32x4*)(sp + 32);
+                    const float tm = p.tmax[((int64_t)g * G + hh) * p.nTp + t];
+                    const float f = hv ? fast_exp2(tm - lse_h) : 0.f;
+                    // exact split of the fp16 values into bf16 high and low parts
+                    bf16x8 bh[2], bl[2];
+                    {
+                        const uint32_t ph[2][4] = {{p0[0], p0[1], p0[2], p0[3]}, {p1[0], p1[1], p1[2], p1[3]}};
+#pragma unroll
+                        for (int st = 0; st < 2; ++st)
+#pragma unroll
+                            for (int h = 0; h < 4; ++h) {
+                                const float a0 = f16_lo_to_float(ph[st][h]), a1 = f16_hi_to_float(ph[st][h]);
+                                const __bf16 h0 = to_bf16(a0), h1 = to_bf16(a1);
+                                bh[st][2 * h] = h0;
+                                bh[st][2 * h + 1] = h1;
+                                bl[st][2 * h] = to_bf16(a0 - (float)h0);
+                                bl[st][2 * h + 1] = to_bf16(a1 - (float)h1);
+                            }
+                    }
+                    // the copies above are the only writes to vt; every lane's part has landed
+                    __builtin_amdgcn_s_waitcnt(0);
+                    wave_lds_exchange();
+#pragma unroll
+                    for (int mb = 0; mb < NB; ++mb) {
+                        f32x4 c = f32x4{};
+#pragma unroll
+                        for (int st = 0; st < 2; ++st) {
+                            // A[i][k] = V[32 st + k][16 mb + i]: lane j16 + 16 q4 reads keys 32 st + 8 q4 ..
+                            // +3 and +4 .. +7 of column 16 mb + j16 (transposing reads: lane x of
+                            // the 16-lane group addresses key r0 + x/4, columns 16 mb + 4 (x%4) ..)
+                            bf16x8 a;
+#pragma unroll
+                            for (int hlf = 0; hlf < 2; ++hlf) {
+                                const int r = 32 * st + 8 * q4 + 4 * hlf + (j16 >> 2);
+                                const int col = 16 * mb + 4 * (j16 & 3);
+                                const int pos = ((col >> 3) ^ (r & 7)) & (CH - 1);
+                                const u32x2 x = lds_read_tr16(vt + r * D + pos * 8 + (col & 7));
+                                const bf16x8 xx = __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], 0u, 0u});
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) a[4 * hlf + u] = xx[u];
+                            }
+                            c = mfma16x16x32(a, bh[st], c);
+                            c = mfma16x16x32(a, bl[st], c);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[mb][r] += f * c[r];
+                    }
+                    wave_lds_exchange();               // the next tile's copies come after these reads
+                }
+                __syncthreads();                          // sTl is rewritten by the next pass
+            }
+            // acc[mb][r] = O^T[16 mb + 4 q4 + r][head j16] of this wave's tiles; sum the waves
+#pragma unroll
+            for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sRed[w][j16][16 * mb + 4 * q4 + r] = acc[mb][r];
+            __syncthreads();
+            float* po = p.part_o + ((int64_t)(wg + g) * G) * D;
+            for (int x = tid; x < G * D; x += 256) {
+                const int h = x / D, d = x % D;
+                po[x] = sRed[0][h][d] + sRed[1][h][d] + sRed[2][h][d] + sRed[3][h][d];
+            }
+            if (i == pre && tid == 0) {
+                p.pvinfo[2 * g] = wg;                                      // first slot's workgroup
+                p.pvinfo[2 * g + 1] = (pre + kc - 1) / per - wg + 1;        // slots
+            }
+            __syncthreads();                              // sRed (the V slices) is rewritten next
+            i = seg_end;
         }
-    }
-    // reduce over the key groups of the wave (lanes dc + DC * kg)
-#pragma unroll
-    for (int off = DC; off < 64; off <<= 1)
-#pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
-    if (kg == 0) {
-#pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sRed[w][g][8 * dc + e] = acc[g][e];
-    }
-    __syncthreads();
-    float* po = p.part_o + (((int64_t)grp * p.npart + blockIdx.x) * G) * D;
-    for (int e = tid; e < G * D; e += 256) {
-        const int g = e / D, d = e % D;
-        po[e] = sRed[0][g][d] + sRed[1][g][d] + sRed[2][g][d] + sRed[3][g][d];
+        pre += kc;
+        ++g;
     }
 }
 
-// Sum of the P.V partials (already normalised by the final LSE) -> bf16 o.
-// One workgroup per (group, row, 32-wide d slice): 8 split classes x 32 d.
+// Sum of the P.V partials of a group (already normalised by the final LSE) ->
+// bf16 o.  One workgroup per (group, row, 32-wide d slice): 8 slot classes x
+// 32 d, the slots of each class summed in order.
 template <int D>
 __global__ __launch_bounds__(256) void mala_dec_sum_combine(const DecParams p) {
     __shared__ float sO[8][32];
@@ -897,12 +1164,11 @@ __global__ __launch_bounds__(256) void mala_dec_sum_combine(const DecParams p) {
     const int G = p.G;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
     if (dec_len(p, b) == 0) return;              // skipped sequence: o is left as it was
-    const int64_t base = (int64_t)grp * p.npart;
+    const int wg0 = p.pvinfo[2 * grp], ns = p.pvinfo[2 * grp + 1];
     const int d = 32 * dq + (tid & 31), cls = tid >> 5;
-    const int nused = (p.kcount[grp] + 3) / 4;   // P.V workgroups that wrote a partial
     float osum = 0.f;
 #pragma unroll 4
-    for (int s = cls; s < nused; s += 8) osum += p.part_o[((base + s) * G + g) * D + d];
+    for (int s = cls; s < ns; s += 8) osum += p.part_o[((int64_t)(wg0 + s + grp) * G + g) * D + d];
     sO[cls][tid & 31] = osum;
     __syncthreads();
     if (tid < 32) {
@@ -1124,9 +1390,9 @@ static hipError_t launch_decode_t(const DecParams& p, bool dense, hipStream_t s)
         const int tasks = ngrp * p.nT;
         int nwg = (tasks + 3) / 4;
         if (nwg > 512) nwg = 512;        // two workgroups (8 waves) per CU
-        hipLaunchKernelGGL((mala_dec_score<D>), dim3(nwg), dim3(256), 0, s, p);
-        hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(decide_threads<GP>()), 0, s, p);
-        hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3((p.nT + 3) / 4, ngrp), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_score<D, GP>), dim3(nwg), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(512), 0, s, p);
+        hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3(p.npv), dim3(256), 0, s, p);
         hipLaunchKernelGGL((mala_dec_sum_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     }
     return hipGetLastError();

@@ -8,6 +8,7 @@ namespace mala {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -52,6 +53,14 @@ __device__ __forceinline__ uint32_t pack2_f16_from_f32bits(uint32_t lo, uint32_t
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// The fp16 values in the low and high halves of a 32-bit word, as fp32.
+__device__ __forceinline__ float f16_lo_to_float(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi_to_float(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+}
 
 // Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
@@ -134,6 +143,17 @@ __device__ __forceinline__ void buffer16_to_lds_asm(const u32x4& r, uint32_t vof
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voffset), "s"(r), "s"(soffset), "{m0}"(m0)
                  : "memory");
+}
+
+// Exchange point for data passed between the lanes of one wave through LDS:
+// __builtin_amdgcn_wave_barrier() alone does not stop the compiler from moving
+// memory accesses across it (it may hoist a lane's LDS read above the LDS write
+// of another lane that it cannot see depends on it).  The memory clobber does;
+// the LDS then executes the wave's accesses in issue order, and the wait makes
+// this wave's earlier LDS operations complete first.
+__device__ __forceinline__ void wave_lds_exchange() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
 }
 
 // Wait for every outstanding memory operation of this wave (including the

@@ -82,7 +82,8 @@ struct DecParams {
     int nwords;
     int64_t k_sb, k_sl, k_sh, v_sb, v_sl, v_sh;
     int B, N, Hq, Hkv, G, nT, nsplit, tiles_per_split;
-    int npart;              // max(nsplit, ceil(nT / 4)): partial outputs per (sequence, KV head)
+    int npart;              // dense path: partial outputs per (sequence, KV head) (= nsplit)
+    int npv;                // P.V workgroups (tau > 0)
     float scale_log2;
     float log2_tau;
     float log2_N;
@@ -91,11 +92,13 @@ struct DecParams {
     float* tmax;            // [B, Hkv, G, nTp] tile row max (base 2); nTp = nT rounded up to 4
     float* tsum;            // [B, Hkv, G, nTp] sum 2^(s - tile max)
     int nTp;
-    float* spill;           // [B, Hkv, G, N]   base-2 scores
+    uint16_t* spill;        // [B, Hkv, nT, G, 64] fp16 2^(score - tile max), tile-major
     int32_t* klist;         // [B, Hkv, nT]     retained tiles, newest first
     int32_t* kcount;        // [B, Hkv]
     float* lse2;            // [B, Hkv, G]      base-2 final log-normaliser
-    float* part_o;          // [B, Hkv, npart, G, d] partial outputs (dense splits or P.V workgroups)
+    int32_t* pvinfo;        // [B, Hkv, 2] first P.V workgroup and slot count of each group's partials
+    float* part_o;          // dense: [B, Hkv, npart, G, d] partial outputs; tau > 0: [npv + B Hkv, G, d]
+                            // (slot workgroup + group)
     float* part_ml;         // [B, Hkv, nsplit, G, 2] partial (max, sum) (dense path)
 };
 

@@ -241,7 +241,7 @@ mala_status mala_decode_varlen(const void* q, mala_t4 kcache, mala_t4 vcache, co
 
 /* Largest workspace mala_decode_noalloc can serve: 64 MiB, enough for
  * mala_decode_workspace_size of 8 sequences x 131072 cached keys x 5 q heads
- * per KV head (about 32 MiB) twice over. */
+ * per KV head (about 16 MiB) four times over. */
 #define MALA_DECODE_NOALLOC_MAX_BYTES (64u << 20)
 
 /* mala_decode for callers that cannot allocate device memory: code under HIP

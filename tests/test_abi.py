@@ -110,7 +110,7 @@ def test_bwd_workspace_and_errors():
 def test_decode_workspace_and_errors():
     lib = mala.load_library()
     n = lib.mala_decode_workspace_size(8, 131072, 5, 1, 128, 64)
-    assert n > 8 * 5 * 131072 * 4
+    assert n > 8 * 5 * 131072 * 2     # at least the fp16 probability spill
     assert lib.mala_decode_workspace_size(8, 131072, 5, 1, 128, 32) == 0
     t = _t4()
     q = ctypes.c_void_p(4096)
@@ -135,12 +135,12 @@ def test_decode_noalloc_refuses_before_touching_the_gpu():
     cap = mala.DECODE_NOALLOC_MAX_BYTES
     hdr = open(os.path.join(ROOT, "include", "mala.h")).read()
     assert f"#define MALA_DECODE_NOALLOC_MAX_BYTES ({cap >> 20}u << 20)" in hdr
-    # the benchmarked decode (8 sequences x 131072 keys, 5 q heads per KV head) fits; 32 sequences do not
+    # the benchmarked decode (8 sequences x 131072 keys, 5 q heads per KV head) fits; 64 sequences do not
     assert 0 < lib.mala_decode_workspace_size(8, 131072, 5, 1, 128, 64) <= cap
-    assert lib.mala_decode_workspace_size(32, 131072, 5, 1, 128, 64) > cap
+    assert lib.mala_decode_workspace_size(64, 131072, 5, 1, 128, 64) > cap
     t = _t4()
     q, o, lse = ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288)
-    big = [q, t, t, 32, 131072, 5, 1, 128, 1.0, 64, o, lse, None, None, None]
+    big = [q, t, t, 64, 131072, 5, 1, 128, 1.0, 64, o, lse, None, None, None]
     assert lib.mala_decode_noalloc(*big) == mala.MALA_ERR_WORKSPACE
     bad = list(big)
     bad[8] = float("nan")

@@ -53,7 +53,7 @@ def test_noalloc_decode_two_calls_then_dense():
 
 def test_noalloc_decode_refuses_oversized_shape_and_leaves_outputs():
     dev = torch.device("cuda:0")
-    B, N, Hq, Hkv, d = 32, 131072, 5, 1, 128
+    B, N, Hq, Hkv, d = 64, 131072, 5, 1, 128
     assert mala.load_library().mala_decode_workspace_size(B, N, Hq, Hkv, d, 64) > mala.DECODE_NOALLOC_MAX_BYTES
     q = torch.zeros((B, Hq, d), dtype=torch.bfloat16, device=dev)
     kc = torch.zeros((B, 64, Hkv, d), dtype=torch.bfloat16, device=dev).expand(B, 64, Hkv, d)
