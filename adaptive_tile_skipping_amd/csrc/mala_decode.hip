@@ -35,6 +35,7 @@ namespace mala {
 
 namespace {
 constexpr int BKD = 64;
+constexpr int kScoreWaves = 8;     // waves per score workgroup: all of a CU's waves in one workgroup
 
 // (max, shifted sum) log-sum-exp pairs in base 2: combine is associative.
 __device__ __forceinline__ void lse_combine(float& m, float& l, float m2, float l2) {
@@ -115,8 +116,9 @@ __device__ __forceinline__ void tile_scores(const DecParams& p, int t, int Nb, c
         }
 }
 
-// Score pass.  Persistent waves each stream a contiguous run of tiles, the
-// next tile's K fragments in flight while the current one is scored.  S^T =
+// Score pass.  Persistent waves, eight per workgroup and one workgroup per CU,
+// each stream a contiguous run of tiles, the next tile's K fragments in flight
+// while the current one is scored.  S^T =
 // K q^T with 16x16x32 bf16 MFMAs: the 16 rows of each of the tile's four key
 // blocks against the group's q heads as the 16 columns (G <= 16).  Per tile and
 // row it yields the base-2 max M and the sum of 2^(s - M); the values
@@ -126,17 +128,17 @@ __device__ __forceinline__ void tile_scores(const DecParams& p, int t, int Nb, c
 // interleaved with the K stream slow the stream down; written in bursts they
 // cost little.
 template <int D, int GP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mala_dec_score(const DecParams p) {
     constexpr int KS = D / 32;           // 16x16x32 steps over d
     constexpr int RUN = 8;               // tiles staged per wave before a flush
-    __shared__ __attribute__((aligned(16))) uint16_t sSp[4][RUN * GP * BKD];   // [wave][tile][row][key]
-    __shared__ float sSt[4][2][GP][RUN];                                       // [wave][max|sum][row][tile]
+    __shared__ __attribute__((aligned(16))) uint16_t sSp[kScoreWaves][RUN * GP * BKD];   // [wave][tile][row][key]
+    __shared__ float sSt[kScoreWaves][2][GP][RUN];                                       // [wave][max|sum][row][tile]
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int i16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
     const int ntask = p.B * p.Hkv * p.nT;
-    const int nwave = gridDim.x * 4;
+    const int nwave = gridDim.x * kScoreWaves;
     const int per = (ntask + nwave - 1) / nwave;
     // wave-uniform, so the per-tile index arithmetic below runs on the scalar unit
     const int gw = __builtin_amdgcn_readfirstlane(w * gridDim.x + blockIdx.x);   // neighbouring runs on different CUs
@@ -704,6 +706,43 @@ __global__ __launch_bounds__(512) void mala_dec_decide(const DecParams p) {
     const float* tmax = p.tmax + (int64_t)grp * G * p.nTp;   // row g at g * nTp
     const float* tsum = p.tsum + (int64_t)grp * G * p.nTp;
 
+    const int nchunk = (nTb + CH - 1) / CH;
+    // This thread's positions of chunk c: v = c CH + TPT tid + j, tile nTb - 1 - v
+    // (TPT consecutive tiles, one 16-byte load per row when they are aligned).
+    float M[TPT][GP], S[TPT][GP];
+    bool valid[TPT];
+    int tile[TPT];
+    auto load_chunk = [&](int c) {
+        const int top = nTb - 1 - (c * CH + TPT * tid);          // tile of j = 0
+#pragma unroll
+        for (int j = 0; j < TPT; ++j) {
+            tile[j] = top - j;
+            valid[j] = tile[j] >= 0;
+        }
+        if (TPT == 4 && (top - 3) >= 0 && ((top - 3) & 3) == 0) {
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                const int64_t at = (int64_t)(g < G ? g : 0) * p.nTp + (top - 3);
+                const f32x4 m4 = *(const f32x4*)(tmax + at);
+                const f32x4 s4 = *(const f32x4*)(tsum + at);
+#pragma unroll
+                for (int j = 0; j < TPT; ++j) { M[j][g] = m4[3 - j]; S[j][g] = s4[3 - j]; }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < TPT; ++j) {
+                const int t = valid[j] ? tile[j] : 0;
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    const int64_t at = (int64_t)(g < G ? g : 0) * p.nTp + t;
+                    M[j][g] = tmax[at];
+                    S[j][g] = tsum[at];
+                }
+            }
+        }
+    };
+    load_chunk(0);
+
     // Row references: the largest tile max, and whether the smallest lies within 96 of it.
     float gref[GP];
     bool linear = lin_ok;
@@ -711,6 +750,15 @@ __global__ __launch_bounds__(512) void mala_dec_decide(const DecParams p) {
         float mx[GP], mn[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) { mx[g] = kNegInf; mn[g] = __builtin_inff(); }
+        if (nchunk == 1) {                     // every tile is in this thread's registers already
+#pragma unroll
+            for (int j = 0; j < TPT; ++j)
+#pragma unroll
+                for (int g = 0; g < GP; ++g) {
+                    mx[g] = valid[j] ? fmaxf(mx[g], M[j][g]) : mx[g];
+                    mn[g] = valid[j] ? fminf(mn[g], M[j][g]) : mn[g];
+                }
+        } else
         for (int t0 = tid; t0 < nTb; t0 += TPT * NTH) {
             float v[TPT][GP];
 #pragma unroll
@@ -755,26 +803,10 @@ __global__ __launch_bounds__(512) void mala_dec_decide(const DecParams p) {
 #pragma unroll
     for (int g = 0; g < GP; ++g) Z[g] = 0.f;
     int kbase = 0;
-    const int nchunk = (nTb + CH - 1) / CH;
     for (int c = 0; c < nchunk; ++c) {
-        // this thread's positions: v = c CH + TPT tid + j, tile nTb - 1 - v
         float a[TPT][GP], x[TPT][GP];
-        bool valid[TPT];
-        int tile[TPT];
         {
-            float M[TPT][GP], S[TPT][GP];
-#pragma unroll
-            for (int j = 0; j < TPT; ++j) {
-                tile[j] = nTb - 1 - (c * CH + TPT * tid + j);
-                valid[j] = tile[j] >= 0;
-                const int t = valid[j] ? tile[j] : 0;
-#pragma unroll
-                for (int g = 0; g < GP; ++g) {
-                    const int64_t at = (int64_t)(g < G ? g : 0) * p.nTp + t;
-                    M[j][g] = tmax[at];
-                    S[j][g] = tsum[at];
-                }
-            }
+            if (c > 0) load_chunk(c);
 #pragma unroll
             for (int j = 0; j < TPT; ++j)
 #pragma unroll
@@ -1388,9 +1420,9 @@ static hipError_t launch_decode_t(const DecParams& p, bool dense, hipStream_t s)
         hipLaunchKernelGGL((mala_dec_dense_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     } else {
         const int tasks = ngrp * p.nT;
-        int nwg = (tasks + 3) / 4;
-        if (nwg > 512) nwg = 512;        // two workgroups (8 waves) per CU
-        hipLaunchKernelGGL((mala_dec_score<D, GP>), dim3(nwg), dim3(256), 0, s, p);
+        int nwg = (tasks + kScoreWaves - 1) / kScoreWaves;
+        if (nwg > 256) nwg = 256;        // one workgroup (8 waves) per CU
+        hipLaunchKernelGGL((mala_dec_score<D, GP>), dim3(nwg), dim3(64 * kScoreWaves), 0, s, p);
         hipLaunchKernelGGL((mala_dec_decide<GP>), dim3(ngrp), dim3(512), 0, s, p);
         hipLaunchKernelGGL((mala_dec_pv<D, GP>), dim3(p.npv), dim3(256), 0, s, p);
         hipLaunchKernelGGL((mala_dec_sum_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
