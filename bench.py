@@ -5,13 +5,21 @@ One step = one pass of the whole path on synthetic inputs resident in HBM:
     one GPU's share of a 40q/8kv-head model split 8 ways by heads), tau = 1,
   * one decode step of 8 sequences against a 131072-token cache (Hq=5,
     Hkv=1, d=128), tau = 1.
-`value` is the dense-equivalent throughput of the step: the FLOPs dense causal
-attention would execute for the same outputs (forward 4d per legal query-key
-pair, backward 10d, decode 4d per cached key and head) divided by the
-measured step time.  The same kernels at tau = 0 (the dense path) are timed in
-the same run for the speedups, the dominant kernel's roofline is measured live
-with HIP events on the launch stream, and the fp64 oracle is timed on a
-bounded sample of the same workload on the host cores.
+`value` is the step's throughput in the method's own (algorithmic) FLOPs per
+second: scores of every legal query-key pair (2d each, the skip decision
+needs them) plus the post-score work of retained pairs (forward 2d for P.V;
+backward 8d for dP, dV, dK and dQ; decode: scores of every cached key and
+head, 2d P.V per retained key and head), divided by the measured step time.
+It is what the GPU actually does per second and stays below the MFMA peak.
+`effective_tflops` gives the dense-equivalent rates the metric name refers
+to (the FLOPs dense causal attention would spend on the same outputs:
+forward 4d per legal pair, backward 10d) -- skipped work is credited there,
+so those rates can exceed the peak.  The same kernels at tau = 0 (the dense
+path) are timed in the same run for the speedups, the dominant kernel's
+roofline is measured live with HIP events on the launch stream, each
+operator's device memory (outputs + workspace) and the allocator's peak
+around the step are reported for tau = 1 and tau = 0, and the fp64 oracle is
+timed on a bounded sample of the same workload on the host cores.
 
 `--workload prefill_128k` instead times the variable-length forward on a
 chunked prefill: the last 16384 queries of the 128K sequence against all of its
@@ -117,6 +125,101 @@ def recorded_traffic():
 def legal_pairs_block(L, Bq, qb):
     r0, r1 = qb * Bq, min(L, qb * Bq + Bq)
     return sum(i + 1 for i in range(r0, r1))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def kept_slots(keep, L, Bq, Bk, kept_value=1):
+    """Legal query-key pairs inside the tiles marked kept in keep[B, H, nQB, nKT]."""
+    import numpy as np
+    nQB, nKT = keep.shape[-2], keep.shape[-1]
+    rows = np.arange(L)
+    j0 = np.arange(nKT)[None, :] * Bk
+    per_row = np.clip(rows[:, None] - j0 + 1, 0, Bk)                   # [L, nKT] legal keys per row and tile
+    pad = np.zeros((nQB * Bq, nKT), dtype=np.int64)
+    pad[:L] = per_row
+    tile_pairs = pad.reshape(nQB, Bq, nKT).sum(1)                       # [nQB, nKT]
+    return float(((keep == kept_value) * tile_pairs).sum())
+
+
+def cpu_baseline(args, inp, dinp, W, WD, tau):
+    """The fp64 oracle timed on the host cores on a bounded sample of the
+    benchmarked step, credited with the same algorithmic FLOPs as `value`.
+    Legs: forward and backward dQ pass on evenly spaced query blocks of the
+    128K sequence; forward and backward dK/dV pass on its first 16384 rows (a
+    causal prefix is a problem of its own: its rows see no later key and
+    their thresholds tau / (i + 1) do not change); the decode step on all
+    eight sequences."""
+    import numpy as np
+
+    import mala_gen as G
+    from oracle import oracle_bwd, oracle_decode, oracle_fwd, oracle_threads
+    B, L, Hq, Hkv, d, Bq, Bk = W["B"], W["L"], W["Hq"], W["Hkv"], W["d"], W["Bq"], W["Bk"]
+    nQB = -(-L // Bq)
+    f64 = {x: G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")}
+    legs = {}
+
+    # forward + dQ pass on sampled query blocks of the full sequence
+    nb = max(1, args.cpu_blocks)
+    qbs = [int((j + 0.5) * nQB / nb) for j in range(nb)]
+    blocks = [h * nQB + qb for h in range(Hq) for qb in qbs]
+    pairs_s = sum(legal_pairs_block(L, Bq, qb) for qb in qbs) * Hq
+    t0 = time.perf_counter()
+    rf = oracle_fwd(f64["q"], f64["k"], f64["v"], tau, Bq, Bk, blocks=blocks)
+    t1 = time.perf_counter()
+    rb = oracle_bwd(f64["q"], f64["k"], f64["v"], rf["o"], f64["dout"], rf["lse"], tau, Bq, Bk,
+                    qunits=blocks, do_dkdv=False)
+    t2 = time.perf_counter()
+    legs["fwd_blocks"] = (2.0 * d * (pairs_s + kept_slots(rf["keep"], L, Bq, Bk)), t1 - t0)
+    # each backward pass decides its tiles (scores of every legal pair) and
+    # recomputes dP for kept ones: dQ pass S, dP, dQ; dK/dV pass S, dP, dV, dK
+    legs["bwd_dq_blocks"] = (2.0 * d * pairs_s + 4.0 * d * kept_slots(rb["keep"], L, Bq, Bk), t2 - t1)
+
+    # forward + dK/dV pass on the causal prefix
+    Lp = min(L, 16384)
+    pre = {x: np.ascontiguousarray(a[:, :Lp]) for x, a in f64.items()}
+    pairs_p = B * Hq * Lp * (Lp + 1) // 2
+    nKTp = -(-Lp // Bk)
+    t0 = time.perf_counter()
+    rp = oracle_fwd(pre["q"], pre["k"], pre["v"], tau, Bq, Bk)
+    t1 = time.perf_counter()
+    rpb = oracle_bwd(pre["q"], pre["k"], pre["v"], rp["o"], pre["dout"], rp["lse"], tau, Bq, Bk,
+                     kunits=list(range(B * Hkv * nKTp)), do_dq=False)
+    t2 = time.perf_counter()
+    legs["fwd_prefix"] = (2.0 * d * (pairs_p + kept_slots(rp["keep"], Lp, Bq, Bk)), t1 - t0)
+    legs["bwd_dkdv_prefix"] = (2.0 * d * pairs_p + 6.0 * d * kept_slots(rpb["keep"], Lp, Bq, Bk), t2 - t1)
+
+    # decode: every sequence of the step
+    dq64 = {x: G.bf16_bits_to_f64(dinp[x]) for x in ("q", "k", "v")}
+    DB, DN, DHq, DHkv, Dd = WD["B"], WD["N"], WD["Hq"], WD["Hkv"], WD["d"]
+    t0 = time.perf_counter()
+    rd = oracle_decode(dq64["q"], dq64["k"], dq64["v"], tau, 64)
+    t1 = time.perf_counter()
+    kept_keys = float(np.minimum(rd["kept_tiles"].astype(np.int64) * 64, DN).sum())
+    legs["decode"] = (2.0 * Dd * DN * DHq * DB + 2.0 * Dd * kept_keys * (DHq // DHkv), t1 - t0)
+
+    flops = sum(fl for fl, _ in legs.values())
+    secs = sum(sec for _, sec in legs.values())
+    return {
+        "value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
+        "cpu_model": cpu_model(), "kind": "oracle",
+        "sample": f"fp64 oracle, tau={tau}: forward + backward dQ pass on {len(blocks)} query blocks of "
+                  f"train_128k ({nb} evenly spaced blocks x {Hq} heads); forward + backward dK/dV pass on the "
+                  f"first {Lp} rows; the decode_128k step (all {DB} sequences); credited with algorithmic FLOPs "
+                  f"as the GPU value, each backward pass with its own decisions and dP; {secs:.1f} s",
+        "legs": {n: {"tflop": round(fl / 1e12, 4), "seconds": round(sec, 2),
+                     "tflops": round(fl / sec / 1e12, 6)} for n, (fl, sec) in legs.items()},
+        "seconds": round(secs, 2)}
+
 
 
 def main_prefill(args):
@@ -623,6 +726,8 @@ def main():
         for _ in range(warmup):
             fwd(t); bwd(t); dec(t)
         torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats(dev)
+        peak_base[t] = torch.cuda.memory_allocated(dev)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = time.perf_counter()
         for s in range(steps):
@@ -632,11 +737,13 @@ def main():
             ev[s][3].record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps * 1e3
+        peak_step[t] = torch.cuda.max_memory_allocated(dev)
         f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
         b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
         dd = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
         return wall, f, b, dd
 
+    peak_base, peak_step = {}, {}
     ms_step, fwd_ms, bwd_ms, dec_ms = timed_steps(tau, args.steps, args.warmup)
     print(f"# tau={tau}: step {ms_step:.3f} ms (fwd {fwd_ms:.3f}, bwd {bwd_ms:.3f}, decode {dec_ms * 1e3:.1f} us)",
           file=sys.stderr, flush=True)
@@ -711,14 +818,37 @@ def main():
     # algorithmic work of each launch (legal slots only)
     alg_fwd = 2.0 * d * pairs + 2.0 * d * slots_f
     alg_bwd = 2.0 * d * pairs + 8.0 * d * slots_b
+    # MFMA work the kernels issue (whole tiles): forward QK^T on every visited
+    # tile and P.V on kept ones; backward the decision scan on every visited
+    # tile (tau > 0 only), then per kept tile S, dP, dV, dK in the dK/dV pass
+    # and S, dP, dQ again in the dQ pass
     exec_fwd = tile_flop * (n_visit + kf)
-    exec_bwd = tile_flop * (n_visit + 4 * kb)
+    exec_bwd = tile_flop * ((n_visit if tau > 0 else 0) + 7 * kb)
     kept_dec = int(keptd.sum().item())
     nT = -(-DN // 64)
     dec_bytes = DB * DN * DHkv * Dd * 2 + kept_dec * 64 * Dd * 2      # all of K + the kept V tiles
     dec_bytes0 = 2 * DB * DN * DHkv * Dd * 2
+    G_dec = DHq // DHkv
+    alg_dec = 2.0 * Dd * DN * DHq * DB + 2.0 * Dd * min(kept_dec * 64, DB * DHkv * DN) * G_dec
 
-    value = (dense_fwd + dense_bwd + dense_dec) / (ms_step * 1e-3) / 1e12
+    value = (alg_fwd + alg_bwd + alg_dec) / (ms_step * 1e-3) / 1e12
+    dense_step = (dense_fwd + dense_bwd + dense_dec) / (ms_step * 1e-3) / 1e12
+
+    # ---- device memory per operator (the library allocates nothing itself:
+    # outputs and workspaces are the caller's, allocated once above)
+    MiB = 1 << 20
+    nbytes = lambda *ts: sum(x.numel() * x.element_size() for x in ts)  # noqa: E731
+    memory = {
+        "unit": "MiB",
+        "inputs": round(nbytes(q, k, v, do, qd, kc, vc) / MiB, 3),
+        "fwd": {"outputs": round(nbytes(o, lse) / MiB, 3), "workspace": round(nbytes(fws) / MiB, 3)},
+        "bwd": {"outputs": round(nbytes(dq, dk, dv) / MiB, 3), "workspace": round(nbytes(bws) / MiB, 3)},
+        "decode": {"outputs": round(nbytes(od, lsed, keptd) / MiB, 3), "workspace": round(nbytes(dws) / MiB, 3)},
+        # allocator peak during the timed steps minus what was allocated before them
+        "transient_in_step": {f"tau={t:g}": round((peak_step[t] - peak_base[t]) / MiB, 3) for t in peak_step},
+        "note": "per rank; the same outputs and workspaces serve tau = 0 and tau > 0, and the library "
+                "allocates nothing during a call; the forward workspace is an fp16 copy of V",
+    }
 
     # ---- roofline of the dominant kernel (by measured time)
     cand = {"mala_fwd_kernel": (fwd_ms, alg_fwd), "mala_bwd (pre+scan+gradient+convert)": (bwd_ms, alg_bwd)}
@@ -753,14 +883,20 @@ def main():
         "decode_us_graph": round(dec_graph, 2),
         "decode_tokens_per_s": round(DB / (dec_us * 1e-6), 1),
         "decode_hbm_gbs": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
+        "value_definition": "algorithmic FLOPs of the step (scores of every legal pair + post-score work of "
+                            "retained pairs, fwd + bwd + decode) / step time",
+        "algorithmic_tflops": {"fwd": round(alg_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+                               "bwd": round(alg_bwd / (bwd_ms * 1e-3) / 1e12, 2)},
         "effective_tflops": {"fwd": round(dense_fwd / (fwd_ms * 1e-3) / 1e12, 2),
-                             "bwd": round(dense_bwd / (bwd_ms * 1e-3) / 1e12, 2)},
+                             "bwd": round(dense_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+                             "step": round(dense_step, 2)},
         "executed_tflops": {"fwd": round(exec_fwd / (fwd_ms * 1e-3) / 1e12, 2),
                             "bwd": round(exec_bwd / (bwd_ms * 1e-3) / 1e12, 2)},
         "skip": {"fwd_kept_tile_frac": round(kf / n_visit, 4), "bwd_kept_tile_frac": round(kb / n_visit, 4),
                  "decode_kept_tile_frac": round(kept_dec / (DB * DHkv * nT), 4)},
         "slots_per_query": {"fwd": round(slots_f / (B * Hq * L), 1), "bwd": round(slots_b / (B * Hq * L), 1)},
         "roofline": roofline,
+        "memory": memory,
         "gen_s": round(t_gen, 1),
     }
     if res0 is not None:
@@ -772,25 +908,7 @@ def main():
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
     if not args.no_cpu:
-        from oracle import oracle_bwd, oracle_fwd, oracle_threads
-        f64 = {x: G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v", "dout")}
-        nb = max(1, args.cpu_blocks)
-        qbs = [int((j + 0.5) * nQB / nb) for j in range(nb)]
-        blocks = [h * nQB + qb for h in range(Hq) for qb in qbs]
-        pairs_s = sum(legal_pairs_block(L, Bq, qb) for qb in qbs) * Hq
-        t0 = time.perf_counter()
-        rf = oracle_fwd(f64["q"], f64["k"], f64["v"], tau, Bq, Bk, blocks=blocks)
-        oracle_bwd(f64["q"], f64["k"], f64["v"], rf["o"], f64["dout"], rf["lse"], tau, Bq, Bk,
-                   qunits=blocks, do_dkdv=False)
-        tcpu = time.perf_counter() - t0
-        credited = (4.0 + 6.0) * d * pairs_s
-        out["cpu_baseline"] = {
-            "value": round(credited / tcpu / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
-            "kind": "oracle",
-            "sample": f"fp64 oracle forward + backward dQ pass on {len(blocks)} query blocks of train_128k "
-                      f"({nb} evenly spaced blocks x {Hq} heads, tau={tau}); credited dense-equivalent "
-                      f"4d (forward) + 6d (S, dP, dQ) FLOPs per legal pair; {tcpu:.1f} s",
-            "seconds": round(tcpu, 2)}
+        out["cpu_baseline"] = cpu_baseline(args, inp, dinp, W, WD, tau)
     print(json.dumps(out), flush=True)
 
 

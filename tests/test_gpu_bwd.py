@@ -3,6 +3,8 @@
 The GPU backward consumes the GPU forward's O and LSE; the oracle backward
 consumes the oracle forward's own O and LSE, so no value from the HIP path
 reaches the oracle."""
+import json
+
 import numpy as np
 import pytest
 import torch
@@ -219,8 +221,16 @@ def test_bwd_d64(L):
 
 
 def test_bwd_gqa_8k():
+    """The matched-scale 8K configuration, tau = 1; prints its parity record
+    (decisions, raw and relative gradient errors per slice, kept tiles) as one
+    JSON line."""
     w = G.WORKLOADS["gqa_8k"]
-    print(run_bwd_case(G.workload_inputs("gqa_8k"), 1.0, w["Bq"], w["Bk"], label="gqa_8k"))
+    r = run_bwd_case(G.workload_inputs("gqa_8k"), 1.0, w["Bq"], w["Bk"], label="gqa_8k")
+    rec = {"parity_record": "gqa_8k backward, tau=1", "dec": r["dec"], "bwd_keep_frac": r["bwd_keep_frac"]}
+    for n in ("dq", "dk", "dv"):
+        rec[n] = {x: (float(r[n][x]) if isinstance(r[n][x], (float, np.floating)) else r[n][x])
+                  for x in ("worst_raw", "global_raw", "slices", "floor_decided", "worst_ratio")}
+    print(json.dumps(rec), flush=True)
 
 
 def test_bwd_train_128k_sampled():

@@ -1,4 +1,6 @@
 """GPU parity of mala_fwd (through the C ABI) against the fp64 oracle."""
+import json
+
 import numpy as np
 import pytest
 import torch
@@ -64,11 +66,16 @@ def run_fwd_case(inp, tau, Bq, Bk, blocks=None, stats_mode=True, label=""):
     kt_g = st["kept_tiles"].cpu().numpy()
     kt_o = (ref["keep"] == 1).sum(-1)
     assert np.array_equal(kt_g[sel & ~bad], kt_o[sel & ~bad])
+    res = dict(dec=dec, o_worst=float(worst), o_global=float(glob),
+               keep_frac=float((ref["keep"] == 1).sum() / max(1, (ref["keep"] != 255).sum())),
+               slots_per_query_gpu=float(ms_g), slots_per_query_oracle=float(ms_o))
     if stats_mode:
         om_g = st["omitted_mass"].cpu().numpy().astype(np.float64)
         a, bb = om_g[rows].mean(), ref["omitted"][rows].mean()
         assert abs(a - bb) <= STAT_TOL * bb + 1e-9, (a, bb)
-    return dict(dec=dec, o_worst=worst, o_global=glob, keep_frac=float((ref["keep"] == 1).sum() / max(1, (ref["keep"] != 255).sum())))
+        res.update(omitted_mean_gpu=float(a), omitted_mean_oracle=float(bb),
+                   omitted_max_oracle=float(ref["omitted"][rows].max()))
+    return res
 
 
 @pytest.mark.parametrize("tau", [0.0, 1.0])
@@ -106,10 +113,12 @@ def test_fwd_strided_views():
 
 
 def test_fwd_gqa_8k():
+    """The matched-scale 8K configuration (B=1, Hq=16, Hkv=4, d=128, half the
+    heads diffuse), tau = 1; prints its parity record as one JSON line."""
     w = G.WORKLOADS["gqa_8k"]
     inp = G.workload_inputs("gqa_8k", with_dout=False)
     r = run_fwd_case(inp, 1.0, w["Bq"], w["Bk"], label="gqa_8k")
-    print(r)
+    print(json.dumps({"parity_record": "gqa_8k forward, tau=1", **r}), flush=True)
 
 
 @pytest.mark.parametrize("stats_mode", [False, True])
