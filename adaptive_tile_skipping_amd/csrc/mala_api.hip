@@ -71,8 +71,9 @@ int device_cus() {
     return n;
 }
 
-// Decode splits per (sequence, KV head): enough workgroups (~2048) to keep
-// many cache loads in flight, never more than the cache has tiles.
+// Decode splits per (sequence, KV head) of the tau = 0 path, one wave each:
+// enough waves (~2048) to keep many cache loads in flight, no more splits
+// with tiles than the cache has tiles, rounded up to whole workgroups of 8.
 void decode_split(int B, int Hkv, int nT, int* nsplit, int* tps) {
     const int ngrp = B * Hkv;
     int ns = (2048 + ngrp - 1) / ngrp;
@@ -81,7 +82,7 @@ void decode_split(int B, int Hkv, int nT, int* nsplit, int* tps) {
     if (ns < 1) ns = 1;
     int t = (nT + ns - 1) / ns;
     ns = (nT + t - 1) / t;
-    *nsplit = ns;
+    *nsplit = (ns + 7) / 8 * 8;         // whole workgroups of 8 splits (the extra ones are empty)
     *tps = t;
 }
 
@@ -446,7 +447,7 @@ mala_status decode_impl(const void* q, mala_t4 kcache, mala_t4 vcache, const int
     p.kcount = (int32_t*)w; w += align256(grp * sizeof(int32_t));
     p.lse2 = (float*)w; w += align256(grp * G * sizeof(float));
     p.pvinfo = (int32_t*)w; w += align256(grp * 2 * sizeof(int32_t));
-    p.npart = p.nsplit;
+    p.npart = p.nsplit / 8;              // dense path: one partial per workgroup of 8 splits
     p.npv = decode_pv_workgroups(B, Hkv, p.nT);
     const size_t nslot = grp * (size_t)p.nsplit > (size_t)p.npv + grp ? grp * (size_t)p.nsplit : (size_t)p.npv + grp;
     p.part_o = (float*)w; w += align256(nslot * G * d * sizeof(float));

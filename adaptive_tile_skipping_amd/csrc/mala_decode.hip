@@ -26,8 +26,8 @@
 //                    fp32 accumulation, one partial per (workgroup, group).
 //   mala_dec_sum_combine  sums a group's partials (already normalised) -> bf16 o.
 // tau = 0 keeps every tile, so the scan is elided: mala_dec_dense is a fused
-// split-K decode (scores, online softmax and P.V per split) and
-// mala_dec_dense_combine merges the splits.
+// split-K decode (scores, online softmax and P.V per split, eight splits
+// merged per workgroup) and mala_dec_dense_combine merges the partials.
 #include "mala_device.h"
 #include "mala_internal.h"
 
@@ -1211,154 +1211,216 @@ __global__ __launch_bounds__(256) void mala_dec_sum_combine(const DecParams p) {
     }
 }
 
-// tau = 0: fused split-K decode.  Each workgroup owns tiles_per_split tiles of
-// one (sequence, KV head); per round its 4 waves stage and score 4 tiles while
-// every thread's V rows for those tiles are already in flight; then the
-// online-softmax update and P.V for the 256 keys.
+// tau = 0: fused split-K decode.  Wave (group, split) streams the split's
+// tiles: K fragments in registers one tile ahead, the V tile staged in the
+// wave's LDS slice, S^T = K q^T and the online softmax per q head, then
+// O^T += V^T P^T on 16x16x32 bf16 MFMAs.  The contraction takes the keys in a
+// permuted order -- position 8 q4 + u of step st is key 32 st + 4 q4 + u and
+// position 8 q4 + 4 + u is key 32 st + 16 + 4 q4 + u -- so a lane's B
+// operand is exactly the eight probabilities its score registers hold, and
+// the transposing V reads take the same order.  P (fp32) is split into a bf16
+// high part and a bf16 low part (the rest, rounded), each taken by its own
+// MFMA: about 16 significant bits of P.  Eight waves per workgroup (one
+// workgroup per CU) take eight consecutive splits of one group; the
+// workgroup merges their (max, sum, output) through LDS and writes one
+// partial, and mala_dec_dense_combine merges a group's partials.
 template <int D, int GP>
-__global__ __launch_bounds__(256) void mala_dec_dense(const DecParams p) {
-    constexpr int DC = D / 8;
-    constexpr int NKG = 256 / DC;
-    constexpr int KPT = 4 * BKD / NKG;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[4][BKD * D];
-    __shared__ float sS[GP][4 * BKD];
-    __shared__ float sAlpha[GP];
-    __shared__ float sState[GP][2];      // running max, sum (base 2)
-    __shared__ float sRed[NKG][D];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
-    const int s = blockIdx.x, grp = blockIdx.y;
-    const int b = grp / p.Hkv, kh = grp % p.Hkv;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mala_dec_dense(const DecParams p) {
+    constexpr int KS = D / 32;           // 16x16x32 steps over d
+    constexpr int NB = D / 16;           // 16-row blocks of d
+    constexpr int CH = D / 8;            // 16-byte chunks per V row
+    constexpr int RPC = 64 / CH;         // V rows per 1 KB copy
+    constexpr int NWV = 8;
+    constexpr int NKL = 4 * KS;          // K load instructions per tile
+    __shared__ __attribute__((aligned(16))) uint16_t sV[NWV][BKD * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[NWV][KS * 64 * 8];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i16 = lane & 15, q4 = lane >> 4;
     const int G = p.G;
+    // The eight waves of a workgroup take eight consecutive splits of one group
+    // (the number of splits per group is a multiple of 8).
+    const int gw = __builtin_amdgcn_readfirstlane((int)blockIdx.x * NWV + w);
+    const int grp = gw / p.nsplit, s = gw % p.nsplit;
+    const int b = grp / p.Hkv, kh = grp % p.Hkv;
     const int Nb = dec_len(p, b);
     const int nTb = (Nb + BKD - 1) / BKD;
     const int t0 = s * p.tiles_per_split;
     const int t1 = (t0 + p.tiles_per_split < nTb) ? t0 + p.tiles_per_split : nTb;   // may be empty
-    bf16x8 qf[D / 16];
-    load_q_frags<D>(p, b, kh, qf);
-    if (tid < GP) { sState[tid][0] = kNegInf; sState[tid][1] = 0.f; }
-    const int dc = tid % DC, kg = tid / DC;
-    float acc[GP][8];
+    const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh + 8 * q4;
+    const uint16_t* vbase = p.v + b * p.v_sb + kh * p.v_sh;
+    uint16_t* vt = sV[w];
+    {
+        // B operand of the scores, kept in this wave's LDS slice (registers go to
+        // the K tiles): column i16 = q head of the group, d = 32 st + 8 q4 ..
+        const bool ok = i16 < G;
+        const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + kh * G + (ok ? i16 : 0)) * D;
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
+        for (int st = 0; st < KS; ++st) {
+            const u32x4 x = ok ? *(const u32x4*)(qrow + 32 * st + 8 * q4) : u32x4{0, 0, 0, 0};
+            *(u32x4*)(&sQ[w][(st * 64 + lane) * 8]) = x;
+        }
+        wave_lds_exchange();
+    }
+    auto qfrag = [&](int st) -> bf16x8 { return *(const bf16x8*)(&sQ[w][(st * 64 + lane) * 8]); };
+    // A operand of the scores: row 16 blk + i16 of the tile, d = 32 st + 8 q4 ..
+    auto load_k = [&](int t, bf16x8 (&kf)[4][KS]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-    const uint16_t* vb = p.v + b * p.v_sb + kh * p.v_sh + 8 * dc;
+        for (int blk = 0; blk < 4; ++blk) {
+            int j = t * BKD + 16 * blk + i16;
+            j = j < Nb ? j : Nb - 1;                   // rows past Nb are masked
+            const uint16_t* row = kbase + (int64_t)j * p.k_sl;
+#pragma unroll
+            for (int st = 0; st < KS; ++st) kf[blk][st] = *(const bf16x8*)(row + 32 * st);
+        }
+    };
+    // V tile -> this wave's LDS slice, 1 KB (RPC rows) per copy: lane l lands at
+    // row RPC k + l / CH, position l % CH, and holds chunk (l % CH) ^ (row % 8)
+    auto stage_v = [&](int t) {
+#pragma unroll
+        for (int k = 0; k < BKD / RPC; ++k) {
+            const int row = RPC * k + lane / CH;
+            int key = t * BKD + row;
+            key = key < Nb ? key : Nb - 1;
+            const int ch = ((lane % CH) ^ (row & 7)) & (CH - 1);
+            global16_to_lds_asm(vbase + (int64_t)key * p.v_sl + 8 * ch, vt + k * RPC * D);
+        }
+    };
+    float m_run = kNegInf, l_run = 0.f;           // of head i16 (identical in its four lanes)
+    f32x4 acc[NB];
+#pragma unroll
+    for (int m = 0; m < NB; ++m) acc[m] = f32x4{};
+
+    // One tile: V(t) is in flight (issued before the next K tile's loads).
+    auto tile = [&](int t, const bf16x8 (&kf)[4][KS], bool more) {
+        f32x4 c[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            c[blk] = f32x4{};
+#pragma unroll
+            for (int st = 0; st < KS; ++st) c[blk] = mfma16x16x32(kf[blk][st], qfrag(st), c[blk]);
+        }
+        // c[blk][r]: head i16, key 16 blk + 4 q4 + r
+        float M = kNegInf;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = t * BKD + 16 * blk + 4 * q4 + r;
+                c[blk][r] = (j < Nb) ? c[blk][r] * p.scale_log2 : kNegInf;
+                M = fmaxf(M, c[blk][r]);
+            }
+        M = fmaxf(M, __shfl_xor(M, 16));
+        M = wave_max_pair(M);
+        const float mn = fmaxf(m_run, M);             // finite: the tile holds a key below Nb
+        const float alpha = fast_exp2(m_run - mn);    // 0 for the first tile
+        float sum = 0.f;
+        bf16x8 bh[2], bl[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float pv = fast_exp2(c[2 * st + hf][u] - mn);
+                    sum += pv;
+                    const __bf16 h = to_bf16(pv);
+                    bh[st][4 * hf + u] = h;
+                    bl[st][4 * hf + u] = to_bf16(pv - (float)h);
+                }
+        sum += __shfl_xor(sum, 16);
+        sum = wave_sum_pair(sum);
+        l_run = l_run * alpha + sum;
+        m_run = mn;
+        if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+            for (int m = 0; m < NB; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[m][r] *= alpha;
+        }
+        // V(t) has landed once at most the next tile's K loads are outstanding
+        if (more) wait_vmcnt<NKL>();
+        else wait_vmcnt<0>();
+        wave_lds_exchange();
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                // A[i][k] = V[key of position k][16 mb + i]: rows 32 st + 16 hlf + 4 q4 .. +3
+                bf16x8 a;
+#pragma unroll
+                for (int hlf = 0; hlf < 2; ++hlf) {
+                    const int r = 32 * st + 16 * hlf + 4 * q4 + (i16 >> 2);
+                    const int col = 16 * mb + 4 * (i16 & 3);
+                    const int pos = ((col >> 3) ^ (r & 7)) & (CH - 1);
+                    const u32x2 x = lds_read_tr16(vt + r * D + pos * 8 + (col & 7));
+                    const bf16x8 xx = __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], 0u, 0u});
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) a[4 * hlf + u] = xx[u];
+                }
+                acc[mb] = mfma16x16x32(a, bh[st], acc[mb]);
+                acc[mb] = mfma16x16x32(a, bl[st], acc[mb]);
+            }
+        }
+        wave_lds_exchange();                          // the next tile's copies come after these reads
+    };
+
+    if (t0 < t1) {
+        bf16x8 ka[4][KS], kb[4][KS];
+        load_k(t0, ka);
+        for (int t = t0; t < t1; t += 2) {
+            stage_v(t);
+            const bool m1 = t + 1 < t1;
+            if (m1) load_k(t + 1, kb);
+            tile(t, ka, m1);
+            if (!m1) break;
+            stage_v(t + 1);
+            const bool m2 = t + 2 < t1;
+            if (m2) load_k(t + 2, ka);
+            tile(t + 1, kb, m2);
+        }
+    }
+    // The workgroup's partial: the eight splits merged (log-sum-exp) through LDS,
+    // then (max, sum) per head and the unnormalised output of partial s / 8.
+    __syncthreads();                                  // every wave is done with its V slice
+    float (*sRed)[GP][D] = reinterpret_cast<float (*)[GP][D]>(&sV[0][0]);            // [wave][head][d]
+    float (*sML)[GP][2] = reinterpret_cast<float (*)[GP][2]>(&sRed[NWV][0][0]);        // [wave][head][max|sum]
+    static_assert(sizeof(sV) >= NWV * GP * (D + 2) * sizeof(float), "reduction buffer");
+    if (i16 < GP) {
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sRed[w][i16][16 * mb + 4 * q4 + r] = acc[mb][r];
+        if (q4 == 0) {
+            sML[w][i16][0] = m_run;
+            sML[w][i16][1] = l_run;
+        }
+    }
     __syncthreads();
-    for (int tb = t0; tb < t1; tb += 4) {
-        const int t = tb + w;
-        if (t < t1) stage_k_tile<D>(p, b, kh, t, Nb, sK[w]);
-        u32x4 vx[KPT];
+    const int part = s / NWV;
+    for (int x = threadIdx.x; x < G * D; x += NWV * 64) {
+        const int g = x / D, d = x % D;
+        float M = kNegInf;
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            int key = tb * BKD + kg * KPT + r;
-            key = (key < t1 * BKD && key < Nb) ? key : 0;
-            vx[r] = *(const u32x4*)(vb + (int64_t)key * p.v_sl);
-        }
-        {
-            f32x16 sc[2];
-            if (t < t1) {
-                __builtin_amdgcn_s_waitcnt(0);
-                tile_scores<D>(p, t, Nb, sK[w], qf, sc);
-            } else {
+        for (int w2 = 0; w2 < NWV; ++w2) M = fmaxf(M, sML[w2][g][0]);
+        float o = 0.f, l = 0.f;
+        if (M != kNegInf) {
 #pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sc[sub][r] = kNegInf;
-            }
-            if (l32 < G) {
-#pragma unroll
-                for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        sS[l32][w * BKD + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3)] = sc[sub][r];
+            for (int w2 = 0; w2 < NWV; ++w2) {
+                const float a = fast_exp2(sML[w2][g][0] - M);   // 0 for an empty split
+                o += a * sRed[w2][g][d];
+                l += a * sML[w2][g][1];
             }
         }
-        __syncthreads();
-        // online softmax over the 256 new scores: 16 threads per row
-        {
-            const int g = tid >> 4, part = tid & 15;
-            float mx = kNegInf;
-            if (g < G)
-                for (int j = part; j < 4 * BKD; j += 16) mx = fmaxf(mx, sS[g][j]);
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-            float mo = kNegInf, lo = 0.f;
-            if (g < G) { mo = sState[g][0]; lo = sState[g][1]; }
-            const float mn = fmaxf(mo, mx);
-            const float muse = (mn == kNegInf) ? 0.f : mn;
-            float sum = 0.f;
-            if (g < G)
-                for (int j = part; j < 4 * BKD; j += 16) {
-                    const float e = fast_exp2(sS[g][j] - muse);
-                    sS[g][j] = e;
-                    sum += e;
-                }
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-            __syncthreads();
-            if (g < G && part == 0) {
-                const float a = (mo == kNegInf) ? 0.f : fast_exp2(mo - muse);
-                sAlpha[g] = a;
-                sState[g][0] = mn;
-                sState[g][1] = lo * a + sum;
-            }
+        const int64_t ix = ((int64_t)grp * p.npart + part) * G + g;
+        p.part_o[ix * D + d] = o;
+        if (d == 0) {
+            p.part_ml[ix * 2 + 0] = M;
+            p.part_ml[ix * 2 + 1] = l;
         }
-        __syncthreads();
-#pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            if (g < G) {
-                const float a = sAlpha[g];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[g][e] *= a;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const int jj = kg * KPT + r;
-            const int key = tb * BKD + jj;
-            if (key >= t1 * BKD || key >= Nb) continue;
-            float vv[8];
-#pragma unroll
-            for (int m2 = 0; m2 < 4; ++m2) {
-                vv[2 * m2] = __uint_as_float(vx[r][m2] << 16);
-                vv[2 * m2 + 1] = __uint_as_float(vx[r][m2] & 0xFFFF0000u);
-            }
-#pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                if (g < G) {
-                    const float pr = sS[g][jj];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[g][e] += pr * vv[e];
-                }
-            }
-        }
-        __syncthreads();
-    }
-    float* po = p.part_o + (((int64_t)grp * p.npart + s) * G) * D;
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int gg = 0; gg < GP; ++gg)
-            if (gg == g)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sRed[kg][8 * dc + e] = acc[gg][e];
-        __syncthreads();
-        if (tid < D) {
-            float sum = 0.f;
-#pragma unroll
-            for (int k2 = 0; k2 < NKG; ++k2) sum += sRed[k2][tid];
-            po[(int64_t)g * D + tid] = sum;
-        }
-        __syncthreads();
-    }
-    if (tid < G) {
-        p.part_ml[(((int64_t)grp * p.nsplit + s) * G + tid) * 2 + 0] = sState[tid][0];
-        p.part_ml[(((int64_t)grp * p.nsplit + s) * G + tid) * 2 + 1] = sState[tid][1];
     }
 }
 
-// One workgroup per (group, row, 32-wide d slice): 8 split classes x 32 d.
 template <int D>
 __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p) {
     __shared__ float sM[256];
@@ -1369,7 +1431,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p)
     const int G = p.G;
     const int b = grp / p.Hkv, kh = grp % p.Hkv;
     const int nTb = (dec_len(p, b) + BKD - 1) / BKD;     // 0: skipped sequence
-    const int64_t base = (int64_t)grp * p.nsplit;
+    const int64_t base = (int64_t)grp * p.npart;
     if (dq == 0 && g == 0) {
         if (tid == 0 && p.kept_tiles) p.kept_tiles[grp] = nTb;
         if (p.bits)
@@ -1382,7 +1444,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p)
     if (nTb == 0) return;                         // o and lse are left as they were
     // global max over splits
     float mx = kNegInf;
-    for (int s = tid; s < p.nsplit; s += 256) mx = fmaxf(mx, p.part_ml[((base + s) * G + g) * 2]);
+    for (int s = tid; s < p.npart; s += 256) mx = fmaxf(mx, p.part_ml[((base + s) * G + g) * 2]);
     sM[tid] = mx;
     __syncthreads();
     for (int off = 128; off >= 1; off >>= 1) {
@@ -1393,7 +1455,7 @@ __global__ __launch_bounds__(256) void mala_dec_dense_combine(const DecParams p)
     const int d = 32 * dq + (tid & 31), cls = tid >> 5;
     float osum = 0.f, lsum = 0.f;
 #pragma unroll 4
-    for (int s = cls; s < p.nsplit; s += 8) {
+    for (int s = cls; s < p.npart; s += 8) {
         const int64_t ix = (base + s) * G + g;
         const float ms = p.part_ml[ix * 2];
         const float a = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
@@ -1416,7 +1478,8 @@ template <int D, int GP>
 static hipError_t launch_decode_t(const DecParams& p, bool dense, hipStream_t s) {
     const int ngrp = p.B * p.Hkv;
     if (dense) {
-        hipLaunchKernelGGL((mala_dec_dense<D, GP>), dim3(p.nsplit, ngrp), dim3(256), 0, s, p);
+        // one wave per (group, split); nsplit is a multiple of 8
+        hipLaunchKernelGGL((mala_dec_dense<D, GP>), dim3(ngrp * p.nsplit / 8), dim3(512), 0, s, p);
         hipLaunchKernelGGL((mala_dec_dense_combine<D>), dim3(ngrp, p.G, D / 32), dim3(256), 0, s, p);
     } else {
         const int tasks = ngrp * p.nT;

@@ -145,6 +145,15 @@ __device__ __forceinline__ void buffer16_to_lds_asm(const u32x4& r, uint32_t vof
                  : "memory");
 }
 
+// 16-byte global -> LDS copy (lane l's 16 bytes land at lds_wave_base + 16 l)
+// from a 64-bit address, issued from inline assembly like buffer16_to_lds_asm:
+// the compiler does not insert a wait for it before later LDS reads, so the
+// caller waits (wait_vmcnt) for exactly the copies it needs.
+__device__ __forceinline__ void global16_to_lds_asm(const void* gptr, void* lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(m0) : "memory");
+}
+
 // Exchange point for data passed between the lanes of one wave through LDS:
 // __builtin_amdgcn_wave_barrier() alone does not stop the compiler from moving
 // memory accesses across it (it may hoist a lane's LDS read above the LDS write

@@ -82,7 +82,7 @@ struct DecParams {
     int nwords;
     int64_t k_sb, k_sl, k_sh, v_sb, v_sl, v_sh;
     int B, N, Hq, Hkv, G, nT, nsplit, tiles_per_split;
-    int npart;              // dense path: partial outputs per (sequence, KV head) (= nsplit)
+    int npart;              // dense path: partials per (sequence, KV head), one per workgroup of 8 splits
     int npv;                // P.V workgroups (tau > 0)
     float scale_log2;
     float log2_tau;

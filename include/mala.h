@@ -36,11 +36,16 @@
  *     the call returns without waiting.  Arguments are validated on the host
  *     before anything is enqueued: an invalid call enqueues nothing.
  *   - tau must be finite and >= 0.
- *   - Arithmetic: scores, softmax state and accumulators in fp32; the P.V
- *     contraction of the forward and decode runs in fp16 (P in [0, 1] rounded
- *     to nearest; V converted exactly from bf16, so |v| must stay within
- *     fp16's range, 65504, beyond which it saturates); the other contractions
- *     take bf16 operands.
+ *   - Arithmetic: scores, softmax state and accumulators in fp32; the other
+ *     contractions take bf16 operands, except the forward's P.V, which runs in
+ *     fp16: P in [0, 1] rounded to nearest, and V converted from bf16 to fp16
+ *     rounding toward zero.  That conversion is exact for v = 0 and for
+ *     2^-17 <= |v| <= 65504 (every bf16 value there is an fp16 value); a
+ *     smaller |v| is truncated toward zero to a multiple of 2^-24 (to 0 below
+ *     2^-24), and a larger one becomes +-65504.  Keep V inside that range for
+ *     mala_fwd (rescale it otherwise); mala_bwd and the decode read bf16 V as
+ *     is.  The decode's P.V takes P as fp16 values split exactly into two bf16
+ *     parts, against bf16 V.
  *   - Supported shapes: (d, Bq, Bk) = (128, 128, 64) or (64, 64, 64) for
  *     mala_fwd / mala_bwd; decode takes d = 128 or 64 with Bk_dec = 64.
  *     Byte ranges addressed through 32-bit buffer resources must stay within

@@ -168,3 +168,42 @@ def test_fwd_workspace_reused_across_shapes():
     assert torch.equal(ob1, ob2) and torch.equal(lb1, lb2)
     assert torch.equal(os_, os_f) and torch.equal(ls_, ls_f)
     run_fwd_case(small, 1.0, 128, 64, label="small after big, own workspace")
+
+
+def _v_as_fp16_rtz(v):
+    """The forward's bf16 -> fp16 V conversion as documented: exact for
+    2^-17 <= |v| <= 65504, truncated toward zero to a multiple of 2^-24 below
+    2^-14 (fp16 subnormals), +-65504 above 65504."""
+    a = np.minimum(np.abs(v), 65504.0)
+    a = np.where(a < 2.0 ** -14, np.floor(a / 2.0 ** -24) * 2.0 ** -24, a)
+    return np.sign(v) * a
+
+
+@pytest.mark.parametrize("scale_exp", [16, -20])
+def test_fwd_v_outside_fp16_range(scale_exp):
+    """V scaled by 2^16 (a third of |v| above 65504) or 2^-20 (every |v| below
+    2^-14): O equals the oracle's on V converted as the header documents, and
+    differs from the oracle on the unconverted V where the conversion loses."""
+    dev = _dev()
+    inp = G.attn_inputs(620, 1, 600, 4, 2, 128, 0.1, diffuse_kv_heads=(1,), with_dout=False)
+    qf, kf, vf = (G.bf16_bits_to_f64(inp[x]) for x in ("q", "k", "v"))
+    vs = vf * 2.0 ** scale_exp                       # exact: bf16 keeps fp32's exponent range
+    vbits = G.round_to_bf16_bits(vs)
+    assert np.array_equal(G.bf16_bits_to_f64(vbits), vs)
+    conv = _v_as_fp16_rtz(vs)
+    if scale_exp > 0:
+        assert (np.abs(vs) > 65504).any()
+    else:
+        assert (np.abs(vs) < 2.0 ** -14).all() and (conv != vs).any()
+    print(f"[fwd] V scaled by 2^{scale_exp} B=1 L=600 Hq=4 Hkv=2 d=128 tau=1", flush=True)
+    q, k = (bf16_tensor(inp[x], dev) for x in ("q", "k"))
+    v = bf16_tensor(vbits, dev)
+    o, lse = mala.mala_fwd(q, k, v, 1.0, 128, 64)
+    torch.cuda.synchronize()
+    ref = oracle_fwd(qf, kf, conv, 1.0, 128, 64)
+    worst, _ = rel_l2_per_head(to_f64(o), ref["o"])
+    assert worst <= O_TOL, worst
+    raw = oracle_fwd(qf, kf, vs, 1.0, 128, 64)
+    worst_raw, _ = rel_l2_per_head(to_f64(o), raw["o"])
+    print({"o_vs_converted_v": worst, "o_vs_unconverted_v": worst_raw}, flush=True)
+    assert worst_raw > 10 * O_TOL
