@@ -1034,6 +1034,7 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
     __shared__ int sTl[TLCAP];
     __shared__ int sWi[4];
     __shared__ int sFound[2];
+    __shared__ int sKc[256];
     float (*sRed)[16][D] = reinterpret_cast<float (*)[16][D]>(&sV[0][0]);   // [wave][head][d], after the tiles
     static_assert(sizeof(sV) >= 4 * 16 * D * sizeof(float), "reduction buffer");
     const int tid = threadIdx.x;
@@ -1043,27 +1044,38 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
     const int ngrp = p.B * p.Hkv;
     const int wg = blockIdx.x;
 
-    // total kept tiles, this workgroup's range [s, e)
-    int T = 0;
-    {
+    // total kept tiles T, this workgroup's range [s, e), and the group holding
+    // item s with its first item.  Up to 256 groups one scan gives all of it
+    // (thread g holds group g's count and prefix), and the counts stay in LDS.
+    int T = 0, per = 0, s = 0, e = 0;
+    if (ngrp <= 256) {
+        const int kc = tid < ngrp ? p.kcount[tid] : 0;
+        sKc[tid] = kc;
+        int tot;
+        const int pre = block_excl_scan_i<4>(kc, tot, sWi);
+        T = tot;
+        if (T == 0) return;
+        per = (T + gridDim.x - 1) / gridDim.x;
+        s = wg * per;
+        e = (s + per < T) ? s + per : T;
+        if (s >= e) return;
+        if (tid < ngrp && pre <= s && s < pre + kc) { sFound[0] = tid; sFound[1] = pre; }
+        __syncthreads();
+    } else {
         int c = 0;
         for (int g = tid; g < ngrp; g += 256) c += p.kcount[g];
         int tot;
         block_excl_scan_i<4>(c, tot, sWi);
         T = tot;
-    }
-    if (T == 0) return;
-    const int per = (T + gridDim.x - 1) / gridDim.x;
-    const int s = wg * per;
-    const int e = (s + per < T) ? s + per : T;
-    if (s >= e) return;
-    // the group holding item s, and its first item
-    {
+        if (T == 0) return;
+        per = (T + gridDim.x - 1) / gridDim.x;
+        s = wg * per;
+        e = (s + per < T) ? s + per : T;
+        if (s >= e) return;
         int carry = 0;
         for (int g0 = 0; g0 < ngrp; g0 += 256) {
             const int g = g0 + tid;
             const int kc = g < ngrp ? p.kcount[g] : 0;
-            int tot;
             const int pre = carry + block_excl_scan_i<4>(kc, tot, sWi);
             if (g < ngrp && pre <= s && s < pre + kc) { sFound[0] = g; sFound[1] = pre; }
             carry += tot;
@@ -1071,12 +1083,13 @@ __global__ __launch_bounds__(256) void mala_dec_pv(const DecParams p) {
         }
         __syncthreads();
     }
+    auto kcount_of = [&](int g) { return ngrp <= 256 ? sKc[g] : p.kcount[g]; };
     int g = sFound[0];
     int pre = sFound[1];
     uint16_t* vt = sV[w];
     int i = s;
     while (i < e) {                                     // uniform over the workgroup
-        const int kc = p.kcount[g];
+        const int kc = kcount_of(g);
         const int seg_end = (pre + kc < e) ? pre + kc : e;
         if (seg_end > i) {
             const int b = g / p.Hkv, kh = g % p.Hkv;
