@@ -57,8 +57,15 @@ def _load():
                                            P, i32, P, i32, P, P, P, P, P, P, P, i32]
     lib.mala_oracle_decode.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, P,
                                        P, P, P, P, P, P, i32]
+    lib.mala_oracle_fwd_forced.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, i32, P, i32, P,
+                                           P, P, P, P, P, P, i32]
+    lib.mala_oracle_decode_forced.argtypes = [P, P, P, i32, i32, i32, i32, i32, f64, i32, P, P,
+                                              P, P, P, P, P, P, i32]
+    lib.mala_oracle_fwd_varlen_forced.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, i32, i32, P, i32, P,
+                                                  P, P, P, P, P, P, i32]
     for f in (lib.mala_oracle_fwd, lib.mala_oracle_fwd_varlen, lib.mala_oracle_bwd, lib.mala_oracle_bwd_varlen,
-              lib.mala_oracle_decode):
+              lib.mala_oracle_decode, lib.mala_oracle_fwd_forced, lib.mala_oracle_decode_forced,
+              lib.mala_oracle_fwd_varlen_forced):
         f.restype = ctypes.c_int
     lib.mala_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -77,11 +84,15 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def oracle_fwd(q, k, v, tau: float, Bq: int, Bk: int, blocks=None, nthreads: int = 0):
+def oracle_fwd(q, k, v, tau: float, Bq: int, Bk: int, blocks=None, forced=None, nthreads: int = 0):
     """Forward rule.  Returns dict(o, lse, keep, margin, kept_slots, omitted).
 
     `blocks`: optional list of flat block ids (b*Hq + h)*nQB + qb; only those
     query blocks are computed (rows of other blocks stay NaN / -1 / 255).
+    `forced`: optional uint8 [B, Hq, nQB, nKT] teacher-forced replay (0 / 1 =
+    the decision a tile's state update follows, 255 = the rule's); keep and
+    margin are then the rule's own, given the forced trajectory, and o, lse
+    and the statistics those of the forced run (mala_oracle_fwd_forced).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, L, Hq, d = q.shape
@@ -94,22 +105,32 @@ def oracle_fwd(q, k, v, tau: float, Bq: int, Bk: int, blocks=None, nthreads: int
     slots = np.full((B, Hq, L), -1, np.int32)
     omitted = np.full((B, Hq, L), np.nan)
     bl = None if blocks is None else np.ascontiguousarray(blocks, dtype=np.int32)
-    rc = _load().mala_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), B, L, Hq, Hkv, d, float(tau), Bq, Bk,
-                                 _ptr(bl), 0 if bl is None else len(bl),
-                                 _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(slots), _ptr(omitted),
-                                 int(nthreads))
+    if forced is None:
+        rc = _load().mala_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), B, L, Hq, Hkv, d, float(tau), Bq, Bk,
+                                     _ptr(bl), 0 if bl is None else len(bl),
+                                     _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(slots), _ptr(omitted),
+                                     int(nthreads))
+    else:
+        fz = np.ascontiguousarray(forced, dtype=np.uint8)
+        if fz.shape != (B, Hq, nQB, nKT):
+            raise ValueError(f"forced must be [B, Hq, nQB, nKT] = {(B, Hq, nQB, nKT)}, got {fz.shape}")
+        rc = _load().mala_oracle_fwd_forced(_ptr(q), _ptr(k), _ptr(v), B, L, Hq, Hkv, d, float(tau), Bq, Bk,
+                                            _ptr(bl), 0 if bl is None else len(bl), _ptr(fz),
+                                            _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(slots),
+                                            _ptr(omitted), int(nthreads))
     if rc:
         raise ValueError(f"oracle_fwd failed with code {rc}")
     return {"o": o, "lse": lse, "keep": keep, "margin": margin, "kept_slots": slots, "omitted": omitted}
 
 
-def oracle_fwd_varlen(q, k, v, cu_q, cu_k, tau: float, Bq: int, Bk: int, blocks=None, nthreads: int = 0):
+def oracle_fwd_varlen(q, k, v, cu_q, cu_k, tau: float, Bq: int, Bk: int, blocks=None, forced=None,
+                      nthreads: int = 0):
     """Variable-length forward (queries at the end of their keys, Lq <= Lk).
 
     q [total_q, Hq, d], k/v [total_k, Hkv, d]; cu_q/cu_k [B+1] cumulative
     lengths.  Returns dict(o, lse [Hq, total_q], keep/margin [B, Hq, nQB, nKT],
-    kept_slots, omitted) with nQB, nKT from the longest sequence; `blocks` as
-    in oracle_fwd with that nQB.
+    kept_slots, omitted) with nQB, nKT from the longest sequence; `blocks` and
+    `forced` (keep's layout) as in oracle_fwd with that nQB.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     cq = np.ascontiguousarray(cu_q, dtype=np.int32)
@@ -127,10 +148,19 @@ def oracle_fwd_varlen(q, k, v, cu_q, cu_k, tau: float, Bq: int, Bk: int, blocks=
     slots = np.full((Hq, Tq), -1, np.int32)
     omitted = np.full((Hq, Tq), np.nan)
     bl = None if blocks is None else np.ascontiguousarray(blocks, dtype=np.int32)
-    rc = _load().mala_oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), B, Hq, Hkv, d,
-                                        float(tau), Bq, Bk, _ptr(bl), 0 if bl is None else len(bl),
-                                        _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(slots),
-                                        _ptr(omitted), int(nthreads))
+    if forced is None:
+        rc = _load().mala_oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), B, Hq, Hkv, d,
+                                            float(tau), Bq, Bk, _ptr(bl), 0 if bl is None else len(bl),
+                                            _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(slots),
+                                            _ptr(omitted), int(nthreads))
+    else:
+        fz = np.ascontiguousarray(forced, dtype=np.uint8)
+        if fz.shape != keep.shape:
+            raise ValueError(f"forced must be [B, Hq, nQB, nKT] = {keep.shape}, got {fz.shape}")
+        rc = _load().mala_oracle_fwd_varlen_forced(_ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), B, Hq, Hkv, d,
+                                                   float(tau), Bq, Bk, _ptr(bl), 0 if bl is None else len(bl),
+                                                   _ptr(fz), _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin),
+                                                   _ptr(slots), _ptr(omitted), int(nthreads))
     if rc:
         raise ValueError(f"oracle_fwd_varlen failed with code {rc}")
     return {"o": o, "lse": lse, "keep": keep, "margin": margin, "kept_slots": slots, "omitted": omitted}
@@ -220,11 +250,13 @@ def oracle_bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, tau: float, Bq: int, Bk
     return out
 
 
-def oracle_decode(q, kc, vc, tau: float, Bkd: int, seqlens=None, nthreads: int = 0):
+def oracle_decode(q, kc, vc, tau: float, Bkd: int, seqlens=None, forced=None, nthreads: int = 0):
     """Decode rule.  Returns dict(o, lse, keep, margin, kept_tiles, omitted).
 
     `seqlens`: optional [B] cache lengths (1 <= N_b <= N); sequence b then
-    sees only its first N_b cache rows (tiles past them stay 255 / NaN)."""
+    sees only its first N_b cache rows (tiles past them stay 255 / NaN).
+    `forced`: optional uint8 [B, Hkv, nT] teacher-forced replay, as in
+    oracle_fwd (mala_oracle_decode_forced)."""
     q, kc, vc = _f64(q), _f64(kc), _f64(vc)
     sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
     B, Hq, d = q.shape
@@ -236,6 +268,16 @@ def oracle_decode(q, kc, vc, tau: float, Bkd: int, seqlens=None, nthreads: int =
     margin = np.full((B, Hkv, nT), np.nan)
     kept = np.full((B, Hkv), -1, np.int32)
     omitted = np.full((B, Hq), np.nan)
+    if forced is not None:
+        fz = np.ascontiguousarray(forced, dtype=np.uint8)
+        if fz.shape != (B, Hkv, nT):
+            raise ValueError(f"forced must be [B, Hkv, nT] = {(B, Hkv, nT)}, got {fz.shape}")
+        rc = _load().mala_oracle_decode_forced(_ptr(q), _ptr(kc), _ptr(vc), B, N, Hq, Hkv, d, float(tau), Bkd,
+                                               _ptr(sl), _ptr(fz), _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin),
+                                               _ptr(kept), _ptr(omitted), int(nthreads))
+        if rc:
+            raise ValueError(f"oracle_decode failed with code {rc}")
+        return {"o": o, "lse": lse, "keep": keep, "margin": margin, "kept_tiles": kept, "omitted": omitted}
     rc = _load().mala_oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), B, N, Hq, Hkv, d, float(tau), Bkd, _ptr(sl),
                                     _ptr(o), _ptr(lse), _ptr(keep), _ptr(margin), _ptr(kept), _ptr(omitted),
                                     int(nthreads))

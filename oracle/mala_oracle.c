@@ -141,6 +141,10 @@ typedef struct {
     double *o, *lse, *margin, *omitted;
     uint8_t* keep;
     int32_t* kept_slots;
+    /* NULL, or [B][Hq][nQB][nKT]: 0 / 1 forces the decision a tile's update
+     * uses, 255 leaves it to the rule (teacher-forced replay, see
+     * mala_oracle_fwd_forced) */
+    const uint8_t* forced;
 } fwd_ctx;
 
 static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
@@ -209,12 +213,14 @@ static int fwd_block(const fwd_ctx* c, int b, int h, int qb) {
         const size_t tidx = (((size_t)b * Hq + h) * c->nQB + qb) * c->nKT + kt;
         if (c->keep) c->keep[tidx] = (uint8_t)keep;
         if (c->margin) c->margin[tidx] = lam;
+        /* the decision the state update follows: the rule's, or a forced one */
+        const int use = (c->forced && c->forced[tidx] != 255) ? (c->forced[tidx] != 0) : keep;
 
         for (int r = 0; r < nr; ++r) {
             if (M[r] == -INFINITY) continue;
             const int jl = off + r0 + r;
             const int nleg = ((jl < j1 - 1) ? jl : j1 - 1) - j0 + 1;
-            if (keep) {
+            if (use) {
                 /* standard online-softmax update with the tile's legal keys */
                 const double mn = (M[r] > m[r]) ? M[r] : m[r];
                 const double alpha = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - mn);
@@ -283,11 +289,11 @@ static int fwd_run(const fwd_ctx* c, const int32_t* blocks, int nblocks, int nth
     return err;
 }
 
-int mala_oracle_fwd(const double* q, const double* k, const double* v,
-                    int B, int L, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
-                    const int32_t* blocks, int nblocks,
-                    double* o, double* lse, uint8_t* keep, double* margin,
-                    int32_t* kept_slots, double* omitted, int nthreads) {
+static int fwd_fixed(const double* q, const double* k, const double* v,
+                     int B, int L, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
+                     const int32_t* blocks, int nblocks, const uint8_t* forced,
+                     double* o, double* lse, uint8_t* keep, double* margin,
+                     int32_t* kept_slots, double* omitted, int nthreads) {
     if (!q || !k || !v || !o || !lse) return OR_EINVAL;
     if (B <= 0 || L <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Bq <= 0 || Bk <= 0) return OR_EINVAL;
     if (Hq % Hkv != 0 || !tau_valid(tau)) return OR_EINVAL;
@@ -306,20 +312,49 @@ int mala_oracle_fwd(const double* q, const double* k, const double* v,
     c.lse_hstride = L;
     c.tau = tau; c.scale = 1.0 / sqrt((double)d);
     c.o = o; c.lse = lse; c.keep = keep; c.margin = margin; c.kept_slots = kept_slots; c.omitted = omitted;
+    c.forced = forced;
     const int err = fwd_run(&c, blocks, nblocks, nthreads);
     free(offs);
     free(lens);
     return err;
 }
 
+int mala_oracle_fwd(const double* q, const double* k, const double* v,
+                    int B, int L, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
+                    const int32_t* blocks, int nblocks,
+                    double* o, double* lse, uint8_t* keep, double* margin,
+                    int32_t* kept_slots, double* omitted, int nthreads) {
+    return fwd_fixed(q, k, v, B, L, Hq, Hkv, d, tau, Bq, Bk, blocks, nblocks, NULL, o, lse, keep, margin,
+                     kept_slots, omitted, nthreads);
+}
+
+/* Teacher-forced replay of the forward: where forced[tile] is 0 or 1 the
+ * tile's state update follows that decision instead of the rule's, so the
+ * rows' retained state is the one a run that took those decisions has.
+ * keep and margin still record the rule's own decision and margin for every
+ * tile, given that state.  With forced = the decisions of another
+ * implementation, each of its decisions is judged from the state it had
+ * itself: a decision that disagrees with the rule there is a genuine
+ * difference (inside or outside the near-tie band), not a consequence of an
+ * earlier one.  O, LSE and the statistics are those of the forced run. */
+int mala_oracle_fwd_forced(const double* q, const double* k, const double* v,
+                           int B, int L, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
+                           const int32_t* blocks, int nblocks, const uint8_t* forced,
+                           double* o, double* lse, uint8_t* keep, double* margin,
+                           int32_t* kept_slots, double* omitted, int nthreads) {
+    if (!forced) return OR_EINVAL;
+    return fwd_fixed(q, k, v, B, L, Hq, Hkv, d, tau, Bq, Bk, blocks, nblocks, forced, o, lse, keep, margin,
+                     kept_slots, omitted, nthreads);
+}
+
 /* Variable-length forward: sequence b has queries cu_q[b] .. cu_q[b+1]-1 and
  * keys cu_k[b] .. cu_k[b+1]-1 of the packed arrays, with its queries at the
  * end of its keys (0 <= Lq <= Lk).  Layouts in the header comment; nQB and
  * nKT from the longest query and key lengths. */
-int mala_oracle_fwd_varlen(const double* q, const double* k, const double* v,
+static int fwd_varlen_impl(const double* q, const double* k, const double* v,
                            const int32_t* cu_q, const int32_t* cu_k,
                            int B, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
-                           const int32_t* blocks, int nblocks,
+                           const int32_t* blocks, int nblocks, const uint8_t* forced,
                            double* o, double* lse, uint8_t* keep, double* margin,
                            int32_t* kept_slots, double* omitted, int nthreads) {
     if (!q || !k || !v || !o || !lse || !cu_q || !cu_k) return OR_EINVAL;
@@ -352,10 +387,34 @@ int mala_oracle_fwd_varlen(const double* q, const double* k, const double* v,
     c.lse_hstride = cu_q[B];
     c.tau = tau; c.scale = 1.0 / sqrt((double)d);
     c.o = o; c.lse = lse; c.keep = keep; c.margin = margin; c.kept_slots = kept_slots; c.omitted = omitted;
+    c.forced = forced;
     const int err = fwd_run(&c, blocks, nblocks, nthreads);
     free(offs);
     free(lens);
     return err;
+}
+
+int mala_oracle_fwd_varlen(const double* q, const double* k, const double* v,
+                           const int32_t* cu_q, const int32_t* cu_k,
+                           int B, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
+                           const int32_t* blocks, int nblocks,
+                           double* o, double* lse, uint8_t* keep, double* margin,
+                           int32_t* kept_slots, double* omitted, int nthreads) {
+    return fwd_varlen_impl(q, k, v, cu_q, cu_k, B, Hq, Hkv, d, tau, Bq, Bk, blocks, nblocks, NULL, o, lse, keep,
+                           margin, kept_slots, omitted, nthreads);
+}
+
+/* Teacher-forced replay of the variable-length forward, as
+ * mala_oracle_fwd_forced (forced has keep's layout, [B][Hq][nQB][nKT]). */
+int mala_oracle_fwd_varlen_forced(const double* q, const double* k, const double* v,
+                                  const int32_t* cu_q, const int32_t* cu_k,
+                                  int B, int Hq, int Hkv, int d, double tau, int Bq, int Bk,
+                                  const int32_t* blocks, int nblocks, const uint8_t* forced,
+                                  double* o, double* lse, uint8_t* keep, double* margin,
+                                  int32_t* kept_slots, double* omitted, int nthreads) {
+    if (!forced) return OR_EINVAL;
+    return fwd_varlen_impl(q, k, v, cu_q, cu_k, B, Hq, Hkv, d, tau, Bq, Bk, blocks, nblocks, forced, o, lse, keep,
+                           margin, kept_slots, omitted, nthreads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -653,9 +712,9 @@ int mala_oracle_bwd_varlen(const double* q, const double* k, const double* v, co
 /* its first N_b cache rows, with L_i = N_b and tiles 0 .. ceil(N_b/Bkd)-1   */
 /* (entries of later tiles are not written).                                 */
 /* ------------------------------------------------------------------------ */
-int mala_oracle_decode(const double* q, const double* kc, const double* vc,
+static int decode_impl(const double* q, const double* kc, const double* vc,
                        int B, int N, int Hq, int Hkv, int d, double tau, int Bkd,
-                       const int32_t* seqlens,
+                       const int32_t* seqlens, const uint8_t* forced,
                        double* o, double* lse, uint8_t* keep, double* margin,
                        int32_t* kept_tiles, double* omitted, int nthreads) {
     if (!q || !kc || !vc || !o || !lse) return OR_EINVAL;
@@ -699,9 +758,12 @@ int mala_oracle_decode(const double* q, const double* kc, const double* vc,
                 const double x = (l[g] == 0.0) ? INFINITY : mx - m[g] - log(l[g]) - th;
                 if (x > lam) lam = x;
             }
-            const int kp = (lam >= 0.0);
-            if (keep) keep[((size_t)b * Hkv + kh) * nTmax + t] = (uint8_t)kp;
-            if (margin) margin[((size_t)b * Hkv + kh) * nTmax + t] = lam;
+            const size_t tidx = ((size_t)b * Hkv + kh) * nTmax + t;
+            const int own = (lam >= 0.0);
+            if (keep) keep[tidx] = (uint8_t)own;
+            if (margin) margin[tidx] = lam;
+            /* the decision the state update follows: the rule's, or a forced one */
+            const int kp = (forced && forced[tidx] != 255) ? (forced[tidx] != 0) : own;
             nkept += kp;
             for (int g = 0; g < G; ++g) {
                 if (kp) {
@@ -742,4 +804,27 @@ int mala_oracle_decode(const double* q, const double* kc, const double* vc,
         free(buf);
     }
     return err;
+}
+
+int mala_oracle_decode(const double* q, const double* kc, const double* vc,
+                       int B, int N, int Hq, int Hkv, int d, double tau, int Bkd,
+                       const int32_t* seqlens,
+                       double* o, double* lse, uint8_t* keep, double* margin,
+                       int32_t* kept_tiles, double* omitted, int nthreads) {
+    return decode_impl(q, kc, vc, B, N, Hq, Hkv, d, tau, Bkd, seqlens, NULL, o, lse, keep, margin, kept_tiles,
+                       omitted, nthreads);
+}
+
+/* Teacher-forced replay of the decode rule, as mala_oracle_fwd_forced:
+ * forced is [B][Hkv][nT] (0 / 1 forces the decision the update follows, 255
+ * leaves it to the rule); keep and margin record the rule's own decision and
+ * margin given that state; kept_tiles counts the decisions followed. */
+int mala_oracle_decode_forced(const double* q, const double* kc, const double* vc,
+                              int B, int N, int Hq, int Hkv, int d, double tau, int Bkd,
+                              const int32_t* seqlens, const uint8_t* forced,
+                              double* o, double* lse, uint8_t* keep, double* margin,
+                              int32_t* kept_tiles, double* omitted, int nthreads) {
+    if (!forced) return OR_EINVAL;
+    return decode_impl(q, kc, vc, B, N, Hq, Hkv, d, tau, Bkd, seqlens, forced, o, lse, keep, margin, kept_tiles,
+                       omitted, nthreads);
 }

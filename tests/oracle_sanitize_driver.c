@@ -26,6 +26,23 @@ int mala_oracle_bwd_varlen(const double*, const double*, const double*, const do
                            double*, double*, int);
 int mala_oracle_decode(const double*, const double*, const double*, int, int, int, int, int, double, int,
                        const int32_t*, double*, double*, uint8_t*, double*, int32_t*, double*, int);
+int mala_oracle_fwd_forced(const double*, const double*, const double*, int, int, int, int, int, double, int, int,
+                           const int32_t*, int, const uint8_t*, double*, double*, uint8_t*, double*, int32_t*,
+                           double*, int);
+int mala_oracle_fwd_varlen_forced(const double*, const double*, const double*, const int32_t*, const int32_t*, int,
+                                  int, int, int, double, int, int, const int32_t*, int, const uint8_t*, double*,
+                                  double*, uint8_t*, double*, int32_t*, double*, int);
+int mala_oracle_decode_forced(const double*, const double*, const double*, int, int, int, int, int, double, int,
+                              const int32_t*, const uint8_t*, double*, double*, uint8_t*, double*, int32_t*, double*,
+                              int);
+
+/* A teacher-forcing array from decisions: every third visited tile flipped,
+ * the rest left to the rule (255). */
+static uint8_t* flip_every_third(const uint8_t* keep, size_t n) {
+    uint8_t* f = (uint8_t*)malloc(n ? n : 1);
+    for (size_t i = 0; i < n; ++i) f[i] = (i % 3 == 0 && keep[i] <= 1) ? (uint8_t)(1 - keep[i]) : 255;
+    return f;
+}
 
 static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
 static double urand(void) {   /* xorshift64*, uniform in [-1, 1) */
@@ -65,6 +82,18 @@ static void fixed_case(int B, int L, int Hq, int Hkv, int d, double tau, int Bq,
     CHECK(rc == 0, "fwd rc");
     if (!sampled)
         for (size_t i = 0; i < nq; ++i) CHECK(isfinite(o[i]), "fwd o finite");
+    {   /* teacher-forced replay over the same outputs */
+        uint8_t* fz = flip_every_third(keep, nt);
+        rc = mala_oracle_fwd_forced(q, k, v, B, L, Hq, Hkv, d, tau, Bq, Bk, sampled ? blocks : NULL, sampled ? 3 : 0,
+                                    fz, o, lse, keep, margin, slots, om, 1);
+        CHECK(rc == 0, "fwd_forced rc");
+        CHECK(mala_oracle_fwd_forced(q, k, v, B, L, Hq, Hkv, d, tau, Bq, Bk, NULL, 0, NULL, o, lse, keep, margin,
+                                     slots, om, 1) != 0, "fwd_forced refuses a NULL forcing array");
+        free(fz);
+        rc = mala_oracle_fwd(q, k, v, B, L, Hq, Hkv, d, tau, Bq, Bk, sampled ? blocks : NULL, sampled ? 3 : 0,
+                             o, lse, keep, margin, slots, om, 1);   /* free-run outputs for the backward */
+        CHECK(rc == 0, "fwd rc (again)");
+    }
     double *dq = darr(nq, 0), *dk = darr(nk, 0), *dv = darr(nk, 0), *dqc = darr(nq, 0), *dkc = darr(nk, 0);
     int32_t kunits[2] = {0, B * Hkv * nKT - 1};
     rc = mala_oracle_bwd(q, k, v, o, dout, lse, B, L, Hq, Hkv, d, tau, Bq, Bk, sampled ? blocks : NULL,
@@ -108,6 +137,16 @@ static void varlen_case(int B, const int* lq, const int* lk, int Hq, int Hkv, in
     int rc = mala_oracle_fwd_varlen(q, k, v, cq, ck, B, Hq, Hkv, d, tau, Bq, Bk, NULL, 0, o, lse, keep, margin, slots,
                                     om, 1);
     CHECK(rc == 0, "fwd_varlen rc");
+    {
+        uint8_t* fz = flip_every_third(keep, nt);
+        double *o2 = darr(nq, 0), *lse2 = darr((size_t)Hq * Tq, 0), *om2 = darr((size_t)Hq * Tq, 0);
+        double* margin2 = darr(nt, 0);
+        uint8_t* keep2 = (uint8_t*)calloc(nt, 1);
+        int32_t* slots2 = (int32_t*)calloc((size_t)Hq * Tq + 1, sizeof(int32_t));
+        CHECK(mala_oracle_fwd_varlen_forced(q, k, v, cq, ck, B, Hq, Hkv, d, tau, Bq, Bk, NULL, 0, fz, o2, lse2, keep2,
+                                            margin2, slots2, om2, 1) == 0, "fwd_varlen_forced rc");
+        free(fz); free(o2); free(lse2); free(om2); free(margin2); free(keep2); free(slots2);
+    }
     double *dq = darr(nq, 0), *dk = darr(nk, 0), *dv = darr(nk, 0), *dqc = darr(nq, 0), *dkc = darr(nk, 0);
     rc = mala_oracle_bwd_varlen(q, k, v, o, dout, lse, cq, ck, B, Hq, Hkv, d, tau, Bq, Bk, NULL, 0, NULL, 0, dq, dk,
                                 dv, keep, margin, dqc, dkc, 1);
@@ -130,6 +169,16 @@ static void decode_case(int B, int N, int Hq, int Hkv, int d, double tau, int Bk
                                 kept, om, 1);
     CHECK(rc == 0, "decode rc");
     for (int i = 0; i < B * Hq; ++i) CHECK(isfinite(lse[i]), "decode lse finite");
+    {
+        uint8_t* fz = flip_every_third(keep, (size_t)B * Hkv * nT);
+        if (with_lens)   /* tiles past a sequence's cache are not visited: keep has 0 there (calloc) */
+            for (int b = 0; b < B; ++b)
+                for (int kh = 0; kh < Hkv; ++kh)
+                    for (int t = (lens[b] + Bkd - 1) / Bkd; t < nT; ++t) fz[((size_t)b * Hkv + kh) * nT + t] = 255;
+        CHECK(mala_oracle_decode_forced(q, kc, vc, B, N, Hq, Hkv, d, tau, Bkd, with_lens ? lens : NULL, fz, o, lse,
+                                        keep, margin, kept, om, 1) == 0, "decode_forced rc");
+        free(fz);
+    }
     lens[0] = N + 1;
     CHECK(mala_oracle_decode(q, kc, vc, B, N, Hq, Hkv, d, tau, Bkd, lens, o, lse, keep, margin, kept, om, 1) != 0,
           "decode refuses a cache length past N");

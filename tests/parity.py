@@ -2,10 +2,13 @@
 
 Decision parity: a GPU decision that differs from the oracle's is *exempt* when
 the oracle's log-margin lies within ln(1 + 1e-3) of zero (the ratio is within
-1e-3 relative of the threshold); once a block has an exempt mismatch, later
-mismatches in the same block (in visit order) are *cascade* mismatches, since
-the two runs no longer share the retained state.  Any other mismatch is
-non-exempt and fails the test.
+1e-3 relative of the threshold).  Once a block has an exempt mismatch, the two
+runs no longer share the retained state, so the forward and decode tests then
+rerun the oracle as a teacher-forced replay of the GPU's decisions
+(forced_decisions): every GPU decision is judged from the GPU's own state, and
+any disagreement outside the band fails.  compare_decisions (the free runs
+side by side) counts later mismatches of such a block as *cascade*; it serves
+the backward, whose tiles do not depend on each other.
 """
 from __future__ import annotations
 
@@ -61,6 +64,30 @@ def compare_decisions(gpu_keep, ora_keep, ora_margin, descending: bool = True, c
                     out["first_nonexempt"] = (int(r), int(t), float(marg[r, t]))
                 perturbed = True
     return out
+
+
+def forced_decisions(gpu_keep, forced_keep, forced_margin):
+    """Compare GPU decisions with the rule's own decisions in the oracle's
+    teacher-forced replay of them (the oracle rerun following the GPU's
+    decisions; forced_keep / forced_margin are its keep and margin).  Each GPU
+    decision is judged from the retained state the GPU itself had, so every
+    disagreement is the GPU's own: exempt when the oracle's margin there lies
+    within the band, non-exempt otherwise.  Nothing is a cascade.
+    Returns dict(total, mismatch, exempt, cascade=0, nonexempt, first_nonexempt).
+    """
+    gk = np.asarray(gpu_keep).astype(np.int64)
+    ok = np.asarray(forced_keep).astype(np.int64)
+    mg = np.asarray(forced_margin, dtype=np.float64)
+    vis = ok != 255
+    mism = vis & (gk != ok)
+    ex = mism & (np.abs(mg) <= BAND)
+    ne = mism & ~ex
+    first = None
+    if ne.any():
+        idx = tuple(int(x) for x in np.argwhere(ne)[0])
+        first = (idx, float(mg[idx]))
+    return dict(total=int(vis.sum()), mismatch=int(mism.sum()), exempt=int(ex.sum()), cascade=0,
+                nonexempt=int(ne.sum()), first_nonexempt=first, replayed=True)
 
 
 def rel_l2(x: np.ndarray, y: np.ndarray) -> float:

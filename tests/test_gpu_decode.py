@@ -6,7 +6,7 @@ import torch
 import adaptive_tile_skipping_amd as mala
 import mala_gen as G
 from oracle import oracle_decode
-from parity import bf16_tensor, compare_decisions, rel_l2_per_head, to_f64, unpack_bits
+from parity import bf16_tensor, compare_decisions, forced_decisions, rel_l2_per_head, to_f64, unpack_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,15 @@ def run_decode_case(di, tau, label="", seqlens=None):
         assert (gk[unv] == 0).all()
         gk = np.where(unv, 255, gk)
     dec = compare_decisions(gk, ref["keep"], ref["margin"], descending=True)
+    if dec["mismatch"]:
+        # teacher-forced replay of the GPU's decisions (see tests/parity.py):
+        # each is judged from the GPU's own state, and the oracle's o, lse and
+        # kept tiles are then those of the GPU's decisions
+        forced = np.where(ref["keep"] == 255, 255, gk).astype(np.uint8)
+        ref = oracle_decode(*(G.bf16_bits_to_f64(di[x]) for x in ("q", "k", "v")), tau, 64, seqlens=seqlens,
+                            forced=forced)
+        dec = dict(forced_decisions(gk, ref["keep"], ref["margin"]), free_run=dec)
+        ref["keep"] = forced                                # the decisions followed
     assert dec["nonexempt"] == 0, dec
     bad = (gk != ref["keep"]).any(-1)                     # [B, Hkv]
     Gq = Hq // Hkv
