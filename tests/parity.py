@@ -87,7 +87,7 @@ def forced_decisions(gpu_keep, forced_keep, forced_margin):
         idx = tuple(int(x) for x in np.argwhere(ne)[0])
         first = (idx, float(mg[idx]))
     return dict(total=int(vis.sum()), mismatch=int(mism.sum()), exempt=int(ex.sum()), cascade=0,
-                nonexempt=int(ne.sum()), first_nonexempt=first, replayed=True)
+                nonexempt=int(ne.sum()), first_nonexempt=first)
 
 
 def rel_l2(x: np.ndarray, y: np.ndarray) -> float:
