@@ -90,6 +90,19 @@ def test_decode_groups(Gq, Hkv, d):
         run_decode_case(di, tau, f"G={Gq}")
 
 
+@pytest.mark.parametrize("Gq,N", [(5, 200_000), (8, 70_000), (16, 40_000)])
+def test_decode_several_chunks(Gq, N):
+    """Caches long enough that the decision pass takes a group's tiles in more
+    than one chunk (2048, 1024 and 512 tiles per chunk for up to 5, up to 8 and
+    16 q heads per KV head), the retained mass and the kept-list position
+    carried from chunk to chunk; also with cache lengths that end inside a
+    later chunk."""
+    di = G.decode_inputs(1300 + Gq, 2, N, Gq, 1, 128)
+    for tau in (0.25, 1.0):
+        run_decode_case(di, tau, f"chunks G={Gq} N={N}")
+    run_decode_case(di, 1.0, f"chunks G={Gq} N={N} lens", seqlens=[N - 5, N // 3 + 7])
+
+
 @pytest.mark.parametrize("tau", [1.0, 0.0])
 def test_decode_128k(tau):
     di = G.workload_inputs("decode_128k")
