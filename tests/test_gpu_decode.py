@@ -103,6 +103,15 @@ def test_decode_several_chunks(Gq, N):
     run_decode_case(di, 1.0, f"chunks G={Gq} N={N} lens", seqlens=[N - 5, N // 3 + 7])
 
 
+def test_decode_many_groups():
+    """More (sequence, KV head) groups than one workgroup scan covers (320 >
+    256): the P.V pass finds its starting group by scanning the kept counts
+    in rounds of 256."""
+    di = G.decode_inputs(1350, 40, 700, 16, 8, 64)
+    for tau in (0.0, 0.25, 1.0):
+        run_decode_case(di, tau, "many groups")
+
+
 @pytest.mark.parametrize("tau", [1.0, 0.0])
 def test_decode_128k(tau):
     di = G.workload_inputs("decode_128k")
