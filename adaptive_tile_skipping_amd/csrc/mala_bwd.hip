@@ -391,8 +391,13 @@ __device__ __forceinline__ int kswz(int r) {
     return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) % QCH;
 }
 
-template <int D, int BQ, bool VARLEN>
+template <int D, int BQ, bool VARLEN, bool WIDE>
 __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
+    // WIDE (tau = 0 only): a workgroup owns two key tiles, wave w keys 32 w ..
+    // 32 w + 31 of them, and takes the block's query halves one after the
+    // other, so each streamed Q / dO block serves twice the keys.
+    constexpr int KT_PER = WIDE ? 2 : 1;       // key tiles per workgroup
+    constexpr int NHALF = WIDE ? 2 : 1;        // query halves per wave and step
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
     constexpr int NQS = BQ / 32;         // query subtiles of the block
@@ -417,13 +422,14 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int w = tid >> 6;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
-    const int kw = w & 1;
-    const int qh = w >> 1;
+    const int kw = WIDE ? w : (w & 1);
+    const int qh0 = WIDE ? 0 : (w >> 1);
 
+    const int nKTu = (p.nKT + KT_PER - 1) / KT_PER;   // units per (batch, KV head)
     const int u = xcd_unit(blockIdx.x, p.chunk);
-    if (u >= p.nunits) return;
-    const int kt = u % p.nKT;               // key tiles in increasing order: longest first
-    const int bk = u / p.nKT;
+    if (u >= p.B * p.Hkv * nKTu) return;
+    const int kt = (u % nKTu) * KT_PER;     // first key tile, in increasing order: longest first
+    const int bk = u / nKTu;
     const int b = bk / p.Hkv;
     const int kh = bk % p.Hkv;
     const SeqView sv = seq_view<BQ, VARLEN>(p, b);
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     // query blocks that can see the tile: from the one holding row j0 - off
     const int qb_lo = (j0 - off > 0 ? j0 - off : 0) / BQ;
     const int qb_hi = (L + BQ - 1) / BQ - 1;
-    const bool dense = p.log2_tau == kNegInf;   // tau = 0: every legal step is kept
+    const bool dense = WIDE || p.log2_tau == kNegInf;   // tau = 0: every legal step is kept
     const uint32_t* trow = p.tbits + ((int64_t)(b * p.Hkv + kh) * p.nKT + kt) * p.nwT;
 
     // Per-lane byte offsets of this lane's 16-byte chunks inside a Q / dO block
@@ -536,6 +542,9 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         const uint16_t* sQb = sQD + buf * 2 * BLK;
         const uint16_t* sGb = sQb + BLK;
         const int64_t bh = (int64_t)b * p.Hq + h;
+#pragma unroll
+        for (int half = 0; half < NHALF; ++half) {
+        const int qh = WIDE ? half : qh0;
         // ---- S = Q K^T and dP = dO V^T for the wave's query subtiles x 32 keys
         f32x16 dp[WSUB];
 #pragma unroll
@@ -585,16 +594,25 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                 dk[dt] = mfma32x32x16(da[ks], tread(sQb, qrow0, dt), dk[dt]);
             }
         }
-        // ---- statistics of the backward's own decisions
-        if (tid == 0) {
-            if (p.kept_tiles) atomicAdd(p.kept_tiles + bh * p.nQB + qb, 1);
-            if (p.bits) atomicOr(p.bits + (bh * p.nQB + qb) * p.nwords + (kt >> 5), 1u << (kt & 31));
+        __builtin_amdgcn_sched_barrier(0);
         }
-        if (p.kept_slots && tid < BQ) {
-            const int i = qb * BQ + tid;
-            const int last = off + i - j0;
-            if (i < L && last >= 0)
-                atomicAdd(p.kept_slots + sv.lse0 + h * sv.lse_hs + i, (last < BK - 1 ? last : BK - 1) + 1);
+        // ---- statistics of the backward's own decisions: each key tile of the
+        // workgroup that the step visits (for a second tile, when it exists and
+        // the block holds a row that sees it)
+#pragma unroll
+        for (int tt = 0; tt < KT_PER; ++tt) {
+            const int ktt = kt + tt, jt = j0 + BK * tt;
+            if (tt > 0 && (jt >= Lk || qb < (jt - off > 0 ? jt - off : 0) / BQ)) continue;
+            if (tid == 0) {
+                if (p.kept_tiles) atomicAdd(p.kept_tiles + bh * p.nQB + qb, 1);
+                if (p.bits) atomicOr(p.bits + (bh * p.nQB + qb) * p.nwords + (ktt >> 5), 1u << (ktt & 31));
+            }
+            if (p.kept_slots && tid < BQ) {
+                const int i = qb * BQ + tid;
+                const int last = off + i - jt;
+                if (i < L && last >= 0)
+                    atomicAdd(p.kept_slots + sv.lse0 + h * sv.lse_hs + i, (last < BK - 1 ? last : BK - 1) + 1);
+            }
         }
         __syncthreads();                         // every wave is done with buffer `buf`
         const int n2 = (nxt >= 0) ? cc.next(lane) : -1;
@@ -605,10 +623,11 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         nxt = n2;
     }
 
-    // ---- epilogue: combine the two query halves, write dK (scaled) and dV
+    // ---- epilogue: combine the two query halves (WIDE: each wave holds all
+    // of its keys' sums), write dK (scaled) and dV
     __syncthreads();
     float* red = reinterpret_cast<float*>(sU);
-    if (qh == 1) {
+    if (!WIDE && qh0 == 1) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -618,7 +637,8 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
             }
     }
     __syncthreads();
-    if (qh == 0) {
+    if (WIDE || qh0 == 0) {
+        if (!WIDE)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -863,9 +883,17 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
         const int grid_s = (p.nunits_scan + per_s - 1) / per_s * per_s;
         hipLaunchKernelGGL((mala_bwd_scan<D, BQ, VARLEN>), dim3(grid_s), dim3(256), 0, s, p);
     }
+    // dK / dV: at tau = 0 two key tiles per workgroup (every step is kept, so
+    // both tiles use each streamed block); otherwise one, over its kept steps
     const int per = 8 * p.chunk;
-    const int grid = (p.nunits + per - 1) / per * per;
-    hipLaunchKernelGGL((mala_bwd_kernel<D, BQ, VARLEN>), dim3(grid), dim3(256), 0, s, p);
+    if (p.log2_tau == -INFINITY) {
+        const int nu = p.B * p.Hkv * ((p.nKT + 1) / 2);
+        const int grid = (nu + per - 1) / per * per;
+        hipLaunchKernelGGL((mala_bwd_kernel<D, BQ, VARLEN, true>), dim3(grid), dim3(256), 0, s, p);
+    } else {
+        const int grid = (p.nunits + per - 1) / per * per;
+        hipLaunchKernelGGL((mala_bwd_kernel<D, BQ, VARLEN, false>), dim3(grid), dim3(256), 0, s, p);
+    }
     const int per_q = 8 * p.chunk_dq;
     const int grid_q = (p.nunits_dq + per_q - 1) / per_q * per_q;
     hipLaunchKernelGGL((mala_bwd_dq<D, BQ, VARLEN>), dim3(grid_q), dim3(BQ / 32 * 64), 0, s, p);

@@ -217,9 +217,10 @@ def test_bwd_ragged_gqa(L, tau):
 
 
 @pytest.mark.parametrize("L", [64, 200])
-def test_bwd_d64(L):
+@pytest.mark.parametrize("tau", [0.0, 1.0])
+def test_bwd_d64(L, tau):
     inp = G.attn_inputs(800 + L, 1, L, 4, 2, 64, 0.2)
-    run_bwd_case(inp, 1.0, 64, 64, label=f"d64 L={L}")
+    run_bwd_case(inp, tau, 64, 64, label=f"d64 L={L}")
 
 
 def test_bwd_gqa_8k():
@@ -235,14 +236,17 @@ def test_bwd_gqa_8k():
     print(json.dumps(rec), flush=True)
 
 
-def test_bwd_train_128k_sampled():
-    """Full-size launch; dq checked on sampled query blocks, dk/dv on the last key tiles."""
+@pytest.mark.parametrize("tau", [1.0, 0.0])
+def test_bwd_train_128k_sampled(tau):
+    """Full-size launch; dq checked on sampled query blocks, dk/dv on the last key
+    tiles (at tau = 0 these are both tiles of one dK/dV workgroup and the first
+    of the next)."""
     w = G.WORKLOADS["train_128k"]
     inp = G.workload_inputs("train_128k")
     nQB, nKT = 131072 // 128, 131072 // 64
     qblocks = [h * nQB + qb for h, qb in ((0, nQB - 1), (2, nQB - 1), (4, nQB - 2), (1, 700))]
     ktiles = [nKT - 1, nKT - 2, nKT - 3]
-    print(run_bwd_case(inp, 1.0, w["Bq"], w["Bk"], qblocks=qblocks, ktiles=ktiles, label="train_128k sampled"))
+    print(run_bwd_case(inp, tau, w["Bq"], w["Bk"], qblocks=qblocks, ktiles=ktiles, label="train_128k sampled"))
 
 
 def test_bwd_workspace_reuse_and_determinism_of_decisions():

@@ -288,10 +288,11 @@ def test_bwd_varlen_mix(tau):
 
 
 @pytest.mark.parametrize("off", [1, 63, 100, 129])
-def test_bwd_varlen_offsets(off):
+@pytest.mark.parametrize("tau", [1.0, 0.0])
+def test_bwd_varlen_offsets(off, tau):
     inp = G.varlen_inputs(560 + off, [200, 129, 0], [200 + off, 129 + off, 50], 6, 2, 128, 0.1,
                           diffuse_kv_heads=(1,))
-    run_bwd_varlen_case(inp, 1.0, 128, 64, label=f"off={off}")
+    run_bwd_varlen_case(inp, tau, 128, 64, label=f"off={off}")
 
 
 def test_bwd_varlen_d64():
