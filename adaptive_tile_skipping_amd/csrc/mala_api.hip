@@ -285,7 +285,6 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     p.dv_sb = dv.sb; p.dv_sl = dv.sl; p.dv_sh = dv.sh;
     p.B = B; p.L = L; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.nQB = (L + Bq - 1) / Bq; p.nKT = (L + Bk - 1) / Bk;
-    p.nunits = B * Hkv * p.nKT;
     p.chunk = 4;
     p.nwT = (p.G * p.nQB + 31) / 32;
     p.nslab = (L + 255) / 256;
@@ -293,6 +292,7 @@ mala_status mala_bwd(mala_t4 q, mala_t4 k, mala_t4 v, mala_t4 o, mala_t4 dout, c
     p.chunk_scan = pick_chunk(Hq, Hkv);
     p.nunits_dq = B * Hq * p.nQB;
     p.chunk_dq = pick_chunk(Hq, Hkv);
+    p.ncu = device_cus();
     p.scale = (float)(1.0 / sqrt((double)d));
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     p.log2_tau = log2_tau(tau);
@@ -367,13 +367,13 @@ mala_status mala_bwd_varlen(mala_t3 q, mala_t3 k, mala_t3 v, mala_t3 o, mala_t3 
     p.nwT = (p.G * p.nQB + 31) / 32;
     p.tbits = (uint32_t*)w; w += align256((size_t)B * Hkv * p.nKT * p.nwT * sizeof(uint32_t));
     p.qbits = (uint32_t*)w;
-    p.nunits = B * Hkv * p.nKT;
     p.chunk = 4;
     p.nslab = (p.nQB * Bq + 255) / 256;
     p.nunits_scan = p.nslab * B * Hq;
     p.chunk_scan = pick_chunk(Hq, Hkv);
     p.nunits_dq = B * Hq * p.nQB;
     p.chunk_dq = pick_chunk(Hq, Hkv);
+    p.ncu = device_cus();
     p.scale = (float)(1.0 / sqrt((double)d));
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
     p.log2_tau = log2_tau(tau);

@@ -425,11 +425,29 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int kw = WIDE ? w : (w & 1);
     const int qh0 = WIDE ? 0 : (w >> 1);
 
+    // Work units: KT_PER adjacent key tiles of one (batch, KV head); `chunk`
+    // consecutive units run on one XCD.
     const int nKTu = (p.nKT + KT_PER - 1) / KT_PER;   // units per (batch, KV head)
+    const int nbk = p.B * p.Hkv;
     const int u = xcd_unit(blockIdx.x, p.chunk);
-    if (u >= p.B * p.Hkv * nKTu) return;
-    const int kt = (u % nKTu) * KT_PER;     // first key tile, in increasing order: longest first
-    const int bk = u / nKTu;
+    int bk, ku;
+    if (p.log2_tau == kNegInf) {
+        // tau = 0: a unit's length is the number of query blocks that see it.
+        // Chunks of adjacent units go in increasing key order across every
+        // (batch, KV head), so the longest units start first.
+        const int ch = u / p.chunk;
+        if (ch >= (nKTu + p.chunk - 1) / p.chunk * nbk) return;
+        bk = ch % nbk;
+        ku = (ch / nbk) * p.chunk + u % p.chunk;
+    } else {
+        // tau > 0: (batch, KV head) major, key units in increasing order, so the
+        // units running together mostly share one KV head's Q / dO blocks in L2
+        if (u >= nbk * nKTu) return;
+        bk = u / nKTu;
+        ku = u % nKTu;
+    }
+    if (ku >= nKTu) return;
+    const int kt = ku * KT_PER;             // first key tile of the unit
     const int b = bk / p.Hkv;
     const int kh = bk % p.Hkv;
     const SeqView sv = seq_view<BQ, VARLEN>(p, b);
@@ -884,16 +902,19 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
         hipLaunchKernelGGL((mala_bwd_scan<D, BQ, VARLEN>), dim3(grid_s), dim3(256), 0, s, p);
     }
     // dK / dV: at tau = 0 two key tiles per workgroup (every step is kept, so
-    // both tiles use each streamed block); otherwise one, over its kept steps
+    // both tiles use each streamed block) when that still leaves a workgroup
+    // for every CU; otherwise one, over its kept steps.  The grid covers the
+    // units padded to whole chunks (the tau = 0 order; see the kernel).
     const int per = 8 * p.chunk;
-    if (p.log2_tau == -INFINITY) {
-        const int nu = p.B * p.Hkv * ((p.nKT + 1) / 2);
-        const int grid = (nu + per - 1) / per * per;
+    const int nbk = p.B * p.Hkv;
+    const bool wide = p.log2_tau == -INFINITY && nbk * ((p.nKT + 1) / 2) >= p.ncu;
+    const int nKTu = wide ? (p.nKT + 1) / 2 : p.nKT;
+    const int nu = (nKTu + p.chunk - 1) / p.chunk * p.chunk * nbk;
+    const int grid = (nu + per - 1) / per * per;
+    if (wide)
         hipLaunchKernelGGL((mala_bwd_kernel<D, BQ, VARLEN, true>), dim3(grid), dim3(256), 0, s, p);
-    } else {
-        const int grid = (p.nunits + per - 1) / per * per;
+    else
         hipLaunchKernelGGL((mala_bwd_kernel<D, BQ, VARLEN, false>), dim3(grid), dim3(256), 0, s, p);
-    }
     const int per_q = 8 * p.chunk_dq;
     const int grid_q = (p.nunits_dq + per_q - 1) / per_q * per_q;
     hipLaunchKernelGGL((mala_bwd_dq<D, BQ, VARLEN>), dim3(grid_q), dim3(BQ / 32 * 64), 0, s, p);

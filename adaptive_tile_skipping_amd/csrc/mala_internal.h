@@ -51,10 +51,11 @@ struct BwdParams {
     int Lpad;           // nQB * Bq
     int64_t q_sb, q_sl, q_sh, k_sb, k_sl, k_sh, v_sb, v_sl, v_sh, o_sb, o_sl, o_sh;
     int64_t do_sb, do_sl, do_sh, dq_sb, dq_sl, dq_sh, dk_sb, dk_sl, dk_sh, dv_sb, dv_sl, dv_sh;
-    int B, L, Hq, Hkv, G, nQB, nKT, nunits, chunk;
+    int B, L, Hq, Hkv, G, nQB, nKT, chunk;       // chunk: adjacent dK/dV units per XCD
     int nwT;            // ceil(G * nQB / 32)
     int nslab, nunits_scan, chunk_scan;   // scan kernel: 256-query slabs, work units
     int nunits_dq, chunk_dq;              // dQ pass: (batch, q head, query block) units
+    int ncu;            // compute units of the device
     float scale;        // 1 / sqrt(d)
     float scale_log2;   // log2(e) / sqrt(d)
     float log2_tau;
