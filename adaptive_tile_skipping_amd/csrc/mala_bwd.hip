@@ -36,7 +36,12 @@
 //                   out with one key per lane and the block's queries in
 //                   registers, so P^T and dS^T feed the dV and dK contractions
 //                   straight from registers, with dO^T and Q^T from transposing
-//                   LDS reads; dK/dV accumulate in registers over steps.
+//                   LDS reads; dK/dV accumulate in registers over steps.  At
+//                   tau = 0, when there are enough units to fill the device, a
+//                   workgroup owns two adjacent key tiles instead: wave w holds
+//                   keys 32 w .. of the 128 and takes the block's two query
+//                   halves in turn, so each streamed block serves twice the
+//                   keys; those units start longest first.
 //   mala_bwd_dq     the dQ pass: one workgroup per (batch, q head, query
 //                   block), waves of 32 queries, visiting the block's kept key
 //                   tiles (all legal tiles when tau = 0) with K and V tiles
