@@ -402,11 +402,13 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     // 32 w + 31 of them, and takes the block's query halves one after the
     // other, so each streamed Q / dO block serves twice the keys.
     constexpr int KT_PER = WIDE ? 2 : 1;       // key tiles per workgroup
-    constexpr int NHALF = WIDE ? 2 : 1;        // query halves per wave and step
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
     constexpr int NQS = BQ / 32;         // query subtiles of the block
-    constexpr int WSUB = NQS / 2;        // query subtiles per wave
+    constexpr int WSUB = NQS / 2;        // query subtiles per wave (one key tile per unit)
+    constexpr int NSUB = WIDE ? NQS : WSUB;   // query subtiles a wave visits per step
+    constexpr int GS = WIDE ? 1 : WSUB;       // query subtiles per phase group
+    constexpr int NGRP = NSUB / GS;
     constexpr int QCH = D / 8;           // 16-byte chunks per row
     constexpr int QSLOTS = BQ * QCH;     // 16-byte chunks per block (each of Q, dO)
     constexpr int QINST = QSLOTS / 256;  // global->LDS copies per lane per block and tensor
@@ -429,6 +431,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     const int hi = lane >> 5;
     const int kw = WIDE ? w : (w & 1);
     const int qh0 = WIDE ? 0 : (w >> 1);
+    const int SUB0 = WIDE ? 0 : WSUB * qh0;   // the wave's first query subtile
 
     // Work units: KT_PER adjacent key tiles of one (batch, KV head); `chunk`
     // consecutive units run on one XCD.
@@ -557,7 +560,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         __syncthreads();
     }
 
-    f32x16 sc[WSUB];
     for (int s = 0; cur >= 0; ++s) {
         const int buf = s & 1;
         const int h = kh * G + cur / p.nQB;
@@ -565,59 +567,108 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         const uint16_t* sQb = sQD + buf * 2 * BLK;
         const uint16_t* sGb = sQb + BLK;
         const int64_t bh = (int64_t)b * p.Hq + h;
+        // every row of the block sees every key of the unit: no causal or
+        // length mask on this step
+        const bool full = (j0 + BK * KT_PER - 1 <= off + qb * BQ) && (qb * BQ + BQ <= L);
+        // The wave's query subtiles go in groups of GS (fewer live registers
+        // than the whole half at once).  The scheduling groups below keep the
+        // LDS operand reads several MFMAs ahead of their use.
 #pragma unroll
-        for (int half = 0; half < NHALF; ++half) {
-        const int qh = WIDE ? half : qh0;
-        // ---- S = Q K^T and dP = dO V^T for the wave's query subtiles x 32 keys
-        f32x16 dp[WSUB];
+        for (int g = 0; g < NGRP; ++g) {
+            const int sub0 = SUB0 + GS * g;        // first query subtile of the group
+            // ---- S = Q K^T and dP = dO V^T for the group's query subtiles x 32 keys
+            f32x16 sc[GS], dp[GS];
 #pragma unroll
-        for (int t = 0; t < WSUB; ++t) {
-            const int row = 32 * (WSUB * qh + t) + l32;
-            sc[t] = f32x16{};
-            dp[t] = f32x16{};
+            for (int t = 0; t < GS; ++t) {
+                const int row = 32 * (sub0 + t) + l32;
+                sc[t] = f32x16{};
+                dp[t] = f32x16{};
 #pragma unroll
-            for (int st = 0; st < KSTEPS; ++st) {
-                const int pc = (2 * st + hi) ^ kswz<QCH>(row);
-                const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
-                const bf16x8 g = *(const bf16x8*)(&sGb[row * D + 8 * pc]);
-                sc[t] = mfma32x32x16(a, kf[st], sc[t]);
-                dp[t] = mfma32x32x16(g, vf[st], dp[t]);
-            }
-        }
-        // ---- P, dS; A operands (key rows x 8 permuted query positions) for dV, dK
-        bf16x8 pa[2 * WSUB], da[2 * WSUB];
-#pragma unroll
-        for (int t = 0; t < WSUB; ++t) {
-            const int qsub = WSUB * qh + t;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int ql = 32 * qsub + 8 * g4 + 4 * hi;
-                const f32x4 lv = *(const f32x4*)(&sRow[buf][0][ql]);
-                const f32x4 dd = *(const f32x4*)(&sRow[buf][1][ql]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * g4 + e;
-                    const int ig = qb * BQ + ql + e;
-                    const bool legal = (jme <= off + ig) && (ig < L);
-                    const float pr = legal ? fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e])) : 0.f;
-                    const float ds = pr * (dp[t][r] - dd[e]);
-                    pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
-                    da[2 * t + (r >> 3)][r & 7] = to_bf16(ds);
+                for (int st = 0; st < KSTEPS; ++st) {
+                    const int pc = (2 * st + hi) ^ kswz<QCH>(row);
+                    const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
+                    const bf16x8 gg = *(const bf16x8*)(&sGb[row * D + 8 * pc]);
+                    sc[t] = mfma32x32x16(a, kf[st], sc[t]);
+                    dp[t] = mfma32x32x16(gg, vf[st], dp[t]);
                 }
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- dV += P^T dO, dK += dS^T Q  (B operands by transposing reads)
+            {   // one operand read per MFMA, PRE MFMAs ahead
+                constexpr int NM = 2 * GS * KSTEPS, PRE = NM < 6 ? NM : 6;
+                __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
-        for (int ks = 0; ks < 2 * WSUB; ++ks) {
-            const int qrow0 = (BQ / 2) * qh + 16 * ks;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                dv[dt] = mfma32x32x16(pa[ks], tread(sGb, qrow0, dt), dv[dt]);
-                dk[dt] = mfma32x32x16(da[ks], tread(sQb, qrow0, dt), dk[dt]);
+                for (int i = 0; i < NM - PRE; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
             }
-        }
-        __builtin_amdgcn_sched_barrier(0);
+            // ---- P, dS; A operands (key rows x 8 permuted query positions) for dV, dK
+            bf16x8 pa[2 * GS], da[2 * GS];
+#pragma unroll
+            for (int t = 0; t < GS; ++t) {
+                const int qsub = sub0 + t;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ql = 32 * qsub + 8 * g4 + 4 * hi;
+                    const f32x4 lv = *(const f32x4*)(&sRow[buf][0][ql]);
+                    const f32x4 dd = *(const f32x4*)(&sRow[buf][1][ql]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * g4 + e;
+                        const float pr = fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e]));
+                        const float ds = pr * (dp[t][r] - dd[e]);
+                        pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
+                        da[2 * t + (r >> 3)][r & 7] = to_bf16(ds);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (!full) {
+                // a diagonal or ragged step: P and dS of the pairs that the
+                // causal order or the sequence end rules out become 0
+#pragma unroll
+                for (int t = 0; t < GS; ++t)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        u32x4 pw = __builtin_bit_cast(u32x4, pa[2 * t + hf]);
+                        u32x4 dw = __builtin_bit_cast(u32x4, da[2 * t + hf]);
+#pragma unroll
+                        for (int k2 = 0; k2 < 4; ++k2) {
+                            uint32_t m = 0;
+#pragma unroll
+                            for (int hh = 0; hh < 2; ++hh) {
+                                const int r = 8 * hf + 2 * k2 + hh;
+                                const int ig = qb * BQ + 32 * (sub0 + t) + 8 * (r >> 2) + 4 * hi + (r & 3);
+                                if ((jme <= off + ig) && (ig < L)) m |= 0xFFFFu << (16 * hh);
+                            }
+                            pw[k2] &= m;
+                            dw[k2] &= m;
+                        }
+                        pa[2 * t + hf] = __builtin_bit_cast(bf16x8, pw);
+                        da[2 * t + hf] = __builtin_bit_cast(bf16x8, dw);
+                    }
+            }
+            // ---- dV += P^T dO, dK += dS^T Q  (B operands by transposing reads)
+#pragma unroll
+            for (int ks = 0; ks < 2 * GS; ++ks) {
+                const int qrow0 = 32 * sub0 + 16 * ks;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    dv[dt] = mfma32x32x16(pa[ks], tread(sGb, qrow0, dt), dv[dt]);
+                    dk[dt] = mfma32x32x16(da[ks], tread(sQb, qrow0, dt), dk[dt]);
+                }
+            }
+            {   // two transposing reads per MFMA, PRE MFMAs ahead
+                constexpr int NM = 2 * GS * 2 * DT, PRE = 4;
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * PRE, 0);
+#pragma unroll
+                for (int i = 0; i < NM - PRE; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // ---- statistics of the backward's own decisions: each key tile of the
         // workgroup that the step visits (for a second tile, when it exists and
