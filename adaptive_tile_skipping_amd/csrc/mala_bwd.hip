@@ -36,12 +36,15 @@
 //                   out with one key per lane and the block's queries in
 //                   registers, so P^T and dS^T feed the dV and dK contractions
 //                   straight from registers, with dO^T and Q^T from transposing
-//                   LDS reads; dK/dV accumulate in registers over steps.  At
-//                   tau = 0, when there are enough units to fill the device, a
-//                   workgroup owns two adjacent key tiles instead: wave w holds
-//                   keys 32 w .. of the 128 and takes the block's two query
-//                   halves in turn, so each streamed block serves twice the
-//                   keys; those units start longest first.
+//                   LDS reads; dK/dV accumulate in registers over steps.  A
+//                   wave takes its 32-query subtiles one at a time through
+//                   scores, softmax and contractions.  At tau = 0, when there
+//                   are enough units to fill the device, a workgroup owns two
+//                   adjacent key tiles instead: wave w holds keys 32 w .. of
+//                   the 128 and takes all four query subtiles of the block, so
+//                   each streamed block serves twice the keys; those units
+//                   start longest first.  The causal mask is applied only on
+//                   steps that cross the diagonal or the sequence end.
 //   mala_bwd_dq     the dQ pass: one workgroup per (batch, q head, query
 //                   block), waves of 32 queries, visiting the block's kept key
 //                   tiles (all legal tiles when tau = 0) with K and V tiles
@@ -399,16 +402,14 @@ __device__ __forceinline__ int kswz(int r) {
 template <int D, int BQ, bool VARLEN, bool WIDE>
 __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     // WIDE (tau = 0 only): a workgroup owns two key tiles, wave w keys 32 w ..
-    // 32 w + 31 of them, and takes the block's query halves one after the
-    // other, so each streamed Q / dO block serves twice the keys.
+    // 32 w + 31 of them, and takes every query subtile of the block, so each
+    // streamed Q / dO block serves twice the keys.
     constexpr int KT_PER = WIDE ? 2 : 1;       // key tiles per workgroup
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
     constexpr int NQS = BQ / 32;         // query subtiles of the block
     constexpr int WSUB = NQS / 2;        // query subtiles per wave (one key tile per unit)
     constexpr int NSUB = WIDE ? NQS : WSUB;   // query subtiles a wave visits per step
-    constexpr int GS = WIDE ? 1 : WSUB;       // query subtiles per phase group
-    constexpr int NGRP = NSUB / GS;
     constexpr int QCH = D / 8;           // 16-byte chunks per row
     constexpr int QSLOTS = BQ * QCH;     // 16-byte chunks per block (each of Q, dO)
     constexpr int QINST = QSLOTS / 256;  // global->LDS copies per lane per block and tensor
@@ -570,30 +571,28 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         // every row of the block sees every key of the unit: no causal or
         // length mask on this step
         const bool full = (j0 + BK * KT_PER - 1 <= off + qb * BQ) && (qb * BQ + BQ <= L);
-        // The wave's query subtiles go in groups of GS (fewer live registers
-        // than the whole half at once).  The scheduling groups below keep the
-        // LDS operand reads several MFMAs ahead of their use.
+        // The wave's 32-query subtiles go one at a time through scores,
+        // softmax and the dV / dK contractions (a whole half at once needs
+        // more registers than the allocator handles well).  The scheduling
+        // groups keep the LDS operand reads several MFMAs ahead of their use.
 #pragma unroll
-        for (int g = 0; g < NGRP; ++g) {
-            const int sub0 = SUB0 + GS * g;        // first query subtile of the group
-            // ---- S = Q K^T and dP = dO V^T for the group's query subtiles x 32 keys
-            f32x16 sc[GS], dp[GS];
-#pragma unroll
-            for (int t = 0; t < GS; ++t) {
-                const int row = 32 * (sub0 + t) + l32;
-                sc[t] = f32x16{};
-                dp[t] = f32x16{};
+        for (int g = 0; g < NSUB; ++g) {
+            const int qs = SUB0 + g;               // query subtile
+            // ---- S = Q K^T and dP = dO V^T for the subtile x the wave's 32 keys
+            f32x16 sc = f32x16{}, dp = f32x16{};
+            {
+                const int row = 32 * qs + l32;
 #pragma unroll
                 for (int st = 0; st < KSTEPS; ++st) {
                     const int pc = (2 * st + hi) ^ kswz<QCH>(row);
                     const bf16x8 a = *(const bf16x8*)(&sQb[row * D + 8 * pc]);
                     const bf16x8 gg = *(const bf16x8*)(&sGb[row * D + 8 * pc]);
-                    sc[t] = mfma32x32x16(a, kf[st], sc[t]);
-                    dp[t] = mfma32x32x16(gg, vf[st], dp[t]);
+                    sc = mfma32x32x16(a, kf[st], sc);
+                    dp = mfma32x32x16(gg, vf[st], dp);
                 }
             }
             {   // one operand read per MFMA, PRE MFMAs ahead
-                constexpr int NM = 2 * GS * KSTEPS, PRE = NM < 6 ? NM : 6;
+                constexpr int NM = 2 * KSTEPS, PRE = NM < 6 ? NM : 6;
                 __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
                 for (int i = 0; i < NM - PRE; ++i) {
@@ -603,23 +602,19 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                 __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
             }
             // ---- P, dS; A operands (key rows x 8 permuted query positions) for dV, dK
-            bf16x8 pa[2 * GS], da[2 * GS];
+            bf16x8 pa[2], da[2];
 #pragma unroll
-            for (int t = 0; t < GS; ++t) {
-                const int qsub = sub0 + t;
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int ql = 32 * qs + 8 * g4 + 4 * hi;
+                const f32x4 lv = *(const f32x4*)(&sRow[buf][0][ql]);
+                const f32x4 dd = *(const f32x4*)(&sRow[buf][1][ql]);
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int ql = 32 * qsub + 8 * g4 + 4 * hi;
-                    const f32x4 lv = *(const f32x4*)(&sRow[buf][0][ql]);
-                    const f32x4 dd = *(const f32x4*)(&sRow[buf][1][ql]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * g4 + e;
-                        const float pr = fast_exp2(__builtin_fmaf(sc[t][r], c2, -lv[e]));
-                        const float ds = pr * (dp[t][r] - dd[e]);
-                        pa[2 * t + (r >> 3)][r & 7] = to_bf16(pr);
-                        da[2 * t + (r >> 3)][r & 7] = to_bf16(ds);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * g4 + e;
+                    const float pr = fast_exp2(__builtin_fmaf(sc[r], c2, -lv[e]));
+                    const float ds = pr * (dp[r] - dd[e]);
+                    pa[r >> 3][r & 7] = to_bf16(pr);
+                    da[r >> 3][r & 7] = to_bf16(ds);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -627,31 +622,29 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                 // a diagonal or ragged step: P and dS of the pairs that the
                 // causal order or the sequence end rules out become 0
 #pragma unroll
-                for (int t = 0; t < GS; ++t)
+                for (int hf = 0; hf < 2; ++hf) {
+                    u32x4 pw = __builtin_bit_cast(u32x4, pa[hf]);
+                    u32x4 dw = __builtin_bit_cast(u32x4, da[hf]);
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        u32x4 pw = __builtin_bit_cast(u32x4, pa[2 * t + hf]);
-                        u32x4 dw = __builtin_bit_cast(u32x4, da[2 * t + hf]);
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        uint32_t m = 0;
 #pragma unroll
-                        for (int k2 = 0; k2 < 4; ++k2) {
-                            uint32_t m = 0;
-#pragma unroll
-                            for (int hh = 0; hh < 2; ++hh) {
-                                const int r = 8 * hf + 2 * k2 + hh;
-                                const int ig = qb * BQ + 32 * (sub0 + t) + 8 * (r >> 2) + 4 * hi + (r & 3);
-                                if ((jme <= off + ig) && (ig < L)) m |= 0xFFFFu << (16 * hh);
-                            }
-                            pw[k2] &= m;
-                            dw[k2] &= m;
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int r = 8 * hf + 2 * k2 + hh;
+                            const int ig = qb * BQ + 32 * qs + 8 * (r >> 2) + 4 * hi + (r & 3);
+                            if ((jme <= off + ig) && (ig < L)) m |= 0xFFFFu << (16 * hh);
                         }
-                        pa[2 * t + hf] = __builtin_bit_cast(bf16x8, pw);
-                        da[2 * t + hf] = __builtin_bit_cast(bf16x8, dw);
+                        pw[k2] &= m;
+                        dw[k2] &= m;
                     }
+                    pa[hf] = __builtin_bit_cast(bf16x8, pw);
+                    da[hf] = __builtin_bit_cast(bf16x8, dw);
+                }
             }
             // ---- dV += P^T dO, dK += dS^T Q  (B operands by transposing reads)
 #pragma unroll
-            for (int ks = 0; ks < 2 * GS; ++ks) {
-                const int qrow0 = 32 * sub0 + 16 * ks;
+            for (int ks = 0; ks < 2; ++ks) {
+                const int qrow0 = 32 * qs + 16 * ks;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     dv[dt] = mfma32x32x16(pa[ks], tread(sGb, qrow0, dt), dv[dt]);
@@ -659,7 +652,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
                 }
             }
             {   // two transposing reads per MFMA, PRE MFMAs ahead
-                constexpr int NM = 2 * GS * 2 * DT, PRE = 4;
+                constexpr int NM = 2 * 2 * DT, PRE = 4;
                 __builtin_amdgcn_sched_group_barrier(0x100, 2 * PRE, 0);
 #pragma unroll
                 for (int i = 0; i < NM - PRE; ++i) {
@@ -874,50 +867,93 @@ void mala_bwd_dq(const BwdParams p) {
         const int buf = s & 1;
         const uint16_t* kb = sK[buf];
         const uint16_t* vb = sV[buf];
-        // S^T = K Q^T and dP^T = V dO^T (one key per register row, this lane's query)
-        f32x16 sc[2], dp[2];
+        const int jo = tcur * BK - off;          // key j0 relative to the row offset: j <= off + i
+        // every row of the block sees every key of the tile: no mask
+        const bool full = (jo + BK - 1 <= qb * BQ) && (qb * BQ + BQ <= L);
+        // Each half of the tile (32 keys) goes through scores, dS and its part
+        // of the dQ contraction in turn; the scheduling groups keep the LDS
+        // operand reads several MFMAs ahead of their use.
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
+            // S^T = K Q^T and dP^T = V dO^T (one key per register row, this lane's query)
+            f32x16 sc = f32x16{}, dp = f32x16{};
             const int row = 32 * sub + l32;
-            sc[sub] = f32x16{};
-            dp[sub] = f32x16{};
 #pragma unroll
             for (int st = 0; st < KSTEPS; ++st) {
                 const bf16x8 a = *(const bf16x8*)(&kb[row * D + 8 * ((2 * st + hi) ^ kswz<QCH>(row))]);
                 const bf16x8 vv = *(const bf16x8*)(&vb[row * D + 8 * ((2 * st + hi) ^ (row % QCH))]);
-                sc[sub] = mfma32x32x16(a, qf[st], sc[sub]);
-                dp[sub] = mfma32x32x16(vv, gf[st], dp[sub]);
+                sc = mfma32x32x16(a, qf[st], sc);
+                dp = mfma32x32x16(vv, gf[st], dp);
             }
-        }
-        // P and dS on legal (causal) entries; dS^T as the B operand of dQ^T
-        bf16x8 dsf[4];
-        const int jo = tcur * BK - off;          // key j0 relative to the row offset: j <= off + i
+            {
+                constexpr int NM = 2 * KSTEPS, PRE = NM < 6 ? NM : 6;
+                __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+                for (int n = 0; n < NM - PRE; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+            }
+            // dS^T as the B operand of dQ^T
+            bf16x8 dsf[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int j = jo + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const bool legal = valid && j <= i;
-                const float pr = legal ? fast_exp2(__builtin_fmaf(sc[sub][r], c2, -lse2)) : 0.f;
-                dsf[2 * sub + (r >> 3)][r & 7] = to_bf16(pr * (dp[sub][r] - dval));
+                const float pr = fast_exp2(__builtin_fmaf(sc[r], c2, -lse2));
+                dsf[r >> 3][r & 7] = to_bf16(pr * (dp[r] - dval));
             }
-        // dQ^T += K^T dS^T, K^T fragments (8 keys of one d per lane) by transposing reads
+            __builtin_amdgcn_sched_barrier(0);
+            if (!full) {
+                // a diagonal or ragged tile: dS of the pairs that the causal
+                // order or the sequence end rules out becomes 0
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+                for (int hf = 0; hf < 2; ++hf) {
+                    u32x4 dw = __builtin_bit_cast(u32x4, dsf[hf]);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                u32x2 half2x[2];
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        uint32_t m = 0;
 #pragma unroll
-                for (int rd = 0; rd < 2; ++rd) {
-                    const int krow = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
-                    const int col = 32 * dt + dsel;
-                    const int phys = ((col >> 3) ^ kswz<QCH>(krow)) * 8 + (col & 7);
-                    half2x[rd] = lds_read_tr16(kb + krow * D + phys);
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int r = 8 * hf + 2 * k2 + hh;
+                            const int j = jo + 32 * sub + 8 * (r >> 2) + 4 * hi + (r & 3);
+                            if (valid && j <= i) m |= 0xFFFFu << (16 * hh);
+                        }
+                        dw[k2] &= m;
+                    }
+                    dsf[hf] = __builtin_bit_cast(bf16x8, dw);
                 }
-                // whole-dword assembly of the operand
-                const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
-                acc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, w4), dsf[ks], acc[dt]);
             }
+            // dQ^T += K^T dS^T over this half's keys, K^T fragments (8 keys of
+            // one d per lane) by transposing reads
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) {
+                    const int ks = 2 * sub + kq;
+                    u32x2 half2x[2];
+#pragma unroll
+                    for (int rd = 0; rd < 2; ++rd) {
+                        const int krow = 16 * ks + 8 * rd + 4 * hi + (j16 >> 2);
+                        const int col = 32 * dt + dsel;
+                        const int phys = ((col >> 3) ^ kswz<QCH>(krow)) * 8 + (col & 7);
+                        half2x[rd] = lds_read_tr16(kb + krow * D + phys);
+                    }
+                    // whole-dword assembly of the operand
+                    const u32x4 w4 = {half2x[0][0], half2x[0][1], half2x[1][0], half2x[1][1]};
+                    acc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, w4), dsf[kq], acc[dt]);
+                }
+            {
+                constexpr int NM = 2 * DT, PRE = 4;
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * PRE, 0);
+#pragma unroll
+                for (int n = 0; n < NM - PRE; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         __syncthreads();                         // every wave is done with buffer `buf`
         const int tn2 = (tnext >= 0) ? next_tile() : -1;
         if (tn2 >= 0) fetch(tn2, buf);
