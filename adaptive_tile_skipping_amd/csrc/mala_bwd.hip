@@ -390,13 +390,19 @@ struct StepCursor {
 
 // LDS row swizzle for tiles read both row-wise (16-byte MFMA operand reads)
 // and transposed (ds_read_b64_tr_b16): 16-byte chunk c of row r lives at chunk
-// c ^ kswz(r).  kswz permutes 0..15 over 16 consecutive rows (row-wise reads
-// are conflict-free) and gives the four rows of a transposing read four
-// different chunk pairs (transposed reads are conflict-free too).  For d = 64
-// (8 chunks) only the second property holds.
+// c ^ kswz(r).  The LDS has 64 four-byte banks, one 256-byte row of a d = 128
+// tile.  A 16-byte read serves 16 lanes per pass: kswz permutes 0..15 over 16
+// consecutive rows, so those lanes (16 rows, one logical chunk) hit 16
+// different chunks.  An 8-byte transposing read serves 32 lanes per pass: four
+// consecutive rows, 64 bytes (four chunks) each; kswz puts each of the four
+// rows in a different group of four chunks (4 (r & 3) + ...), so the pass
+// covers all 64 banks once.  For d = 64 (8 chunks, two rows per bank line) the
+// earlier form is kept: the four rows of a transposing read get four
+// different chunk pairs.
 template <int QCH>
 __device__ __forceinline__ int kswz(int r) {
-    return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) % QCH;
+    if constexpr (QCH == 16) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1)) % QCH;
 }
 
 template <int D, int BQ, bool VARLEN, bool WIDE>
