@@ -216,6 +216,20 @@ def test_bwd_ragged_gqa(L, tau):
     run_bwd_case(inp, tau, 128, 64, label=f"ragged L={L}")
 
 
+@pytest.mark.parametrize("L", [900, 1000])
+def test_bwd_dense_two_tile_form_ragged(L):
+    """tau = 0 with enough (batch, KV head) x key-tile pairs for the two-key-tile
+    dK/dV form: B * Hkv * ceil(nKT / 2) reaches the device's CU count.  The
+    lengths end inside a query block and inside a key tile; L = 900 gives an odd
+    number of key tiles (the last workgroup holds one), L = 1000 an even one.
+    Diagonal and ragged steps take the masked path, the others the unmasked one."""
+    B, Hq, Hkv = 4, 16, 8
+    nKT = -(-L // 64)
+    assert B * Hkv * ((nKT + 1) // 2) >= torch.cuda.get_device_properties(0).multi_processor_count
+    inp = G.attn_inputs(870 + L, B, L, Hq, Hkv, 128, 0.1, diffuse_kv_heads=(2, 5))
+    run_bwd_case(inp, 0.0, 128, 64, label=f"two-tile dense L={L}")
+
+
 @pytest.mark.parametrize("L", [64, 200])
 @pytest.mark.parametrize("tau", [0.0, 1.0])
 def test_bwd_d64(L, tau):

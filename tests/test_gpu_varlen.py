@@ -364,17 +364,20 @@ def test_autograd_wrappers_match_direct_calls():
         assert torch.equal(a, b)
 
 
-def test_varlen_many_ragged_sequences_fwd_bwd():
+@pytest.mark.parametrize("tau", [1.0, 0.0])
+def test_varlen_many_ragged_sequences_fwd_bwd(tau):
     """40 sequences of random lengths (empty chunks, single tokens, chunks onto
-    caches, fresh prompts) with 5 q heads per KV head."""
+    caches, fresh prompts) with 5 q heads per KV head.  At tau = 0 the 40 x 2
+    (sequence, KV head) pairs x 4 key-tile pairs take the two-key-tile dK/dV
+    form, whose steps meet diagonals shifted by the cache offsets."""
     rng = np.random.default_rng(620)
     lk = rng.integers(0, 400, size=40)
     lq = np.array([rng.integers(0, k + 1) if rng.random() < 0.7 else k for k in lk])
     lq[3], lk[3] = 1, 1
     lq[5] = 0
     inp = G.varlen_inputs(620, lq, lk, 10, 2, 128, 0.1, diffuse_kv_heads=(1,))
-    print(run_varlen_case(inp, 1.0, 128, 64, label="40 ragged"))
-    print(run_bwd_varlen_case(inp, 1.0, 128, 64, label="40 ragged"))
+    print(run_varlen_case(inp, tau, 128, 64, label="40 ragged"))
+    print(run_bwd_varlen_case(inp, tau, 128, 64, label="40 ragged"))
 
 
 def test_varlen_larger_max_seqlen_changes_nothing():
