@@ -512,11 +512,6 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
     auto fetch = [&](int idx, int buf) {
         const int f_h = kh * G + idx / p.nQB, f_qb = idx % p.nQB;
         const int row0 = f_qb * BQ;
-        // row terms: waves 0..1 copy lse2 / D (BQ floats each)
-        if (w < 2 && lane * 4 < BQ) {
-            const float* src = (w == 0 ? p.rowc : p.rowd) + sv.row0 + f_h * sv.row_hs + row0;
-            load16_to_lds(src + 4 * lane, &sRow[buf][w][0]);
-        }
         // the blocks' rows through buffer resources ending at row L-1, so the
         // rows past L read as zero without per-lane clamps
         const int nrow = (L - row0 < BQ) ? L - row0 : BQ;
@@ -530,6 +525,12 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
         for (int n = 0; n < QINST; ++n) {
             buffer16_to_lds(rq, qoff[n], dq_ + (n * 4 + w) * 64 * 16);
             buffer16_to_lds(rg, goff[n], dg_ + (n * 4 + w) * 64 * 16);
+        }
+        // row terms: waves 0..1 copy lse2 / D (BQ floats each); last, so the
+        // resources above are not held across this lane-divergent branch
+        if (w < 2 && lane * 4 < BQ) {
+            const float* src = (w == 0 ? p.rowc : p.rowd) + sv.row0 + f_h * sv.row_hs + row0;
+            load16_to_lds(src + 4 * lane, &sRow[buf][w][0]);
         }
     };
     // every copy of the step fetched last may stay in flight
@@ -558,10 +559,13 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
 
     StepCursor cc;
     cc.init(dense, trow, p.nwT, qb_lo, qb_hi, p.nQB, G);
-    int cur = cc.next(lane), nxt = -1;
+    // The step index is the same in every lane; read as uniform, the copies'
+    // buffer resources stay scalar (no per-copy waterfall loop).
+    auto next_step = [&]() -> int { return __builtin_amdgcn_readfirstlane(cc.next(lane)); };
+    int cur = next_step(), nxt = -1;
     if (cur >= 0) {
         fetch(cur, 0);
-        nxt = cc.next(lane);
+        nxt = next_step();
         if (nxt >= 0) fetch(nxt, 1);
         wait_prev(nxt >= 0);
         __syncthreads();
@@ -688,7 +692,7 @@ __global__ __launch_bounds__(256) void mala_bwd_kernel(const BwdParams p) {
             }
         }
         __syncthreads();                         // every wave is done with buffer `buf`
-        const int n2 = (nxt >= 0) ? cc.next(lane) : -1;
+        const int n2 = (nxt >= 0) ? next_step() : -1;
         if (n2 >= 0) fetch(n2, buf);
         wait_prev(n2 >= 0);                      // the next step's blocks have landed
         __syncthreads();
