@@ -47,10 +47,11 @@ class MalaTileStats(ctypes.Structure):
 EXPORTS = ("mala_fwd", "mala_fwd_workspace_size", "mala_fwd_varlen", "mala_fwd_varlen_workspace_size",
            "mala_bwd", "mala_bwd_workspace_size", "mala_bwd_varlen", "mala_bwd_varlen_workspace_size",
            "mala_decode", "mala_decode_workspace_size", "mala_decode_varlen", "mala_decode_noalloc",
-           "mala_status_string", "mala_version")
+           "mala_probe_mfma", "mala_probe_mfma_flop", "mala_probe_read", "mala_status_string", "mala_version")
 
-# include/mala.h: MALA_DECODE_NOALLOC_MAX_BYTES
+# include/mala.h: MALA_DECODE_NOALLOC_MAX_BYTES, MALA_PROBE_SINK_WORDS
 DECODE_NOALLOC_MAX_BYTES = 64 << 20
+PROBE_SINK_WORDS = 256 * 1024
 
 _lib = None
 
@@ -94,6 +95,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.mala_decode_varlen.restype = I
     lib.mala_decode_noalloc.argtypes = [P, MalaT4, MalaT4, I, I, I, I, I, F, I, P, P, P, P, P]
     lib.mala_decode_noalloc.restype = I
+    lib.mala_probe_mfma.argtypes = [I, P, P]
+    lib.mala_probe_mfma.restype = I
+    lib.mala_probe_mfma_flop.argtypes = [I]
+    lib.mala_probe_mfma_flop.restype = ctypes.c_double
+    lib.mala_probe_read.argtypes = [P, S, P, P]
+    lib.mala_probe_read.restype = I
     lib.mala_status_string.argtypes = [I]
     lib.mala_status_string.restype = ctypes.c_char_p
     lib.mala_version.restype = ctypes.c_char_p
@@ -443,6 +450,29 @@ def mala_decode_noalloc(q, kcache, vcache, tau: float = 1.0, Bk_dec: int = 64, o
                                             _ptr(o), _ptr(lse), _ptr(kept_tiles), _ptr(decision_bits), _stream(q))
     _check("mala_decode_noalloc", rc)
     return o, lse, kept_tiles
+
+
+def probe_mfma(iters: int, sink: torch.Tensor) -> float:
+    """Enqueue the back-to-back bf16 MFMA probe (include/mala.h:
+    mala_probe_mfma) on the current stream; returns the launch's FLOP count."""
+    _dev_check(sink)
+    _expect(sink, (PROBE_SINK_WORDS,), torch.float32, "sink", sink.device, contiguous=True)
+    lib = load_library()
+    _check("mala_probe_mfma", lib.mala_probe_mfma(int(iters), _ptr(sink), _stream(sink)))
+    return float(lib.mala_probe_mfma_flop(int(iters)))
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor) -> int:
+    """Enqueue the streaming-read probe (include/mala.h: mala_probe_read) over
+    the bytes of a contiguous device tensor; returns the bytes read."""
+    _dev_check(src, sink)
+    if not src.is_contiguous():
+        raise ValueError("probe_read: src must be contiguous")
+    _expect(sink, (PROBE_SINK_WORDS,), torch.int32, "sink", src.device, contiguous=True)
+    nbytes = src.numel() * src.element_size()
+    lib = load_library()
+    _check("mala_probe_read", lib.mala_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(src)))
+    return nbytes
 
 
 class MalaAttention(torch.autograd.Function):

@@ -122,6 +122,48 @@ def recorded_traffic():
         return None
 
 
+def measure_sustained(mala, dev, kcache, flush, reps: int = 5):
+    """What the part sustains, from the library's two measurement probes
+    (include/mala.h: mala_probe_mfma, mala_probe_read): back-to-back bf16
+    MFMAs on register operands with no memory traffic, and a plain streaming
+    read of a 1 GiB buffer (four times the last-level cache), and the same
+    read of the decode's K cache alone after `flush()` (the bytes the decode's
+    score pass must read, in one launch of their own size).  Median of `reps`
+    timed launches after one untimed launch of each."""
+    import numpy as np
+    import torch
+    fsink = torch.empty(mala.PROBE_SINK_WORDS, dtype=torch.float32, device=dev)
+    isink = torch.empty(mala.PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    buf = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        work = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return work, e0.elapsed_time(e1)
+
+    iters = 150000                        # ~20 ms per launch at ~1.9 PFLOP/s
+    timed(lambda: mala.probe_mfma(iters, fsink))
+    mfma = [w / (ms * 1e-3) / 1e12 for w, ms in (timed(lambda: mala.probe_mfma(iters, fsink)) for _ in range(reps))]
+    timed(lambda: mala.probe_read(buf, isink))
+    rd = [w / (ms * 1e-3) / 1e9 for w, ms in (timed(lambda: mala.probe_read(buf, isink)) for _ in range(reps))]
+    del buf
+    kus = []
+    for _ in range(reps + 1):
+        flush()
+        kus.append(timed(lambda: mala.probe_read(kcache, isink))[1] * 1e3)
+    return {"mfma_bf16_tflops": round(float(np.median(mfma)), 1), "hbm_read_gbs": round(float(np.median(rd)), 1),
+            "read_kcache_us": round(float(np.median(kus[1:])), 2),
+            "read_kcache_gbs": round(kcache.numel() * kcache.element_size() / (float(np.median(kus[1:])) * 1e-6)
+                                     / 1e9, 1),
+            "note": "library probes, same process: back-to-back 32x32x16 bf16 MFMAs on register operands (two "
+                    "4-wave workgroups per CU, no memory traffic); a streaming read of 1 GiB (one 8-wave "
+                    "workgroup per CU, 16-byte loads), and of the decode's 268 MB K cache alone after a 512 MB "
+                    "flushing read; median of %d launches each" % reps}
+
+
 def legal_pairs_block(L, Bq, qb):
     r0, r1 = qb * Bq, min(L, qb * Bq + Bq)
     return sum(i + 1 for i in range(r0, r1))
@@ -832,6 +874,10 @@ def main():
     alg_dec = 2.0 * Dd * DN * DHq * DB + 2.0 * Dd * min(kept_dec * 64, DB * DHkv * DN) * G_dec
 
     value = (alg_fwd + alg_bwd + alg_dec) / (ms_step * 1e-3) / 1e12
+
+    # ---- what the part sustains, for reading the rates against (after the
+    # timed work, so the probes' load does not precede it)
+    sustained = measure_sustained(mala, dev, kc, lambda: torch.sum(flush, dim=0, out=sink))
     dense_step = (dense_fwd + dense_bwd + dense_dec) / (ms_step * 1e-3) / 1e12
 
     # ---- device memory per operator (the library allocates nothing itself:
@@ -858,7 +904,8 @@ def main():
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": recorded_traffic() if dom == "mala_fwd_kernel" else None,
-                "algorithmic_tflop_per_launch": round(dflop / 1e12, 3), "launch_ms": round(dms, 4)}
+                "algorithmic_tflop_per_launch": round(dflop / 1e12, 3), "launch_ms": round(dms, 4),
+                "frac_of_sustained": round(achieved / sustained["mfma_bf16_tflops"], 4)}
 
     out = {
         "metric": METRIC,
@@ -896,12 +943,17 @@ def main():
                  "decode_kept_tile_frac": round(kept_dec / (DB * DHkv * nT), 4)},
         "slots_per_query": {"fwd": round(slots_f / (B * Hq * L), 1), "bwd": round(slots_b / (B * Hq * L), 1)},
         "roofline": roofline,
+        "sustained": sustained,
+        "fwd_bwd_executed_tflops": round((exec_fwd + exec_bwd) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
+        "decode_frac_of_sustained_read": round(dec_bytes / (dec_us * 1e-6) / 1e9 / sustained["hbm_read_gbs"], 4),
         "memory": memory,
         "gen_s": round(t_gen, 1),
     }
     if res0 is not None:
         out["tau0"] = {k2: round(v2, 4) for k2, v2 in res0.items()}
         out["tau0"]["decode_hbm_gbs"] = round(dec_bytes0 / (res0["decode_us"] * 1e-6) / 1e9, 1)
+        out["tau0"]["decode_frac_of_sustained_read"] = round(
+            dec_bytes0 / (res0["decode_us"] * 1e-6) / 1e9 / sustained["hbm_read_gbs"], 4)
         out["speedup_vs_tau0"] = {"fwd": round(res0["fwd_ms"] / fwd_ms, 3), "bwd": round(res0["bwd_ms"] / bwd_ms, 3),
                                   "decode": round(res0["decode_us"] / dec_us, 3),
                                   "step": round(res0["ms_per_step"] / ms_step, 3)}

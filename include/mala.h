@@ -269,6 +269,35 @@ mala_status mala_decode_noalloc(const void* q, mala_t4 kcache, mala_t4 vcache, i
                                 int d, float tau, int Bk_dec, void* o, float* lse, int32_t* kept_tiles,
                                 uint32_t* decision_bits, void* stream);
 
+/* Measurement aids, for callers that read the attention kernels' rates
+ * against what this part sustains as well as against its published peaks.
+ * They compute nothing of the attention method.  Both enqueue one kernel on
+ * `stream` and return before it finishes; time them with events on that
+ * stream.
+ *
+ * Words of the sink buffer either probe may write. */
+#define MALA_PROBE_SINK_WORDS (256u * 1024u)
+
+/* Back-to-back 32x32x16 bf16 MFMAs on register operands, no memory traffic:
+ * a grid of two 4-wave workgroups per compute unit, each wave running
+ * `iters` rounds of four independent MFMAs.  mala_probe_mfma_flop(iters) is
+ * the launch's FLOP count (2*32*32*16 per MFMA).
+ *   sink: DEVICE memory of MALA_PROBE_SINK_WORDS floats (caller-owned);
+ *   one value per wave is written to it.
+ * MALA_ERR_INVALID_ARG for iters < 1 or a null sink (nothing enqueued);
+ * MALA_ERR_HIP if the launch fails. */
+mala_status mala_probe_mfma(int iters, float* sink, void* stream);
+double mala_probe_mfma_flop(int iters);
+
+/* A plain streaming read of `bytes` bytes at `src` (DEVICE memory, 16-byte
+ * aligned, bytes a positive multiple of 16): one 8-wave workgroup per
+ * compute unit, grid-stride 16-byte loads, eight in flight per lane.
+ *   sink: DEVICE memory of MALA_PROBE_SINK_WORDS uint32 (caller-owned); one
+ *   word per thread (the XOR of what it read) is written to it.
+ * MALA_ERR_INVALID_ARG for a null pointer, a misaligned src or a bad size
+ * (nothing enqueued); MALA_ERR_HIP if the launch fails. */
+mala_status mala_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static string naming a status code. */
 const char* mala_status_string(mala_status s);
 
