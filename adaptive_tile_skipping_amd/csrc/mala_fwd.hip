@@ -241,15 +241,24 @@ void mala_fwd_kernel(const FwdParams p) {
         // ending at key L-1, so rows past L read as zero (they are masked by
         // causality).  V: one resource over the padded fp16 copy, the tile offset
         // in a scalar (every access stays inside the copy).
-        uint32_t koff[INST], voff[INST];
+        // V: copy n covers V^T rows NW * 64 / (BK / 8) further down than copy 0
+        // with the same swizzle, so one lane offset serves every copy and the
+        // rest goes into the scalar offset.
+        uint32_t koff[INST];
     #pragma unroll
         for (int n = 0; n < INST; ++n) {
             const int sl = (n * NW + w) * 64 + lane;
             const int r = sl / QCH, pc = sl % QCH;
             koff[n] = (uint32_t)((r * p.k_sl + 8 * (pc ^ (r % QCH))) * 2);
-            const int dr = sl / (BK / 8), vc = sl % (BK / 8);
-            voff[n] = (uint32_t)((dr * BK + 8 * (vc ^ ((dr >> 1) & 7))) * 2);
         }
+        constexpr uint32_t VSTEP = (uint32_t)(NW * 64 / (BK / 8)) * BK * 2;   // bytes between copies
+        uint32_t voff;
+        {
+            const int sl = w * 64 + lane;
+            const int dr = sl / (BK / 8), vc = sl % (BK / 8);
+            voff = (uint32_t)((dr * BK + 8 * (vc ^ ((dr >> 1) & 7))) * 2);
+        }
+        static_assert((NW * 64) % ((BK / 8) * 16) == 0, "copy n keeps the V^T swizzle of copy 0");
         // The copies are issued from inline assembly (no compiler-inserted waits
         // before the reads of the other buffers); the wait before each barrier
         // covers them.
@@ -267,7 +276,7 @@ void mala_fwd_kernel(const FwdParams p) {
             const uint32_t so = (uint32_t)(kt * BK * D * 2);
     #pragma unroll
             for (int n = 0; n < INST; ++n)
-                buffer16_to_lds_asm(vrs, voff[n], so,
+                buffer16_to_lds_asm(vrs, voff, so + n * VSTEP,
                                     reinterpret_cast<unsigned char*>(sV[buf]) + (n * NW + w) * 64 * 16);
         };
         // S^T = K Q^T for the tile in sK[buf]; raw (unscaled) scores
@@ -355,9 +364,9 @@ void mala_fwd_kernel(const FwdParams p) {
         // One tile: decide tile kt from (m, l); then, in one straight-line block per
         // (keep, pending) case, issue the P.V MFMAs of the pending tile, then the
         // score MFMAs of tile kt-1 interleaved with the softmax of tile kt (whose P
-        // reuses the registers the P.V just consumed).  snext becomes the next
-        // tile's scur through a register copy at the end of the loop (a loop
-        // unrolled by two, with the roles swapped, does not fit in 256 VGPRs).
+        // reuses the registers the P.V just consumed).  The loop below runs two
+        // tiles per iteration with the two score buffers in swapped roles, so
+        // snext of one tile is scur of the next with no register copy.
         auto tile = [&](int kt, f32x16* scur, f32x16* snext) {
             const int buf = kt & 1;
             const float M = Mraw * c2;
@@ -489,11 +498,14 @@ void mala_fwd_kernel(const FwdParams p) {
             if (kt >= 1) Mraw = mask_max(kt - 1, snext);
         };
 
-        for (int kt = kt_first; kt >= 0; --kt) {
+        // Two tiles per iteration, the score buffers swapping roles (one V lane
+        // offset instead of one per copy leaves the registers this needs).
+        int kt = kt_first;
+        for (; kt >= 1; kt -= 2) {
             tile(kt, sA, sB);
-            sA[0] = sB[0];
-            sA[1] = sB[1];
+            tile(kt - 1, sB, sA);
         }
+        if (kt == 0) tile(0, sA, sB);
         if (pending) {
             wait_all_then_barrier();
             if (__ballot(pend_alpha != 1.f) != 0ull) {
