@@ -1263,18 +1263,22 @@ void mala_dec_dense(const DecParams p) {
     const uint16_t* kbase = p.k + b * p.k_sb + kh * p.k_sh + 8 * q4;
     const uint16_t* vbase = p.v + b * p.v_sb + kh * p.v_sh;
     uint16_t* vt = sV[w];
+    // B operand of the scores, kept in this wave's LDS slice (registers go to
+    // the K tiles): column i16 = q head of the group, d = 32 st + 8 q4 ..
+    // Loaded first and written to LDS once the first K tile's loads are out,
+    // so the kernel's first cache reads do not wait for it.
+    u32x4 qx[KS];
     {
-        // B operand of the scores, kept in this wave's LDS slice (registers go to
-        // the K tiles): column i16 = q head of the group, d = 32 st + 8 q4 ..
         const bool ok = i16 < G;
         const uint16_t* qrow = p.q + ((int64_t)b * p.Hq + kh * G + (ok ? i16 : 0)) * D;
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-            const u32x4 x = ok ? *(const u32x4*)(qrow + 32 * st + 8 * q4) : u32x4{0, 0, 0, 0};
-            *(u32x4*)(&sQ[w][(st * 64 + lane) * 8]) = x;
-        }
-        wave_lds_exchange();
+        for (int st = 0; st < KS; ++st) qx[st] = ok ? *(const u32x4*)(qrow + 32 * st + 8 * q4) : u32x4{0, 0, 0, 0};
     }
+    auto stage_q = [&]() {
+#pragma unroll
+        for (int st = 0; st < KS; ++st) *(u32x4*)(&sQ[w][(st * 64 + lane) * 8]) = qx[st];
+        wave_lds_exchange();
+    };
     auto qfrag = [&](int st) -> bf16x8 { return *(const bf16x8*)(&sQ[w][(st * 64 + lane) * 8]); };
     // A operand of the scores: row 16 blk + i16 of the tile, d = 32 st + 8 q4 ..
     auto load_k = [&](int t, bf16x8 (&kf)[4][KS]) {
@@ -1381,6 +1385,7 @@ void mala_dec_dense(const DecParams p) {
     if (t0 < t1) {
         bf16x8 ka[4][KS], kb[4][KS];
         load_k(t0, ka);
+        stage_q();
         for (int t = t0; t < t1; t += 2) {
             stage_v(t);
             const bool m1 = t + 1 < t1;
